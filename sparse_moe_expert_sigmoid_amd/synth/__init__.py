@@ -1,0 +1,286 @@
+"""Seeded synthetic inputs for the routed-MoE layer (host side).
+
+This module draws numbers only; it holds none of the layer's arithmetic.
+The tests feed the same arrays to the CPU oracle and to the HIP path, and the
+benchmark uses them as its workload.  The generator itself is the C file
+beside this one (counter-based SplitMix64, documented there).
+
+The layer shapes and value distributions follow the workloads of the two
+models the pages convert:
+
+* Kimi-Linear-48B-A3B (DETAILS.md of the LiteRT-LM conversion, "Conversion
+  notes", bullet on the mixture of experts): 256 routed experts, top 8,
+  sigmoid scores with a selection bias, weights renormalised and scaled by
+  2.446, int8 experts with one scale per output row and expert; the APEX-GGUF
+  model card ("Method") gives the expert intermediate size 2048.
+* Qwen3-30B-A3B (litert-community model card, "Available Artifacts" and
+  "Conversion Notes"): 128 experts, top 8, softmax router renormalised over
+  the 8, int4 experts in blocks of 32 with fp32 scales raised to 2^-14.
+
+The hidden sizes (2304, 2048), the Qwen3 intermediate size (768) and all
+value distributions are not on the pages; they are this workload's synthetic
+choices (stated in the layer specs below).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the generator with gcc (always recompiles)."""
+    import subprocess
+    src = os.path.join(_HERE, "synth.c")
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
+           "-fPIC", "-std=c11", "-Wall", "-o", tmp, src, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    u64, i64, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
+    lib.synth_key.argtypes = [u64, u64]
+    lib.synth_key.restype = u64
+    lib.synth_hash.argtypes = [u64, u64, u64, i64, vp]
+    lib.synth_splitmix64.argtypes = [u64, i64, vp]
+    lib.synth_uniform.argtypes = [u64, u64, i64, ctypes.c_float, ctypes.c_float, vp]
+    lib.synth_normal.argtypes = [u64, u64, i64, ctypes.c_double, vp]
+    lib.synth_randint8.argtypes = [u64, u64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.synth_scale.argtypes = [u64, u64, i64, ctypes.c_float, u64, vp, ctypes.c_int,
+                                ctypes.c_float, vp]
+    lib.synth_pack_int4.argtypes = [vp, i64, vp]
+    for f in ("synth_splitmix64", "synth_hash", "synth_uniform", "synth_normal", "synth_randint8",
+              "synth_scale", "synth_pack_int4"):
+        getattr(lib, f).restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+# --------------------------------------------------------------------------
+# primitive draws
+# --------------------------------------------------------------------------
+
+def splitmix64(state: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint64)
+    _load().synth_splitmix64(state, n, _ptr(out))
+    return out
+
+
+def hashes(seed: int, tid: int, n: int, start: int = 0) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint64)
+    _load().synth_hash(seed, tid, start, n, _ptr(out))
+    return out
+
+
+def uniform(seed: int, tid: int, shape, lo: float, hi: float) -> np.ndarray:
+    out = np.empty(shape, dtype=np.float32)
+    _load().synth_uniform(seed, tid, out.size, lo, hi, _ptr(out))
+    return out
+
+
+def normal(seed: int, tid: int, shape, std: float) -> np.ndarray:
+    out = np.empty(shape, dtype=np.float32)
+    _load().synth_normal(seed, tid, out.size, float(std), _ptr(out))
+    return out
+
+
+def randint8(seed: int, tid: int, shape, lo: int, hi: int) -> np.ndarray:
+    out = np.empty(shape, dtype=np.int8)
+    _load().synth_randint8(seed, tid, out.size, lo, hi, _ptr(out))
+    return out
+
+
+# int4 scale values that exercise the 2^-14 clamp: zero, an fp32 subnormal,
+# 2^-20 and just below 2^-14; about 1 in 1024 blocks draws one of them and
+# about 1 in 1024 others sits exactly at 2^-14.
+CLAMP_SPECIALS = np.array([0.0, 1e-40, 2.0 ** -20, 0.999 * 2.0 ** -14], dtype=np.float32)
+TWO_M14 = np.float32(2.0 ** -14)
+
+
+def scales(seed: int, tid: int, shape, c: float, special_tid: int = 0) -> np.ndarray:
+    out = np.empty(shape, dtype=np.float32)
+    sp = CLAMP_SPECIALS
+    _load().synth_scale(seed, tid, out.size, float(np.float32(c)), special_tid, _ptr(sp),
+                        len(sp), float(TWO_M14), _ptr(out))
+    return out
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Two int4 codes per byte along the last axis (element 2i in the low nibble)."""
+    assert codes.dtype == np.int8 and codes.shape[-1] % 2 == 0
+    codes = np.ascontiguousarray(codes)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] // 2,), dtype=np.uint8)
+    _load().synth_pack_int4(_ptr(codes), out.size, _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# layer specs
+# --------------------------------------------------------------------------
+
+ROUTER_SIGMOID_BIAS = "sigmoid_bias"
+ROUTER_SOFTMAX = "softmax"
+FMT_FP32 = "fp32"
+FMT_INT8_ROW = "int8_row"
+FMT_INT4_B32 = "int4_b32"
+
+KIMI_ROUTED_SCALE = float(np.float32(2.446))
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    name: str
+    T: int
+    d: int
+    E: int
+    k: int
+    inter: int
+    router: str
+    scale: float
+    fmt: str
+    shared: Optional[str]        # None, FMT_FP32 or FMT_INT8_ROW
+    shared_inter: int
+    wseed: int                   # weights (router, bias, experts, shared)
+    xseed: int                   # activations
+
+    @property
+    def R(self) -> int:          # routed rows: every token picks k experts
+        return self.T * self.k
+
+
+def _seed(i: int) -> int:
+    return 0x4D6F4500 + i
+
+
+SPECS = {
+    # Tiny single layer: T=32, d=512, 32 experts, top 8, I=256, fp32 shared.
+    "tiny": LayerSpec("tiny", 32, 512, 32, 8, 256, ROUTER_SIGMOID_BIAS, KIMI_ROUTED_SCALE,
+                      FMT_INT8_ROW, FMT_FP32, 256, _seed(0), _seed(0)),
+    # Kimi-shaped decode step: T=8, d=2304, 256 experts, top 8, I=2048, int8 shared.
+    "kimi_decode": LayerSpec("kimi_decode", 8, 2304, 256, 8, 2048, ROUTER_SIGMOID_BIAS,
+                             KIMI_ROUTED_SCALE, FMT_INT8_ROW, FMT_INT8_ROW, 2048,
+                             _seed(1), _seed(1)),
+    # The same layer at prefill, T=1024 (same weights, new activations).
+    "kimi_prefill": LayerSpec("kimi_prefill", 1024, 2304, 256, 8, 2048, ROUTER_SIGMOID_BIAS,
+                              KIMI_ROUTED_SCALE, FMT_INT8_ROW, FMT_INT8_ROW, 2048,
+                              _seed(1), _seed(2)),
+    # Qwen3-shaped layer: d=2048, 128 experts, softmax top 8, I=768, int4 b32, no shared.
+    "qwen_decode": LayerSpec("qwen_decode", 1, 2048, 128, 8, 768, ROUTER_SOFTMAX, 1.0,
+                             FMT_INT4_B32, None, 0, _seed(3), _seed(3)),
+    "qwen_prefill": LayerSpec("qwen_prefill", 128, 2048, 128, 8, 768, ROUTER_SOFTMAX, 1.0,
+                              FMT_INT4_B32, None, 0, _seed(3), _seed(13)),
+}
+
+
+def spec(name: str, **kw) -> LayerSpec:
+    s = SPECS[name]
+    return replace(s, **kw) if kw else s
+
+
+# tensor ids inside one seed
+TID_X, TID_WR, TID_BIAS = 1, 2, 3
+TID_GU, TID_GU_S, TID_DN, TID_DN_S = 4, 5, 6, 7
+TID_SH_GU, TID_SH_GU_S, TID_SH_DN, TID_SH_DN_S = 8, 9, 10, 11
+TID_GU_SPECIAL, TID_DN_SPECIAL, TID_SH_GU_SPECIAL, TID_SH_DN_SPECIAL = 12, 13, 14, 15
+
+
+@dataclass
+class ExpertWeights:
+    """Weights of a set of SwiGLU experts in one storage format.
+
+    fmt == int8_row: gu [E, 2I, d] int8, gu_s [E, 2I] fp32, dn [E, d, I] int8, dn_s [E, d]
+    fmt == int4_b32: gu [E, 2I, d] int8 codes in [-8, 7], gu_s [E, 2I, d/32]
+                     dn [E, d, I] int8 codes,               dn_s [E, d, I/32]
+                     (gu_packed / dn_packed hold the nibble-packed copies)
+    fmt == fp32:     gu [E, 2I, d] fp32, dn [E, d, I] fp32, no scales
+    Rows 0..I-1 of gu are the gate projection, rows I..2I-1 the up projection.
+    """
+    fmt: str
+    E: int
+    d: int
+    inter: int
+    gu: np.ndarray
+    dn: np.ndarray
+    gu_s: Optional[np.ndarray] = None
+    dn_s: Optional[np.ndarray] = None
+    gu_packed: Optional[np.ndarray] = None
+    dn_packed: Optional[np.ndarray] = None
+
+
+@dataclass
+class LayerInputs:
+    spec: LayerSpec
+    x: np.ndarray
+    wr: np.ndarray
+    bias: Optional[np.ndarray]
+    experts: ExpertWeights
+    shared: Optional[ExpertWeights] = None
+    extra: dict = field(default_factory=dict)
+
+
+def make_experts(fmt: str, E: int, d: int, inter: int, seed: int, tids) -> ExpertWeights:
+    t_gu, t_gu_s, t_dn, t_dn_s, t_gu_sp, t_dn_sp = tids
+    if fmt == FMT_FP32:
+        gu = normal(seed, t_gu, (E, 2 * inter, d), 1.0 / math.sqrt(d))
+        dn = normal(seed, t_dn, (E, d, inter), 1.0 / math.sqrt(inter))
+        return ExpertWeights(fmt, E, d, inter, gu, dn)
+    if fmt == FMT_INT8_ROW:
+        gu = randint8(seed, t_gu, (E, 2 * inter, d), -127, 127)
+        dn = randint8(seed, t_dn, (E, d, inter), -127, 127)
+        gu_s = scales(seed, t_gu_s, (E, 2 * inter), 1.0 / (127.0 * math.sqrt(d)))
+        dn_s = scales(seed, t_dn_s, (E, d), 1.0 / (127.0 * math.sqrt(inter)))
+        return ExpertWeights(fmt, E, d, inter, gu, dn, gu_s, dn_s)
+    if fmt == FMT_INT4_B32:
+        assert d % 32 == 0 and inter % 32 == 0
+        gu = randint8(seed, t_gu, (E, 2 * inter, d), -8, 7)
+        dn = randint8(seed, t_dn, (E, d, inter), -8, 7)
+        gu_s = scales(seed, t_gu_s, (E, 2 * inter, d // 32), 1.0 / (8.0 * math.sqrt(d)),
+                      special_tid=t_gu_sp)
+        dn_s = scales(seed, t_dn_s, (E, d, inter // 32), 1.0 / (8.0 * math.sqrt(inter)),
+                      special_tid=t_dn_sp)
+        return ExpertWeights(fmt, E, d, inter, gu, dn, gu_s, dn_s,
+                             pack_int4(gu), pack_int4(dn))
+    raise ValueError(fmt)
+
+
+def make_x(s: LayerSpec, T: Optional[int] = None) -> np.ndarray:
+    return normal(s.xseed, TID_X, (s.T if T is None else T, s.d), 1.0)
+
+
+def make_layer(s: LayerSpec, with_x: bool = True) -> LayerInputs:
+    wr = normal(s.wseed, TID_WR, (s.E, s.d), 1.0 / math.sqrt(s.d))
+    bias = (uniform(s.wseed, TID_BIAS, (s.E,), -0.1, 0.1)
+            if s.router == ROUTER_SIGMOID_BIAS else None)
+    experts = make_experts(s.fmt, s.E, s.d, s.inter, s.wseed,
+                           (TID_GU, TID_GU_S, TID_DN, TID_DN_S, TID_GU_SPECIAL, TID_DN_SPECIAL))
+    shared = None
+    if s.shared is not None:
+        shared = make_experts(s.shared, 1, s.d, s.shared_inter, s.wseed,
+                              (TID_SH_GU, TID_SH_GU_S, TID_SH_DN, TID_SH_DN_S,
+                               TID_SH_GU_SPECIAL, TID_SH_DN_SPECIAL))
+    x = make_x(s) if with_x else None
+    return LayerInputs(s, x, wr, bias, experts, shared)
