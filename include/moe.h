@@ -1,0 +1,178 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) routed mixture-of-experts layer.
+ *
+ * The layer, per token x (fp32, length d):
+ *   1. router logits l = Wr x (Wr: E x d, fp32);
+ *   2. selection of k experts and their weights (moe_route);
+ *   3. grouping of the (token, slot) pairs by expert (moe_permute);
+ *   4. each selected expert's SwiGLU FFN, weights dequantised in-kernel
+ *      (moe_expert_ffn; the shared expert is one more call with one expert);
+ *   5. y = sum_j w_j * FFN_{e_j}(x) + shared(x) [+ residual] (moe_combine).
+ * Sources: the Kimi-Linear-48B-A3B-Instruct LiteRT-LM DETAILS.md ("Conversion
+ * notes": the mixture-of-experts and int8-quantization bullets; "Runtime": an
+ * unsupported activation is rejected at setup with a message) and the
+ * litert-community Qwen3-30B-A3B model card ("Available Artifacts": int4
+ * block-32 experts with fp32 scales, fp32 router; "Conversion Notes": the
+ * moe op computes only the routed experts, softmax/top-8/renormalisation,
+ * scales below 2^-14 raised to 2^-14, residual add outside the op).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns all
+ *    memory; the library allocates nothing on the call path.  Every device
+ *    pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *    and return without synchronising the host; data-dependent sizes (how
+ *    many rows each expert received) stay on the device.
+ *  - Errors are return codes; nothing aborts or throws across the ABI.  All
+ *    argument checks are host code and run before anything is enqueued; on
+ *    failure nothing is launched and moe_last_error() names the argument.
+ *  - T == 0 is a valid no-op.  A moe_ctx must not be used by two host
+ *    threads at once.  Work enqueued on one stream runs in order; calls that
+ *    share a workspace must not overlap on different streams.
+ *  - Results are deterministic: the same inputs give the same bits on every
+ *    run, and a token's router logits do not depend on T.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_INVALID = 1,      /* a bad argument (null, negative, misaligned, k > E ...)      */
+    MOE_E_UNSUPPORTED = 2,  /* valid but not implemented (other activation, odd sizes ...) */
+    MOE_E_DEVICE = 3,       /* a HIP runtime error; the message carries HIP's text          */
+    MOE_E_WORKSPACE = 4     /* workspace pointer NULL or smaller than moe_workspace_size   */
+} moe_status;
+
+typedef enum {
+    /* sigmoid scores s = 1/(1+exp(-l)); top k on s + bias; w = scale * s / sum(s)
+       (DETAILS.md, Conversion notes, mixture-of-experts bullet; scale 2.446) */
+    MOE_ROUTER_SIGMOID_BIAS = 0,
+    /* p = softmax(l) over all E; top k on p; w = scale * p / sum(p) (Qwen3 card,
+       Conversion Notes; scale 1) */
+    MOE_ROUTER_SOFTMAX = 1
+} moe_router;
+
+typedef enum {
+    MOE_W_FP32 = 0,      /* plain fp32 weights, no scales                              */
+    MOE_W_INT8_ROW = 1,  /* int8 codes, one fp32 scale per output row and expert:
+                            w = q * s[row] (DETAILS.md, quantization of the int8 file) */
+    MOE_W_INT4_B32 = 2   /* int4 codes in blocks of 32 along the input axis with fp32
+                            scales raised to 2^-14: w = q * max(s[row][i/32], 2^-14)
+                            (Qwen3 card, Available Artifacts and Conversion Notes).
+                            Two codes per byte, two's complement: input element 2i in
+                            the low nibble of byte i, element 2i+1 in the high nibble */
+} moe_wfmt;
+
+typedef enum {
+    MOE_ACT_SILU = 0     /* h = silu(gate x) * (up x), silu(z) = z / (1 + exp(-z)) */
+} moe_act;
+
+/* A set of SwiGLU experts.  [host] struct holding device pointers.
+ *   fmt        one of moe_wfmt
+ *   n_experts  E >= 1
+ *   d          model width; a multiple of 64
+ *   inter      expert intermediate width I; a multiple of 64
+ *   w_gate_up  [E][2I][d]: rows 0..I-1 are the gate projection, rows I..2I-1 the
+ *              up projection, input axis contiguous.  int8: int8_t; int4: uint8_t
+ *              with d/2 bytes per row; fp32: float
+ *   s_gate_up  int8: [E][2I]; int4: [E][2I][d/32]; fp32: NULL
+ *   w_down     [E][d][I] (int4: [E][d][I/2] bytes)
+ *   s_down     int8: [E][d]; int4: [E][d][I/32]; fp32: NULL                         */
+typedef struct {
+    int fmt;
+    int n_experts;
+    int d;
+    int inter;
+    const void* w_gate_up;
+    const float* s_gate_up;
+    const void* w_down;
+    const float* s_down;
+} moe_weights;
+
+/* Context on HIP device `device`; reads its properties once.  [host] *out. */
+moe_status moe_create(int device, moe_ctx** out);
+void moe_destroy(moe_ctx* ctx);
+
+/* Message for the last failed call on this context ("" if none).  The pointer
+   stays valid until the next call on the context.  With ctx == NULL, the
+   message of the last moe_create failure in this process. */
+const char* moe_last_error(const moe_ctx* ctx);
+const char* moe_status_string(moe_status status);
+
+/* Bytes of device workspace that moe_route and moe_expert_ffn need
+   for a layer of T tokens, top k of E experts, width d, intermediate width
+   `inter` and weight format `fmt` (the larger of the two calls; one buffer
+   may serve all of them in turn on one stream).  [host] *bytes.
+   For the shared expert (one expert over T rows) pass k = 1, E = 1. */
+moe_status moe_workspace_size(const moe_ctx* ctx, int T, int k, int E, int d, int inter,
+                              int fmt, size_t* bytes);
+
+/* Router (DETAILS.md, mixture-of-experts bullet; Qwen3 card, Conversion Notes).
+ *   x         [T][d] fp32 activations
+ *   w_router  [E][d] fp32
+ *   bias      [E] fp32 selection bias (sigmoid router; NULL = zero); must be NULL
+ *             for the softmax router
+ *   k         1 <= k <= min(E, 16); E <= 1024; d a multiple of 64
+ *   scale     multiplies the renormalised weights (2.446 for the Kimi-style
+ *             sigmoid router, 1 for softmax); finite
+ *   topk_idx  [T][k] int32 out: expert ids by descending selection key, ties to
+ *             the lower id
+ *   topk_w    [T][k] fp32 out: weights, same order
+ * The logits are fp32 sums in a fixed order per token; the selection keys are
+ * fp32. */
+moe_status moe_route(moe_ctx* ctx, int router, const float* x, const float* w_router,
+                     const float* bias, int T, int d, int E, int k, float scale,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Group the T*k (token, slot) pairs by expert (Qwen3 card, Conversion Notes:
+ * only the routed experts are computed for each token).  Stable: within an
+ * expert, rows follow (t, j) order.
+ *   topk_idx   [T][k] int32 in [0, E) (entries outside are given no row and
+ *              their token_row is -1)
+ *   offsets    [E+1] out: rows of expert e are offsets[e] .. offsets[e+1]-1
+ *   row_token  [T*k] out: token of each row
+ *   token_row  [T*k] out: row of pair (t, j) at index t*k + j                     */
+moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
+                       int32_t* offsets, int32_t* row_token, int32_t* token_row, void* stream);
+
+/* Expert SwiGLU FFNs over grouped rows (DETAILS.md, mixture-of-experts bullet:
+ * the routed experts with SiLU; Qwen3 card, Accuracy: activation 'silu').
+ *   rows_out[r] = W_down[e] (silu(W_gate[e] x[row_token[r]]) * W_up[e] x[row_token[r]])
+ * for every row r of every expert e, with weights dequantised in-kernel.
+ *   act        MOE_ACT_SILU; anything else returns MOE_E_UNSUPPORTED with a message
+ *   x          [T][d] fp32
+ *   row_token  [R] or NULL (row r reads token r)
+ *   offsets    [E+1] device, as written by moe_permute; NULL only when E == 1,
+ *              meaning one expert over rows 0 .. R_max-1
+ *   R_max      number of rows the caller sized rows_out for (T*k for routed
+ *              experts, T for the shared expert); offsets[E] must not exceed it
+ *   rows_out   [R_max][d] fp32 out (rows beyond offsets[E] are not written)    */
+moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const float* x, int T,
+                          const int32_t* row_token, const int32_t* offsets, int R_max,
+                          float* rows_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (DETAILS.md, mixture-of-experts bullet: routed experts and
+ * the shared expert; Qwen3 card, Conversion Notes: the residual add sits after
+ * the moe op).
+ *   y[t] = sum_{j<k} topk_w[t][j] * rows[token_row[t*k+j]]  (slot order)
+ *          + shared[t] (if not NULL) + residual[t] (if not NULL)
+ *   rows [R][d], token_row [T*k], topk_w [T][k], shared/residual/y [T][d] fp32.
+ *   y may alias residual.                                                          */
+moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row,
+                       const float* topk_w, const float* shared, const float* residual,
+                       int T, int k, int d, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,189 @@
+"""ctypes binding over libmoe_mi355x.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Functions carry the C names (moe_route, moe_permute, moe_expert_ffn,
+moe_combine, ...) and take torch tensors on the GPU (their data pointers are
+passed through) plus plain integers.  If the library is missing this module
+raises at import of the context; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = range(5)
+MOE_ROUTER_SIGMOID_BIAS, MOE_ROUTER_SOFTMAX = 0, 1
+MOE_W_FP32, MOE_W_INT8_ROW, MOE_W_INT4_B32 = 0, 1, 2
+MOE_ACT_SILU = 0
+
+ROUTER = {"sigmoid_bias": MOE_ROUTER_SIGMOID_BIAS, "softmax": MOE_ROUTER_SOFTMAX}
+FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B32}
+
+EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
+           "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("n_experts", ctypes.c_int), ("d", ctypes.c_int),
+                ("inter", ctypes.c_int), ("w_gate_up", ctypes.c_void_p),
+                ("s_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m sparse_moe_expert_sigmoid_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moe_create.argtypes = [ci, ctypes.POINTER(vp)]
+    lib.moe_destroy.argtypes = [vp]
+    lib.moe_destroy.restype = None
+    lib.moe_last_error.argtypes = [vp]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ci]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_workspace_size.argtypes = [vp, ci, ci, ci, ci, ci, ci, ctypes.POINTER(sz)]
+    lib.moe_route.argtypes = [vp, ci, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, vp, vp, vp, sz,
+                              vp]
+    lib.moe_permute.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp]
+    lib.moe_expert_ffn.argtypes = [vp, ctypes.POINTER(moe_weights), ci, vp, ci, vp, vp, ci, vp,
+                                   vp, sz, vp]
+    lib.moe_combine.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, vp, vp]
+    for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
+              "moe_combine"):
+        getattr(lib, f).restype = ci
+    _lib = lib
+    return lib
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+class Context:
+    """A moe_ctx on one device."""
+
+    def __init__(self, device: int = 0):
+        self.lib = load_library()
+        h = ctypes.c_void_p()
+        st = self.lib.moe_create(device, ctypes.byref(h))
+        if st != MOE_OK:
+            raise MoeError(st, self.lib.moe_last_error(None).decode())
+        self.handle = h
+        self.device = device
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st: int):
+        if st != MOE_OK:
+            raise MoeError(st, self.lib.moe_last_error(self.handle).decode())
+
+    # ---- the C calls, same names ----
+    def moe_workspace_size(self, T, k, E, d, inter, fmt) -> int:
+        n = ctypes.c_size_t()
+        self._check(self.lib.moe_workspace_size(self.handle, T, k, E, d, inter, fmt,
+                                                ctypes.byref(n)))
+        return n.value
+
+    def moe_route(self, router, x, w_router, bias, T, d, E, k, scale, topk_idx, topk_w, ws,
+                  stream=None, ws_bytes=None):
+        self._check(self.lib.moe_route(
+            self.handle, router, _p(x), _p(w_router), _p(bias), T, d, E, k, scale, _p(topk_idx),
+            _p(topk_w), _p(ws), ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
+            _stream(stream)))
+
+    def moe_permute(self, topk_idx, T, k, E, offsets, row_token, token_row, stream=None):
+        self._check(self.lib.moe_permute(self.handle, _p(topk_idx), T, k, E, _p(offsets),
+                                         _p(row_token), _p(token_row), _stream(stream)))
+
+    def moe_expert_ffn(self, weights: "DeviceExperts", act, x, T, row_token, offsets, R_max,
+                       rows_out, ws, stream=None, ws_bytes=None):
+        w = weights.struct()
+        self._check(self.lib.moe_expert_ffn(
+            self.handle, ctypes.byref(w), act, _p(x), T, _p(row_token), _p(offsets), R_max,
+            _p(rows_out), _p(ws),
+            ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes, _stream(stream)))
+
+    def moe_combine(self, rows, token_row, topk_w, shared, residual, T, k, d, y, stream=None):
+        self._check(self.lib.moe_combine(self.handle, _p(rows), _p(token_row), _p(topk_w),
+                                         _p(shared), _p(residual), T, k, d, _p(y),
+                                         _stream(stream)))
+
+
+@dataclass
+class DeviceExperts:
+    """Expert weights resident on the GPU in one of the moe_wfmt formats."""
+    fmt: int
+    n_experts: int
+    d: int
+    inter: int
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    s_gate_up: Optional[torch.Tensor] = None
+    s_down: Optional[torch.Tensor] = None
+
+    def struct(self) -> moe_weights:
+        return moe_weights(self.fmt, self.n_experts, self.d, self.inter, _p(self.w_gate_up),
+                           _p(self.s_gate_up), _p(self.w_down), _p(self.s_down))
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.w_gate_up, self.w_down, self.s_gate_up, self.s_down)
+                   if t is not None)
+
+    @staticmethod
+    def upload(w, device) -> "DeviceExperts":
+        """From a synth.ExpertWeights (host numpy)."""
+        fmt = FMT[w.fmt]
+        if w.fmt == "int4_b32":
+            gu, dn = w.gu_packed, w.dn_packed
+        else:
+            gu, dn = w.gu, w.dn
+        t = lambda a: None if a is None else torch.from_numpy(a).to(device)
+        return DeviceExperts(fmt, w.E, w.d, w.inter, t(gu), t(dn), t(w.gu_s), t(w.dn_s))
+
+    def clone(self) -> "DeviceExperts":
+        c = lambda a: None if a is None else a.clone()
+        return DeviceExperts(self.fmt, self.n_experts, self.d, self.inter, c(self.w_gate_up),
+                             c(self.w_down), c(self.s_gate_up), c(self.s_down))

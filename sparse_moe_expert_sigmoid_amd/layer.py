@@ -1,0 +1,87 @@
+"""One routed-MoE layer on the GPU: the five calls of the C ABI in order.
+
+    y = combine(expert_ffn(permute(route(x))), shared_ffn(x)) [+ residual]
+
+(route -> permute -> routed expert FFN -> shared expert FFN -> combine).  This
+class only owns device buffers and issues the calls on one stream; all
+arithmetic is in the HIP library.  Buffers are allocated when the layer is
+built or when T changes, never inside forward() at a fixed T.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from .binding import (Context, DeviceExperts, MOE_ACT_SILU, ROUTER)
+
+
+class MoELayer:
+    def __init__(self, ctx: Context, router: str, k: int, scale: float, w_router: torch.Tensor,
+                 bias: Optional[torch.Tensor], experts: DeviceExperts,
+                 shared: Optional[DeviceExperts] = None):
+        self.ctx = ctx
+        self.router = ROUTER[router]
+        self.k, self.scale = k, float(scale)
+        self.w_router, self.bias = w_router, bias
+        self.experts, self.shared = experts, shared
+        self.E, self.d = experts.n_experts, experts.d
+        self.device = w_router.device
+        self._T = None
+
+    @staticmethod
+    def from_inputs(ctx: Context, inputs, device="cuda:0") -> "MoELayer":
+        """Upload a synth.LayerInputs."""
+        s = inputs.spec
+        wr = torch.from_numpy(inputs.wr).to(device)
+        bias = torch.from_numpy(inputs.bias).to(device) if inputs.bias is not None else None
+        ex = DeviceExperts.upload(inputs.experts, device)
+        sh = DeviceExperts.upload(inputs.shared, device) if inputs.shared is not None else None
+        return MoELayer(ctx, s.router, s.k, s.scale, wr, bias, ex, sh)
+
+    def with_weights(self, experts: DeviceExperts, shared: Optional[DeviceExperts]) -> "MoELayer":
+        """Same router, other expert weights (e.g. a copy in other HBM pages)."""
+        return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
+                        self.scale, self.w_router, self.bias, experts, shared)
+
+    def alloc(self, T: int):
+        if self._T == T:
+            return
+        dev, k, d, E = self.device, self.k, self.d, self.E
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        R = T * k
+        self.idx = torch.empty((T, k), **i32)
+        self.w = torch.empty((T, k), **f32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.row_token = torch.empty(R, **i32)
+        self.token_row = torch.empty(R, **i32)
+        self.rows = torch.empty((R, d), **f32)
+        self.sh_out = torch.empty((T, d), **f32) if self.shared is not None else None
+        self.y = torch.empty((T, d), **f32)
+        need = self.ctx.moe_workspace_size(T, k, E, d, self.experts.inter, self.experts.fmt)
+        if self.shared is not None:
+            need = max(need, self.ctx.moe_workspace_size(T, 1, 1, d, self.shared.inter,
+                                                         self.shared.fmt))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self._T = T
+
+    def forward(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None, stream=None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T, d = x.shape
+        self.alloc(T)
+        c, k, E = self.ctx, self.k, self.E
+        c.moe_route(self.router, x, self.w_router, self.bias, T, d, E, k, self.scale, self.idx,
+                    self.w, self.ws, stream)
+        c.moe_permute(self.idx, T, k, E, self.offsets, self.row_token, self.token_row, stream)
+        c.moe_expert_ffn(self.experts, MOE_ACT_SILU, x, T, self.row_token, self.offsets, T * k,
+                         self.rows, self.ws, stream)
+        if self.shared is not None:
+            c.moe_expert_ffn(self.shared, MOE_ACT_SILU, x, T, None, None, T, self.sh_out,
+                             self.ws, stream)
+        y = self.y if out is None else out
+        c.moe_combine(self.rows, self.token_row, self.w, self.sh_out, residual, T, k, d, y,
+                      stream)
+        return y
+
+    __call__ = forward

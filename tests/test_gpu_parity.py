@@ -1,0 +1,356 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every input comes from the seeded generator; both sides read the same
+arrays.  Shapes follow the layer workloads (tiny, Kimi-shaped decode and
+prefill, Qwen3-shaped int4 decode and prefill) plus edge cases: T = 0 and 1,
+ragged expert row counts, every token on the same experts (many tiles per
+expert), E = k, and int4 scales at, below and far below 2^-14.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_moe_expert_sigmoid_amd import synth as S
+from tests.parity import compare_outputs, compare_route, oracle_keys
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _log(**kw):
+    path = os.environ.get("MOE_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(kw) + "\n")
+    print(kw, flush=True)
+
+
+def inputs(name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _CACHE:
+        _CACHE[key] = S.make_layer(S.spec(name, **kw))
+    return _CACHE[key]
+
+
+@pytest.fixture(scope="module")
+def ctx(gpu):
+    from sparse_moe_expert_sigmoid_amd import Context
+    return Context(0)
+
+
+_LAYERS = {}
+
+
+def device_layer(ctx, name, **kw):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import MoELayer
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _LAYERS:
+        _LAYERS.clear()
+        torch.cuda.empty_cache()
+        _LAYERS[key] = MoELayer.from_inputs(ctx, inputs(name, **kw))
+    return _LAYERS[key]
+
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def run_route(ctx, L, x):
+    import torch
+    T = x.shape[0]
+    layer = L
+    layer.alloc(T)
+    xd = to_dev(x)
+    ctx.moe_route(layer.router, xd, layer.w_router, layer.bias, T, layer.d, layer.E, layer.k,
+                  layer.scale, layer.idx, layer.w, layer.ws)
+    torch.cuda.synchronize()
+    return layer.idx.cpu().numpy().copy(), layer.w.cpu().numpy().copy()
+
+
+# ------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_decode", "kimi_prefill", "qwen_decode",
+                                  "qwen_prefill"])
+def test_route_parity(ctx, name):
+    inp = inputs(name)
+    s = inp.spec
+    L = device_layer(ctx, name)
+    print(f"[route] {name} T={s.T} E={s.E} d={s.d}", flush=True)
+    gidx, gw = run_route(ctx, L, inp.x)
+    oidx, ow, ogap, logits = oracle.route(s.router, inp.x, inp.wr, inp.bias, s.k, s.scale,
+                                          want_logits=True)
+    keys = oracle_keys(s.router, logits, inp.bias)
+    exc = compare_route(gidx, gw, oidx, ow, ogap, keys, s.scale)
+    _log(test="route", config=name, T=s.T, excused=len(exc),
+         near_ties=int((ogap < 1e-6).sum()))
+
+
+def test_route_batch_invariance(ctx):
+    inp = inputs("kimi_prefill")
+    L = device_layer(ctx, "kimi_prefill")
+    idx_full, w_full = run_route(ctx, L, inp.x)
+    for c in range(4):
+        idx_c, w_c = run_route(ctx, L, inp.x[256 * c: 256 * (c + 1)])
+        assert np.array_equal(idx_c, idx_full[256 * c: 256 * (c + 1)])
+        assert np.array_equal(w_c, w_full[256 * c: 256 * (c + 1)])
+    for t in (0, 5, 1023):
+        idx_1, w_1 = run_route(ctx, L, inp.x[t:t + 1])
+        assert np.array_equal(idx_1[0], idx_full[t]) and np.array_equal(w_1[0], w_full[t])
+
+
+# ------------------------------------------------------------------ permute
+
+def _check_permute(ctx, idx, E):
+    import torch
+    T, k = idx.shape
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda:0")
+    row_token = torch.empty(T * k, dtype=torch.int32, device="cuda:0")
+    token_row = torch.empty(T * k, dtype=torch.int32, device="cuda:0")
+    ctx.moe_permute(to_dev(idx.astype(np.int32)), T, k, E, offsets, row_token, token_row)
+    torch.cuda.synchronize()
+    oo, ort, otr = oracle.permute(idx, E)
+    assert np.array_equal(offsets.cpu().numpy(), oo)
+    assert np.array_equal(row_token.cpu().numpy(), ort)
+    assert np.array_equal(token_row.cpu().numpy(), otr)
+
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_decode", "kimi_prefill", "qwen_prefill"])
+def test_permute_parity(ctx, name):
+    inp = inputs(name)
+    s = inp.spec
+    idx, _, _ = oracle.route(s.router, inp.x, inp.wr, inp.bias, s.k, s.scale)
+    _check_permute(ctx, idx, s.E)
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 256), (37, 8, 32), (4096, 8, 256), (300, 16, 1024),
+                                   (5, 3, 3), (70, 1, 7)])
+def test_permute_synthetic(ctx, T, k, E):
+    # distinct experts per token drawn from the generator; includes skew
+    u = S.uniform(77, T, (T, E), 0, 1).astype(np.float64)
+    u[:, : min(E, 4)] += 0.5                       # four popular experts
+    idx = np.argsort(-u, axis=1, kind="stable")[:, :k].astype(np.int32)
+    _check_permute(ctx, idx, E)
+
+
+def test_permute_all_same_experts(ctx):
+    idx = np.tile(np.array([9, 3, 200, 17, 0, 255, 128, 64], np.int32), (500, 1))
+    _check_permute(ctx, idx, 256)
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def _ffn_case(ctx, experts_host, dev_experts, x, idx, E):
+    import torch
+    T = x.shape[0]
+    k = idx.shape[1]
+    offsets, row_token, token_row = oracle.permute(idx, E)
+    R = T * k
+    rows = torch.full((R, dev_experts.d), float("nan"), dtype=torch.float32, device="cuda:0")
+    need = ctx.moe_workspace_size(T, k, E, dev_experts.d, dev_experts.inter, dev_experts.fmt)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    ctx.moe_expert_ffn(dev_experts, 0, to_dev(x), T, to_dev(row_token), to_dev(offsets), R, rows,
+                       ws)
+    torch.cuda.synchronize()
+    g = rows.cpu().numpy()
+    o = oracle.expert_rows(oracle.Experts.of(experts_host), x, row_token, offsets)
+    return compare_outputs(g, o)
+
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_decode", "qwen_decode", "qwen_prefill"])
+def test_expert_ffn_parity(ctx, name):
+    inp = inputs(name)
+    s = inp.spec
+    L = device_layer(ctx, name)
+    idx, _, _ = oracle.route(s.router, inp.x, inp.wr, inp.bias, s.k, s.scale)
+    ratio = _ffn_case(ctx, inp.experts, L.experts, inp.x, idx, s.E)
+    _log(test="expert_ffn", config=name, fmt=s.fmt, err_over_max=ratio)
+
+
+def test_expert_ffn_kimi_prefill_sampled(ctx):
+    # full T=1024 routing on the GPU; oracle rows for the rows of 3 experts
+    import torch
+    inp = inputs("kimi_prefill")
+    s = inp.spec
+    L = device_layer(ctx, "kimi_prefill")
+    idx, _, _ = oracle.route(s.router, inp.x, inp.wr, inp.bias, s.k, s.scale)
+    offsets, row_token, token_row = oracle.permute(idx, s.E)
+    R = s.T * s.k
+    rows = torch.empty((R, s.d), dtype=torch.float32, device="cuda:0")
+    L.alloc(s.T)
+    ctx.moe_expert_ffn(L.experts, 0, to_dev(inp.x), s.T, to_dev(row_token), to_dev(offsets), R,
+                       rows, L.ws)
+    torch.cuda.synchronize()
+    g = rows.cpu().numpy()
+    counts = np.diff(offsets)
+    picks = [int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30))),
+             int(np.flatnonzero(counts > 0)[len(np.flatnonzero(counts > 0)) // 2])]
+    picks = sorted(set(picks))
+    sel = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in picks])
+    sub_off = np.zeros(s.E + 1, np.int32)
+    for e in picks:
+        sub_off[e + 1] = counts[e]
+    sub_off = np.cumsum(sub_off).astype(np.int32)
+    order = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in sorted(set(picks))])
+    o = oracle.expert_rows(oracle.Experts.of(inp.experts), inp.x, row_token[order], sub_off)
+    ratio = compare_outputs(g[order], o)
+    _log(test="expert_ffn_sampled", config="kimi_prefill", rows=int(sel.size),
+         err_over_max=ratio)
+
+
+def test_shared_expert_identity_rows(ctx):
+    import torch
+    inp = inputs("kimi_decode")
+    s = inp.spec
+    L = device_layer(ctx, "kimi_decode")
+    out = torch.empty((s.T, s.d), dtype=torch.float32, device="cuda:0")
+    L.alloc(s.T)
+    ctx.moe_expert_ffn(L.shared, 0, to_dev(inp.x), s.T, None, None, s.T, out, L.ws)
+    torch.cuda.synchronize()
+    o = oracle.expert_rows(oracle.Experts.of(inp.shared), inp.x, None,
+                           np.array([0, s.T], np.int32))
+    compare_outputs(out.cpu().numpy(), o)
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("T,k,d,with_shared,with_res", [(8, 8, 2304, True, False),
+                                                        (37, 8, 512, True, True),
+                                                        (5, 3, 64, False, True)])
+def test_combine_parity(ctx, T, k, d, with_shared, with_res):
+    import torch
+    R = T * k
+    rows = S.normal(5, 1, (R, d), 1.0)
+    perm = np.argsort(S.uniform(5, 2, (R,), 0, 1)).astype(np.int32)
+    w = S.uniform(5, 3, (T, k), 0, 1)
+    sh = S.normal(5, 4, (T, d), 1.0) if with_shared else None
+    res = S.normal(5, 6, (T, d), 1.0) if with_res else None
+    y = torch.empty((T, d), dtype=torch.float32, device="cuda:0")
+    ctx.moe_combine(to_dev(rows), to_dev(perm), to_dev(w), to_dev(sh) if sh is not None else None,
+                    to_dev(res) if res is not None else None, T, k, d, y)
+    torch.cuda.synchronize()
+    o = oracle.combine(rows, perm, w, sh, res)
+    assert np.allclose(y.cpu().numpy(), o, rtol=1e-6, atol=1e-6 * np.abs(o).max())
+
+
+# ------------------------------------------------------------------ whole layer
+
+def _layer_vs_oracle(ctx, name, tokens=None, **kw):
+    import torch
+    inp = inputs(name, **kw)
+    s = inp.spec
+    L = device_layer(ctx, name, **kw)
+    xd = to_dev(inp.x)
+    y = L(xd)
+    torch.cuda.synchronize()
+    gy = y.cpu().numpy()
+    gidx = L.idx.cpu().numpy()
+    gw = L.w.cpu().numpy()
+    oy, oidx, ow, ogap = oracle.layer_of(inp, tokens=tokens)
+    sel = np.arange(s.T) if tokens is None else np.asarray(tokens)
+    _, _, _, logits = oracle.route(s.router, inp.x[sel], inp.wr, inp.bias, s.k, s.scale,
+                                   want_logits=True)
+    keys = oracle_keys(s.router, logits, inp.bias)
+    exc = compare_route(gidx[sel], gw[sel], oidx, ow, ogap, keys, s.scale)
+    keep = np.setdiff1d(np.arange(len(sel)), exc)
+    ratio = compare_outputs(gy[sel], oy, keep)
+    _log(test="layer", config=name, T=s.T, E=s.E, checked_tokens=len(sel), excused=len(exc),
+         err_over_max=ratio)
+    return gy
+
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_decode", "qwen_decode", "qwen_prefill"])
+def test_layer_parity(ctx, name):
+    print(f"[layer] {name}", flush=True)
+    _layer_vs_oracle(ctx, name)
+
+
+def test_layer_parity_kimi_prefill_sampled(ctx):
+    tokens = np.unique(np.concatenate([np.arange(0, 1024, 41), [1, 2, 511, 1022, 1023]]))
+    _layer_vs_oracle(ctx, "kimi_prefill", tokens=tokens)
+
+
+def test_layer_ragged_tiny_T37(ctx):
+    _layer_vs_oracle(ctx, "tiny", T=37, xseed=0x4D6F4599)
+
+
+def test_layer_single_token(ctx):
+    _layer_vs_oracle(ctx, "tiny", T=1, xseed=0x4D6F4598)
+
+
+def test_layer_every_token_on_same_experts(ctx):
+    # bias +1 on 8 experts: they win for every token (64 rows each: 4 tiles per expert)
+    import torch
+    inp = inputs("tiny", T=64, xseed=0x4D6F4597)
+    forced = inp.bias.copy()
+    forced[[1, 4, 6, 10, 11, 20, 25, 31]] = 1.0
+    inp2 = S.LayerInputs(inp.spec, inp.x, inp.wr, forced, inp.experts, inp.shared)
+    from sparse_moe_expert_sigmoid_amd import MoELayer, Context
+    L = MoELayer.from_inputs(ctx, inp2)
+    y = L(to_dev(inp.x))
+    torch.cuda.synchronize()
+    oy, oidx, ow, ogap = oracle.layer_of(inp2)
+    assert np.array_equal(np.sort(L.idx.cpu().numpy(), 1), np.sort(oidx, 1))
+    compare_outputs(y.cpu().numpy(), oy)
+
+
+def test_layer_E_equals_k(ctx):
+    _layer_vs_oracle(ctx, "tiny", E=8, T=20, xseed=0x4D6F4596)
+
+
+def test_layer_zero_tokens_is_noop(ctx):
+    import torch
+    L = device_layer(ctx, "tiny")
+    x = torch.empty((0, 512), dtype=torch.float32, device="cuda:0")
+    y = L(x)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512)
+
+
+def test_int4_clamp_inputs_present():
+    inp = inputs("qwen_decode")
+    s = inp.experts.gu_s
+    assert np.count_nonzero(s < S.TWO_M14) > 0 and np.count_nonzero(s == S.TWO_M14) > 0
+
+
+def test_layer_determinism(ctx):
+    import torch
+    inp = inputs("kimi_decode")
+    L = device_layer(ctx, "kimi_decode")
+    xd = to_dev(inp.x)
+    a = L(xd).clone()
+    b = L(xd).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ errors through the ABI
+
+def test_abi_errors(ctx):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import binding as B
+    L = device_layer(ctx, "tiny")
+    L.alloc(4)
+    x = torch.zeros((4, 512), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(B.MoeError) as e:
+        ctx.moe_route(0, x, L.w_router, L.bias, 4, 512, 32, 33, 2.446, L.idx, L.w, L.ws)
+    assert e.value.status == B.MOE_E_INVALID and "k=33" in str(e.value)
+    with pytest.raises(B.MoeError) as e:
+        ctx.moe_route(1, x, L.w_router, L.bias, 4, 512, 32, 8, 1.0, L.idx, L.w, L.ws)
+    assert e.value.status == B.MOE_E_INVALID and "bias" in str(e.value)
+    with pytest.raises(B.MoeError) as e:
+        ctx.moe_route(0, x, L.w_router, L.bias, 4, 512, 32, 8, 2.446, L.idx, L.w, L.ws,
+                      ws_bytes=16)
+    assert e.value.status == B.MOE_E_WORKSPACE
+    with pytest.raises(B.MoeError) as e:
+        ctx.moe_expert_ffn(L.experts, 1, x, 4, L.row_token, L.offsets, 32, L.rows, L.ws)
+    assert e.value.status == B.MOE_E_UNSUPPORTED and "activation" in str(e.value)
+    with pytest.raises(B.MoeError) as e:
+        ctx.moe_combine(L.rows, L.token_row, L.w, None, None, 4, 8, 510, L.y)
+    assert e.value.status == B.MOE_E_UNSUPPORTED
