@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark: one routed-MoE layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi_decode]
+
+A step is the whole hot path over one batch: route -> permute -> routed expert
+FFN -> shared expert FFN -> combine, all through the C ABI.  Inputs and
+weights are resident in HBM before timing starts.  The default workload is
+the Kimi-shaped decode step (T=8 tokens, d=2304, 256 experts, top 8, I=2048,
+int8 per-row experts, int8 shared expert).
+
+Weight copies: the step alternates between `--copies` identical copies of the
+expert weights (and the shared expert) in separate HBM allocations, so no
+step finds its weights in the 256 MB last-level cache from the step before.
+
+Output: one JSON line (metric, value = tokens/s, ms_per_step, roofline of the
+dominant kernel measured with HIP events on its own stream in a second,
+separately timed pass, and the CPU oracle timed on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / TFLOP/s (prefill), % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
+
+WORKLOADS = {
+    # name: (layer spec, chunks, description)
+    "kimi_decode": ("kimi_decode", 1,
+                    "Kimi-shaped MoE layer decode step: T=8, d=2304, E=256, top-8, "
+                    "sigmoid+bias router x2.446, I=2048 SwiGLU, int8 per-row experts, "
+                    "int8 shared expert I=2048"),
+    "kimi_prefill": ("kimi_prefill", 1,
+                     "Kimi-shaped MoE layer prefill: T=1024, same layer as kimi_decode"),
+    "kimi_prefill_4x256": ("kimi_prefill", 4,
+                           "Kimi-shaped MoE layer prefill, T=1024 as 4 chunks of 256"),
+    "qwen_decode": ("qwen_decode", 1,
+                    "Qwen3-shaped MoE layer decode: T=1, d=2048, E=128, top-8 softmax, "
+                    "I=768 SwiGLU, int4 block-32 experts, no shared expert"),
+    "qwen_prefill": ("qwen_prefill", 1, "Qwen3-shaped MoE layer, T=128"),
+    "tiny": ("tiny", 1, "tiny MoE layer: T=32, d=512, E=32, top-8, I=256"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(ew, e_list):
+    """Codes + scales of the listed experts (host arrays), gate_up and down separately."""
+    if ew.fmt == "int4_b32":
+        gu = ew.gu_packed[0].nbytes + ew.gu_s[0].nbytes
+        dn = ew.dn_packed[0].nbytes + ew.dn_s[0].nbytes
+    elif ew.fmt == "int8_row":
+        gu = ew.gu[0].nbytes + ew.gu_s[0].nbytes
+        dn = ew.dn[0].nbytes + ew.dn_s[0].nbytes
+    else:
+        gu, dn = ew.gu[0].nbytes, ew.dn[0].nbytes
+    n = len(e_list)
+    return gu * n, dn * n
+
+
+def cpu_baseline(inputs, budget_s: float):
+    """The oracle, as it stands, on the same layer and tokens; bounded repeat count."""
+    import oracle
+    s = inputs.spec
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    T_sample = min(s.T, 8)
+    tokens = np.arange(T_sample)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.layer_of(inputs, tokens=tokens)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    return {"value": T_sample * reps / el, "unit": "tokens/s", "cores": min(threads, T_sample),
+            "kind": "oracle",
+            "sample": f"{reps} x oracle layer on tokens 0..{T_sample - 1} of this workload "
+                      f"(fp64 C, OpenMP over tokens), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="kimi_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=None)
+    ap.add_argument("--path", default="fused", choices=["fused", "staged"],
+                    help="fused: one moe_forward call per step; staged: moe_route, "
+                         "moe_permute, moe_expert_ffn (routed, shared), moe_combine")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X and "
+              "has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_moe_expert_sigmoid_amd import Context, MoELayer, synth as S
+    from sparse_moe_expert_sigmoid_amd.binding import DeviceExperts
+
+    spec_name, chunks, desc = WORKLOADS[args.workload]
+    spec = S.spec(spec_name)
+    decode = spec.T <= 16
+    steps = args.steps or (200 if decode else 40)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 5)
+
+    log(f"[bench] workload {args.workload}: generating inputs")
+    inputs = S.make_layer(spec)
+    dev = torch.device("cuda:0")
+    ctx = Context(0)
+    base = MoELayer.from_inputs(ctx, inputs, dev)
+    layer_bytes = base.experts.nbytes + (base.shared.nbytes if base.shared else 0)
+    # enough copies that one step's weights are never cache-resident from the last
+    copies = args.copies or max(2, min(32, math.ceil(2.0e9 / layer_bytes) + 1))
+    layers = [base]
+    for _ in range(copies - 1):
+        layers.append(base.with_weights(base.experts.clone(),
+                                        base.shared.clone() if base.shared else None))
+    x = torch.from_numpy(inputs.x).to(dev)
+    Tc = spec.T // chunks
+    xs = [x[i * Tc:(i + 1) * Tc].contiguous() for i in range(chunks)]
+    for L in layers:
+        L.alloc(Tc)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] {copies} weight copies of {layer_bytes / 1e9:.3f} GB; T={spec.T} "
+        f"({chunks} chunk(s)); warmup {warmup}, steps {steps}")
+
+    def step(i):
+        L = layers[i % copies]
+        for c in range(chunks):
+            if args.path == "fused":
+                L.forward_fused(xs[c], stream=stream)
+            else:
+                L.forward(xs[c], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / steps
+    tok_s = spec.T / (ms_per_step / 1e3)
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, {tok_s:,.0f} tokens/s (wall {wall:.3f} s)")
+
+    # ---- algorithmic work of one step, from the actual routing
+    idx = layers[0].idx.cpu().numpy() if chunks == 1 else None
+    if chunks > 1:
+        idx_all = []
+        for c in range(chunks):
+            layers[0].forward(xs[c], stream=stream)
+            torch.cuda.synchronize()
+            idx_all.append(layers[0].idx.cpu().numpy().copy())
+        touched_per_chunk = [np.unique(a) for a in idx_all]
+    else:
+        touched_per_chunk = [np.unique(idx)]
+    d, I, k, E = spec.d, spec.inter, spec.k, spec.E
+    gu_b = dn_b = 0
+    for t in touched_per_chunk:
+        a, b = expert_bytes(inputs.experts, t)
+        gu_b += a
+        dn_b += b
+    sh_gu = sh_dn = 0
+    if inputs.shared is not None:
+        sh_gu, sh_dn = expert_bytes(inputs.shared, [0])
+        sh_gu *= chunks
+        sh_dn *= chunks
+    act_bytes = spec.T * d * 4 * 2                      # x read once, y written once
+    router_bytes = (E * d + (E if inputs.bias is not None else 0)) * 4 * chunks
+    step_bytes = gu_b + dn_b + sh_gu + sh_dn + act_bytes + router_bytes
+    Is = spec.shared_inter if inputs.shared is not None else 0
+    step_flops = 2.0 * (spec.T * k * 3 * d * I + spec.T * 3 * d * Is + spec.T * d * E)
+    gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    tflops = step_flops / (ms_per_step / 1e3) / 1e12
+
+    # ---- second pass: per-kernel durations from HIP events on the launch stream
+    kernels = {}
+    roofline = None
+    if not args.no_kernel_timing:
+        ctx.moe_timing(64 * steps)
+        for i in range(steps):
+            step(warmup + i)
+        torch.cuda.synchronize()
+        kt = ctx.moe_timing_read()
+        ctx.moe_timing(0)
+        kernels = {n: {"launches": int(c), "avg_us": t / c * 1e3} for n, (c, t) in kt.items()}
+        dom = "ffn_i4_gate_up" if spec.fmt == "int4_b32" else "ffn_i8_gate_up"
+        if dom in kt:
+            launches, tot_ms = kt[dom]
+            # algorithmic bytes of the gate/up launches of one step: codes + scales of
+            # every touched expert (routed) or the shared expert, activation digits
+            # read once (2 bytes per input), h written once (fp32)
+            R = spec.T * k
+            # (x as 2-byte digits; h written as 2-byte digits + one fp32 scale per 64)
+            per_step = (gu_b + sh_gu + spec.T * d * 2
+                        + (R * I + spec.T * Is) * 2 + (R * I + spec.T * Is) // 64 * 4)
+            launches_per_step = launches / steps
+            bytes_per_launch = per_step / launches_per_step
+            avg_s = tot_ms / launches / 1e3
+            achieved = bytes_per_launch / avg_s / 1e9
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "bytes_per_launch": int(bytes_per_launch),
+                        "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(inputs, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if spec.fmt != "fp32" else "f32",
+        "data": "synthetic (seeded generator; random weights of the stated shapes)",
+        "config": {"workload": desc, "T": spec.T, "chunks": chunks, "d": d, "E": E, "k": k,
+                   "inter": I, "router": spec.router, "expert_format": spec.fmt,
+                   "shared_expert": spec.shared, "weight_copies": copies,
+                   "entry_point": "moe_forward" if args.path == "fused" else
+                   "moe_route+moe_permute+moe_expert_ffn x2+moe_combine",
+                   "parallelism": "single GPU"},
+        "hbm_gbps_algorithmic": round(gbs, 1),
+        "tflops_algorithmic": round(tflops, 3),
+        "step_bytes_algorithmic": int(step_bytes),
+        "step_flops_algorithmic": step_flops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

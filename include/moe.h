@@ -76,11 +76,26 @@ typedef enum {
     MOE_ACT_SILU = 0     /* h = silu(gate x) * (up x), silu(z) = z / (1 + exp(-z)) */
 } moe_act;
 
+/* Byte order of the int8/int4 codes in HBM (scales are always row-major).
+ * MOE_LAYOUT_ROWS:  [E][N][K] codes, input axis contiguous (int4: K/2 bytes per row).
+ * MOE_LAYOUT_TILED: the same bytes regrouped as matrix-core operands, so that a
+ *   wavefront streams whole 1 KB blocks: per expert, for each group of 16 rows
+ *   (n/16) and each 64-wide input step (int8; int4: each 128-wide span) one
+ *   1 KB block in lane order, lane = n%16 + 16*g.  int8: g = (k%64)/16, the lane
+ *   holds k%16 = 0..15.  int4: g = (k%32)/8, the lane holds 4 bytes per block of
+ *   32 (its 8 codes, two per byte, low nibble first) for the span's 4 blocks.
+ *   moe_tile_weights converts; it is the faster layout for every shape. */
+typedef enum {
+    MOE_LAYOUT_ROWS = 0,
+    MOE_LAYOUT_TILED = 1
+} moe_layout;
+
 /* A set of SwiGLU experts.  [host] struct holding device pointers.
  *   fmt        one of moe_wfmt
+ *   layout     one of moe_layout (MOE_LAYOUT_ROWS for fp32)
  *   n_experts  E >= 1
- *   d          model width; a multiple of 64
- *   inter      expert intermediate width I; a multiple of 64
+ *   d          model width; a multiple of 64 (int4: of 128)
+ *   inter      expert intermediate width I; a multiple of 64 (int4: of 128)
  *   w_gate_up  [E][2I][d]: rows 0..I-1 are the gate projection, rows I..2I-1 the
  *              up projection, input axis contiguous.  int8: int8_t; int4: uint8_t
  *              with d/2 bytes per row; fp32: float
@@ -89,6 +104,7 @@ typedef enum {
  *   s_down     int8: [E][d]; int4: [E][d][I/32]; fp32: NULL                         */
 typedef struct {
     int fmt;
+    int layout;
     int n_experts;
     int d;
     int inter;
@@ -97,6 +113,15 @@ typedef struct {
     const void* w_down;
     const float* s_down;
 } moe_weights;
+
+/* Copy row-major int8/int4 codes into MOE_LAYOUT_TILED order (a byte
+ * permutation; scales are not touched).  src: weights with layout
+ * MOE_LAYOUT_ROWS; dst_gate_up / dst_down: device buffers of the same byte
+ * sizes as src's codes, not overlapping them.  Enqueued on `stream`.  For a
+ * one-time conversion at load; the result is used with the same scales and
+ * layout = MOE_LAYOUT_TILED. */
+moe_status moe_tile_weights(moe_ctx* ctx, const moe_weights* src, void* dst_gate_up,
+                            void* dst_down, void* stream);
 
 /* Context on HIP device `device`; reads its properties once.  [host] *out. */
 moe_status moe_create(int device, moe_ctx** out);
@@ -171,6 +196,60 @@ moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const flo
 moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row,
                        const float* topk_w, const float* shared, const float* residual,
                        int T, int k, int d, float* y, void* stream);
+
+/* A whole layer for moe_forward.  [host] struct holding device pointers.
+ *   router, k, scale, w_router [E][d], bias [E] or NULL: as for moe_route
+ *   experts: the routed experts (E = experts.n_experts)
+ *   shared:  the shared expert (shared.n_experts == 1), or shared.n_experts == 0
+ *            for none; same d as the routed experts                              */
+typedef struct {
+    int router;
+    int k;
+    float scale;
+    const float* w_router;
+    const float* bias;
+    moe_weights experts;
+    moe_weights shared;
+} moe_layer;
+
+/* Workspace for moe_forward on T tokens.  [host] *bytes. */
+moe_status moe_layer_workspace_size(const moe_ctx* ctx, const moe_layer* layer, int T,
+                                    size_t* bytes);
+
+/* The whole layer in one call: the same result, bit for bit in the router
+ * outputs and to rounding in y, as moe_route, moe_permute, moe_expert_ffn on
+ * the routed experts, moe_expert_ffn on the shared expert and moe_combine in
+ * turn (DETAILS.md, mixture-of-experts bullet: routed experts weighted by the
+ * router, shared expert added; the residual is added after the moe op, Qwen3
+ * card, Conversion Notes).  Fewer launches: x is encoded once and, when the
+ * shared expert has the routed experts' format, its tiles run inside the
+ * routed experts' launches.
+ *   x [T][d], residual [T][d] or NULL, y [T][d] out (may alias residual)
+ *   topk_idx [T][k], topk_w [T][k]: outputs, or NULL to keep them internal
+ * Checks and errors as for the separate calls. */
+moe_status moe_forward(moe_ctx* ctx, const moe_layer* layer, int act, const float* x, int T,
+                       const float* residual, float* y, int32_t* topk_idx, float* topk_w,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing, a measurement aid for benchmarks; off by default.
+ * moe_timing(ctx, capacity > 0) creates 2*capacity HIP events (host-side
+ * allocation, outside any call path) and from then on brackets every kernel
+ * launch of the calls above with a pair of events recorded on that launch's
+ * stream; capacity = 0 switches it off and frees the events.  Event records
+ * add a little GPU time between kernels, so time plain runs separately.
+ * moe_timing_read synchronises on the recorded events and returns, per
+ * kernel that ran, the number of launches and their summed duration, then
+ * forgets them; out[] receives at most max_out entries and *n_out the number
+ * of kernels seen.  Launches beyond the capacity are not timed (the read
+ * still returns MOE_OK and moe_last_error() says how many were missed). */
+typedef struct {
+    const char* name;     /* static string, e.g. "ffn_i8_gate_up" */
+    long long launches;
+    double total_ms;
+} moe_kernel_time;
+
+moe_status moe_timing(moe_ctx* ctx, int capacity);
+moe_status moe_timing_read(moe_ctx* ctx, moe_kernel_time* out, int max_out, int* n_out);
 
 #ifdef __cplusplus
 }

@@ -22,12 +22,15 @@ MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = range(
 MOE_ROUTER_SIGMOID_BIAS, MOE_ROUTER_SOFTMAX = 0, 1
 MOE_W_FP32, MOE_W_INT8_ROW, MOE_W_INT4_B32 = 0, 1, 2
 MOE_ACT_SILU = 0
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 
 ROUTER = {"sigmoid_bias": MOE_ROUTER_SIGMOID_BIAS, "softmax": MOE_ROUTER_SOFTMAX}
 FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B32}
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
-           "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine")
+           "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+           "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
+           "moe_tile_weights")
 
 
 class MoeError(RuntimeError):
@@ -37,10 +40,22 @@ class MoeError(RuntimeError):
 
 
 class moe_weights(ctypes.Structure):
-    _fields_ = [("fmt", ctypes.c_int), ("n_experts", ctypes.c_int), ("d", ctypes.c_int),
+    _fields_ = [("fmt", ctypes.c_int), ("layout", ctypes.c_int), ("n_experts", ctypes.c_int),
+                ("d", ctypes.c_int),
                 ("inter", ctypes.c_int), ("w_gate_up", ctypes.c_void_p),
                 ("s_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("s_down", ctypes.c_void_p)]
+
+
+class moe_layer(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_int), ("k", ctypes.c_int), ("scale", ctypes.c_float),
+                ("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("experts", moe_weights), ("shared", moe_weights)]
+
+
+class moe_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_longlong),
+                ("total_ms", ctypes.c_double)]
 
 
 _lib = None
@@ -70,8 +85,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_expert_ffn.argtypes = [vp, ctypes.POINTER(moe_weights), ci, vp, ci, vp, vp, ci, vp,
                                    vp, sz, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, vp, vp]
+    lib.moe_layer_workspace_size.argtypes = [vp, ctypes.POINTER(moe_layer), ci,
+                                             ctypes.POINTER(sz)]
+    lib.moe_forward.argtypes = [vp, ctypes.POINTER(moe_layer), ci, vp, ci, vp, vp, vp, vp, vp, sz,
+                                vp]
+    lib.moe_tile_weights.argtypes = [vp, ctypes.POINTER(moe_weights), vp, vp, vp]
+    lib.moe_timing.argtypes = [vp, ci]
+    lib.moe_timing_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), ci,
+                                    ctypes.POINTER(ci)]
     for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
-              "moe_combine"):
+              "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
+              "moe_forward", "moe_tile_weights"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -144,6 +168,35 @@ class Context:
             _p(rows_out), _p(ws),
             ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes, _stream(stream)))
 
+    def moe_layer_workspace_size(self, layer: "moe_layer", T) -> int:
+        n = ctypes.c_size_t()
+        self._check(self.lib.moe_layer_workspace_size(self.handle, ctypes.byref(layer), T,
+                                                      ctypes.byref(n)))
+        return n.value
+
+    def moe_forward(self, layer: "moe_layer", act, x, T, residual, y, topk_idx, topk_w, ws,
+                    stream=None, ws_bytes=None):
+        self._check(self.lib.moe_forward(
+            self.handle, ctypes.byref(layer), act, _p(x), T, _p(residual), _p(y), _p(topk_idx),
+            _p(topk_w), _p(ws), ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
+            _stream(stream)))
+
+    def moe_tile_weights(self, src: "DeviceExperts", dst_gate_up, dst_down, stream=None):
+        w = src.struct()
+        self._check(self.lib.moe_tile_weights(self.handle, ctypes.byref(w), _p(dst_gate_up),
+                                              _p(dst_down), _stream(stream)))
+
+    def moe_timing(self, capacity: int):
+        self._check(self.lib.moe_timing(self.handle, capacity))
+
+    def moe_timing_read(self) -> dict:
+        """{kernel name: (launches, total ms)} since the last read."""
+        buf = (moe_kernel_time * 32)()
+        n = ctypes.c_int()
+        self._check(self.lib.moe_timing_read(self.handle, buf, 32, ctypes.byref(n)))
+        return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms)
+                for i in range(min(n.value, 32))}
+
     def moe_combine(self, rows, token_row, topk_w, shared, residual, T, k, d, y, stream=None):
         self._check(self.lib.moe_combine(self.handle, _p(rows), _p(token_row), _p(topk_w),
                                          _p(shared), _p(residual), T, k, d, _p(y),
@@ -161,10 +214,22 @@ class DeviceExperts:
     w_down: torch.Tensor
     s_gate_up: Optional[torch.Tensor] = None
     s_down: Optional[torch.Tensor] = None
+    layout: int = MOE_LAYOUT_ROWS
 
     def struct(self) -> moe_weights:
-        return moe_weights(self.fmt, self.n_experts, self.d, self.inter, _p(self.w_gate_up),
-                           _p(self.s_gate_up), _p(self.w_down), _p(self.s_down))
+        return moe_weights(self.fmt, self.layout, self.n_experts, self.d, self.inter,
+                           _p(self.w_gate_up), _p(self.s_gate_up), _p(self.w_down),
+                           _p(self.s_down))
+
+    def tiled(self, ctx: "Context") -> "DeviceExperts":
+        """A copy of the codes in MOE_LAYOUT_TILED order (scales shared)."""
+        if self.fmt == MOE_W_FP32 or self.layout == MOE_LAYOUT_TILED:
+            return self
+        gu = torch.empty_like(self.w_gate_up)
+        dn = torch.empty_like(self.w_down)
+        ctx.moe_tile_weights(self, gu, dn)
+        return DeviceExperts(self.fmt, self.n_experts, self.d, self.inter, gu, dn,
+                             self.s_gate_up, self.s_down, MOE_LAYOUT_TILED)
 
     @property
     def nbytes(self) -> int:
@@ -186,4 +251,4 @@ class DeviceExperts:
     def clone(self) -> "DeviceExperts":
         c = lambda a: None if a is None else a.clone()
         return DeviceExperts(self.fmt, self.n_experts, self.d, self.inter, c(self.w_gate_up),
-                             c(self.w_down), c(self.s_gate_up), c(self.s_down))
+                             c(self.w_down), c(self.s_gate_up), c(self.s_down), self.layout)

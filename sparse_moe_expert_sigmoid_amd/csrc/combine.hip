@@ -23,25 +23,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= (long long)T * d4) return;
   const int t = (int)(q / d4), c = (int)(q % d4);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int r = token_row[(size_t)t * k + j];
-    if (r < 0) continue;
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(rows + (size_t)r * d + 4 * c);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
-  }
   const size_t o = (size_t)t * d + 4 * c;
+  // all loads are issued before any arithmetic: row ids and weights, then rows
+  int r[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    r[j] = j < k ? token_row[(size_t)t * k + j] : -1;
+    wj[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+  }
+  const float4 sh = shared ? *reinterpret_cast<const float4*>(shared + o)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 rs = residual ? *reinterpret_cast<const float4*>(residual + o)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    v[j] = r[j] >= 0 ? *reinterpret_cast<const float4*>(rows + (size_t)r[j] * d + 4 * c)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (r[j] < 0) continue;
+    acc.x = fmaf(wj[j], v[j].x, acc.x);
+    acc.y = fmaf(wj[j], v[j].y, acc.y);
+    acc.z = fmaf(wj[j], v[j].z, acc.z);
+    acc.w = fmaf(wj[j], v[j].w, acc.w);
+  }
   if (shared) {
-    const float4 v = *reinterpret_cast<const float4*>(shared + o);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    acc.x += sh.x; acc.y += sh.y; acc.z += sh.z; acc.w += sh.w;
   }
   if (residual) {
-    const float4 v = *reinterpret_cast<const float4*>(residual + o);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    acc.x += rs.x; acc.y += rs.y; acc.z += rs.z; acc.w += rs.w;
   }
   *reinterpret_cast<float4*>(y + o) = acc;
 }
@@ -53,6 +66,7 @@ hipError_t launch_combine(const float* rows, const int32_t* token_row, const flo
                           float* y, hipStream_t s) {
   const long long n = (long long)T * (d / 4);
   const int blocks = (int)((n + 255) / 256);
+  TimedLaunch tl(K_COMBINE, s);
   hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, rows, token_row, w, shared,
                      residual, T, k, d, y);
   return hipGetLastError();

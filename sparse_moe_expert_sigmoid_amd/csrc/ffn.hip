@@ -11,20 +11,26 @@
 // card, Available Artifacts and Conversion Notes), and plain fp32.
 //
 // Quantised formats run on the int8 matrix cores.  The int8/int4 codes are
-// the MFMA A operand as stored (no dequantisation to floating point at all);
-// the fp32 activations are written as two int8 digits per element against a
-// power-of-two scale per row, v = 2^-p (d0 + d1/256), so
+// the MFMA A operand as stored (no dequantisation to floating point); the
+// fp32 activations are written as two int8 digits against a power-of-two
+// scale, v = 2^-p (d0 + d1/256), so that
 //   sum_k q_k v_k = 2^-p (sum_k q_k d0_k + 2^-8 sum_k q_k d1_k)
-// is two exact int32 MFMA accumulations.  The encoding error is below
-// 2^-16 of the row's largest |v| (16-bit fixed point per row), far inside the
-// fp32 tolerance of the layer; accumulation is exact integer arithmetic.
+// is two exact int32 MFMA accumulations.  The encoding error is at most
+// 2^-16 of the largest |v| sharing the scale.  x uses one scale per row; h
+// uses one scale per row and 64-column block, chosen in the gate/up epilogue
+// (so h never exists in fp32 memory and no separate pass is needed); the
+// down projection folds each 64-column block's int32 sums into fp32 with
+// that block's scale.
 //
 // Work split: a tile is up to 16 rows of one expert (the MFMA N side); a
-// workgroup of 4 wavefronts owns 64 output columns of one tile, each
-// wavefront 16 (the MFMA M side).  The tile's activation digits sit in LDS;
-// the weight rows stream from HBM with 16-byte loads, each byte read once
-// per tile.  Tiles are found on the device from the expert offsets, so no
-// count is ever copied back to the host.
+// workgroup owns 64 output columns of one tile, one wavefront per 16 columns
+// (the MFMA M side), optionally KS wavefronts per 16 columns each taking a
+// K slice (int32 partial sums are added exactly).  Weight rows stream from
+// HBM with 16-byte loads, each byte read once per tile; activation digits are
+// read straight from L2 (no LDS staging, so occupancy is set by registers
+// only).  Tiles are found on the device from the expert offsets, so no count
+// is copied back to the host; the routed and the shared expert can share one
+// launch (group 0 and group 1 below).
 #include "internal.h"
 
 namespace moe {
@@ -32,12 +38,32 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kLdsPad = 16;  // bytes added per LDS row of digits
+// ------------------------------------------------------------------ digits
+// p such that max|v| * 2^p lies in (63.5, 127]; 0 for an all-zero set.
+__device__ inline int digit_exponent(float m) {
+  if (!(m > 0.0f)) return 0;
+  int ex;
+  frexpf(m, &ex);  // m = f * 2^ex, f in [0.5, 1)
+  int p = 7 - ex;
+  if (ldexpf(m, p) > 127.0f) p -= 1;
+  return p;
+}
 
-// ------------------------------------------------------------------ encode
-// One wavefront per row: p = 7 - exponent(max|v|) (minus 1 if that overshoots
-// 127), a = v * 2^p (exact), d0 = rint(a), d1 = rint((a - d0) * 256), both
-// clamped to [-127, 127]; sig = 2^-p (0 for an all-zero row).
+// v * 2^p = d0 + d1/256 (+ error <= 2^-9), both digits in [-127, 127].
+__device__ inline void two_digits(float v, int p, int& d0, int& d1) {
+  const float a = ldexpf(v, p);
+  float f0 = fminf(fmaxf(rintf(a), -127.0f), 127.0f);
+  float f1 = fminf(fmaxf(rintf((a - f0) * 256.0f), -127.0f), 127.0f);
+  d0 = (int)f0;
+  d1 = (int)f1;
+}
+
+__device__ inline unsigned pack4(int a, int b, int c, int d) {
+  return (unsigned)(a & 0xff) | ((unsigned)(b & 0xff) << 8) | ((unsigned)(c & 0xff) << 16) |
+         ((unsigned)(d & 0xff) << 24);
+}
+
+// One wavefront per row: q[r] = [d0 digits (K) | d1 digits (K)], sig[r] = 2^-p.
 __global__ __launch_bounds__(256) void encode_rows_kernel(const float* __restrict__ v, int n,
                                                           int K, int8_t* __restrict__ q,
                                                           float* __restrict__ sig) {
@@ -52,156 +78,113 @@ __global__ __launch_bounds__(256) void encode_rows_kernel(const float* __restric
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-  int p = 0;
-  if (m > 0.0f) {
-    int ex;
-    frexpf(m, &ex);              // m = f * 2^ex, f in [0.5, 1)
-    p = 7 - ex;
-    if (ldexpf(m, p) > 127.0f) p -= 1;
-  }
-  int8_t* q0 = q + (size_t)r * 2 * K;
-  int8_t* q1 = q0 + K;
+  const int p = digit_exponent(m);
+  unsigned* q0 = reinterpret_cast<unsigned*>(q + (size_t)r * 2 * K);
+  unsigned* q1 = reinterpret_cast<unsigned*>(q + (size_t)r * 2 * K + K);
   for (int c = lane; c < K / 4; c += kWave) {
     const float4 a = *reinterpret_cast<const float4*>(row + 4 * c);
-    float av[4] = {a.x, a.y, a.z, a.w};
-    char4 o0, o1;
-    signed char d0v[4], d1v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float s = m > 0.0f ? ldexpf(av[u], p) : 0.0f;
-      float d0 = rintf(s);
-      d0 = fminf(fmaxf(d0, -127.0f), 127.0f);
-      float d1 = rintf((s - d0) * 256.0f);
-      d1 = fminf(fmaxf(d1, -127.0f), 127.0f);
-      d0v[u] = (signed char)(int)d0;
-      d1v[u] = (signed char)(int)d1;
-    }
-    o0 = make_char4(d0v[0], d0v[1], d0v[2], d0v[3]);
-    o1 = make_char4(d1v[0], d1v[1], d1v[2], d1v[3]);
-    *reinterpret_cast<char4*>(q0 + 4 * c) = o0;
-    *reinterpret_cast<char4*>(q1 + 4 * c) = o1;
+    int x0, y0, x1, y1, x2, y2, x3, y3;
+    two_digits(a.x, p, x0, y0);
+    two_digits(a.y, p, x1, y1);
+    two_digits(a.z, p, x2, y2);
+    two_digits(a.w, p, x3, y3);
+    q0[c] = pack4(x0, x1, x2, x3);
+    q1[c] = pack4(y0, y1, y2, y3);
   }
   if (lane == 0) sig[r] = m > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
 }
 
-// Copy the tile's digit rows (2*K bytes each) into LDS rows of `ldr` bytes.
-__device__ inline void stage_rows(int8_t* lds, int ldr, const int8_t* __restrict__ src, int K,
-                                  const int32_t* __restrict__ row_token, int r0, int nr) {
-  const int per_row = (2 * K) / 16;  // 16-byte chunks
+// ------------------------------------------------------------------ work items
+// Group 0: routed experts (rows grouped by `offsets`, rows read token
+// row_token[r]); group 1: optional second expert set, e.g. the shared expert
+// (one expert, identity rows).  Tiles of group 1 follow group 0's.
+struct Group {
+  int E, inter, R, tiles;
+  const void* wgu;
+  const float* sgu;
+  const void* wdn;
+  const float* sdn;
+  const int32_t* row_token;  // NULL = identity
+  const int32_t* offsets;    // NULL = one expert over R rows
+  int8_t* hq;                // [R][2][inter]
+  float* hs;                 // [R][inter/64]
+  float* out;                // [R][d]
+};
+
+struct Job {
+  int g, e, r0, nr;
+};
+
+__device__ inline bool find_job(const Group& g0, const Group& g1, int mt, int tile, Job& j) {
+  const Group& G = tile < g0.tiles ? g0 : g1;
+  const int t = tile < g0.tiles ? tile : tile - g0.tiles;
+  if (tile >= g0.tiles && t >= g1.tiles) return false;
+  Tile tl;
+  if (!find_tile(G.offsets, G.E, G.R, mt, t, tl)) return false;
+  j.g = tile < g0.tiles ? 0 : 1;
+  j.e = tl.e;
+  j.r0 = tl.r0;
+  j.nr = tl.nr;
+  return true;
+}
+
+// Copy `nr` digit rows of `rowbytes` bytes (row j from src row map(j)) into
+// LDS rows of `ldr` bytes.
+__device__ inline void stage_rows(int8_t* lds, int ldr, const int8_t* __restrict__ src,
+                                  int rowbytes, const int32_t* __restrict__ row_token, int r0,
+                                  int nr) {
+  const int per_row = rowbytes / 16;
   for (int q = threadIdx.x; q < nr * per_row; q += blockDim.x) {
     const int j = q / per_row, c = q % per_row;
     const int src_row = row_token ? row_token[r0 + j] : r0 + j;
-    const v4i val = *reinterpret_cast<const v4i*>(src + (size_t)src_row * 2 * K + 16 * c);
+    const v4i val = *reinterpret_cast<const v4i*>(src + (size_t)src_row * rowbytes + 16 * c);
     *reinterpret_cast<v4i*>(lds + j * ldr + 16 * c) = val;
   }
 }
 
-// ------------------------------------------------------------------ int8
-// MODE 0: gate/up with SwiGLU epilogue -> h [R][I].
-// MODE 1: down -> rows [R][d].
-// K = reduction length; W points at expert 0's matrix [E][N][K] (N = 2I or d).
-template <int MODE>
-__global__ __launch_bounds__(256) void ffn_i8_kernel(const int8_t* __restrict__ W,
-                                                     const float* __restrict__ S,
-                                                     const int8_t* __restrict__ act_q,
-                                                     const float* __restrict__ act_s,
-                                                     const int32_t* __restrict__ row_token,
-                                                     const int32_t* __restrict__ offsets, int E,
-                                                     int K, int N_out, int R,
-                                                     float* __restrict__ out) {
-  extern __shared__ int8_t lds[];
-  Tile tl;
-  if (!find_tile(offsets, E, R, kTileRows, blockIdx.y, tl)) return;
-  const int ldr = 2 * K + kLdsPad;
-  stage_rows(lds, ldr, act_q, K, MODE == 0 ? row_token : nullptr, tl.r0, tl.nr);
-  __syncthreads();
+// ------------------------------------------------------------------ weight layouts
+// kRows:  [E][N][K] int8 (int4: [E][N][K/2] bytes), input axis contiguous.
+// kTiled: the same bytes arranged as MFMA A operands.  int8: for each group of
+//   16 rows and each 64-wide K step one 1 KB block in lane order, lane
+//   l = row%16 + 16*((k%64)/16) holding k%16 = 0..15.  int4: for each group of
+//   16 rows and each 128-wide K span one 1 KB block, lane l = row%16 +
+//   16*((k%32)/8) holding 4 bytes per block of 32 (elements 8g..8g+7, two per
+//   byte, low nibble first) for the span's 4 blocks in order.
+// A wavefront streaming one row group then reads whole 1 KB blocks per
+// instruction.
+constexpr int kRows = 0, kTiled = 1;
 
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int c0 = (blockIdx.x * (blockDim.x / kWave) + wave) * 16;  // output columns
-  if (c0 >= N_out) return;
-  const int i = lane & 15, g = lane >> 4;
-  const size_t rows_per_expert = MODE == 0 ? (size_t)2 * N_out : (size_t)N_out;
-  const int8_t* wa = W + ((size_t)tl.e * rows_per_expert + c0 + i) * K + 16 * g;
-  const int8_t* wb = wa + (size_t)N_out * K;  // up rows (MODE 0 only)
-  const bool jv = i < tl.nr;
-  const int8_t* b0 = lds + i * ldr + 16 * g;
-  const int8_t* b1 = b0 + K;
+template <int LAY>
+__device__ inline const int8_t* i8_operand_base(const int8_t* W, size_t row0, int K, int i,
+                                                int g, int lane) {
+  return LAY == kRows ? W + (row0 + i) * K + 16 * g : W + row0 * K + 16 * lane;
+}
+template <int LAY>
+__device__ inline v4i i8_load(const int8_t* base, int step) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const v4i*>(base + (LAY == kRows ? 64 : 1024) * step));
+}
 
-  v4i acc_a0 = {0, 0, 0, 0}, acc_a1 = {0, 0, 0, 0};
-  v4i acc_b0 = {0, 0, 0, 0}, acc_b1 = {0, 0, 0, 0};
-  constexpr int U = 4;
-  int k = 0;
-  for (; k + U * kKStep <= K; k += U * kKStep) {
-    v4i ra[U], rb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ra[u] = *reinterpret_cast<const v4i*>(wa + k + u * kKStep);
-      if (MODE == 0) rb[u] = *reinterpret_cast<const v4i*>(wb + k + u * kKStep);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v4i x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-      if (jv) {
-        x0 = *reinterpret_cast<const v4i*>(b0 + k + u * kKStep);
-        x1 = *reinterpret_cast<const v4i*>(b1 + k + u * kKStep);
-      }
-      acc_a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0, acc_a0, 0, 0, 0);
-      acc_a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1, acc_a1, 0, 0, 0);
-      if (MODE == 0) {
-        acc_b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0, acc_b0, 0, 0, 0);
-        acc_b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1, acc_b1, 0, 0, 0);
-      }
-    }
-  }
-  for (; k < K; k += kKStep) {
-    const v4i ra = *reinterpret_cast<const v4i*>(wa + k);
-    v4i rb = {0, 0, 0, 0};
-    if (MODE == 0) rb = *reinterpret_cast<const v4i*>(wb + k);
-    v4i x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-    if (jv) {
-      x0 = *reinterpret_cast<const v4i*>(b0 + k);
-      x1 = *reinterpret_cast<const v4i*>(b1 + k);
-    }
-    acc_a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra, x0, acc_a0, 0, 0, 0);
-    acc_a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra, x1, acc_a1, 0, 0, 0);
-    if (MODE == 0) {
-      acc_b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb, x0, acc_b0, 0, 0, 0);
-      acc_b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb, x1, acc_b1, 0, 0, 0);
-    }
-  }
-
-  // D layout (16x16): lane holds rows 4g..4g+3 (weight rows) of column i (tile row).
-  if (!jv) return;
-  const int r = tl.r0 + i;
-  const int src = (MODE == 0 && row_token) ? row_token[r] : r;
-  const float sig = act_s[MODE == 0 ? src : r];
-  float res[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int n = c0 + 4 * g + c;
-    const float va = (float)acc_a0[c] + (float)acc_a1[c] * (1.0f / 256.0f);
-    if (MODE == 0) {
-      const float* se = S + (size_t)tl.e * 2 * N_out;
-      const float gate = se[n] * sig * va;
-      const float vb = (float)acc_b0[c] + (float)acc_b1[c] * (1.0f / 256.0f);
-      const float up = se[N_out + n] * sig * vb;
-      res[c] = silu_f(gate) * up;
-    } else {
-      res[c] = S[(size_t)tl.e * N_out + n] * sig * va;
-    }
-  }
-  *reinterpret_cast<float4*>(out + (size_t)r * N_out + c0 + 4 * g) =
-      make_float4(res[0], res[1], res[2], res[3]);
+template <int LAY>
+__device__ inline const uint8_t* i4_operand_base(const uint8_t* W, size_t row0, int K, int i,
+                                                 int g, int lane) {
+  return LAY == kRows ? W + (row0 + i) * (K / 2) + 4 * g : W + row0 * (K / 2) + 16 * lane;
+}
+// the 4 words (one per block of 32) of span m
+template <int LAY>
+__device__ inline v4i i4_load(const uint8_t* base, int m) {
+  if (LAY == kTiled)
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(base + 1024 * m));
+  const unsigned* p = reinterpret_cast<const unsigned*>(base + 64 * m);
+  return v4i{(int)p[0], (int)p[4], (int)p[8], (int)p[12]};
 }
 
 // ------------------------------------------------------------------ int4
-// Codes packed two per byte (element 2i low nibble).  One 16x16x32 MFMA per
-// block of 32 inputs, so each block's integer sum gets its own scale
-// max(s, 2^-14) before it joins the fp32 accumulator.
+// 8 codes of one 4-byte word -> 8 sign-extended bytes in element order.
 __device__ inline long unpack8_int4(unsigned w) {
-  // nibbles -> sign-extended bytes, element order kept
   const unsigned lo = w & 0x0F0F0F0Fu;          // elements 0,2,4,6
   const unsigned hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1,3,5,7
+  // nibble n -> byte n - 16*(n >= 8): ((n ^ 0x88) - 0x08) ^ 0x80, bytewise, no borrows
   const unsigned slo = ((lo ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u;
   const unsigned shi = ((hi ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u;
   const unsigned o0 = __builtin_amdgcn_perm(shi, slo, 0x05010400u);  // e0 e1 e2 e3
@@ -209,80 +192,346 @@ __device__ inline long unpack8_int4(unsigned w) {
   return (long)(((unsigned long)o1 << 32) | o0);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void ffn_i4_kernel(const uint8_t* __restrict__ W,
-                                                     const float* __restrict__ S,
-                                                     const int8_t* __restrict__ act_q,
-                                                     const float* __restrict__ act_s,
-                                                     const int32_t* __restrict__ row_token,
-                                                     const int32_t* __restrict__ offsets, int E,
-                                                     int K, int N_out, int R,
-                                                     float* __restrict__ out) {
+constexpr float kScaleFloor = 1.0f / 16384.0f;  // int4 block scales are raised to 2^-14
+
+// ------------------------------------------------------------------ gate/up
+// FMT 1: int8 rows; FMT 2: int4 blocks of 32.  Block = 4*KS wavefronts:
+// column group cg = wave % 4 (16 h-columns each), K slice kp = wave / 4.
+// LDS: the tile's x digit rows (mt rows of 2d bytes), then reductions.
+template <int FMT, int LAY, int KS>
+__global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, int d, int mt,
+                                                           const int8_t* __restrict__ xq,
+                                                           const float* __restrict__ xs) {
   extern __shared__ int8_t lds[];
-  Tile tl;
-  if (!find_tile(offsets, E, R, kTileRows, blockIdx.y, tl)) return;
-  const int ldr = 2 * K + kLdsPad;
-  stage_rows(lds, ldr, act_q, K, MODE == 0 ? row_token : nullptr, tl.r0, tl.nr);
+  __shared__ float red_max[4][16];
+  // K-slice partials: int8 path 16 ints per lane, int4 path 8 floats per lane
+  __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 16 : 1];
+  Job job;
+  if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+  const Group& G = job.g == 0 ? g0 : g1;
+  if ((int)blockIdx.x * 64 >= G.inter) return;
+  const int I = G.inter;
+  const int ldr = 2 * d + 16;
+  stage_rows(lds, ldr, xq, 2 * d, G.row_token, job.r0, job.nr);
   __syncthreads();
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int c0 = (blockIdx.x * (blockDim.x / kWave) + wave) * 16;
-  if (c0 >= N_out) return;
+  const int cg = wave & 3, kp = wave >> 2;
+  const int c0 = blockIdx.x * 64 + cg * 16;  // this wavefront's 16 h-columns
   const int i = lane & 15, g = lane >> 4;
-  const int nblk = K / 32;
-  const size_t rows_per_expert = MODE == 0 ? (size_t)2 * N_out : (size_t)N_out;
-  const size_t row_a = (size_t)tl.e * rows_per_expert + c0 + i;
-  const uint8_t* wa = W + row_a * (K / 2) + 4 * g;
-  const uint8_t* wb = wa + (size_t)N_out * (K / 2);
-  // scales of this lane's four output rows 4g..4g+3
-  const float* sa = S + ((size_t)tl.e * rows_per_expert + c0 + 4 * g) * nblk;
-  const float* sb = sa + (size_t)N_out * nblk;
-  const bool jv = i < tl.nr;
-  const int8_t* b0 = lds + i * ldr + 8 * g;
-  const int8_t* b1 = b0 + K;
-  const float floor_s = 1.0f / 16384.0f;  // 2^-14
+  const bool jv = i < job.nr;
+  const int r = job.r0 + i;
+  const int tok = jv ? (G.row_token ? G.row_token[r] : r) : 0;
+  const int8_t* xb0 = lds + i * ldr;
+  const int8_t* xb1 = xb0 + d;
+  const size_t row0 = (size_t)job.e * 2 * I + c0;
 
-  float fa[4] = {0.f, 0.f, 0.f, 0.f}, fb[4] = {0.f, 0.f, 0.f, 0.f};
-  const v4i zero = {0, 0, 0, 0};
-  for (int b = 0; b < nblk; ++b) {
-    const long a = unpack8_int4(*reinterpret_cast<const unsigned*>(wa + 16 * b));
-    long bb = 0;
-    if (MODE == 0) bb = unpack8_int4(*reinterpret_cast<const unsigned*>(wb + 16 * b));
-    long x0 = 0, x1 = 0;
-    if (jv) {
-      x0 = *reinterpret_cast<const long*>(b0 + 32 * b);
-      x1 = *reinterpret_cast<const long*>(b1 + 32 * b);
+  float gate[4], up[4];
+  if (FMT == 1) {
+    const int nsteps = d / kKStep;
+    const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
+    const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wgu), row0, d, i, g,
+                                            lane);
+    const int8_t* wb = wa + (size_t)I * d;
+    v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+    constexpr int U = 4;
+    for (int s = s_beg; s < s_end; s += U) {
+      v4i ra[U], rb[U], x0[U], x1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ss = min(s + u, s_end - 1);
+        ra[u] = i8_load<LAY>(wa, ss);
+        rb[u] = i8_load<LAY>(wb, ss);
+        x0[u] = v4i{0, 0, 0, 0};
+        x1[u] = v4i{0, 0, 0, 0};
+        if (jv) {
+          x0[u] = *reinterpret_cast<const v4i*>(xb0 + ss * kKStep + 16 * g);
+          x1[u] = *reinterpret_cast<const v4i*>(xb1 + ss * kKStep + 16 * g);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s + u < s_end) {
+          a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0[u], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1[u], a1, 0, 0, 0);
+          b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0[u], b0, 0, 0, 0);
+          b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1[u], b1, 0, 0, 0);
+        }
+      }
     }
-    const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, x0, zero, 0, 0, 0);
-    const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, x1, zero, 0, 0, 0);
+    // exact int32 reduction of the K slices (order-free)
+    if (KS > 1) {
+      int* red = reinterpret_cast<int*>(red_acc);
+      if (kp > 0) {
+        int* dst = red + (((kp - 1) * 4 + cg) * 64 + lane) * 16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          dst[c] = a0[c]; dst[4 + c] = a1[c]; dst[8 + c] = b0[c]; dst[12 + c] = b1[c];
+        }
+      }
+      __syncthreads();
+      if (kp == 0) {
+        for (int q = 1; q < KS; ++q) {
+          const int* src = red + (((q - 1) * 4 + cg) * 64 + lane) * 16;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            a0[c] += src[c]; a1[c] += src[4 + c]; b0[c] += src[8 + c]; b1[c] += src[12 + c];
+          }
+        }
+      }
+    }
+    const float sig = jv ? xs[tok] : 0.0f;
+    const float* se = G.sgu + (size_t)job.e * 2 * I;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float s = fmaxf(sa[(size_t)c * nblk + b], floor_s);
-      fa[c] = fmaf(s, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
+      const int n = c0 + 4 * g + c;
+      gate[c] = se[n] * sig * ((float)a0[c] + (float)a1[c] * (1.0f / 256.0f));
+      up[c] = se[I + n] * sig * ((float)b0[c] + (float)b1[c] * (1.0f / 256.0f));
     }
-    if (MODE == 0) {
-      const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(bb, x0, zero, 0, 0, 0);
-      const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(bb, x1, zero, 0, 0, 0);
+  } else {
+    // int4: one 16x16x32 MFMA pair per block of 32 inputs; each block's int32
+    // sum (256*d0-part + d1-part, exact in fp32 since |.| < 2^24) is scaled by
+    // max(s, 2^-14) into the fp32 accumulator.
+    const int nb = d / 32, nspan = d / 128;
+    const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
+    const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wgu), row0, d, i,
+                                             g, lane);
+    const uint8_t* wb = wa + (size_t)I * (d / 2);
+    const float* sa = G.sgu + ((size_t)job.e * 2 * I + c0 + 4 * g) * nb;
+    const float* sb = sa + (size_t)I * nb;
+    float fa[4] = {0.f, 0.f, 0.f, 0.f}, fb[4] = {0.f, 0.f, 0.f, 0.f};
+    const v4i zero = {0, 0, 0, 0};
+    for (int m = m_beg; m < m_end; ++m) {
+      const v4i wa4 = i4_load<LAY>(wa, m);
+      const v4i wb4 = i4_load<LAY>(wb, m);
+      long x0[4], x1[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float s = fmaxf(sb[(size_t)c * nblk + b], floor_s);
-        fb[c] = fmaf(s, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+      for (int q = 0; q < 4; ++q) {
+        x0[q] = 0;
+        x1[q] = 0;
+        if (jv) {
+          x0[q] = *reinterpret_cast<const long*>(xb0 + 128 * m + 32 * q + 8 * g);
+          x1[q] = *reinterpret_cast<const long*>(xb1 + 128 * m + 32 * q + 8 * g);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * m + q;
+        const long qa = unpack8_int4((unsigned)wa4[q]);
+        const long qb = unpack8_int4((unsigned)wb4[q]);
+        const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], zero, 0, 0, 0);
+        const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], zero, 0, 0, 0);
+        const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], zero, 0, 0, 0);
+        const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], zero, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float s1 = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
+          const float s2 = fmaxf(sb[(size_t)c * nb + b], kScaleFloor);
+          fa[c] = fmaf(s1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
+          fb[c] = fmaf(s2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+        }
+      }
+    }
+    if (KS > 1) {  // fp32 partials added in slice order
+      if (kp > 0) {
+        float* dst = red_acc + (((kp - 1) * 4 + cg) * 64 + lane) * 8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { dst[c] = fa[c]; dst[4 + c] = fb[c]; }
+      }
+      __syncthreads();
+      if (kp == 0) {
+        for (int q = 1; q < KS; ++q) {
+          const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 8;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) { fa[c] += src[c]; fb[c] += src[4 + c]; }
+        }
+      }
+    }
+    const float sig = jv ? xs[tok] * (1.0f / 256.0f) : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      gate[c] = fa[c] * sig;
+      up[c] = fb[c] * sig;
+    }
+  }
+
+  // ---- epilogue: h = silu(gate) * up, encoded per (row, 64-column block)
+  float h[4];
+  float mx = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    h[c] = silu_f(gate[c]) * up[c];
+    mx = fmaxf(mx, fabsf(h[c]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  if (kp == 0 && g == 0) red_max[cg][i] = mx;
+  __syncthreads();
+  if (kp != 0 || !jv) return;
+  mx = fmaxf(fmaxf(red_max[0][i], red_max[1][i]), fmaxf(red_max[2][i], red_max[3][i]));
+  const int p = digit_exponent(mx);
+  int d0[4], d1[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) two_digits(h[c], p, d0[c], d1[c]);
+  int8_t* hrow = G.hq + (size_t)r * 2 * I;
+  const int col = c0 + 4 * g;
+  *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
+  *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
+  if (cg == 0 && g == 0)
+    G.hs[(size_t)r * (I / 64) + blockIdx.x] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+}
+
+// ------------------------------------------------------------------ down
+// LDS: the tile's h digit rows (mt rows of 2I bytes), their block scales
+// (mt x I/64 floats), then the K-slice partials.
+template <int FMT, int LAY, int KS>
+__global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int d, int mt) {
+  extern __shared__ int8_t lds[];
+  __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 4 : 1];
+  Job job;
+  if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+  const Group& G = job.g == 0 ? g0 : g1;
+  const int I = G.inter;
+  const int ldr = 2 * I + 16;
+  const int nhb = I / 64;
+  float* lds_s = reinterpret_cast<float*>(lds + (size_t)mt * ldr);
+  stage_rows(lds, ldr, G.hq, 2 * I, nullptr, job.r0, job.nr);
+  for (int q = threadIdx.x; q < job.nr * nhb; q += blockDim.x)
+    lds_s[q] = G.hs[(size_t)(job.r0 + q / nhb) * nhb + q % nhb];
+  __syncthreads();
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int cg = wave & 3, kp = wave >> 2;
+  const int c0 = blockIdx.x * 64 + cg * 16;  // output columns of this wavefront
+  const int i = lane & 15, g = lane >> 4;
+  const bool jv = i < job.nr;
+  const int r = job.r0 + i;
+  const int8_t* hb0 = lds + i * ldr;
+  const int8_t* hb1 = hb0 + I;
+  const float* hsr = lds_s + i * nhb;
+  const size_t row0 = (size_t)job.e * d + c0;
+  const v4i zero = {0, 0, 0, 0};
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+
+  if (FMT == 1) {
+    const int nsteps = I / kKStep;
+    const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
+    const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g,
+                                            lane);
+    constexpr int U = 4;
+    for (int s = s_beg; s < s_end; s += U) {
+      v4i ra[U], x0[U], x1[U];
+      float sg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ss = min(s + u, s_end - 1);
+        ra[u] = i8_load<LAY>(wa, ss);
+        x0[u] = zero;
+        x1[u] = zero;
+        sg[u] = 0.0f;
+        if (jv) {
+          x0[u] = *reinterpret_cast<const v4i*>(hb0 + ss * kKStep + 16 * g);
+          x1[u] = *reinterpret_cast<const v4i*>(hb1 + ss * kKStep + 16 * g);
+          sg[u] = hsr[ss];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s + u < s_end) {
+          const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0[u], zero, 0, 0, 0);
+          const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1[u], zero, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[c] = fmaf(sg[u], fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[c]);
+        }
+      }
+    }
+  } else {
+    const int nb = I / 32, nspan = I / 128;
+    const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
+    const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wdn), row0, I, i, g,
+                                             lane);
+    const float* sa = G.sdn + ((size_t)job.e * d + c0 + 4 * g) * nb;
+    for (int m = m_beg; m < m_end; ++m) {
+      const v4i w4 = i4_load<LAY>(wa, m);
+      long x0[4], x1[4];
+      float sg[2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x0[q] = 0;
+        x1[q] = 0;
+        if (jv) {
+          x0[q] = *reinterpret_cast<const long*>(hb0 + 128 * m + 32 * q + 8 * g);
+          x1[q] = *reinterpret_cast<const long*>(hb1 + 128 * m + 32 * q + 8 * g);
+        }
+      }
+      sg[0] = jv ? hsr[2 * m] * (1.0f / 256.0f) : 0.0f;
+      sg[1] = jv ? hsr[2 * m + 1] * (1.0f / 256.0f) : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 4 * m + q;
+        const long wq = unpack8_int4((unsigned)w4[q]);
+        const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], zero, 0, 0, 0);
+        const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], zero, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float sw = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
+          acc[c] = fmaf(sw * sg[q >> 1], (float)(p0[c] * 256 + p1[c]), acc[c]);
+        }
       }
     }
   }
-
+  if (KS > 1) {
+    if (kp > 0) {
+      float* dst = red_acc + (((kp - 1) * 4 + cg) * 64 + lane) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[c] = acc[c];
+    }
+    __syncthreads();
+    if (kp != 0) return;
+    for (int q = 1; q < KS; ++q) {
+      const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += src[c];
+    }
+  }
   if (!jv) return;
-  const int r = tl.r0 + i;
-  const int src = (MODE == 0 && row_token) ? row_token[r] : r;
-  const float sig = act_s[MODE == 0 ? src : r] * (1.0f / 256.0f);
   float res[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    if (MODE == 0) res[c] = silu_f(fa[c] * sig) * (fb[c] * sig);
-    else res[c] = fa[c] * sig;
+    const int n = c0 + 4 * g + c;
+    res[c] = FMT == 1 ? G.sdn[(size_t)job.e * d + n] * acc[c] : acc[c];
   }
-  *reinterpret_cast<float4*>(out + (size_t)r * N_out + c0 + 4 * g) =
+  *reinterpret_cast<float4*>(G.out + (size_t)r * d + c0 + 4 * g) =
       make_float4(res[0], res[1], res[2], res[3]);
+}
+
+// ------------------------------------------------------------------ layout conversion
+// Row-major codes -> tiled codes (a byte permutation; see the layout note).
+// One thread per 16-byte lane chunk of the tiled output.
+template <int FMT>
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t* __restrict__ src,
+                                                           uint8_t* __restrict__ dst,
+                                                           long long nrows, int K) {
+  const long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // chunk id
+  const int bytes_per_row = FMT == 1 ? K : K / 2;
+  const long long nchunks = nrows * bytes_per_row / 16;
+  if (q >= nchunks) return;
+  const int lane = (int)(q % 64);
+  const long long blk = q / 64;  // 1 KB block: (row group, step/span)
+  const int per_group = FMT == 1 ? K / 64 : K / 128;
+  const long long rg = blk / per_group;
+  const int st = (int)(blk % per_group);
+  const int i = lane & 15, g = lane >> 4;
+  const uint8_t* row = src + (rg * 16 + i) * bytes_per_row;
+  v4i v;
+  if (FMT == 1) {
+    v = *reinterpret_cast<const v4i*>(row + 64 * st + 16 * g);
+  } else {
+    const unsigned* p = reinterpret_cast<const unsigned*>(row + 64 * st + 4 * g);
+    v = v4i{(int)p[0], (int)p[4], (int)p[8], (int)p[12]};
+  }
+  *reinterpret_cast<v4i*>(dst + 16 * q) = v;
 }
 
 // ------------------------------------------------------------------ fp32
@@ -328,53 +577,107 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
   }
 }
 
-int g_max_lds = 64 * 1024;
+int g_cu_count = 256;
+
+template <int FMT, int LAY>
+hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8_t* xq,
+                       const float* xs, hipStream_t s) {
+  const int tiles = a.tiles + b.tiles;
+  const int imax = a.inter > b.inter ? a.inter : b.inter;
+  // split K across more wavefronts when the tiles alone cannot fill the chip
+  const long long blocks = (long long)tiles * (imax / 64);
+  const int ks = blocks >= 2LL * g_cu_count ? 1 : (blocks >= g_cu_count / 2 ? 2 : 4);
+  const size_t lds_gu = (size_t)mt * (2 * d + 16);
+  {
+    TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
+    dim3 grid(imax / 64, tiles);
+    if (ks == 1)
+      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 1>), grid, dim3(256), lds_gu, s, a, b, d, mt,
+                         xq, xs);
+    else if (ks == 2)
+      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 2>), grid, dim3(512), lds_gu, s, a, b, d, mt,
+                         xq, xs);
+    else
+      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 4>), grid, dim3(1024), lds_gu, s, a, b, d, mt,
+                         xq, xs);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const long long dblocks = (long long)tiles * (d / 64);
+  const int dks = dblocks >= 2LL * g_cu_count ? 1 : (dblocks >= g_cu_count / 2 ? 2 : 4);
+  const size_t lds_dn = (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
+  TimedLaunch tl(FMT == 1 ? K_FFN_I8_DOWN : K_FFN_I4_DOWN, s);
+  dim3 grid(d / 64, tiles);
+  if (dks == 1)
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 1>), grid, dim3(256), lds_dn, s, a, b, d, mt);
+  else if (dks == 2)
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 2>), grid, dim3(512), lds_dn, s, a, b, d, mt);
+  else
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 4>), grid, dim3(1024), lds_dn, s, a, b, d, mt);
+  return hipGetLastError();
+}
 
 }  // namespace
 
-void set_max_lds(int bytes) { g_max_lds = bytes; }
+void set_device_info(int cu_count) { g_cu_count = cu_count > 0 ? cu_count : 256; }
 
 hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig,
                               hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  TimedLaunch tl(K_ENCODE_ROWS, s);
   hipLaunchKernelGGL(encode_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, v, n, K, q, sig);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_quant(int fmt, const void* wgu, const float* sgu, const void* wdn,
-                            const float* sdn, int E, int d, int inter, const float* x, int T,
-                            const int32_t* row_token, const int32_t* offsets, int R,
-                            float* rows_out, const FfnWs& ws, hipStream_t s) {
-  hipError_t err = launch_encode_rows(x, T, d, ws.xq, ws.xs, s);
-  if (err != hipSuccess) return err;
-  const int tiles = offsets ? max_tiles(R, E, kTileRows) : (R + kTileRows - 1) / kTileRows;
-  const size_t lds_gu = (size_t)kTileRows * (2 * d + kLdsPad);
-  const size_t lds_dn = (size_t)kTileRows * (2 * inter + kLdsPad);
-  if ((int)lds_gu > g_max_lds || (int)lds_dn > g_max_lds) return hipErrorInvalidValue;
-  dim3 grid_gu((inter + 63) / 64, tiles), grid_dn((d + 63) / 64, tiles);
-  if (fmt == 1) {
-    hipLaunchKernelGGL(ffn_i8_kernel<0>, grid_gu, dim3(256), lds_gu, s,
-                       static_cast<const int8_t*>(wgu), sgu, ws.xq, ws.xs, row_token, offsets,
-                       E, d, inter, R, ws.h);
-  } else {
-    hipLaunchKernelGGL(ffn_i4_kernel<0>, grid_gu, dim3(256), lds_gu, s,
-                       static_cast<const uint8_t*>(wgu), sgu, ws.xq, ws.xs, row_token, offsets,
-                       E, d, inter, R, ws.h);
-  }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  err = launch_encode_rows(ws.h, R, inter, ws.hq, ws.hs, s);
-  if (err != hipSuccess) return err;
-  if (fmt == 1) {
-    hipLaunchKernelGGL(ffn_i8_kernel<1>, grid_dn, dim3(256), lds_dn, s,
-                       static_cast<const int8_t*>(wdn), sdn, ws.hq, ws.hs, row_token, offsets,
-                       E, inter, d, R, rows_out);
-  } else {
-    hipLaunchKernelGGL(ffn_i4_kernel<1>, grid_dn, dim3(256), lds_dn, s,
-                       static_cast<const uint8_t*>(wdn), sdn, ws.hq, ws.hs, row_token, offsets,
-                       E, inter, d, R, rows_out);
-  }
+hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nrows, int K,
+                               hipStream_t s) {
+  const long long chunks = nrows * (fmt == 1 ? K : K / 2) / 16;
+  if (chunks <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((chunks + 255) / 256);
+  if (fmt == 1)
+    hipLaunchKernelGGL(tile_weights_kernel<1>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), nrows, K);
+  else
+    hipLaunchKernelGGL(tile_weights_kernel<2>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), nrows, K);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
+                            const FfnWs& ws, bool x_encoded, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (!x_encoded) {
+    err = launch_encode_rows(x, T, d, ws.xq, ws.xs, s);
+    if (err != hipSuccess) return err;
+  }
+  // rows per tile: at most 16 (the MFMA N side); small batches use fewer so
+  // that the staged activation rows take less LDS
+  const int mt = T < kTileRows ? (T > 0 ? T : 1) : kTileRows;
+  Group grp[2] = {};
+  for (int q = 0; q < nsets; ++q) {
+    const FfnSet& f = sets[q];
+    Group& G = grp[q];
+    G.E = f.E;
+    G.inter = f.inter;
+    G.R = f.R;
+    G.tiles = f.offsets ? max_tiles(f.R, f.E, mt) : (f.R + mt - 1) / mt;
+    G.wgu = f.wgu;
+    G.sgu = f.sgu;
+    G.wdn = f.wdn;
+    G.sdn = f.sdn;
+    G.row_token = f.row_token;
+    G.offsets = f.offsets;
+    G.hq = f.hq;
+    G.hs = f.hs;
+    G.out = f.out;
+  }
+  if (nsets < 2) grp[1].inter = grp[0].inter;
+  const bool tiled = sets[0].layout == 1;
+  if (sets[0].fmt == 1)
+    return tiled ? launch_pair<1, kTiled>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)
+                 : launch_pair<1, kRows>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s);
+  return tiled ? launch_pair<2, kTiled>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)
+               : launch_pair<2, kRows>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s);
 }
 
 hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int inter,
@@ -383,10 +686,14 @@ hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int 
                           hipStream_t s) {
   (void)T;
   const int tiles = offsets ? max_tiles(R, E, kTileRows) : (R + kTileRows - 1) / kTileRows;
-  hipLaunchKernelGGL(ffn_f32_kernel<0>, dim3((inter + 3) / 4, tiles), dim3(256), 0, s, wgu, x,
-                     row_token, offsets, E, d, inter, R, h);
+  {
+    TimedLaunch tl(K_FFN_F32_GATE_UP, s);
+    hipLaunchKernelGGL(ffn_f32_kernel<0>, dim3((inter + 3) / 4, tiles), dim3(256), 0, s, wgu,
+                       x, row_token, offsets, E, d, inter, R, h);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  TimedLaunch tl(K_FFN_F32_DOWN, s);
   hipLaunchKernelGGL(ffn_f32_kernel<1>, dim3((d + 3) / 4, tiles), dim3(256), 0, s, wdn, h,
                      row_token, offsets, E, inter, d, R, rows_out);
   return hipGetLastError();

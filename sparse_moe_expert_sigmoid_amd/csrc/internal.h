@@ -25,23 +25,24 @@ inline size_t route_ws_bytes(int T, int d, int E) {
   return align_up(chunks * (size_t)T * (size_t)E * sizeof(float), 256);
 }
 
-// Expert FFN, quantised formats:
-//   xq   [T][2][d] int8   activations as two int8 digits (see encode_rows)
-//   xs   [T] fp32         per-row power-of-two scale of xq
-//   h    [R][I] fp32      silu(gate) * up
-//   hq   [R][2][I] int8   h as two digits
-//   hs   [R] fp32
-// fp32 format: only h.
+// Expert FFN, quantised formats (per expert set q = 0, 1):
+//   xq    [T][2][d] int8     activations as two int8 digits (see ffn.hip)
+//   xs    [T] fp32           per-row power-of-two scale of xq
+//   hq[q] [R_q][2][I_q] int8 h = silu(gate) * up as two digits
+//   hs[q] [R_q][I_q/64] fp32 scale per row and 64-column block
+// fp32 format: h [R][I] fp32 only.
 struct FfnWs {
   int8_t* xq;
   float* xs;
+  int8_t* hq[2];
+  float* hs[2];
   float* h;
-  int8_t* hq;
-  float* hs;
   size_t bytes;
 };
 
-inline FfnWs ffn_ws_layout(void* base, int T, int R, int d, int inter, bool quantised) {
+// rows/inter of up to two expert sets sharing one x
+inline FfnWs ffn_ws_layout(void* base, int T, int d, int nsets, const int* R, const int* inter,
+                           bool quantised) {
   FfnWs w{};
   size_t off = 0;
   char* b = static_cast<char*>(base);
@@ -50,16 +51,35 @@ inline FfnWs ffn_ws_layout(void* base, int T, int R, int d, int inter, bool quan
     off = align_up(off + n, 256);
     return p;
   };
-  w.h = reinterpret_cast<float*>(take((size_t)R * inter * sizeof(float)));
   if (quantised) {
     w.xq = reinterpret_cast<int8_t*>(take((size_t)T * 2 * d));
     w.xs = reinterpret_cast<float*>(take((size_t)T * sizeof(float)));
-    w.hq = reinterpret_cast<int8_t*>(take((size_t)R * 2 * inter));
-    w.hs = reinterpret_cast<float*>(take((size_t)R * sizeof(float)));
+    for (int q = 0; q < nsets; ++q) {
+      w.hq[q] = reinterpret_cast<int8_t*>(take((size_t)R[q] * 2 * inter[q]));
+      w.hs[q] = reinterpret_cast<float*>(take((size_t)R[q] * (inter[q] / 64) * sizeof(float)));
+    }
+  } else {
+    w.h = reinterpret_cast<float*>(take((size_t)R[0] * inter[0] * sizeof(float)));
   }
   w.bytes = off;
   return w;
 }
+
+// One expert set for the quantised FFN launchers.
+struct FfnSet {
+  int fmt;                   // 1 = int8 rows, 2 = int4 blocks of 32
+  int layout;                // 0 = rows, 1 = tiled (both sets of one launch alike)
+  int E, inter, R;
+  const void* wgu;
+  const float* sgu;
+  const void* wdn;
+  const float* sdn;
+  const int32_t* row_token;  // NULL = identity
+  const int32_t* offsets;    // NULL = one expert over R rows
+  int8_t* hq;
+  float* hs;
+  float* out;                // [R][d]
+};
 
 // Upper bound on the number of FFN tiles (kTileRows rows of one expert each)
 // for R rows spread over E experts: sum_e ceil(c_e/MT) <= n + (R - n)/MT with
@@ -68,6 +88,31 @@ inline int max_tiles(int R, int E, int mt) {
   int n = R < E ? R : E;
   return n + (R - n + mt - 1) / mt;
 }
+
+// ---------------------------------------------------------------- kernel timer
+// Measurement aid (off unless a context turns it on): each launch is
+// bracketed by a pair of HIP events on its own stream.
+enum KernelId {
+  K_ROUTER_LOGITS, K_ROUTER_TOPK, K_PERMUTE, K_FILL, K_ENCODE_ROWS,
+  K_FFN_I8_GATE_UP, K_FFN_I8_DOWN, K_FFN_I4_GATE_UP, K_FFN_I4_DOWN,
+  K_FFN_F32_GATE_UP, K_FFN_F32_DOWN, K_COMBINE, K_COUNT
+};
+extern const char* const kKernelNames[K_COUNT];
+
+struct KernelTimer;
+extern thread_local KernelTimer* g_timer;  // set by the API for the duration of a call
+void timer_begin(int id, hipStream_t s);
+void timer_end(hipStream_t s);
+
+struct TimedLaunch {
+  hipStream_t s;
+  TimedLaunch(int id, hipStream_t st) : s(st) {
+    if (g_timer) timer_begin(id, s);
+  }
+  ~TimedLaunch() {
+    if (g_timer) timer_end(s);
+  }
+};
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.
@@ -79,10 +124,14 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig,
                               hipStream_t s);
-hipError_t launch_ffn_quant(int fmt, const void* wgu, const float* sgu, const void* wdn,
-                            const float* sdn, int E, int d, int inter, const float* x, int T,
-                            const int32_t* row_token, const int32_t* offsets, int R,
-                            float* rows_out, const FfnWs& ws, hipStream_t s);
+// Encodes x (unless x_encoded) and runs gate/up then down for 1 or 2 expert
+// sets (same format) in one pair of launches.
+hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
+                            const FfnWs& ws, bool x_encoded, hipStream_t s);
+void set_device_info(int cu_count);
+// Row-major codes [nrows][K] (int4: K/2 bytes per row) -> tiled layout.
+hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nrows, int K,
+                               hipStream_t s);
 hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int inter,
                           const float* x, int T, const int32_t* row_token,
                           const int32_t* offsets, int R, float* rows_out, float* h,

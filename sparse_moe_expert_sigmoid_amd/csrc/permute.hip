@@ -115,6 +115,7 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  TimedLaunch tl(K_FILL, s);
   hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
@@ -132,6 +133,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
   int seg = (int)((n + W - 1) / W);
   seg = (seg + kWave - 1) / kWave * kWave;
   const size_t lds = (size_t)W * E * 12 + (size_t)E * 4;
+  TimedLaunch tl(K_PERMUTE, s);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(W * kWave), lds, s, idx, (int)n, k, E, seg,
                      offsets, row_token, token_row);
   return hipGetLastError();

@@ -8,19 +8,19 @@
 // Two kernels.  The first writes partial logits, each a sum over a fixed
 // 256-wide slice of the input in ascending order; the second adds the slices
 // in order, so a token's logits never depend on T or on the launch shape.
-// The second kernel runs one wavefront per token: k rounds of a 64-bit
-// wavefront arg-max over order-preserving keys (fp32 key bits, then the
-// inverted expert id, so ties go to the lower id).
+// The second kernel runs one workgroup per token and ranks the selection keys
+// by counting (no sequential arg-max rounds).
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kSub = 64;  // inputs staged in LDS per step
-
-// partial[c][t][e] = sum over i in [256c, 256c + 256) of Wr[e][i] * x[t][i].
-// Block: 256 threads as a 16 x 16 grid, each thread PE x PT outputs.
-template <int TE, int TT>
+// partial[c][t][e] = sum over i in [256c, 256c + 256) of Wr[e][i] * x[t][i],
+// one fmaf chain per output in ascending i (the same chain in every variant).
+// Block: 256 threads as a 16 x 16 grid, each thread PE x PT outputs; kSub
+// inputs are staged in LDS per step (the whole 256-chunk for the small tile,
+// so a decode launch makes one trip to memory).
+template <int TE, int TT, int kSub>
 __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ x,
                                                             const float* __restrict__ wr,
                                                             int T, int d, int E,
@@ -83,17 +83,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     }
 }
 
-__device__ inline unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned lo = __shfl_xor((unsigned)(v & 0xffffffffu), o, kWave);
-    const unsigned hi = __shfl_xor((unsigned)(v >> 32), o, kWave);
-    const unsigned long long u = ((unsigned long long)hi << 32) | lo;
-    v = u > v ? u : v;
-  }
-  return v;
-}
-
 __device__ inline float wave_max_f(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
@@ -112,105 +101,104 @@ __device__ inline unsigned ordered_bits(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// One wavefront per token; NPL experts per lane (e = lane + 64 m).
-template <int NPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial,
-                                                          int nchunk,
-                                                          const float* __restrict__ bias,
-                                                          int T, int E, int k, int router,
-                                                          float scale, int32_t* __restrict__ idx,
-                                                          float* __restrict__ w) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;
-
-  float score[NPL];
-  unsigned long long key[NPL];
+// One workgroup per token.  Each thread owns EPT experts (e = tid + 256 m):
+// it adds the logit slices in order, forms the score and the selection key
+// (fp32 bits made order-preserving, then the inverted expert id, so ties go to
+// the lower id), and counts how many keys in LDS beat its own; a rank below k
+// is the expert's output slot.  Weights are scale * s_j / sum_j s_j with the
+// sum taken in slot order.
+template <int EPT>
+__global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ partial,
+                                                            int nchunk,
+                                                            const float* __restrict__ bias,
+                                                            int T, int E, int k, int router,
+                                                            float scale,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ w) {
+  __shared__ unsigned long long keys[256 * EPT];
+  __shared__ float red[4];
+  __shared__ float sel_s[kMaxK];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  float sc[EPT];
+  unsigned long long key[EPT];
 #pragma unroll
-  for (int m = 0; m < NPL; ++m) {
-    const int e = lane + kWave * m;
+  for (int m = 0; m < EPT; ++m) {
+    const int e = tid + 256 * m;
     float l = 0.0f;
     if (e < E) {
+#pragma unroll 4
       for (int c = 0; c < nchunk; ++c) l += partial[((size_t)c * T + t) * E + e];
     }
-    score[m] = l;
+    sc[m] = l;
   }
-  if (router == 0) {  // sigmoid + selection bias
+  if (router == 0) {
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-      const int e = lane + kWave * m;
-      const float s = 1.0f / (1.0f + expf(-score[m]));
-      score[m] = s;
-      const float kap = s + (bias ? bias[e < E ? e : 0] : 0.0f);
-      key[m] = e < E ? ((unsigned long long)ordered_bits(kap) << 32) | (0xffffffffu - (unsigned)e)
-                     : 0ull;
+    for (int m = 0; m < EPT; ++m) {
+      const int e = tid + 256 * m;
+      const float s = 1.0f / (1.0f + expf(-sc[m]));
+      sc[m] = s;
+      const float kap = s + (bias && e < E ? bias[e] : 0.0f);
+      key[m] = ((unsigned long long)ordered_bits(kap) << 32) | (0xffffffffu - (unsigned)e);
     }
-  } else {  // softmax over all E
+  } else {
     float mx = -INFINITY;
 #pragma unroll
-    for (int m = 0; m < NPL; ++m)
-      if (lane + kWave * m < E) mx = fmaxf(mx, score[m]);
+    for (int m = 0; m < EPT; ++m)
+      if (tid + 256 * m < E) mx = fmaxf(mx, sc[m]);
     mx = wave_max_f(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
     float z = 0.0f;
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-      const int e = lane + kWave * m;
-      const float p = e < E ? expf(score[m] - mx) : 0.0f;
-      score[m] = p;
+    for (int m = 0; m < EPT; ++m) {
+      const float p = tid + 256 * m < E ? expf(sc[m] - mx) : 0.0f;
+      sc[m] = p;
       z += p;
     }
     z = wave_sum_f(z);
+    if (lane == 0) red[wave] = z;
+    __syncthreads();
+    z = (red[0] + red[1]) + (red[2] + red[3]);
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-      const int e = lane + kWave * m;
-      const float p = score[m] / z;
-      score[m] = p;
-      key[m] = e < E ? ((unsigned long long)ordered_bits(p) << 32) | (0xffffffffu - (unsigned)e)
-                     : 0ull;
-    }
-  }
-
-  float sel_s[kMaxK];
-  int sel_e[kMaxK];
-  float denom = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    sel_s[j] = 0.0f;
-    sel_e[j] = 0;
-    if (j < k) {
-      unsigned long long best = 0ull;
-#pragma unroll
-      for (int m = 0; m < NPL; ++m) best = key[m] > best ? key[m] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xffffffffu - (unsigned)(best & 0xffffffffu));
-      const int owner = e & (kWave - 1), mm = e / kWave;
-      float s_own = 0.0f;
-#pragma unroll
-      for (int m = 0; m < NPL; ++m)
-        if (lane == owner && m == mm) {
-          s_own = score[m];
-          key[m] = 0ull;
-        }
-      const float s = __shfl(s_own, owner, kWave);
-      sel_s[j] = s;
-      sel_e[j] = e;
-      denom += s;
+    for (int m = 0; m < EPT; ++m) {
+      const int e = tid + 256 * m;
+      const float p = sc[m] / z;
+      sc[m] = p;
+      key[m] = ((unsigned long long)ordered_bits(p) << 32) | (0xffffffffu - (unsigned)e);
     }
   }
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j < k && lane == j) {
-      idx[(size_t)t * k + j] = sel_e[j];
-      w[(size_t)t * k + j] = scale * (sel_s[j] / denom);
+  for (int m = 0; m < EPT; ++m) keys[tid + 256 * m] = tid + 256 * m < E ? key[m] : 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) {
+    const int e = tid + 256 * m;
+    if (e >= E) continue;
+    int rank = 0;
+#pragma unroll 16
+    for (int q = 0; q < E; ++q) rank += keys[q] > key[m] ? 1 : 0;
+    if (rank < k) {
+      idx[(size_t)t * k + rank] = e;
+      sel_s[rank] = sc[m];
     }
+  }
+  __syncthreads();
+  if (tid < k) {
+    float denom = 0.0f;
+    for (int j = 0; j < k; ++j) denom += sel_s[j];
+    w[(size_t)t * k + tid] = scale * (sel_s[tid] / denom);
+  }
 }
 
-template <int NPL>
-hipError_t launch_topk(const float* partial, int nchunk, const float* bias, int T, int E, int k,
-                       int router, float scale, int32_t* idx, float* w, hipStream_t s) {
-  dim3 grid((T + 3) / 4);
-  hipLaunchKernelGGL(router_topk_kernel<NPL>, grid, dim3(256), 0, s, partial, nchunk, bias, T,
-                     E, k, router, scale, idx, w);
+template <int EPT>
+hipError_t launch_select(const float* partial, int nchunk, const float* bias, int T, int E, int k,
+                         int router, float scale, int32_t* idx, float* w, hipStream_t s) {
+  TimedLaunch tl(K_ROUTER_TOPK, s);
+  hipLaunchKernelGGL(router_select_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, bias,
+                     T, E, k, router, scale, idx, w);
   return hipGetLastError();
 }
 
@@ -220,23 +208,23 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
+  {
+  TimedLaunch tl(K_ROUTER_LOGITS, s);
   if (T <= 32) {
     dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
-    hipLaunchKernelGGL((router_logits_kernel<16, 16>), grid, dim3(256), 0, s, x, wr, T, d, E,
-                       partial);
+    hipLaunchKernelGGL((router_logits_kernel<16, 16, 256>), grid, dim3(256), 0, s, x, wr, T, d,
+                       E, partial);
   } else {
     dim3 grid((E + 63) / 64, (T + 63) / 64, nchunk);
-    hipLaunchKernelGGL((router_logits_kernel<64, 64>), grid, dim3(256), 0, s, x, wr, T, d, E,
-                       partial);
+    hipLaunchKernelGGL((router_logits_kernel<64, 64, 64>), grid, dim3(256), 0, s, x, wr, T, d,
+                       E, partial);
+  }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int npl = (E + kWave - 1) / kWave;
-  if (npl <= 1) return launch_topk<1>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
-  if (npl <= 2) return launch_topk<2>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
-  if (npl <= 4) return launch_topk<4>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
-  if (npl <= 8) return launch_topk<8>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
-  return launch_topk<16>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
+  if (E <= 256) return launch_select<1>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
+  if (E <= 512) return launch_select<2>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
+  return launch_select<4>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
 }
 
 }  // namespace moe

@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-from .binding import (Context, DeviceExperts, MOE_ACT_SILU, ROUTER)
+from .binding import (Context, DeviceExperts, MOE_ACT_SILU, ROUTER, moe_layer, moe_weights)
 
 
 class MoELayer:
@@ -28,15 +28,23 @@ class MoELayer:
         self.E, self.d = experts.n_experts, experts.d
         self.device = w_router.device
         self._T = None
+        self._fused_T = None
+        self.desc = moe_layer(self.router, k, self.scale, w_router.data_ptr(),
+                              bias.data_ptr() if bias is not None else None, experts.struct(),
+                              shared.struct() if shared is not None else moe_weights())
 
     @staticmethod
-    def from_inputs(ctx: Context, inputs, device="cuda:0") -> "MoELayer":
-        """Upload a synth.LayerInputs."""
+    def from_inputs(ctx: Context, inputs, device="cuda:0", tiled: bool = True) -> "MoELayer":
+        """Upload a synth.LayerInputs; quantised codes go to the tiled layout unless
+        tiled=False."""
         s = inputs.spec
         wr = torch.from_numpy(inputs.wr).to(device)
         bias = torch.from_numpy(inputs.bias).to(device) if inputs.bias is not None else None
         ex = DeviceExperts.upload(inputs.experts, device)
         sh = DeviceExperts.upload(inputs.shared, device) if inputs.shared is not None else None
+        if tiled:
+            ex = ex.tiled(ctx)
+            sh = sh.tiled(ctx) if sh is not None else None
         return MoELayer(ctx, s.router, s.k, s.scale, wr, bias, ex, sh)
 
     def with_weights(self, experts: DeviceExperts, shared: Optional[DeviceExperts]) -> "MoELayer":
@@ -82,6 +90,20 @@ class MoELayer:
         y = self.y if out is None else out
         c.moe_combine(self.rows, self.token_row, self.w, self.sh_out, residual, T, k, d, y,
                       stream)
+        return y
+
+    def forward_fused(self, x: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                      stream=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The same layer through the single moe_forward call."""
+        T, d = x.shape
+        self.alloc(T)
+        if self._fused_T != T:
+            need = self.ctx.moe_layer_workspace_size(self.desc, T)
+            self.fws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._fused_T = T
+        y = self.y if out is None else out
+        self.ctx.moe_forward(self.desc, MOE_ACT_SILU, x, T, residual, y, self.idx, self.w,
+                             self.fws, stream)
         return y
 
     __call__ = forward

@@ -46,14 +46,14 @@ def ctx(gpu):
 _LAYERS = {}
 
 
-def device_layer(ctx, name, **kw):
+def device_layer(ctx, name, tiled=True, **kw):
     import torch
     from sparse_moe_expert_sigmoid_amd import MoELayer
-    key = (name, tuple(sorted(kw.items())))
+    key = (name, tiled, tuple(sorted(kw.items())))
     if key not in _LAYERS:
         _LAYERS.clear()
         torch.cuda.empty_cache()
-        _LAYERS[key] = MoELayer.from_inputs(ctx, inputs(name, **kw))
+        _LAYERS[key] = MoELayer.from_inputs(ctx, inputs(name, **kw), tiled=tiled)
     return _LAYERS[key]
 
 
@@ -241,11 +241,11 @@ def test_combine_parity(ctx, T, k, d, with_shared, with_res):
 
 # ------------------------------------------------------------------ whole layer
 
-def _layer_vs_oracle(ctx, name, tokens=None, **kw):
+def _layer_vs_oracle(ctx, name, tokens=None, tiled=True, **kw):
     import torch
     inp = inputs(name, **kw)
     s = inp.spec
-    L = device_layer(ctx, name, **kw)
+    L = device_layer(ctx, name, tiled=tiled, **kw)
     xd = to_dev(inp.x)
     y = L(xd)
     torch.cuda.synchronize()
@@ -269,6 +269,55 @@ def _layer_vs_oracle(ctx, name, tokens=None, **kw):
 def test_layer_parity(ctx, name):
     print(f"[layer] {name}", flush=True)
     _layer_vs_oracle(ctx, name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_decode", "qwen_prefill"])
+def test_layer_parity_row_layout(ctx, name):
+    _layer_vs_oracle(ctx, name, tiled=False)
+
+
+def _tile_reference(codes_rows, fmt):
+    """Byte order of the tiled layout, written from its definition in include/moe.h."""
+    N, nbytes = codes_rows.shape
+    out = np.empty(N * nbytes, np.uint8)
+    pos = 0
+    if fmt == "int8_row":
+        K = nbytes
+        for n16 in range(N // 16):
+            for st in range(K // 64):
+                for lane in range(64):
+                    i, g = lane % 16, lane // 16
+                    out[pos:pos + 16] = codes_rows[16 * n16 + i, 64 * st + 16 * g:64 * st + 16 * g + 16]
+                    pos += 16
+    else:
+        K = 2 * nbytes
+        for n16 in range(N // 16):
+            for sp in range(K // 128):
+                for lane in range(64):
+                    i, g = lane % 16, lane // 16
+                    for q in range(4):          # the span's 4 blocks of 32
+                        b = 4 * sp + q
+                        o = (32 * b + 8 * g) // 2
+                        out[pos:pos + 4] = codes_rows[16 * n16 + i, o:o + 4]
+                        pos += 4
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["int8_row", "int4_b32"])
+def test_tile_weights_layout(ctx, fmt):
+    import torch
+    from sparse_moe_expert_sigmoid_amd.binding import DeviceExperts
+    E, d, I = 2, 256, 128
+    w = S.make_experts(fmt, E, d, I, 31, (4, 5, 6, 7, 12, 13))
+    dev = DeviceExperts.upload(w, "cuda:0")
+    t = dev.tiled(ctx)
+    torch.cuda.synchronize()
+    gu_rows = (w.gu_packed if fmt == "int4_b32" else w.gu.view(np.uint8)).reshape(E * 2 * I, -1)
+    dn_rows = (w.dn_packed if fmt == "int4_b32" else w.dn.view(np.uint8)).reshape(E * d, -1)
+    got_gu = t.w_gate_up.cpu().numpy().view(np.uint8).reshape(-1)
+    got_dn = t.w_down.cpu().numpy().view(np.uint8).reshape(-1)
+    assert np.array_equal(got_gu, _tile_reference(np.ascontiguousarray(gu_rows), fmt))
+    assert np.array_equal(got_dn, _tile_reference(np.ascontiguousarray(dn_rows), fmt))
 
 
 def test_layer_parity_kimi_prefill_sampled(ctx):
@@ -328,6 +377,61 @@ def test_layer_determinism(ctx):
     b = L(xd).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ moe_forward (one call)
+
+def _forward_vs_oracle(ctx, name, tokens=None, residual=False, **kw):
+    import torch
+    inp = inputs(name, **kw)
+    s = inp.spec
+    L = device_layer(ctx, name, **kw)
+    xd = to_dev(inp.x)
+    res = S.normal(0x5EED, 9, (s.T, s.d), 1.0) if residual else None
+    y = L.forward_fused(xd, residual=to_dev(res) if residual else None)
+    torch.cuda.synchronize()
+    gy = y.cpu().numpy()
+    oy, oidx, ow, ogap = oracle.layer_of(inp, tokens=tokens)
+    sel = np.arange(s.T) if tokens is None else np.asarray(tokens)
+    if residual:
+        oy = oy + res[sel].astype(np.float64)
+    _, _, _, logits = oracle.route(s.router, inp.x[sel], inp.wr, inp.bias, s.k, s.scale,
+                                   want_logits=True)
+    keys = oracle_keys(s.router, logits, inp.bias)
+    exc = compare_route(L.idx.cpu().numpy()[sel], L.w.cpu().numpy()[sel], oidx, ow, ogap, keys,
+                        s.scale)
+    keep = np.setdiff1d(np.arange(len(sel)), exc)
+    ratio = compare_outputs(gy[sel], oy, keep)
+    _log(test="forward", config=name, T=s.T, checked_tokens=len(sel), excused=len(exc),
+         err_over_max=ratio, residual=residual)
+
+
+@pytest.mark.parametrize("name", ["tiny", "kimi_decode", "qwen_decode", "qwen_prefill"])
+def test_forward_parity(ctx, name):
+    _forward_vs_oracle(ctx, name)
+
+
+def test_forward_kimi_prefill_sampled_with_residual(ctx):
+    tokens = np.unique(np.concatenate([np.arange(3, 1024, 53), [0, 1023]]))
+    _forward_vs_oracle(ctx, "kimi_prefill", tokens=tokens, residual=True)
+
+
+def test_forward_matches_staged_router_outputs(ctx):
+    import torch
+    inp = inputs("kimi_decode")
+    L = device_layer(ctx, "kimi_decode")
+    xd = to_dev(inp.x)
+    L(xd)
+    torch.cuda.synchronize()
+    idx_a, w_a = L.idx.clone(), L.w.clone()
+    L.forward_fused(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, L.idx) and torch.equal(w_a, L.w)
+
+
+def test_forward_ragged_and_single_token(ctx):
+    _forward_vs_oracle(ctx, "tiny", T=37, xseed=0x4D6F4599)
+    _forward_vs_oracle(ctx, "tiny", T=1, xseed=0x4D6F4598)
 
 
 # ------------------------------------------------------------------ errors through the ABI
