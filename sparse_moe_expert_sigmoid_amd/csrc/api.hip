@@ -17,7 +17,8 @@ namespace moe {
 const char* const kKernelNames[K_COUNT] = {
     "router_logits", "router_topk",     "permute",         "fill",
     "encode_rows",   "ffn_i8_gate_up",  "ffn_i8_down",     "ffn_i4_gate_up",
-    "ffn_i4_down",   "ffn_f32_gate_up", "ffn_f32_down",    "combine"};
+    "ffn_i4_down",   "ffn_f32_gate_up", "ffn_f32_down",    "combine",
+    "router_tail"};
 
 // Event pairs recorded around launches while a context has timing on.
 struct KernelTimer {
@@ -65,6 +66,7 @@ struct moe_ctx {
   char err[512];
   bool timing;
   moe::KernelTimer timer;
+  unsigned* ticket;  // device counter for last-workgroup hand-offs; zero between launches
 };
 
 namespace {
@@ -219,6 +221,21 @@ moe_status moe_create(int device, moe_ctx** out) {
   snprintf(ctx->arch, sizeof(ctx->arch), "%s", prop.gcnArchName);
   ctx->err[0] = '\0';
   ctx->timing = false;
+  ctx->ticket = nullptr;
+  {
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    e = hipSetDevice(device);
+    if (e == hipSuccess) e = hipMalloc(&ctx->ticket, 256);
+    if (e == hipSuccess) e = hipMemset(ctx->ticket, 0, 256);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (prev >= 0) (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+      if (ctx->ticket) (void)hipFree(ctx->ticket);
+      delete ctx;
+      return fail(nullptr, MOE_E_DEVICE, "moe_create: device counter: %s", hipGetErrorString(e));
+    }
+  }
   moe::set_device_info(ctx->cu_count);
   *out = ctx;
   return MOE_OK;
@@ -228,6 +245,10 @@ void moe_destroy(moe_ctx* ctx) {
   if (!ctx) return;
   if (moe::g_timer == &ctx->timer) moe::g_timer = nullptr;
   release_timer(ctx->timer);
+  if (ctx->ticket) {
+    DeviceGuard g(ctx->device);
+    (void)hipFree(ctx->ticket);
+  }
   delete ctx;
 }
 
@@ -525,16 +546,27 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
   const int E = L->experts.n_experts, d = L->experts.d, k = L->k, R = T * k;
   int32_t* idx = topk_idx ? topk_idx : f.idx;
   float* w = topk_w ? topk_w : f.w;
-  hipError_t e = moe::launch_router(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale,
-                                    idx, w, f.partial, s);
-  if (e == hipSuccess)
-    e = moe::launch_permute(idx, T, k, E, f.offsets, f.row_token, f.token_row, s);
-  if (e != hipSuccess) return device_result(ctx, e, "moe_forward");
   const bool has_sh = L->shared.n_experts > 0;
   const bool fused = has_sh && L->shared.fmt == L->experts.fmt &&
                      L->shared.layout == L->experts.layout && L->experts.fmt != MOE_W_FP32;
   const moe_weights& X = L->experts;
   const moe_weights& S = L->shared;
+  // small batches: router, x encoding and grouping in one launch
+  const bool small = T <= moe::kSmallT && X.fmt != MOE_W_FP32 && (fused || !has_sh);
+  hipError_t e;
+  if (small) {
+    int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
+    moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, fused ? 2 : 1, Rs, Is, true);
+    e = moe::launch_router_small(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale, idx,
+                                 w, f.partial, lay.xq, lay.xs, f.offsets, f.row_token,
+                                 f.token_row, ctx->ticket, s);
+  } else {
+    e = moe::launch_router(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale, idx, w,
+                           f.partial, s);
+    if (e == hipSuccess)
+      e = moe::launch_permute(idx, T, k, E, f.offsets, f.row_token, f.token_row, s);
+  }
+  if (e != hipSuccess) return device_result(ctx, e, "moe_forward");
   if (fused) {
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, 2, Rs, Is, true);
@@ -544,7 +576,7 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
         {S.fmt, S.layout, 1, S.inter, T, S.w_gate_up, S.s_gate_up, S.w_down, S.s_down, nullptr,
          nullptr,
          lay.hq[1], lay.hs[1], f.sh_rows}};
-    e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, false, s);
+    e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, small, s);
   } else {
     auto run = [&](const moe_weights& W, int Ew, int Rw, const int32_t* rt, const int32_t* of,
                    float* out) -> hipError_t {
@@ -559,7 +591,8 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
       moe::FfnSet set{W.fmt, W.layout, Ew, W.inter, Rw, W.w_gate_up, W.s_gate_up, W.w_down,
                       W.s_down, rt,
                       of, lay.hq[0], lay.hs[0], out};
-      return moe::launch_ffn_quant(&set, 1, d, x, T, lay, false, s);
+      // x was encoded by the small-batch router when only routed experts run here
+      return moe::launch_ffn_quant(&set, 1, d, x, T, lay, small && &W == &X, s);
     };
     e = run(X, E, R, f.row_token, f.offsets, f.rows);
     if (e == hipSuccess && has_sh) e = run(S, 1, T, nullptr, nullptr, f.sh_rows);

@@ -38,60 +38,13 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// ------------------------------------------------------------------ digits
-// p such that max|v| * 2^p lies in (63.5, 127]; 0 for an all-zero set.
-__device__ inline int digit_exponent(float m) {
-  if (!(m > 0.0f)) return 0;
-  int ex;
-  frexpf(m, &ex);  // m = f * 2^ex, f in [0.5, 1)
-  int p = 7 - ex;
-  if (ldexpf(m, p) > 127.0f) p -= 1;
-  return p;
-}
-
-// v * 2^p = d0 + d1/256 (+ error <= 2^-9), both digits in [-127, 127].
-__device__ inline void two_digits(float v, int p, int& d0, int& d1) {
-  const float a = ldexpf(v, p);
-  float f0 = fminf(fmaxf(rintf(a), -127.0f), 127.0f);
-  float f1 = fminf(fmaxf(rintf((a - f0) * 256.0f), -127.0f), 127.0f);
-  d0 = (int)f0;
-  d1 = (int)f1;
-}
-
-__device__ inline unsigned pack4(int a, int b, int c, int d) {
-  return (unsigned)(a & 0xff) | ((unsigned)(b & 0xff) << 8) | ((unsigned)(c & 0xff) << 16) |
-         ((unsigned)(d & 0xff) << 24);
-}
-
-// One wavefront per row: q[r] = [d0 digits (K) | d1 digits (K)], sig[r] = 2^-p.
+// One wavefront per row (see encode_row).
 __global__ __launch_bounds__(256) void encode_rows_kernel(const float* __restrict__ v, int n,
                                                           int K, int8_t* __restrict__ q,
                                                           float* __restrict__ sig) {
-  const int lane = threadIdx.x & (kWave - 1);
   const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (r >= n) return;
-  const float* row = v + (size_t)r * K;
-  float m = 0.0f;
-  for (int c = lane; c < K / 4; c += kWave) {
-    const float4 a = *reinterpret_cast<const float4*>(row + 4 * c);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-  const int p = digit_exponent(m);
-  unsigned* q0 = reinterpret_cast<unsigned*>(q + (size_t)r * 2 * K);
-  unsigned* q1 = reinterpret_cast<unsigned*>(q + (size_t)r * 2 * K + K);
-  for (int c = lane; c < K / 4; c += kWave) {
-    const float4 a = *reinterpret_cast<const float4*>(row + 4 * c);
-    int x0, y0, x1, y1, x2, y2, x3, y3;
-    two_digits(a.x, p, x0, y0);
-    two_digits(a.y, p, x1, y1);
-    two_digits(a.z, p, x2, y2);
-    two_digits(a.w, p, x3, y3);
-    q0[c] = pack4(x0, x1, x2, x3);
-    q1[c] = pack4(y0, y1, y2, y3);
-  }
-  if (lane == 0) sig[r] = m > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+  encode_row(v + (size_t)r * K, K, q + (size_t)r * 2 * K, sig + r);
 }
 
 // ------------------------------------------------------------------ work items
@@ -208,7 +161,7 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 16 : 1];
   Job job;
   if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
-  const Group& G = job.g == 0 ? g0 : g1;
+  const Group G = job.g == 0 ? g0 : g1;
   if ((int)blockIdx.x * 64 >= G.inter) return;
   const int I = G.inter;
   const int ldr = 2 * d + 16;
@@ -390,7 +343,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 4 : 1];
   Job job;
   if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
-  const Group& G = job.g == 0 ? g0 : g1;
+  const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
   const int ldr = 2 * I + 16;
   const int nhb = I / 64;
@@ -418,7 +371,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
     const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
     const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g,
                                             lane);
-    constexpr int U = 4;
+    constexpr int U = KS == 1 ? 8 : 4;  // one weight stream per wavefront: 8 KB in flight
     for (int s = s_beg; s < s_end; s += U) {
       v4i ra[U], x0[U], x1[U];
       float sg[U];
@@ -504,6 +457,290 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   }
   *reinterpret_cast<float4*>(G.out + (size_t)r * d + c0 + 4 * g) =
       make_float4(res[0], res[1], res[2], res[3]);
+}
+
+// ------------------------------------------------------------------ prefill GEMM
+// Many rows per expert: a tile is up to 64 rows (4 groups of 16); a
+// workgroup of 8 wavefronts owns 128 output columns (16 per wavefront) of one
+// tile.  The tile's activation digits are staged in LDS 256 inputs at a time
+// (double-buffered) and shared by the 8 wavefronts; each wavefront streams its
+// weight rows and runs 4 row groups x 2 digits MFMAs per weight fragment, so
+// every weight byte read from HBM feeds up to 64 rows.  Software pipeline per
+// chunk c: weight fragments of chunk c+1 and the activation digits of chunk
+// c+1 are loaded into registers, chunk c is computed, the digits go to the
+// other LDS buffer, one barrier.
+constexpr int kGemmRows = 64, kGemmChunk = 256, kGemmWaves = 8;
+constexpr int kGemmLdr = 2 * kGemmChunk + 16;              // LDS bytes per staged row
+constexpr int kGemmStage = kGemmRows * 32 / (kGemmWaves * kWave);  // 16-B pieces per thread
+
+// Loads (into registers) this thread's pieces of the digit rows of one chunk:
+// piece q = tid + 512 u covers row q/32, digit (q%32)/16, bytes 16*(q%16).
+struct StageRegs {
+  v4i v[kGemmStage];
+};
+
+__device__ inline void stage_load(StageRegs& st, const int8_t* __restrict__ base, int rowbytes,
+                                  int plane, const int* rows, int nr, int k0, int nst) {
+#pragma unroll
+  for (int u = 0; u < kGemmStage; ++u) {
+    const int q = threadIdx.x + u * kGemmWaves * kWave;
+    const int j = q >> 5, c = q & 31;
+    st.v[u] = v4i{0, 0, 0, 0};
+    if (j < nr && 16 * (c & 15) < nst * kKStep)
+      st.v[u] = *reinterpret_cast<const v4i*>(base + (size_t)rows[j] * rowbytes +
+                                              (c < 16 ? 0 : plane) + k0 + 16 * (c & 15));
+  }
+}
+
+__device__ inline void stage_store(const StageRegs& st, int8_t* buf) {
+#pragma unroll
+  for (int u = 0; u < kGemmStage; ++u) {
+    const int q = threadIdx.x + u * kGemmWaves * kWave;
+    const int j = q >> 5, c = q & 31;
+    *reinterpret_cast<v4i*>(buf + j * kGemmLdr + (c < 16 ? 0 : kGemmChunk) + 16 * (c & 15)) =
+        st.v[u];
+  }
+}
+
+template <int LAY>
+__global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, int d,
+                                                           const int8_t* __restrict__ xq,
+                                                           const float* __restrict__ xs) {
+  __shared__ __attribute__((aligned(16))) int8_t bsm[2][kGemmRows * kGemmLdr];
+  __shared__ float red_max[kGemmWaves][kGemmRows];
+  __shared__ int tok_sm[kGemmRows];
+  Job job;
+  if (!find_job(g0, g1, kGemmRows, blockIdx.y, job)) return;
+  const Group G = job.g == 0 ? g0 : g1;
+  const int I = G.inter;
+  if ((int)blockIdx.x * 128 >= I) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int c0 = blockIdx.x * 128 + wave * 16;
+  const bool active = c0 < I;  // every wavefront stays for the barriers
+  const int i = lane & 15, g = lane >> 4;
+  const int ntg = (job.nr + 15) / 16;
+  for (int j = threadIdx.x; j < kGemmRows; j += blockDim.x)
+    tok_sm[j] = j < job.nr ? (G.row_token ? G.row_token[job.r0 + j] : job.r0 + j) : 0;
+  __syncthreads();
+
+  const size_t row0 = (size_t)job.e * 2 * I + (active ? c0 : 0);
+  const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wgu), row0, d, i, g, lane);
+  const int8_t* wb = wa + (size_t)I * d;
+  v4i acc[4][4];  // [row group][gate d0, gate d1, up d0, up d1]
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[t][q] = v4i{0, 0, 0, 0};
+
+  const int nchunk = (d + kGemmChunk - 1) / kGemmChunk;
+  v4i ra[4], rb[4];
+  {
+    const int nst = min(kGemmChunk, d) / kKStep;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = i8_load<LAY>(wa, min(u, nst - 1));
+      rb[u] = i8_load<LAY>(wb, min(u, nst - 1));
+    }
+    StageRegs st;
+    stage_load(st, xq, 2 * d, d, tok_sm, job.nr, 0, nst);
+    stage_store(st, bsm[0]);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nchunk; ++c) {
+    const int k0 = c * kGemmChunk;
+    const int nst = min(kGemmChunk, d - k0) / kKStep;
+    const bool more = c + 1 < nchunk;
+    const int k1 = k0 + kGemmChunk;
+    const int nst1 = more ? min(kGemmChunk, d - k1) / kKStep : 1;
+    v4i na[4], nb[4];
+    StageRegs st;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        na[u] = i8_load<LAY>(wa, k1 / kKStep + min(u, nst1 - 1));
+        nb[u] = i8_load<LAY>(wb, k1 / kKStep + min(u, nst1 - 1));
+      }
+      stage_load(st, xq, 2 * d, d, tok_sm, job.nr, k1, nst1);
+    }
+    const int8_t* buf = bsm[c & 1];
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < nst) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (t < ntg) {
+              const int8_t* brow = buf + (16 * t + i) * kGemmLdr;
+              const v4i x0 = *reinterpret_cast<const v4i*>(brow + 64 * u + 16 * g);
+              const v4i x1 = *reinterpret_cast<const v4i*>(brow + kGemmChunk + 64 * u + 16 * g);
+              acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0, acc[t][0], 0, 0, 0);
+              acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1, acc[t][1], 0, 0, 0);
+              acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0, acc[t][2], 0, 0, 0);
+              acc[t][3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1, acc[t][3], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    if (more) {
+      stage_store(st, bsm[(c + 1) & 1]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ra[u] = na[u];
+        rb[u] = nb[u];
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: h per row group, one scale per row and 64-column half
+  const float* se = G.sgu + (size_t)job.e * 2 * I;
+  float h[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = 16 * t + i;
+    const bool rv = active && t < ntg && j < job.nr;
+    const float sig = rv ? xs[tok_sm[j]] : 0.0f;
+    float mx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int n = c0 + 4 * g + c;
+      const float gt = rv ? se[n] * sig * ((float)acc[t][0][c] + (float)acc[t][1][c] * (1.0f / 256.0f)) : 0.0f;
+      const float upv = rv ? se[I + n] * sig * ((float)acc[t][2][c] + (float)acc[t][3][c] * (1.0f / 256.0f)) : 0.0f;
+      h[t][c] = silu_f(gt) * upv;
+      mx = fmaxf(mx, fabsf(h[t][c]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    if (g == 0) red_max[wave][j] = mx;
+  }
+  __syncthreads();
+  if (!active) return;
+  const int half = wave >> 2;  // 64-column scale block inside the 128 columns
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = 16 * t + i;
+    if (t >= ntg || j >= job.nr) continue;
+    float mx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_max[4 * half + w][j]);
+    const int p = digit_exponent(mx);
+    int d0[4], d1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) two_digits(h[t][c], p, d0[c], d1[c]);
+    const int r = job.r0 + j;
+    int8_t* hrow = G.hq + (size_t)r * 2 * I;
+    const int col = c0 + 4 * g;
+    *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
+    *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
+    if ((wave & 3) == 0 && g == 0)
+      G.hs[(size_t)r * (I / 64) + blockIdx.x * 2 + half] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+  }
+}
+
+template <int LAY>
+__global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int d) {
+  __shared__ __attribute__((aligned(16))) int8_t bsm[2][kGemmRows * kGemmLdr];
+  __shared__ float ssm[2][kGemmRows][kGemmChunk / kKStep];
+  __shared__ int row_sm[kGemmRows];
+  Job job;
+  if (!find_job(g0, g1, kGemmRows, blockIdx.y, job)) return;
+  const Group G = job.g == 0 ? g0 : g1;
+  const int I = G.inter;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int c0 = blockIdx.x * 128 + wave * 16;
+  const bool active = c0 < d;
+  const int i = lane & 15, g = lane >> 4;
+  const int ntg = (job.nr + 15) / 16;
+  const int nhb = I / 64;
+  for (int j = threadIdx.x; j < kGemmRows; j += blockDim.x) row_sm[j] = job.r0 + j;
+  const size_t row0 = (size_t)job.e * d + (active ? c0 : 0);
+  const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g, lane);
+  float acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[t][c] = 0.0f;
+  const v4i zero = {0, 0, 0, 0};
+  __syncthreads();
+
+  // per-chunk block scales: thread q < nr*4 holds row q/4, block q%4
+  const float* hs_base = G.hs;
+  const int r0 = job.r0, nr = job.nr;
+#define SCALE_LOAD(K0, NST)                                                          \
+  ((threadIdx.x < (unsigned)(nr * 4) && (int)(threadIdx.x & 3) < (NST))              \
+       ? hs_base[(size_t)(r0 + (threadIdx.x >> 2)) * nhb + (K0) / kKStep + (threadIdx.x & 3)] \
+       : 0.0f)
+  const int nchunk = (I + kGemmChunk - 1) / kGemmChunk;
+  v4i ra[4];
+  {
+    const int nst = min(kGemmChunk, I) / kKStep;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ra[u] = i8_load<LAY>(wa, min(u, nst - 1));
+    StageRegs st;
+    stage_load(st, G.hq, 2 * I, I, row_sm, job.nr, 0, nst);
+    const float sv = SCALE_LOAD(0, nst);
+    stage_store(st, bsm[0]);
+    if (threadIdx.x < kGemmRows * 4) ssm[0][threadIdx.x >> 2][threadIdx.x & 3] = sv;
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nchunk; ++c) {
+    const int k0 = c * kGemmChunk;
+    const int nst = min(kGemmChunk, I - k0) / kKStep;
+    const bool more = c + 1 < nchunk;
+    const int k1 = k0 + kGemmChunk;
+    const int nst1 = more ? min(kGemmChunk, I - k1) / kKStep : 1;
+    v4i na[4];
+    StageRegs st;
+    float sv = 0.0f;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) na[u] = i8_load<LAY>(wa, k1 / kKStep + min(u, nst1 - 1));
+      stage_load(st, G.hq, 2 * I, I, row_sm, job.nr, k1, nst1);
+      sv = SCALE_LOAD(k1, nst1);
+    }
+    const int8_t* buf = bsm[c & 1];
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < nst) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (t < ntg) {
+              const int8_t* brow = buf + (16 * t + i) * kGemmLdr;
+              const v4i x0 = *reinterpret_cast<const v4i*>(brow + 64 * u + 16 * g);
+              const v4i x1 = *reinterpret_cast<const v4i*>(brow + kGemmChunk + 64 * u + 16 * g);
+              const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0, zero, 0, 0, 0);
+              const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1, zero, 0, 0, 0);
+              const float sg = ssm[c & 1][16 * t + i][u];
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[t][q] = fmaf(sg, fmaf((float)p1[q], 1.0f / 256.0f, (float)p0[q]), acc[t][q]);
+            }
+          }
+        }
+      }
+    }
+    if (more) {
+      stage_store(st, bsm[(c + 1) & 1]);
+      if (threadIdx.x < kGemmRows * 4) ssm[(c + 1) & 1][threadIdx.x >> 2][threadIdx.x & 3] = sv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ra[u] = na[u];
+    }
+    __syncthreads();
+  }
+#undef SCALE_LOAD
+  if (!active) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = 16 * t + i;
+    if (t >= ntg || j >= job.nr) continue;
+    const float* sd = G.sdn + (size_t)job.e * d + c0 + 4 * g;
+    *reinterpret_cast<float4*>(G.out + (size_t)(job.r0 + j) * d + c0 + 4 * g) =
+        make_float4(sd[0] * acc[t][0], sd[1] * acc[t][1], sd[2] * acc[t][2], sd[3] * acc[t][3]);
+  }
 }
 
 // ------------------------------------------------------------------ layout conversion
@@ -643,12 +880,46 @@ hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nr
   return hipGetLastError();
 }
 
+template <int LAY>
+hipError_t launch_gemm_pair(const Group& a, const Group& b, int d, const int8_t* xq,
+                            const float* xs, hipStream_t s) {
+  const int tiles = a.tiles + b.tiles;
+  const int imax = a.inter > b.inter ? a.inter : b.inter;
+  {
+    TimedLaunch tl(K_FFN_I8_GATE_UP, s);
+    hipLaunchKernelGGL(gate_up_gemm_kernel<LAY>, dim3((imax + 127) / 128, tiles), dim3(512), 0, s,
+                       a, b, d, xq, xs);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  TimedLaunch tl(K_FFN_I8_DOWN, s);
+  hipLaunchKernelGGL(down_gemm_kernel<LAY>, dim3((d + 127) / 128, tiles), dim3(512), 0, s, a, b,
+                     d);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
                             const FfnWs& ws, bool x_encoded, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (!x_encoded) {
     err = launch_encode_rows(x, T, d, ws.xq, ws.xs, s);
     if (err != hipSuccess) return err;
+  }
+  // int8 with many rows per expert: grouped GEMM tiles of 64 rows
+  if (sets[0].fmt == 1 && sets[0].R >= 16LL * sets[0].E) {
+    Group grp[2] = {};
+    for (int q = 0; q < nsets; ++q) {
+      const FfnSet& f = sets[q];
+      Group& G = grp[q];
+      G.E = f.E; G.inter = f.inter; G.R = f.R;
+      G.tiles = f.offsets ? max_tiles(f.R, f.E, kGemmRows) : (f.R + kGemmRows - 1) / kGemmRows;
+      G.wgu = f.wgu; G.sgu = f.sgu; G.wdn = f.wdn; G.sdn = f.sdn;
+      G.row_token = f.row_token; G.offsets = f.offsets;
+      G.hq = f.hq; G.hs = f.hs; G.out = f.out;
+    }
+    if (nsets < 2) grp[1].inter = grp[0].inter;
+    return sets[0].layout == 1 ? launch_gemm_pair<kTiled>(grp[0], grp[1], d, ws.xq, ws.xs, s)
+                               : launch_gemm_pair<kRows>(grp[0], grp[1], d, ws.xq, ws.xs, s);
   }
   // rows per tile: at most 16 (the MFMA N side); small batches use fewer so
   // that the staged activation rows take less LDS

@@ -95,7 +95,7 @@ inline int max_tiles(int R, int E, int mt) {
 enum KernelId {
   K_ROUTER_LOGITS, K_ROUTER_TOPK, K_PERMUTE, K_FILL, K_ENCODE_ROWS,
   K_FFN_I8_GATE_UP, K_FFN_I8_DOWN, K_FFN_I4_GATE_UP, K_FFN_I4_DOWN,
-  K_FFN_F32_GATE_UP, K_FFN_F32_DOWN, K_COMBINE, K_COUNT
+  K_FFN_F32_GATE_UP, K_FFN_F32_DOWN, K_COMBINE, K_ROUTER_TAIL, K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];
 
@@ -119,6 +119,15 @@ struct TimedLaunch {
 hipError_t launch_router(int router, const float* x, const float* wr, const float* bias, int T,
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s);
+// Up to kSmallT tokens: logits, then one launch for selection, x encoding
+// (xq/xs, see the FFN workspace) and the permutation; `ticket` is a zeroed
+// device counter that the launch leaves zeroed.
+constexpr int kSmallT = 16;
+hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
+                               int T, int d, int E, int k, float scale, int32_t* idx, float* w,
+                               float* partial, int8_t* xq, float* xs, int32_t* offsets,
+                               int32_t* row_token, int32_t* token_row, unsigned* ticket,
+                               hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
@@ -195,6 +204,60 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
 }
 
 __device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// ---- two-digit int8 encoding of fp32 activations (used by the FFN kernels)
+// v = 2^-p (d0 + d1/256) + e, |e| <= 2^-p / 512, d0, d1 in [-127, 127], with p
+// chosen per set of values so that max|v| * 2^p lies in (63.5, 127].
+// p such that max|v| * 2^p lies in (63.5, 127]; 0 for an all-zero set.
+__device__ inline int digit_exponent(float m) {
+  if (!(m > 0.0f)) return 0;
+  int ex;
+  frexpf(m, &ex);  // m = f * 2^ex, f in [0.5, 1)
+  int p = 7 - ex;
+  if (ldexpf(m, p) > 127.0f) p -= 1;
+  return p;
+}
+
+__device__ inline void two_digits(float v, int p, int& d0, int& d1) {
+  const float a = ldexpf(v, p);
+  const float f0 = fminf(fmaxf(rintf(a), -127.0f), 127.0f);
+  const float f1 = fminf(fmaxf(rintf((a - f0) * 256.0f), -127.0f), 127.0f);
+  d0 = (int)f0;
+  d1 = (int)f1;
+}
+
+__device__ inline unsigned pack4(int a, int b, int c, int d) {
+  return (unsigned)(a & 0xff) | ((unsigned)(b & 0xff) << 8) | ((unsigned)(c & 0xff) << 16) |
+         ((unsigned)(d & 0xff) << 24);
+}
+
+// One wavefront encodes one row of K values (K % 4 == 0): q = [d0 x K | d1 x K],
+// *sig = 2^-p (0 for an all-zero row).
+__device__ inline void encode_row(const float* __restrict__ row, int K, int8_t* __restrict__ q,
+                                  float* __restrict__ sig) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = 0.0f;
+  for (int c = lane; c < K / 4; c += kWave) {
+    const float4 a = *reinterpret_cast<const float4*>(row + 4 * c);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const int p = digit_exponent(m);
+  unsigned* q0 = reinterpret_cast<unsigned*>(q);
+  unsigned* q1 = reinterpret_cast<unsigned*>(q + K);
+  for (int c = lane; c < K / 4; c += kWave) {
+    const float4 a = *reinterpret_cast<const float4*>(row + 4 * c);
+    int x0, y0, x1, y1, x2, y2, x3, y3;
+    two_digits(a.x, p, x0, y0);
+    two_digits(a.y, p, x1, y1);
+    two_digits(a.z, p, x2, y2);
+    two_digits(a.w, p, x3, y3);
+    q0[c] = pack4(x0, x1, x2, x3);
+    q1[c] = pack4(y0, y1, y2, y3);
+  }
+  if (lane == 0) *sig = m > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+}
 
 #endif
 

@@ -101,12 +101,97 @@ __device__ inline unsigned ordered_bits(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// One workgroup per token.  Each thread owns EPT experts (e = tid + 256 m):
-// it adds the logit slices in order, forms the score and the selection key
-// (fp32 bits made order-preserving, then the inverted expert id, so ties go to
-// the lower id), and counts how many keys in LDS beat its own; a rank below k
-// is the expert's output slot.  Weights are scale * s_j / sum_j s_j with the
-// sum taken in slot order.
+// Selection for one token by a group of 256 threads (gtid = thread in the
+// group; every group of the workgroup calls this in step, also for tokens past
+// T with active = false, because it contains workgroup barriers).  Each thread
+// owns EPT experts (e = gtid + 256 m): it adds the logit slices in order, forms
+// the score and the selection key (fp32 bits made order-preserving, then the
+// inverted expert id, so ties go to the lower id), and counts how many keys in
+// LDS beat its own; a rank below k is the expert's output slot.  Weights are
+// scale * s_j / sum_j s_j with the sum taken in slot order.
+template <int EPT>
+__device__ inline void select_token(const float* __restrict__ partial, int nchunk,
+                                    const float* __restrict__ bias, int T, int E, int k,
+                                    int router, float scale, int t, bool active, int gtid,
+                                    unsigned long long* keys, float* red, float* sel_s,
+                                    int32_t* __restrict__ idx, float* __restrict__ w,
+                                    int* idx_lds) {
+  const int lane = gtid & (kWave - 1), wave = gtid / kWave;
+  float sc[EPT];
+  unsigned long long key[EPT];
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) {
+    const int e = gtid + 256 * m;
+    float l = 0.0f;
+    if (active && e < E) {
+#pragma unroll 4
+      for (int c = 0; c < nchunk; ++c) l += partial[((size_t)c * T + t) * E + e];
+    }
+    sc[m] = l;
+  }
+  if (router == 0) {
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+      const int e = gtid + 256 * m;
+      const float s = 1.0f / (1.0f + expf(-sc[m]));
+      sc[m] = s;
+      const float kap = s + (bias && e < E ? bias[e] : 0.0f);
+      key[m] = ((unsigned long long)ordered_bits(kap) << 32) | (0xffffffffu - (unsigned)e);
+    }
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < EPT; ++m)
+      if (gtid + 256 * m < E) mx = fmaxf(mx, sc[m]);
+    mx = wave_max_f(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float z = 0.0f;
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+      const float p = gtid + 256 * m < E ? expf(sc[m] - mx) : 0.0f;
+      sc[m] = p;
+      z += p;
+    }
+    z = wave_sum_f(z);
+    if (lane == 0) red[wave] = z;
+    __syncthreads();
+    z = (red[0] + red[1]) + (red[2] + red[3]);
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+      const int e = gtid + 256 * m;
+      const float p = sc[m] / z;
+      sc[m] = p;
+      key[m] = ((unsigned long long)ordered_bits(p) << 32) | (0xffffffffu - (unsigned)e);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) keys[gtid + 256 * m] = gtid + 256 * m < E ? key[m] : 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) {
+    const int e = gtid + 256 * m;
+    if (!active || e >= E) continue;
+    int rank = 0;
+#pragma unroll 16
+    for (int q = 0; q < E; ++q) rank += keys[q] > key[m] ? 1 : 0;
+    if (rank < k) {
+      idx[(size_t)t * k + rank] = e;
+      if (idx_lds) idx_lds[t * k + rank] = e;
+      sel_s[rank] = sc[m];
+    }
+  }
+  __syncthreads();
+  if (active && gtid < k) {
+    float denom = 0.0f;
+    for (int j = 0; j < k; ++j) denom += sel_s[j];
+    w[(size_t)t * k + gtid] = scale * (sel_s[gtid] / denom);
+  }
+}
+
+// One workgroup per token.
 template <int EPT>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ partial,
                                                             int nchunk,
@@ -118,79 +203,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   __shared__ unsigned long long keys[256 * EPT];
   __shared__ float red[4];
   __shared__ float sel_s[kMaxK];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  float sc[EPT];
-  unsigned long long key[EPT];
-#pragma unroll
-  for (int m = 0; m < EPT; ++m) {
-    const int e = tid + 256 * m;
-    float l = 0.0f;
-    if (e < E) {
-#pragma unroll 4
-      for (int c = 0; c < nchunk; ++c) l += partial[((size_t)c * T + t) * E + e];
-    }
-    sc[m] = l;
-  }
-  if (router == 0) {
-#pragma unroll
-    for (int m = 0; m < EPT; ++m) {
-      const int e = tid + 256 * m;
-      const float s = 1.0f / (1.0f + expf(-sc[m]));
-      sc[m] = s;
-      const float kap = s + (bias && e < E ? bias[e] : 0.0f);
-      key[m] = ((unsigned long long)ordered_bits(kap) << 32) | (0xffffffffu - (unsigned)e);
-    }
-  } else {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < EPT; ++m)
-      if (tid + 256 * m < E) mx = fmaxf(mx, sc[m]);
-    mx = wave_max_f(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    float z = 0.0f;
-#pragma unroll
-    for (int m = 0; m < EPT; ++m) {
-      const float p = tid + 256 * m < E ? expf(sc[m] - mx) : 0.0f;
-      sc[m] = p;
-      z += p;
-    }
-    z = wave_sum_f(z);
-    if (lane == 0) red[wave] = z;
-    __syncthreads();
-    z = (red[0] + red[1]) + (red[2] + red[3]);
-#pragma unroll
-    for (int m = 0; m < EPT; ++m) {
-      const int e = tid + 256 * m;
-      const float p = sc[m] / z;
-      sc[m] = p;
-      key[m] = ((unsigned long long)ordered_bits(p) << 32) | (0xffffffffu - (unsigned)e);
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < EPT; ++m) keys[tid + 256 * m] = tid + 256 * m < E ? key[m] : 0ull;
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < EPT; ++m) {
-    const int e = tid + 256 * m;
-    if (e >= E) continue;
-    int rank = 0;
-#pragma unroll 16
-    for (int q = 0; q < E; ++q) rank += keys[q] > key[m] ? 1 : 0;
-    if (rank < k) {
-      idx[(size_t)t * k + rank] = e;
-      sel_s[rank] = sc[m];
-    }
-  }
-  __syncthreads();
-  if (tid < k) {
-    float denom = 0.0f;
-    for (int j = 0; j < k; ++j) denom += sel_s[j];
-    w[(size_t)t * k + tid] = scale * (sel_s[tid] / denom);
-  }
+  select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, blockIdx.x, true, threadIdx.x,
+                    keys, red, sel_s, idx, w, nullptr);
 }
 
 template <int EPT>
@@ -199,6 +213,83 @@ hipError_t launch_select(const float* partial, int nchunk, const float* bias, in
   TimedLaunch tl(K_ROUTER_TOPK, s);
   hipLaunchKernelGGL(router_select_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, bias,
                      T, E, k, router, scale, idx, w);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ small T: fused tail
+// After the logits kernel, one workgroup per token selects that token's
+// experts (select_token) and encodes its row of x as two-digit int8; the last
+// workgroup to finish (release fence + atomic ticket; acquire fence) groups
+// the T*k pairs by expert (stable counting sort) and resets the ticket.
+template <int EPT>
+__global__ __launch_bounds__(256) void router_tail_kernel(
+    const float* __restrict__ partial, int nchunk, const float* __restrict__ x, int d,
+    const float* __restrict__ bias, int T, int E, int k, int router, float scale,
+    int32_t* __restrict__ idx, float* __restrict__ w, int8_t* __restrict__ xq,
+    float* __restrict__ xs, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ token_row, unsigned* ticket) {
+  __shared__ unsigned long long keys[256 * EPT];
+  __shared__ float red[4];
+  __shared__ float sel_s[kMaxK];
+  __shared__ int is_last;
+  __shared__ int idx_sm[kSmallT * kMaxK];
+  __shared__ int cnt[kMaxE];
+  const int tid = threadIdx.x, t = blockIdx.x;
+  select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, t, true, tid, keys, red, sel_s,
+                    idx, w, nullptr);
+  if (tid < kWave) encode_row(x + (size_t)t * d, d, xq + (size_t)t * 2 * d, xs + t);
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(ticket, 1u) == (unsigned)(gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  const int n = T * k;
+  for (int q = tid; q < n; q += blockDim.x) idx_sm[q] = idx[q];
+  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  for (int q = tid; q < n; q += blockDim.x) atomicAdd(&cnt[idx_sm[q]], 1);
+  __syncthreads();
+  if (tid < kWave) {
+    int carry = 0;
+    for (int b0 = 0; b0 < E; b0 += kWave) {
+      const int e = b0 + tid;
+      const int v = e < E ? cnt[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(incl, o, kWave);
+        if (tid >= o) incl += u;
+      }
+      if (e < E) {
+        offsets[e] = carry + incl - v;
+        cnt[e] = carry + incl - v;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (tid == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  for (int q = tid; q < n; q += blockDim.x) {
+    const int e = idx_sm[q];
+    int rank = 0;
+    for (int p = 0; p < q; ++p) rank += idx_sm[p] == e ? 1 : 0;
+    const int pos = cnt[e] + rank;
+    row_token[pos] = q / k;
+    token_row[q] = pos;
+  }
+  if (tid == 0) *ticket = 0u;
+}
+
+template <int EPT>
+hipError_t launch_tail(const float* partial, int nchunk, const float* x, int d, const float* bias,
+                       int T, int E, int k, int router, float scale, int32_t* idx, float* w,
+                       int8_t* xq, float* xs, int32_t* offsets, int32_t* row_token,
+                       int32_t* token_row, unsigned* ticket, hipStream_t s) {
+  TimedLaunch tl(K_ROUTER_TAIL, s);
+  hipLaunchKernelGGL(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
+                     bias, T, E, k, router, scale, idx, w, xq, xs, offsets, row_token, token_row,
+                     ticket);
   return hipGetLastError();
 }
 
@@ -225,6 +316,30 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
   if (E <= 256) return launch_select<1>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
   if (E <= 512) return launch_select<2>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
   return launch_select<4>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
+}
+
+hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
+                               int T, int d, int E, int k, float scale, int32_t* idx, float* w,
+                               float* partial, int8_t* xq, float* xs, int32_t* offsets,
+                               int32_t* row_token, int32_t* token_row, unsigned* ticket,
+                               hipStream_t s) {
+  const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
+  {
+    TimedLaunch tl(K_ROUTER_LOGITS, s);
+    dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
+    hipLaunchKernelGGL((router_logits_kernel<16, 16, 256>), grid, dim3(256), 0, s, x, wr, T, d,
+                       E, partial);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (E <= 256)
+    return launch_tail<1>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs,
+                          offsets, row_token, token_row, ticket, s);
+  if (E <= 512)
+    return launch_tail<2>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs,
+                          offsets, row_token, token_row, ticket, s);
+  return launch_tail<4>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs,
+                        offsets, row_token, token_row, ticket, s);
 }
 
 }  // namespace moe

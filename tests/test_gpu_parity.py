@@ -349,6 +349,16 @@ def test_layer_every_token_on_same_experts(ctx):
     compare_outputs(y.cpu().numpy(), oy)
 
 
+def test_layer_gemm_path_edges(ctx):
+    # >= 16 rows per expert selects the 64-row GEMM tiles; d = 320 and I = 192
+    # leave short K chunks and half-empty column blocks; experts with more than
+    # 64 rows take several tiles; the int8 shared expert (I = 128) rides along.
+    kw = dict(T=200, d=320, E=8, k=2, inter=192, shared="int8_row", shared_inter=128,
+              xseed=0x4D6F4595)
+    _layer_vs_oracle(ctx, "tiny", **kw)
+    _forward_vs_oracle(ctx, "tiny", **kw)
+
+
 def test_layer_E_equals_k(ctx):
     _layer_vs_oracle(ctx, "tiny", E=8, T=20, xseed=0x4D6F4596)
 
