@@ -191,7 +191,8 @@ moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const flo
  * the moe op).
  *   y[t] = sum_{j<k} topk_w[t][j] * rows[token_row[t*k+j]]  (slot order)
  *          + shared[t] (if not NULL) + residual[t] (if not NULL)
- *   rows [R][d], token_row [T*k], topk_w [T][k], shared/residual/y [T][d] fp32.
+ *   rows [R][d], token_row [T*k] (NULL: rows already in (token, slot) order, row
+ *   t*k + j), topk_w [T][k], shared/residual/y [T][d] fp32.
  *   y may alias residual.                                                          */
 moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row,
                        const float* topk_w, const float* shared, const float* residual,

@@ -66,7 +66,6 @@ struct moe_ctx {
   char err[512];
   bool timing;
   moe::KernelTimer timer;
-  unsigned* ticket;  // device counter for last-workgroup hand-offs; zero between launches
 };
 
 namespace {
@@ -221,21 +220,7 @@ moe_status moe_create(int device, moe_ctx** out) {
   snprintf(ctx->arch, sizeof(ctx->arch), "%s", prop.gcnArchName);
   ctx->err[0] = '\0';
   ctx->timing = false;
-  ctx->ticket = nullptr;
-  {
-    int prev = -1;
-    (void)hipGetDevice(&prev);
-    e = hipSetDevice(device);
-    if (e == hipSuccess) e = hipMalloc(&ctx->ticket, 256);
-    if (e == hipSuccess) e = hipMemset(ctx->ticket, 0, 256);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (prev >= 0) (void)hipSetDevice(prev);
-    if (e != hipSuccess) {
-      if (ctx->ticket) (void)hipFree(ctx->ticket);
-      delete ctx;
-      return fail(nullptr, MOE_E_DEVICE, "moe_create: device counter: %s", hipGetErrorString(e));
-    }
-  }
+
   moe::set_device_info(ctx->cu_count);
   *out = ctx;
   return MOE_OK;
@@ -245,10 +230,6 @@ void moe_destroy(moe_ctx* ctx) {
   if (!ctx) return;
   if (moe::g_timer == &ctx->timer) moe::g_timer = nullptr;
   release_timer(ctx->timer);
-  if (ctx->ticket) {
-    DeviceGuard g(ctx->device);
-    (void)hipFree(ctx->ticket);
-  }
   delete ctx;
 }
 
@@ -468,7 +449,8 @@ moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const flo
   } else {
     moe::FfnWs lay = moe::ffn_ws_layout(ws, T, w->d, 1, &R_max, &inter, true);
     moe::FfnSet set{w->fmt, w->layout, w->n_experts, w->inter, R_max, w->w_gate_up, w->s_gate_up,
-                    w->w_down, w->s_down, row_token, offsets, lay.hq[0], lay.hs[0], rows_out};
+                    w->w_down, w->s_down, row_token, offsets, lay.hq[0], lay.hs[0], rows_out,
+                    nullptr, 1};
     e = moe::launch_ffn_quant(&set, 1, w->d, x, T, lay, false, (hipStream_t)stream);
   }
   return device_result(ctx, e, "moe_expert_ffn");
@@ -558,8 +540,7 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, fused ? 2 : 1, Rs, Is, true);
     e = moe::launch_router_small(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale, idx,
-                                 w, f.partial, lay.xq, lay.xs, f.offsets, f.row_token,
-                                 f.token_row, ctx->ticket, s);
+                                 w, f.partial, lay.xq, lay.xs, s);
   } else {
     e = moe::launch_router(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale, idx, w,
                            f.partial, s);
@@ -572,10 +553,9 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, 2, Rs, Is, true);
     moe::FfnSet sets[2] = {
         {X.fmt, X.layout, E, X.inter, R, X.w_gate_up, X.s_gate_up, X.w_down, X.s_down, f.row_token,
-         f.offsets, lay.hq[0], lay.hs[0], f.rows},
+         f.offsets, lay.hq[0], lay.hs[0], f.rows, small ? idx : nullptr, k},
         {S.fmt, S.layout, 1, S.inter, T, S.w_gate_up, S.s_gate_up, S.w_down, S.s_down, nullptr,
-         nullptr,
-         lay.hq[1], lay.hs[1], f.sh_rows}};
+         nullptr, lay.hq[1], lay.hs[1], f.sh_rows, nullptr, 1}};
     e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, small, s);
   } else {
     auto run = [&](const moe_weights& W, int Ew, int Rw, const int32_t* rt, const int32_t* of,
@@ -588,18 +568,18 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
                                    of, Rw, out, lay.h, s);
       }
       moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, 1, &Rw, &Iw, true);
+      const bool pairs = small && &W == &X;
       moe::FfnSet set{W.fmt, W.layout, Ew, W.inter, Rw, W.w_gate_up, W.s_gate_up, W.w_down,
-                      W.s_down, rt,
-                      of, lay.hq[0], lay.hs[0], out};
+                      W.s_down, rt, of, lay.hq[0], lay.hs[0], out, pairs ? idx : nullptr, k};
       // x was encoded by the small-batch router when only routed experts run here
       return moe::launch_ffn_quant(&set, 1, d, x, T, lay, small && &W == &X, s);
     };
     e = run(X, E, R, f.row_token, f.offsets, f.rows);
     if (e == hipSuccess && has_sh) e = run(S, 1, T, nullptr, nullptr, f.sh_rows);
   }
-  if (e == hipSuccess)
-    e = moe::launch_combine(f.rows, f.token_row, w, has_sh ? f.sh_rows : nullptr, residual, T,
-                            k, d, y, s);
+  if (e == hipSuccess)  // small batches leave the rows in (token, slot) order
+    e = moe::launch_combine(f.rows, small ? nullptr : f.token_row, w,
+                            has_sh ? f.sh_rows : nullptr, residual, T, k, d, y, s);
   return device_result(ctx, e, "moe_forward");
 }
 
@@ -647,9 +627,9 @@ moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row
   if (d % 4 != 0)
     return fail(ctx, MOE_E_UNSUPPORTED, "moe_combine: d=%d is not a multiple of 4", d);
   if (T == 0) return MOE_OK;
-  if (!rows || !token_row || !topk_w || !y)
+  if (!rows || !topk_w || !y)
     return fail(ctx, MOE_E_INVALID, "moe_combine: %s is NULL",
-                !rows ? "rows" : !token_row ? "token_row" : !topk_w ? "topk_w" : "y");
+                !rows ? "rows" : !topk_w ? "topk_w" : "y");
   if (!aligned16(rows) || !aligned16(token_row) || !aligned16(topk_w) || !aligned16(shared) ||
       !aligned16(residual) || !aligned16(y))
     return fail(ctx, MOE_E_INVALID, "moe_combine: a pointer is not 16-byte aligned");

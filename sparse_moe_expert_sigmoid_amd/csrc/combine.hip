@@ -1,4 +1,5 @@
 // Weighted combine: y[t] = sum_j w[t][j] * rows[token_row[t*k + j]]
+// (token_row NULL: rows already in (token, slot) order, row t*k + j)
 // (slot order) + shared[t] + residual[t].  The routed experts' outputs are
 // weighted by the router weights and the shared expert is added with weight 1
 // (Kimi-Linear LiteRT-LM DETAILS.md, Conversion notes, mixture-of-experts
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float wj[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    r[j] = j < k ? token_row[(size_t)t * k + j] : -1;
+    r[j] = j < k ? (token_row ? token_row[(size_t)t * k + j] : t * k + j) : -1;
     wj[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
   const float4 sh = shared ? *reinterpret_cast<const float4*>(shared + o)

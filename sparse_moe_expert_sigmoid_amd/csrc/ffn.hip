@@ -31,6 +31,8 @@
 // only).  Tiles are found on the device from the expert offsets, so no count
 // is copied back to the host; the routed and the shared expert can share one
 // launch (group 0 and group 1 below).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace moe {
@@ -62,6 +64,8 @@ struct Group {
   int8_t* hq;                // [R][2][inter]
   float* hs;                 // [R][inter/64]
   float* out;                // [R][d]
+  const int32_t* pairs_idx;  // non-NULL: group the R = T*k pairs of topk_idx [T][k] on the fly
+  int k;
 };
 
 struct Job {
@@ -81,18 +85,90 @@ __device__ inline bool find_job(const Group& g0, const Group& g1, int mt, int ti
   return true;
 }
 
-// Copy `nr` digit rows of `rowbytes` bytes (row j from src row map(j)) into
-// LDS rows of `ldr` bytes.
-__device__ inline void stage_rows(int8_t* lds, int ldr, const int8_t* __restrict__ src,
-                                  int rowbytes, const int32_t* __restrict__ row_token, int r0,
-                                  int nr) {
-  const int per_row = rowbytes / 16;
-  for (int q = threadIdx.x; q < nr * per_row; q += blockDim.x) {
-    const int j = q / per_row, c = q % per_row;
-    const int src_row = row_token ? row_token[r0 + j] : r0 + j;
-    const v4i val = *reinterpret_cast<const v4i*>(src + (size_t)src_row * rowbytes + 16 * c);
-    *reinterpret_cast<v4i*>(lds + j * ldr + 16 * c) = val;
+// Workgroup-level tile lookup for the decode kernels: rows[j] is the row of
+// the group's h / out arrays and toks[j] the row of x for tile row j < nr.
+// Groups with pairs_idx group the T*k (token, slot) pairs of topk_idx on the
+// fly (no permutation pass): per-expert counts by an LDS histogram, the tile
+// by a scan over experts, its pairs by ballots in (t, j) order; the row of a
+// pair is its index t*k + j, so outputs land in (token, slot) order.
+__device__ inline bool find_rows(const Group& g0, const Group& g1, int mt, int tile, Job& job,
+                                 int* rows, int* toks, int* hist, int* sh, bool need_toks) {
+  const bool first = tile < g0.tiles;
+  if (!first && tile - g0.tiles >= g1.tiles) return false;
+  const Group G = first ? g0 : g1;
+  const int t = first ? tile : tile - g0.tiles;
+  job.g = first ? 0 : 1;
+  if (G.pairs_idx == nullptr) {
+    Tile tl;
+    if (!find_tile(G.offsets, G.E, G.R, mt, t, tl)) return false;
+    job.e = tl.e;
+    job.r0 = tl.r0;
+    job.nr = tl.nr;
+    for (int j = threadIdx.x; j < tl.nr; j += blockDim.x) {
+      rows[j] = tl.r0 + j;
+      if (need_toks) toks[j] = G.row_token ? G.row_token[tl.r0 + j] : tl.r0 + j;
+    }
+    __syncthreads();
+    return true;
   }
+  const int n = G.R, E = G.E, lane = threadIdx.x & (kWave - 1);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  for (int q = threadIdx.x; q < n; q += blockDim.x) {
+    const int e = G.pairs_idx[q];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    int base = 0, found = -1, lo = 0, cnt = 0;
+    for (int c0 = 0; c0 < E && found < 0; c0 += kWave) {
+      const int e = c0 + lane;
+      const int ce = e < E ? hist[e] : 0;
+      const int nt = (ce + mt - 1) / mt;
+      int incl = nt;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+      }
+      const int total = __shfl(incl, kWave - 1, kWave);
+      if (t < base + total) {
+        const unsigned long long m = __ballot(base + incl > t);
+        const int L = __ffsll((long long)m) - 1;
+        found = c0 + L;
+        lo = (t - base - __shfl(incl - nt, L, kWave)) * mt;
+        cnt = __shfl(ce, L, kWave);
+      }
+      base += total;
+    }
+    if (lane == 0) {
+      sh[0] = found;
+      sh[1] = lo;
+      sh[2] = found < 0 ? 0 : min(mt, cnt - lo);
+    }
+  }
+  __syncthreads();
+  if (sh[0] < 0) return false;
+  job.e = sh[0];
+  job.r0 = sh[1];
+  job.nr = sh[2];
+  if (threadIdx.x < kWave) {
+    const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    int rank0 = 0;
+    for (int q0 = 0; q0 < n; q0 += kWave) {
+      const int q = q0 + lane;
+      const bool hit = q < n && G.pairs_idx[q] == job.e;
+      const unsigned long long m = __ballot(hit);
+      const int rk = rank0 + __popcll(m & below) - job.r0;
+      if (hit && rk >= 0 && rk < job.nr) {
+        rows[rk] = q;
+        if (need_toks) toks[rk] = q / G.k;
+      }
+      rank0 += __popcll(m);
+    }
+  }
+  __syncthreads();
+  return true;
 }
 
 // ------------------------------------------------------------------ weight layouts
@@ -150,8 +226,10 @@ constexpr float kScaleFloor = 1.0f / 16384.0f;  // int4 block scales are raised 
 // ------------------------------------------------------------------ gate/up
 // FMT 1: int8 rows; FMT 2: int4 blocks of 32.  Block = 4*KS wavefronts:
 // column group cg = wave % 4 (16 h-columns each), K slice kp = wave / 4.
-// LDS: the tile's x digit rows (mt rows of 2d bytes), then reductions.
-template <int FMT, int LAY, int KS>
+// PAIRS (small batches): rows are the (token, slot) pairs grouped in-kernel.
+// The tile's activation digit rows are staged in LDS (mt rows of 2d bytes); a
+// workgroup covers NCB column blocks of 64 in turn.
+template <int FMT, int LAY, int KS, bool PAIRS, int NCB>
 __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, int d, int mt,
                                                            const int8_t* __restrict__ xq,
                                                            const float* __restrict__ xs) {
@@ -159,226 +237,276 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
   __shared__ float red_max[4][16];
   // K-slice partials: int8 path 16 ints per lane, int4 path 8 floats per lane
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 16 : 1];
+  __shared__ int rows_sm[kTileRows], toks_sm[kTileRows], sh_sm[3];
+  {
+    const bool first = (int)blockIdx.y < g0.tiles;
+    if ((int)blockIdx.x * 64 * NCB >= (first ? g0.inter : g1.inter)) return;
+  }
   Job job;
-  if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+  if (PAIRS) {  // the expert histogram uses the dynamic LDS area
+    if (!find_rows(g0, g1, mt, blockIdx.y, job, rows_sm, toks_sm, reinterpret_cast<int*>(lds),
+                   sh_sm, true))
+      return;
+  } else {
+    if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+  }
   const Group G = job.g == 0 ? g0 : g1;
-  if ((int)blockIdx.x * 64 >= G.inter) return;
   const int I = G.inter;
   const int ldr = 2 * d + 16;
-  stage_rows(lds, ldr, xq, 2 * d, G.row_token, job.r0, job.nr);
-  __syncthreads();
+  {
+    const int per_row = (2 * d) / 16;
+    for (int q = threadIdx.x; q < job.nr * per_row; q += blockDim.x) {
+      const int j = q / per_row, c = q % per_row;
+      const int src = PAIRS ? toks_sm[j] : G.row_token ? G.row_token[job.r0 + j] : job.r0 + j;
+      *reinterpret_cast<v4i*>(lds + j * ldr + 16 * c) =
+          *reinterpret_cast<const v4i*>(xq + (size_t)src * 2 * d + 16 * c);
+    }
+    __syncthreads();
+  }
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
-  const int c0 = blockIdx.x * 64 + cg * 16;  // this wavefront's 16 h-columns
   const int i = lane & 15, g = lane >> 4;
   const bool jv = i < job.nr;
-  const int r = job.r0 + i;
-  const int tok = jv ? (G.row_token ? G.row_token[r] : r) : 0;
+  const int r = !jv ? 0 : PAIRS ? rows_sm[i] : job.r0 + i;
+  const int tok = !jv ? 0 : PAIRS ? toks_sm[i] : (G.row_token ? G.row_token[r] : r);
   const int8_t* xb0 = lds + i * ldr;
   const int8_t* xb1 = xb0 + d;
-  const size_t row0 = (size_t)job.e * 2 * I + c0;
+  const float sigx = jv ? xs[tok] : 0.0f;
 
-  float gate[4], up[4];
-  if (FMT == 1) {
-    const int nsteps = d / kKStep;
-    const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
-    const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wgu), row0, d, i, g,
-                                            lane);
-    const int8_t* wb = wa + (size_t)I * d;
-    v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
-    constexpr int U = 4;
-    for (int s = s_beg; s < s_end; s += U) {
-      v4i ra[U], rb[U], x0[U], x1[U];
+#pragma unroll 1
+  for (int cbi = 0; cbi < NCB; ++cbi) {
+    const int cb = blockIdx.x * NCB + cbi;  // 64-column block
+    if (cb * 64 >= I) break;                // uniform over the workgroup
+    const int c0 = cb * 64 + cg * 16;       // this wavefront's 16 h-columns
+    const size_t row0 = (size_t)job.e * 2 * I + c0;
+
+    float gate[4], up[4];
+    if (FMT == 1) {
+      const int nsteps = d / kKStep;
+      const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
+      const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wgu), row0, d, i, g,
+                                              lane);
+      const int8_t* wb = wa + (size_t)I * d;
+      v4i a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+      constexpr int U = 4;
+      for (int s = s_beg; s < s_end; s += U) {
+        v4i ra[U], rb[U], x0[U], x1[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ss = min(s + u, s_end - 1);
-        ra[u] = i8_load<LAY>(wa, ss);
-        rb[u] = i8_load<LAY>(wb, ss);
-        x0[u] = v4i{0, 0, 0, 0};
-        x1[u] = v4i{0, 0, 0, 0};
-        if (jv) {
-          x0[u] = *reinterpret_cast<const v4i*>(xb0 + ss * kKStep + 16 * g);
-          x1[u] = *reinterpret_cast<const v4i*>(xb1 + ss * kKStep + 16 * g);
+        for (int u = 0; u < U; ++u) {
+          const int ss = min(s + u, s_end - 1);
+          ra[u] = i8_load<LAY>(wa, ss);
+          rb[u] = i8_load<LAY>(wb, ss);
+          x0[u] = v4i{0, 0, 0, 0};
+          x1[u] = v4i{0, 0, 0, 0};
+          if (jv) {
+            x0[u] = *reinterpret_cast<const v4i*>(xb0 + ss * kKStep + 16 * g);
+            x1[u] = *reinterpret_cast<const v4i*>(xb1 + ss * kKStep + 16 * g);
+          }
         }
-      }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (s + u < s_end) {
-          a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0[u], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1[u], a1, 0, 0, 0);
-          b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0[u], b0, 0, 0, 0);
-          b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1[u], b1, 0, 0, 0);
-        }
-      }
-    }
-    // exact int32 reduction of the K slices (order-free)
-    if (KS > 1) {
-      int* red = reinterpret_cast<int*>(red_acc);
-      if (kp > 0) {
-        int* dst = red + (((kp - 1) * 4 + cg) * 64 + lane) * 16;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          dst[c] = a0[c]; dst[4 + c] = a1[c]; dst[8 + c] = b0[c]; dst[12 + c] = b1[c];
-        }
-      }
-      __syncthreads();
-      if (kp == 0) {
-        for (int q = 1; q < KS; ++q) {
-          const int* src = red + (((q - 1) * 4 + cg) * 64 + lane) * 16;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            a0[c] += src[c]; a1[c] += src[4 + c]; b0[c] += src[8 + c]; b1[c] += src[12 + c];
+        for (int u = 0; u < U; ++u) {
+          if (s + u < s_end) {
+            a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0[u], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1[u], a1, 0, 0, 0);
+            b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0[u], b0, 0, 0, 0);
+            b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1[u], b1, 0, 0, 0);
           }
         }
       }
-    }
-    const float sig = jv ? xs[tok] : 0.0f;
-    const float* se = G.sgu + (size_t)job.e * 2 * I;
+      // exact int32 reduction of the K slices (order-free)
+      if (KS > 1) {
+        int* red = reinterpret_cast<int*>(red_acc);
+        if (kp > 0) {
+          int* dst = red + (((kp - 1) * 4 + cg) * 64 + lane) * 16;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int n = c0 + 4 * g + c;
-      gate[c] = se[n] * sig * ((float)a0[c] + (float)a1[c] * (1.0f / 256.0f));
-      up[c] = se[I + n] * sig * ((float)b0[c] + (float)b1[c] * (1.0f / 256.0f));
-    }
-  } else {
-    // int4: one 16x16x32 MFMA pair per block of 32 inputs; each block's int32
-    // sum (256*d0-part + d1-part, exact in fp32 since |.| < 2^24) is scaled by
-    // max(s, 2^-14) into the fp32 accumulator.
-    const int nb = d / 32, nspan = d / 128;
-    const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
-    const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wgu), row0, d, i,
-                                             g, lane);
-    const uint8_t* wb = wa + (size_t)I * (d / 2);
-    const float* sa = G.sgu + ((size_t)job.e * 2 * I + c0 + 4 * g) * nb;
-    const float* sb = sa + (size_t)I * nb;
-    float fa[4] = {0.f, 0.f, 0.f, 0.f}, fb[4] = {0.f, 0.f, 0.f, 0.f};
-    const v4i zero = {0, 0, 0, 0};
-    for (int m = m_beg; m < m_end; ++m) {
-      const v4i wa4 = i4_load<LAY>(wa, m);
-      const v4i wb4 = i4_load<LAY>(wb, m);
-      long x0[4], x1[4];
+          for (int c = 0; c < 4; ++c) {
+            dst[c] = a0[c]; dst[4 + c] = a1[c]; dst[8 + c] = b0[c]; dst[12 + c] = b1[c];
+          }
+        }
+        __syncthreads();
+        if (kp == 0) {
+          for (int q = 1; q < KS; ++q) {
+            const int* src = red + (((q - 1) * 4 + cg) * 64 + lane) * 16;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x0[q] = 0;
-        x1[q] = 0;
-        if (jv) {
-          x0[q] = *reinterpret_cast<const long*>(xb0 + 128 * m + 32 * q + 8 * g);
-          x1[q] = *reinterpret_cast<const long*>(xb1 + 128 * m + 32 * q + 8 * g);
+            for (int c = 0; c < 4; ++c) {
+              a0[c] += src[c]; a1[c] += src[4 + c]; b0[c] += src[8 + c]; b1[c] += src[12 + c];
+            }
+          }
         }
       }
+      const float* se = G.sgu + (size_t)job.e * 2 * I;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = 4 * m + q;
-        const long qa = unpack8_int4((unsigned)wa4[q]);
-        const long qb = unpack8_int4((unsigned)wb4[q]);
-        const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], zero, 0, 0, 0);
-        const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], zero, 0, 0, 0);
-        const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], zero, 0, 0, 0);
-        const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], zero, 0, 0, 0);
+      for (int c = 0; c < 4; ++c) {
+        const int n = c0 + 4 * g + c;
+        gate[c] = se[n] * sigx * ((float)a0[c] + (float)a1[c] * (1.0f / 256.0f));
+        up[c] = se[I + n] * sigx * ((float)b0[c] + (float)b1[c] * (1.0f / 256.0f));
+      }
+    } else {
+      // int4: one 16x16x32 MFMA pair per block of 32 inputs; each block's int32
+      // sum (256*d0-part + d1-part, exact in fp32 since |.| < 2^24) is scaled by
+      // max(s, 2^-14) into the fp32 accumulator.
+      const int nb = d / 32, nspan = d / 128;
+      const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
+      const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wgu), row0, d, i,
+                                               g, lane);
+      const uint8_t* wb = wa + (size_t)I * (d / 2);
+      const float* sa = G.sgu + ((size_t)job.e * 2 * I + c0 + 4 * g) * nb;
+      const float* sb = sa + (size_t)I * nb;
+      float fa[4] = {0.f, 0.f, 0.f, 0.f}, fb[4] = {0.f, 0.f, 0.f, 0.f};
+      const v4i zero = {0, 0, 0, 0};
+      for (int m = m_beg; m < m_end; ++m) {
+        const v4i wa4 = i4_load<LAY>(wa, m);
+        const v4i wb4 = i4_load<LAY>(wb, m);
+        long x0[4], x1[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float s1 = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
-          const float s2 = fmaxf(sb[(size_t)c * nb + b], kScaleFloor);
-          fa[c] = fmaf(s1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
-          fb[c] = fmaf(s2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+        for (int q = 0; q < 4; ++q) {
+          x0[q] = 0;
+          x1[q] = 0;
+          if (jv) {
+            x0[q] = *reinterpret_cast<const long*>(xb0 + 128 * m + 32 * q + 8 * g);
+            x1[q] = *reinterpret_cast<const long*>(xb1 + 128 * m + 32 * q + 8 * g);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int b = 4 * m + q;
+          const long qa = unpack8_int4((unsigned)wa4[q]);
+          const long qb = unpack8_int4((unsigned)wb4[q]);
+          const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], zero, 0, 0, 0);
+          const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], zero, 0, 0, 0);
+          const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], zero, 0, 0, 0);
+          const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], zero, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float s1 = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
+            const float s2 = fmaxf(sb[(size_t)c * nb + b], kScaleFloor);
+            fa[c] = fmaf(s1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
+            fb[c] = fmaf(s2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+          }
         }
       }
-    }
-    if (KS > 1) {  // fp32 partials added in slice order
-      if (kp > 0) {
-        float* dst = red_acc + (((kp - 1) * 4 + cg) * 64 + lane) * 8;
+      if (KS > 1) {  // fp32 partials added in slice order
+        if (kp > 0) {
+          float* dst = red_acc + (((kp - 1) * 4 + cg) * 64 + lane) * 8;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { dst[c] = fa[c]; dst[4 + c] = fb[c]; }
-      }
-      __syncthreads();
-      if (kp == 0) {
-        for (int q = 1; q < KS; ++q) {
-          const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 8;
+          for (int c = 0; c < 4; ++c) { dst[c] = fa[c]; dst[4 + c] = fb[c]; }
+        }
+        __syncthreads();
+        if (kp == 0) {
+          for (int q = 1; q < KS; ++q) {
+            const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 8;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) { fa[c] += src[c]; fb[c] += src[4 + c]; }
+            for (int c = 0; c < 4; ++c) { fa[c] += src[c]; fb[c] += src[4 + c]; }
+          }
         }
       }
-    }
-    const float sig = jv ? xs[tok] * (1.0f / 256.0f) : 0.0f;
+      const float sig = sigx * (1.0f / 256.0f);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      gate[c] = fa[c] * sig;
-      up[c] = fb[c] * sig;
+      for (int c = 0; c < 4; ++c) {
+        gate[c] = fa[c] * sig;
+        up[c] = fb[c] * sig;
+      }
     }
-  }
 
-  // ---- epilogue: h = silu(gate) * up, encoded per (row, 64-column block)
-  float h[4];
-  float mx = 0.0f;
+    // ---- epilogue: h = silu(gate) * up, encoded per (row, 64-column block)
+    float h[4];
+    float mx = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    h[c] = silu_f(gate[c]) * up[c];
-    mx = fmaxf(mx, fabsf(h[c]));
+    for (int c = 0; c < 4; ++c) {
+      h[c] = silu_f(gate[c]) * up[c];
+      mx = fmaxf(mx, fabsf(h[c]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    if (kp == 0 && g == 0) red_max[cg][i] = mx;
+    __syncthreads();
+    if (kp == 0 && jv) {
+      mx = fmaxf(fmaxf(red_max[0][i], red_max[1][i]), fmaxf(red_max[2][i], red_max[3][i]));
+      const int p = digit_exponent(mx);
+      int d0[4], d1[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) two_digits(h[c], p, d0[c], d1[c]);
+      int8_t* hrow = G.hq + (size_t)r * 2 * I;
+      const int col = c0 + 4 * g;
+      *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
+      *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
+      if (cg == 0 && g == 0)
+        G.hs[(size_t)r * (I / 64) + cb] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+    }
+    if (NCB > 1) __syncthreads();  // red_max is reused by the next column block
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  if (kp == 0 && g == 0) red_max[cg][i] = mx;
-  __syncthreads();
-  if (kp != 0 || !jv) return;
-  mx = fmaxf(fmaxf(red_max[0][i], red_max[1][i]), fmaxf(red_max[2][i], red_max[3][i]));
-  const int p = digit_exponent(mx);
-  int d0[4], d1[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) two_digits(h[c], p, d0[c], d1[c]);
-  int8_t* hrow = G.hq + (size_t)r * 2 * I;
-  const int col = c0 + 4 * g;
-  *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
-  *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
-  if (cg == 0 && g == 0)
-    G.hs[(size_t)r * (I / 64) + blockIdx.x] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
 }
 
 // ------------------------------------------------------------------ down
 // LDS: the tile's h digit rows (mt rows of 2I bytes), their block scales
 // (mt x I/64 floats), then the K-slice partials.
-template <int FMT, int LAY, int KS>
+// NG: 16-row weight groups per wavefront (2 for int8 without K split, so each
+// workgroup streams 128 output rows and its prologue is amortised over more
+// bytes).
+template <int FMT, int LAY, int KS, bool PAIRS, int NG>
 __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int d, int mt) {
   extern __shared__ int8_t lds[];
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 4 : 1];
+  __shared__ int rows_sm[kTileRows], sh_sm[3];
   Job job;
-  if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+  if (PAIRS) {  // the expert histogram borrows the h staging area
+    if (!find_rows(g0, g1, mt, blockIdx.y, job, rows_sm, nullptr, reinterpret_cast<int*>(lds),
+                   sh_sm, false))
+      return;
+  } else {
+    if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+  }
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
   const int ldr = 2 * I + 16;
   const int nhb = I / 64;
   float* lds_s = reinterpret_cast<float*>(lds + (size_t)mt * ldr);
-  stage_rows(lds, ldr, G.hq, 2 * I, nullptr, job.r0, job.nr);
-  for (int q = threadIdx.x; q < job.nr * nhb; q += blockDim.x)
-    lds_s[q] = G.hs[(size_t)(job.r0 + q / nhb) * nhb + q % nhb];
-  __syncthreads();
+  if (!PAIRS) {  // small batches read their few h rows straight from L2 (no LDS, more
+  // workgroups resident)
+    const int per_row = (2 * I) / 16;
+    for (int q = threadIdx.x; q < job.nr * per_row; q += blockDim.x) {
+      const int j = q / per_row, c = q % per_row;
+      *reinterpret_cast<v4i*>(lds + j * ldr + 16 * c) =
+          *reinterpret_cast<const v4i*>(G.hq + (size_t)(job.r0 + j) * 2 * I + 16 * c);
+    }
+    for (int q = threadIdx.x; q < job.nr * nhb; q += blockDim.x)
+      lds_s[q] = G.hs[(size_t)(job.r0 + q / nhb) * nhb + q % nhb];
+    __syncthreads();
+  }
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
-  const int c0 = blockIdx.x * 64 + cg * 16;  // output columns of this wavefront
+  const int c0 = blockIdx.x * 64 * NG + cg * 16 * NG;  // output rows of this wavefront
   const int i = lane & 15, g = lane >> 4;
   const bool jv = i < job.nr;
-  const int r = job.r0 + i;
-  const int8_t* hb0 = lds + i * ldr;
+  const int r = !jv ? 0 : PAIRS ? rows_sm[i] : job.r0 + i;
+  const int8_t* hb0 = PAIRS ? G.hq + (size_t)r * 2 * I : lds + i * ldr;
   const int8_t* hb1 = hb0 + I;
-  const float* hsr = lds_s + i * nhb;
+  const float* hsr = PAIRS ? G.hs + (size_t)r * nhb : lds_s + i * nhb;
   const size_t row0 = (size_t)job.e * d + c0;
   const v4i zero = {0, 0, 0, 0};
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[NG][4];
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[q][c] = 0.0f;
 
   if (FMT == 1) {
     const int nsteps = I / kKStep;
     const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
     const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g,
                                             lane);
-    constexpr int U = KS == 1 ? 8 : 4;  // one weight stream per wavefront: 8 KB in flight
+    // 8 KB of weights in flight per wavefront
+    constexpr int U = KS == 1 ? 8 / NG : 4;
     for (int s = s_beg; s < s_end; s += U) {
-      v4i ra[U], x0[U], x1[U];
+      v4i ra[NG][U], x0[U], x1[U];
       float sg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ss = min(s + u, s_end - 1);
-        ra[u] = i8_load<LAY>(wa, ss);
+#pragma unroll
+        for (int q = 0; q < NG; ++q) ra[q][u] = i8_load<LAY>(wa + (size_t)16 * q * I, ss);
         x0[u] = zero;
         x1[u] = zero;
         sg[u] = 0.0f;
@@ -391,11 +519,14 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (s + u < s_end) {
-          const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0[u], zero, 0, 0, 0);
-          const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1[u], zero, 0, 0, 0);
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc[c] = fmaf(sg[u], fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[c]);
+          for (int q = 0; q < NG; ++q) {
+            const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[q][u], x0[u], zero, 0, 0, 0);
+            const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[q][u], x1[u], zero, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              acc[q][c] = fmaf(sg[u], fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[q][c]);
+          }
         }
       }
     }
@@ -429,34 +560,37 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float sw = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
-          acc[c] = fmaf(sw * sg[q >> 1], (float)(p0[c] * 256 + p1[c]), acc[c]);
+          acc[0][c] = fmaf(sw * sg[q >> 1], (float)(p0[c] * 256 + p1[c]), acc[0][c]);
         }
       }
     }
   }
-  if (KS > 1) {
+  if (KS > 1) {  // (NG == 1 whenever KS > 1)
     if (kp > 0) {
       float* dst = red_acc + (((kp - 1) * 4 + cg) * 64 + lane) * 4;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dst[c] = acc[c];
+      for (int c = 0; c < 4; ++c) dst[c] = acc[0][c];
     }
     __syncthreads();
     if (kp != 0) return;
     for (int q = 1; q < KS; ++q) {
       const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 4;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += src[c];
+      for (int c = 0; c < 4; ++c) acc[0][c] += src[c];
     }
   }
   if (!jv) return;
-  float res[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int n = c0 + 4 * g + c;
-    res[c] = FMT == 1 ? G.sdn[(size_t)job.e * d + n] * acc[c] : acc[c];
+  for (int q = 0; q < NG; ++q) {
+    float res[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int n = c0 + 16 * q + 4 * g + c;
+      res[c] = FMT == 1 ? G.sdn[(size_t)job.e * d + n] * acc[q][c] : acc[q][c];
+    }
+    *reinterpret_cast<float4*>(G.out + (size_t)r * d + c0 + 16 * q + 4 * g) =
+        make_float4(res[0], res[1], res[2], res[3]);
   }
-  *reinterpret_cast<float4*>(G.out + (size_t)r * d + c0 + 4 * g) =
-      make_float4(res[0], res[1], res[2], res[3]);
 }
 
 // ------------------------------------------------------------------ prefill GEMM
@@ -816,7 +950,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 
 int g_cu_count = 256;
 
-template <int FMT, int LAY>
+template <int FMT, int LAY, bool PAIRS>
 hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8_t* xq,
                        const float* xs, hipStream_t s) {
   const int tiles = a.tiles + b.tiles;
@@ -824,33 +958,40 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   // split K across more wavefronts when the tiles alone cannot fill the chip
   const long long blocks = (long long)tiles * (imax / 64);
   const int ks = blocks >= 2LL * g_cu_count ? 1 : (blocks >= g_cu_count / 2 ? 2 : 4);
-  const size_t lds_gu = (size_t)mt * (2 * d + 16);
+  const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
+  const size_t lds_gu = std::max((size_t)mt * (2 * d + 16), emax);
   {
     TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
     dim3 grid(imax / 64, tiles);
     if (ks == 1)
-      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 1>), grid, dim3(256), lds_gu, s, a, b, d, mt,
-                         xq, xs);
+      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 1, PAIRS, 1>), grid, dim3(256), lds_gu, s, a, b,
+                         d, mt, xq, xs);
     else if (ks == 2)
-      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 2>), grid, dim3(512), lds_gu, s, a, b, d, mt,
-                         xq, xs);
+      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 2, PAIRS, 1>), grid, dim3(512), lds_gu, s, a, b,
+                         d, mt, xq, xs);
     else
-      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 4>), grid, dim3(1024), lds_gu, s, a, b, d, mt,
-                         xq, xs);
+      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 4, PAIRS, 1>), grid, dim3(1024), lds_gu, s, a, b,
+                         d, mt, xq, xs);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long dblocks = (long long)tiles * (d / 64);
   const int dks = dblocks >= 2LL * g_cu_count ? 1 : (dblocks >= g_cu_count / 2 ? 2 : 4);
-  const size_t lds_dn = (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
+  const size_t lds_dn =
+      PAIRS ? emax : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
   TimedLaunch tl(FMT == 1 ? K_FFN_I8_DOWN : K_FFN_I4_DOWN, s);
-  dim3 grid(d / 64, tiles);
-  if (dks == 1)
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 1>), grid, dim3(256), lds_dn, s, a, b, d, mt);
+  if (FMT == 1 && dks == 1 && d % 128 == 0)
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 1, PAIRS, 2>), dim3(d / 128, tiles), dim3(256),
+                       lds_dn, s, a, b, d, mt);
+  else if (dks == 1)
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 1, PAIRS, 1>), dim3(d / 64, tiles), dim3(256),
+                       lds_dn, s, a, b, d, mt);
   else if (dks == 2)
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 2>), grid, dim3(512), lds_dn, s, a, b, d, mt);
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 2, PAIRS, 1>), dim3(d / 64, tiles), dim3(512),
+                       lds_dn, s, a, b, d, mt);
   else
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 4>), grid, dim3(1024), lds_dn, s, a, b, d, mt);
+    hipLaunchKernelGGL((down_kernel<FMT, LAY, 4, PAIRS, 1>), dim3(d / 64, tiles), dim3(1024),
+                       lds_dn, s, a, b, d, mt);
   return hipGetLastError();
 }
 
@@ -906,7 +1047,7 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     if (err != hipSuccess) return err;
   }
   // int8 with many rows per expert: grouped GEMM tiles of 64 rows
-  if (sets[0].fmt == 1 && sets[0].R >= 16LL * sets[0].E) {
+  if (sets[0].fmt == 1 && sets[0].pairs_idx == nullptr && sets[0].R >= 16LL * sets[0].E) {
     Group grp[2] = {};
     for (int q = 0; q < nsets; ++q) {
       const FfnSet& f = sets[q];
@@ -941,14 +1082,18 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     G.hq = f.hq;
     G.hs = f.hs;
     G.out = f.out;
+    G.pairs_idx = f.pairs_idx;
+    G.k = f.k;
   }
   if (nsets < 2) grp[1].inter = grp[0].inter;
   const bool tiled = sets[0].layout == 1;
-  if (sets[0].fmt == 1)
-    return tiled ? launch_pair<1, kTiled>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)
-                 : launch_pair<1, kRows>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s);
-  return tiled ? launch_pair<2, kTiled>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)
-               : launch_pair<2, kRows>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s);
+  const bool pairs = sets[0].pairs_idx != nullptr || (nsets > 1 && sets[1].pairs_idx != nullptr);
+#define MOE_PAIR(F, L)                                                               \
+  (pairs ? launch_pair<F, L, true>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)           \
+         : launch_pair<F, L, false>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s))
+  if (sets[0].fmt == 1) return tiled ? MOE_PAIR(1, kTiled) : MOE_PAIR(1, kRows);
+  return tiled ? MOE_PAIR(2, kTiled) : MOE_PAIR(2, kRows);
+#undef MOE_PAIR
 }
 
 hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int inter,

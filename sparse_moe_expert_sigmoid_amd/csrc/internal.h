@@ -79,6 +79,8 @@ struct FfnSet {
   int8_t* hq;
   float* hs;
   float* out;                // [R][d]
+  const int32_t* pairs_idx;  // non-NULL: rows are the R = T*k pairs of topk_idx, grouped in-kernel
+  int k;
 };
 
 // Upper bound on the number of FFN tiles (kTileRows rows of one expert each)
@@ -119,15 +121,13 @@ struct TimedLaunch {
 hipError_t launch_router(int router, const float* x, const float* wr, const float* bias, int T,
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s);
-// Up to kSmallT tokens: logits, then one launch for selection, x encoding
-// (xq/xs, see the FFN workspace) and the permutation; `ticket` is a zeroed
-// device counter that the launch leaves zeroed.
+// Up to kSmallT tokens: logits, then one launch for selection and the x
+// encoding (xq/xs, see the FFN workspace); no permutation (the FFN groups the
+// pairs itself, FfnSet::pairs_idx).
 constexpr int kSmallT = 16;
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, int32_t* offsets,
-                               int32_t* row_token, int32_t* token_row, unsigned* ticket,
-                               hipStream_t s);
+                               float* partial, int8_t* xq, float* xs, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);

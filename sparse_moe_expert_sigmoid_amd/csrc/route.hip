@@ -218,78 +218,35 @@ hipError_t launch_select(const float* partial, int nchunk, const float* bias, in
 
 // ------------------------------------------------------------------ small T: fused tail
 // After the logits kernel, one workgroup per token selects that token's
-// experts (select_token) and encodes its row of x as two-digit int8; the last
-// workgroup to finish (release fence + atomic ticket; acquire fence) groups
-// the T*k pairs by expert (stable counting sort) and resets the ticket.
+// experts (select_token) and encodes its row of x as two-digit int8 for the
+// FFN kernels, which then group the (token, slot) pairs themselves.
 template <int EPT>
 __global__ __launch_bounds__(256) void router_tail_kernel(
     const float* __restrict__ partial, int nchunk, const float* __restrict__ x, int d,
     const float* __restrict__ bias, int T, int E, int k, int router, float scale,
     int32_t* __restrict__ idx, float* __restrict__ w, int8_t* __restrict__ xq,
-    float* __restrict__ xs, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ token_row, unsigned* ticket) {
+    float* __restrict__ xs) {
   __shared__ unsigned long long keys[256 * EPT];
   __shared__ float red[4];
   __shared__ float sel_s[kMaxK];
-  __shared__ int is_last;
-  __shared__ int idx_sm[kSmallT * kMaxK];
-  __shared__ int cnt[kMaxE];
-  const int tid = threadIdx.x, t = blockIdx.x;
-  select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, t, true, tid, keys, red, sel_s,
-                    idx, w, nullptr);
-  if (tid < kWave) encode_row(x + (size_t)t * d, d, xq + (size_t)t * 2 * d, xs + t);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(ticket, 1u) == (unsigned)(gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  const int n = T * k;
-  for (int q = tid; q < n; q += blockDim.x) idx_sm[q] = idx[q];
-  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
-  __syncthreads();
-  for (int q = tid; q < n; q += blockDim.x) atomicAdd(&cnt[idx_sm[q]], 1);
-  __syncthreads();
-  if (tid < kWave) {
-    int carry = 0;
-    for (int b0 = 0; b0 < E; b0 += kWave) {
-      const int e = b0 + tid;
-      const int v = e < E ? cnt[e] : 0;
-      int incl = v;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int u = __shfl_up(incl, o, kWave);
-        if (tid >= o) incl += u;
-      }
-      if (e < E) {
-        offsets[e] = carry + incl - v;
-        cnt[e] = carry + incl - v;
-      }
-      carry += __shfl(incl, kWave - 1, kWave);
-    }
-    if (tid == 0) offsets[E] = carry;
+  const int t = blockIdx.x;
+  // the row of x is read into L1/L2 while the selection's loads are in flight
+  if (threadIdx.x < kWave) {
+    const float* row = x + (size_t)t * d;
+    for (int c = threadIdx.x; c < d / 4; c += kWave) __builtin_prefetch(row + 4 * c, 0, 3);
   }
-  __syncthreads();
-  for (int q = tid; q < n; q += blockDim.x) {
-    const int e = idx_sm[q];
-    int rank = 0;
-    for (int p = 0; p < q; ++p) rank += idx_sm[p] == e ? 1 : 0;
-    const int pos = cnt[e] + rank;
-    row_token[pos] = q / k;
-    token_row[q] = pos;
-  }
-  if (tid == 0) *ticket = 0u;
+  select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, t, true, threadIdx.x, keys,
+                    red, sel_s, idx, w, nullptr);
+  if (threadIdx.x < kWave) encode_row(x + (size_t)t * d, d, xq + (size_t)t * 2 * d, xs + t);
 }
 
 template <int EPT>
 hipError_t launch_tail(const float* partial, int nchunk, const float* x, int d, const float* bias,
                        int T, int E, int k, int router, float scale, int32_t* idx, float* w,
-                       int8_t* xq, float* xs, int32_t* offsets, int32_t* row_token,
-                       int32_t* token_row, unsigned* ticket, hipStream_t s) {
+                       int8_t* xq, float* xs, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TAIL, s);
   hipLaunchKernelGGL(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
-                     bias, T, E, k, router, scale, idx, w, xq, xs, offsets, row_token, token_row,
-                     ticket);
+                     bias, T, E, k, router, scale, idx, w, xq, xs);
   return hipGetLastError();
 }
 
@@ -320,9 +277,7 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
 
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, int32_t* offsets,
-                               int32_t* row_token, int32_t* token_row, unsigned* ticket,
-                               hipStream_t s) {
+                               float* partial, int8_t* xq, float* xs, hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
   {
     TimedLaunch tl(K_ROUTER_LOGITS, s);
@@ -333,13 +288,10 @@ hipError_t launch_router_small(int router, const float* x, const float* wr, cons
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (E <= 256)
-    return launch_tail<1>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs,
-                          offsets, row_token, token_row, ticket, s);
+    return launch_tail<1>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs, s);
   if (E <= 512)
-    return launch_tail<2>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs,
-                          offsets, row_token, token_row, ticket, s);
-  return launch_tail<4>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs,
-                        offsets, row_token, token_row, ticket, s);
+    return launch_tail<2>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs, s);
+  return launch_tail<4>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs, s);
 }
 
 }  // namespace moe

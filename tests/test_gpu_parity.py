@@ -426,6 +426,42 @@ def test_forward_kimi_prefill_sampled_with_residual(ctx):
     _forward_vs_oracle(ctx, "kimi_prefill", tokens=tokens, residual=True)
 
 
+def test_forward_small_batch_edges(ctx):
+    # T <= 16 groups the (token, slot) pairs inside the FFN kernels: few experts
+    # with many rows each, an int8 shared expert in the same launches, T = 16.
+    kw = dict(T=16, E=8, k=4, shared="int8_row", shared_inter=128, xseed=0x4D6F4594)
+    _forward_vs_oracle(ctx, "tiny", **kw)
+    kw1 = dict(T=3, E=8, k=8, shared="int8_row", shared_inter=128, xseed=0x4D6F4593)
+    _forward_vs_oracle(ctx, "tiny", **kw1)
+
+
+def test_forward_small_batch_all_tokens_same_experts(ctx):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import MoELayer
+    inp = inputs("tiny", T=16, shared="int8_row", shared_inter=128, xseed=0x4D6F4592)
+    forced = inp.bias.copy()
+    forced[[2, 3, 5, 7, 11, 13, 17, 19]] = 1.0
+    inp2 = S.LayerInputs(inp.spec, inp.x, inp.wr, forced, inp.experts, inp.shared)
+    L = MoELayer.from_inputs(ctx, inp2)
+    y = L.forward_fused(to_dev(inp.x))
+    torch.cuda.synchronize()
+    oy, oidx, ow, ogap = oracle.layer_of(inp2)
+    assert np.array_equal(np.sort(L.idx.cpu().numpy(), 1), np.sort(oidx, 1))
+    compare_outputs(y.cpu().numpy(), oy)
+
+
+def test_combine_identity_rows(ctx):
+    import torch
+    T, k, d = 6, 4, 128
+    rows = S.normal(8, 1, (T * k, d), 1.0)
+    w = S.uniform(8, 3, (T, k), 0, 1)
+    y = torch.empty((T, d), dtype=torch.float32, device="cuda:0")
+    ctx.moe_combine(to_dev(rows), None, to_dev(w), None, None, T, k, d, y)
+    torch.cuda.synchronize()
+    o = oracle.combine(rows, np.arange(T * k, dtype=np.int32), w)
+    assert np.allclose(y.cpu().numpy(), o, rtol=1e-6, atol=1e-6 * np.abs(o).max())
+
+
 def test_forward_matches_staged_router_outputs(ctx):
     import torch
     inp = inputs("kimi_decode")
