@@ -72,6 +72,28 @@ def expert_bytes(ew, e_list):
     return gu * n, dn * n
 
 
+def counter_traffic(workload: str, kernel_prefix: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (profiles/<workload>.md), or None when that summary is
+    missing or was taken from a different version of the kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}.md")
+    src = os.path.join(ROOT, "sparse_moe_expert_sigmoid_amd", "csrc", "ffn.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha:
+        return None
+    if not fields.get("dominant_kernel", "").startswith(kernel_prefix):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(inputs, budget_s: float):
     """The oracle, as it stands, on the same layer and tokens; bounded repeat count."""
     import oracle
@@ -106,6 +128,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="after timing, copy BYTES once device-to-device (a kernel of known "
+                         "traffic, used to calibrate hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -226,11 +251,21 @@ def main():
             bytes_per_launch = per_step / launches_per_step
             avg_s = tot_ms / launches / 1e3
             achieved = bytes_per_launch / avg_s / 1e9
+            traffic = counter_traffic(args.workload, "gate_up_kernel")
             roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "bytes_per_launch": int(bytes_per_launch),
                         "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    if args.copy_probe > 0:
+        # a fill kernel (writes N bytes) and an elementwise kernel (reads N, writes N)
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.add(src, 0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu:
