@@ -13,6 +13,11 @@ Weight copies: the step alternates between `--copies` identical copies of the
 expert weights (and the shared expert) in separate HBM allocations, so no
 step finds its weights in the 256 MB last-level cache from the step before.
 
+Stack workloads (--workload kimi_stack_decode | kimi_stack_prefill): 26
+distinct Kimi-shaped layers (about 95 GB of weights, drawn on the GPU, so cold
+by size) with the residual between layers and a Zipf-skewed selection bias; a
+step is one pass through all 26 layers, replayed as one HIP graph at T=1.
+
 Output: one JSON line (metric, value = tokens/s, ms_per_step, roofline of the
 dominant kernel measured with HIP events on its own stream in a second,
 separately timed pass, and the CPU oracle timed on a bounded sample).
@@ -35,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / TFLOP/s (prefill), % roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 
 WORKLOADS = {
     # name: (layer spec, chunks, description)
@@ -51,6 +57,19 @@ WORKLOADS = {
                     "I=768 SwiGLU, int4 block-32 experts, no shared expert"),
     "qwen_prefill": ("qwen_prefill", 1, "Qwen3-shaped MoE layer, T=128"),
     "tiny": ("tiny", 1, "tiny MoE layer: T=32, d=512, E=32, top-8, I=256"),
+}
+
+
+STACK_WORKLOADS = {
+    # name: (T, description)
+    "kimi_stack_decode": (1, "stack of 26 distinct Kimi-shaped MoE layers with the residual "
+                             "between layers, T=1 decode, Zipf-skewed selection bias (64 "
+                             "experts take ~73% of selections), int8 experts and shared "
+                             "expert, ~95 GB of weights; the 26 layers replayed as one HIP "
+                             "graph"),
+    "kimi_stack_prefill": (4096, "stack of 26 distinct Kimi-shaped MoE layers with the residual "
+                                 "between layers, T=4096 prefill, Zipf-skewed selection bias, "
+                                 "int8 experts and shared expert, ~95 GB of weights"),
 }
 
 
@@ -115,12 +134,194 @@ def cpu_baseline(inputs, budget_s: float):
                       f"(fp64 C, OpenMP over tokens), {el:.1f} s"}
 
 
+def cpu_baseline_stack(st, budget_s: float):
+    """The oracle on the first tokens of the stack's input, layer after layer
+    until the budget is spent; tokens/s extrapolated to all layers.  Only the
+    oracle calls are timed (the host draws each layer's selected experts
+    between them)."""
+    import oracle
+    from sparse_moe_expert_sigmoid_amd import synth as S
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n_tok = min(st.T, threads, 16)
+    x = np.ascontiguousarray(S.stack_x(st)[:n_tok])
+    spent, layers_done = 0.0, 0
+    for l in range(st.layers):
+        s = st.layer(l)
+        wr, bias = S.stack_router(st, l)
+        t0 = time.perf_counter()
+        idx, w, _ = oracle.route(s.router, x, wr, bias, s.k, s.scale)
+        spent += time.perf_counter() - t0
+        uniq = np.unique(idx)
+        remap = np.full(s.E, -1, np.int64)
+        remap[uniq] = np.arange(len(uniq))
+        ex = oracle.Experts.of(S.expert_slice(s, uniq))
+        sh = oracle.Experts.of(S.expert_slice(s, [0], shared=True))
+        t0 = time.perf_counter()
+        offsets, row_token, token_row = oracle.permute(remap[idx].astype(np.int32), len(uniq))
+        rows = oracle.expert_rows(ex, x, row_token, offsets)
+        shr = oracle.expert_rows(sh, x, None, np.array([0, n_tok], np.int32))
+        y = oracle.combine(rows, token_row, w, shared=shr, residual=x)
+        spent += time.perf_counter() - t0
+        x = y.astype(np.float32)
+        layers_done += 1
+        if spent >= budget_s:
+            break
+    per_layer = spent / layers_done
+    return {"value": n_tok / (per_layer * st.layers), "unit": "tokens/s",
+            "cores": min(threads, n_tok), "kind": "oracle",
+            "sample": f"tokens 0..{n_tok - 1} through layers 0..{layers_done - 1} of the "
+                      f"{st.layers}-layer stack ({spent:.1f} s of oracle time), extrapolated "
+                      f"to {st.layers} layers"}
+
+
+def run_stack(args):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import Context, MoEStack, synth as S
+
+    T, desc = STACK_WORKLOADS[args.workload]
+    decode = T <= 16
+    steps = args.steps or (50 if decode else 5)
+    warmup = args.warmup if args.warmup is not None else (5 if decode else 1)
+    st = S.stack_spec(T)
+    dev = torch.device("cuda:0")
+    ctx = Context(0)
+    log(f"[bench] workload {args.workload}: drawing {st.layers} layers on the GPU")
+    stk = MoEStack.from_synth(ctx, st, dev, log=log)
+    x0 = torch.from_numpy(S.stack_x(st)).to(dev)
+    stream = torch.cuda.current_stream()
+    stk.forward(x0, stream=stream)
+    torch.cuda.synchronize()
+    use_graph = decode and not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            stk.forward(x0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            stk.forward(x0)
+        step = g.replay
+    else:
+        def step():
+            stk.forward(x0, stream=stream)
+    log(f"[bench] {stk.weight_bytes / 1e9:.1f} GB of weights; T={T}; "
+        f"{'HIP graph' if use_graph else 'eager'}; warmup {warmup}, steps {steps}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    tok_s = T / (ms_per_step / 1e3)
+    log(f"[bench] {ms_per_step:.3f} ms/step, {tok_s:,.1f} tokens/s (wall {wall:.3f} s)")
+
+    # ---- algorithmic work, from each layer's actual routing
+    s0 = st.layer(0)
+    d, I, Is, E, k = s0.d, s0.inter, s0.shared_inter, s0.E, s0.k
+    e_gu, e_dn = 2 * I * d + 2 * I * 4, d * I + d * 4          # codes + fp32 row scales
+    sh_gu, sh_dn = 2 * Is * d + 2 * Is * 4, d * Is + d * 4
+    touched, masses = [], []
+    for l in range(st.layers):
+        counts = np.bincount(stk.idx[l].cpu().numpy().ravel(), minlength=E)
+        touched.append(int((counts > 0).sum()))
+        masses.append(round(float(np.sort(counts)[::-1][:64].sum()) / counts.sum(), 4))
+    router_b = (E * d + E) * 4
+    step_bytes = sum(n * (e_gu + e_dn) + sh_gu + sh_dn + router_b + T * d * 4 * 2
+                     for n in touched)
+    step_flops = st.layers * 2.0 * (T * k * 3 * d * I + T * 3 * d * Is + T * d * E)
+    gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    tflops = step_flops / (ms_per_step / 1e3) / 1e12
+
+    kernels, roofline = {}, None
+    if not args.no_kernel_timing:
+        ctx.moe_timing(64 * st.layers * steps)
+        for _ in range(steps):
+            stk.forward(x0, stream=stream)
+        torch.cuda.synchronize()
+        kt = ctx.moe_timing_read()
+        ctx.moe_timing(0)
+        kernels = {n: {"launches": int(c), "avg_us": t / c * 1e3} for n, (c, t) in kt.items()}
+        R = T * k
+        if "ffn_i8_gate_up_gemm" in kt:
+            launches, tot_ms = kt["ffn_i8_gate_up_gemm"]
+            per_step_flops = st.layers * 2.0 * (R * 2 * I * d + T * 2 * Is * d)
+            per_launch = per_step_flops / (launches / steps)
+            avg_s = tot_ms / launches / 1e3
+            achieved = per_launch / avg_s / 1e12
+            roofline = {"bound": "mfma", "kernel": "ffn_i8_gate_up_gemm",
+                        "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                        "traffic": None, "flops_per_launch": per_launch,
+                        "avg_launch_us": round(avg_s * 1e6, 2),
+                        "frac_of_bf16_peak": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        elif "ffn_i8_gate_up" in kt:
+            launches, tot_ms = kt["ffn_i8_gate_up"]
+            per_step = sum(n * e_gu + sh_gu + T * d * 2 + (R * I + T * Is) * 2
+                           + (R * I + T * Is) // 64 * 4 for n in touched)
+            per_launch = per_step / (launches / steps)
+            avg_s = tot_ms / launches / 1e3
+            achieved = per_launch / avg_s / 1e9
+            roofline = {"bound": "hbm", "kernel": "ffn_i8_gate_up",
+                        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "bytes_per_launch": int(per_launch),
+                        "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_stack(st, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded generator, weights drawn on the GPU; random weights of the "
+                "stated shapes)",
+        "config": {"workload": desc, "T": T, "layers": st.layers, "d": d, "E": E, "k": k,
+                   "inter": I, "router": s0.router, "expert_format": s0.fmt,
+                   "shared_expert": s0.shared, "zipf_alpha": st.alpha,
+                   "hip_graph": use_graph, "entry_point": "moe_forward per layer",
+                   "parallelism": "single GPU"},
+        "hbm_gbps_algorithmic": round(gbs, 1),
+        "hbm_frac_algorithmic": round(gbs / HBM_PEAK_GBS, 4),
+        "tflops_algorithmic": round(tflops, 3),
+        "step_bytes_algorithmic": int(step_bytes),
+        "step_flops_algorithmic": step_flops,
+        "top64_mass_per_layer": masses,
+        "touched_experts_per_layer": touched,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="kimi_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="kimi_decode",
+                    choices=sorted(WORKLOADS) + sorted(STACK_WORKLOADS))
+    ap.add_argument("--no-graph", action="store_true",
+                    help="stack decode: launch the layers eagerly instead of replaying a HIP graph")
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--path", default="fused", choices=["fused", "staged"],
                     help="fused: one moe_forward call per step; staged: moe_route, "
@@ -138,9 +339,11 @@ def main():
               "has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in STACK_WORKLOADS:
+        return run_stack(args)
+
     import torch
     from sparse_moe_expert_sigmoid_amd import Context, MoELayer, synth as S
-    from sparse_moe_expert_sigmoid_amd.binding import DeviceExperts
 
     spec_name, chunks, desc = WORKLOADS[args.workload]
     spec = S.spec(spec_name)

@@ -1027,13 +1027,13 @@ hipError_t launch_gemm_pair(const Group& a, const Group& b, int d, const int8_t*
   const int tiles = a.tiles + b.tiles;
   const int imax = a.inter > b.inter ? a.inter : b.inter;
   {
-    TimedLaunch tl(K_FFN_I8_GATE_UP, s);
+    TimedLaunch tl(K_FFN_I8_GATE_UP_GEMM, s);
     hipLaunchKernelGGL(gate_up_gemm_kernel<LAY>, dim3((imax + 127) / 128, tiles), dim3(512), 0, s,
                        a, b, d, xq, xs);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  TimedLaunch tl(K_FFN_I8_DOWN, s);
+  TimedLaunch tl(K_FFN_I8_DOWN_GEMM, s);
   hipLaunchKernelGGL(down_gemm_kernel<LAY>, dim3((d + 127) / 128, tiles), dim3(512), 0, s, a, b,
                      d);
   return hipGetLastError();

@@ -1,0 +1,106 @@
+"""A stack of routed-MoE layers with the residual outside each layer:
+
+    x_{l+1} = x_l + MoE_l(x_l)            (one moe_forward call per layer)
+
+The residual add sits after the moe op (Qwen3-30B-A3B model card,
+"Conversion Notes"), so each layer passes its input as moe_forward's
+residual.  Activations ping-pong between two [T, d] buffers; the input x_0 is
+never written, so a captured HIP graph of the whole stack can be replayed on
+the same input.  All buffers, including one workspace shared by every layer,
+are allocated by alloc(T), never inside forward().
+"""
+from __future__ import annotations
+
+from typing import Callable, List, Optional
+
+import torch
+
+from .binding import MOE_ACT_SILU, Context, DeviceExperts, MOE_W_INT8_ROW
+from .layer import MoELayer
+
+
+class MoEStack:
+    def __init__(self, ctx: Context, layers: List[MoELayer]):
+        assert layers, "empty stack"
+        self.ctx = ctx
+        self.layers = layers
+        self.d, self.k = layers[0].d, layers[0].k
+        self.device = layers[0].device
+        self._T = None
+
+    @property
+    def weight_bytes(self) -> int:
+        n = 0
+        for L in self.layers:
+            n += L.experts.nbytes + (L.shared.nbytes if L.shared is not None else 0)
+            n += L.w_router.numel() * 4 + (L.bias.numel() * 4 if L.bias is not None else 0)
+        return n
+
+    def alloc(self, T: int):
+        if self._T == T:
+            return
+        dev, k, d = self.device, self.k, self.d
+        self.buf = [torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.idx = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in self.layers]
+        self.w = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in self.layers]
+        need = max(self.ctx.moe_layer_workspace_size(L.desc, T) for L in self.layers)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self._T = T
+
+    def forward(self, x0: torch.Tensor, stream=None,
+                before_layer: Optional[Callable[[int, torch.Tensor], None]] = None,
+                after_layer: Optional[Callable[[int, torch.Tensor, torch.Tensor], None]] = None
+                ) -> torch.Tensor:
+        """Runs every layer on x0 [T, d]; returns x_L (one of the two buffers).
+
+        before_layer(l, x_l) may modify x_l in place before layer l reads it
+        (x_0 itself is passed for l = 0); after_layer(l, x_l, x_{l+1}) sees
+        each layer's input and output.  Both run on the host between the
+        enqueues, so they are for tests, not for timed or captured runs."""
+        T, d = x0.shape
+        assert d == self.d and x0.dtype == torch.float32 and x0.is_contiguous()
+        self.alloc(T)
+        cur = x0
+        for l, L in enumerate(self.layers):
+            if before_layer is not None:
+                before_layer(l, cur)
+            out = self.buf[l % 2]
+            self.ctx.moe_forward(L.desc, MOE_ACT_SILU, cur, T, cur, out, self.idx[l], self.w[l],
+                                 self.ws, stream)
+            if after_layer is not None:
+                after_layer(l, cur, out)
+            cur = out
+        return cur
+
+    __call__ = forward
+
+    # ------------------------------------------------------------------
+    @staticmethod
+    def from_synth(ctx: Context, st, device="cuda:0", layers: Optional[int] = None,
+                   log: Optional[Callable[[str], None]] = None) -> "MoEStack":
+        """Builds the Kimi-shaped stack `st` (a synth.StackSpec): router weights
+        and biases drawn on the host, expert codes and scales drawn on the GPU
+        by the generator's device twin, codes converted to the tiled layout."""
+        from . import synth
+        n = st.layers if layers is None else layers
+        out = []
+        for l in range(n):
+            s = st.layer(l)
+            wr, bias = synth.stack_router(st, l)
+            parts = []
+            for shared in (False, True):
+                gu, gu_s, dn, dn_s = synth.dev_int8_experts(s, device, shared=shared)
+                E = 1 if shared else s.E
+                inter = s.shared_inter if shared else s.inter
+                rows = DeviceExperts(MOE_W_INT8_ROW, E, s.d, inter, gu, dn, gu_s, dn_s)
+                parts.append(rows.tiled(ctx))
+                del rows, gu, dn
+            L = MoELayer(ctx, s.router, s.k, s.scale, torch.from_numpy(wr).to(device),
+                         torch.from_numpy(bias).to(device), parts[0], parts[1])
+            out.append(L)
+            if log is not None and (l == 0 or (l + 1) % 5 == 0 or l + 1 == n):
+                torch.cuda.synchronize()
+                log(f"[stack] layer {l + 1}/{n} built")
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return MoEStack(ctx, out)

@@ -36,8 +36,14 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the generator with gcc (always recompiles)."""
+_DEV_LIB_PATH = os.path.join(_HERE, "libmoe_synth_dev.so")
+_dev_lib = None
+_HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def build(verbose: bool = False, device: bool = True) -> str:
+    """Compile the host generator with gcc and its device twin with hipcc for
+    gfx950 (always recompiles both; device=False skips the twin)."""
     import subprocess
     src = os.path.join(_HERE, "synth.c")
     tmp = _LIB_PATH + ".tmp"
@@ -47,6 +53,18 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
+    if device:
+        dsrc = os.path.join(_HERE, "synth_dev.hip")
+        dtmp = _DEV_LIB_PATH + ".tmp"
+        cmd = [_HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+               "-ffp-contract=off", "-Wall", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "-o", dtmp, dsrc]
+        if verbose:
+            print(" ".join(cmd))
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {dsrc}:\n{r.stderr}")
+        os.replace(dtmp, _DEV_LIB_PATH)
     return _LIB_PATH
 
 
@@ -65,11 +83,14 @@ def _load():
     lib.synth_uniform.argtypes = [u64, u64, i64, ctypes.c_float, ctypes.c_float, vp]
     lib.synth_normal.argtypes = [u64, u64, i64, ctypes.c_double, vp]
     lib.synth_randint8.argtypes = [u64, u64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.synth_randint8_at.argtypes = [u64, u64, u64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.synth_scale_at.argtypes = [u64, u64, u64, i64, ctypes.c_float, u64, vp, ctypes.c_int,
+                                   ctypes.c_float, vp]
     lib.synth_scale.argtypes = [u64, u64, i64, ctypes.c_float, u64, vp, ctypes.c_int,
                                 ctypes.c_float, vp]
     lib.synth_pack_int4.argtypes = [vp, i64, vp]
     for f in ("synth_splitmix64", "synth_hash", "synth_uniform", "synth_normal", "synth_randint8",
-              "synth_scale", "synth_pack_int4"):
+              "synth_scale", "synth_pack_int4", "synth_randint8_at", "synth_scale_at"):
         getattr(lib, f).restype = None
     _lib = lib
     return lib
@@ -108,9 +129,10 @@ def normal(seed: int, tid: int, shape, std: float) -> np.ndarray:
     return out
 
 
-def randint8(seed: int, tid: int, shape, lo: int, hi: int) -> np.ndarray:
+def randint8(seed: int, tid: int, shape, lo: int, hi: int, start: int = 0) -> np.ndarray:
+    """Elements start .. start+size-1 of the int8 tensor (seed, tid)."""
     out = np.empty(shape, dtype=np.int8)
-    _load().synth_randint8(seed, tid, out.size, lo, hi, _ptr(out))
+    _load().synth_randint8_at(seed, tid, start, out.size, lo, hi, _ptr(out))
     return out
 
 
@@ -121,11 +143,65 @@ CLAMP_SPECIALS = np.array([0.0, 1e-40, 2.0 ** -20, 0.999 * 2.0 ** -14], dtype=np
 TWO_M14 = np.float32(2.0 ** -14)
 
 
-def scales(seed: int, tid: int, shape, c: float, special_tid: int = 0) -> np.ndarray:
+def scales(seed: int, tid: int, shape, c: float, special_tid: int = 0,
+           start: int = 0) -> np.ndarray:
+    """Elements start .. start+size-1 of the scale tensor (seed, tid)."""
     out = np.empty(shape, dtype=np.float32)
     sp = CLAMP_SPECIALS
-    _load().synth_scale(seed, tid, out.size, float(np.float32(c)), special_tid, _ptr(sp),
-                        len(sp), float(TWO_M14), _ptr(out))
+    _load().synth_scale_at(seed, tid, start, out.size, float(np.float32(c)), special_tid,
+                           _ptr(sp), len(sp), float(TWO_M14), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# device twin (libmoe_synth_dev.so): the same draws written straight into HBM
+# --------------------------------------------------------------------------
+
+def _load_dev():
+    global _dev_lib
+    if _dev_lib is not None:
+        return _dev_lib
+    if not os.path.exists(_DEV_LIB_PATH):
+        raise RuntimeError(f"{_DEV_LIB_PATH} is not built; run build() first")
+    lib = ctypes.CDLL(_DEV_LIB_PATH)
+    u64, i64, vp, ci = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.synth_dev_randint8.argtypes = [u64, u64, u64, i64, ci, ci, vp, vp]
+    lib.synth_dev_scale.argtypes = [u64, u64, u64, i64, ctypes.c_float, u64, vp, ci,
+                                    ctypes.c_float, vp, vp]
+    lib.synth_dev_randint8.restype = ci
+    lib.synth_dev_scale.restype = ci
+    _dev_lib = lib
+    return lib
+
+
+def _stream_handle(stream):
+    import torch
+    st = torch.cuda.current_stream() if stream is None else stream
+    return st.cuda_stream
+
+
+def dev_randint8(seed: int, tid: int, out, lo: int, hi: int, start: int = 0, stream=None):
+    """Fill the int8 torch tensor `out` (contiguous, on the GPU) with elements
+    start .. start+numel-1 of the tensor (seed, tid)."""
+    assert out.is_contiguous() and out.dtype.itemsize == 1
+    rc = _load_dev().synth_dev_randint8(seed, tid, start, out.numel(), lo, hi, out.data_ptr(),
+                                        _stream_handle(stream))
+    if rc != 0:
+        raise RuntimeError(f"synth_dev_randint8 failed (hip error {rc})")
+    return out
+
+
+def dev_scales(seed: int, tid: int, out, c: float, special_tid: int = 0, start: int = 0,
+               stream=None):
+    """Fill the fp32 torch tensor `out` on the GPU with scale elements
+    start .. start+numel-1 of (seed, tid), as scales() draws them."""
+    assert out.is_contiguous() and out.dtype.itemsize == 4
+    sp = CLAMP_SPECIALS
+    rc = _load_dev().synth_dev_scale(seed, tid, start, out.numel(), float(np.float32(c)),
+                                     special_tid, _ptr(sp), len(sp), float(TWO_M14),
+                                     out.data_ptr(), _stream_handle(stream))
+    if rc != 0:
+        raise RuntimeError(f"synth_dev_scale failed (hip error {rc})")
     return out
 
 
@@ -284,3 +360,147 @@ def make_layer(s: LayerSpec, with_x: bool = True) -> LayerInputs:
                                TID_SH_GU_SPECIAL, TID_SH_DN_SPECIAL))
     x = make_x(s) if with_x else None
     return LayerInputs(s, x, wr, bias, experts, shared)
+
+
+# --------------------------------------------------------------------------
+# slices of one layer's experts (host), and whole layers drawn on the device
+# --------------------------------------------------------------------------
+
+_ROUTED_TIDS = (TID_GU, TID_GU_S, TID_DN, TID_DN_S, TID_GU_SPECIAL, TID_DN_SPECIAL)
+_SHARED_TIDS = (TID_SH_GU, TID_SH_GU_S, TID_SH_DN, TID_SH_DN_S, TID_SH_GU_SPECIAL,
+                TID_SH_DN_SPECIAL)
+
+
+def expert_slice(s: LayerSpec, experts, shared: bool = False) -> ExpertWeights:
+    """The listed experts of the layer (routed, or the shared one with
+    experts=[0]) as an ExpertWeights with E = len(experts), in list order;
+    equal to indexing the arrays make_layer() draws, without drawing the rest."""
+    fmt = s.shared if shared else s.fmt
+    inter = s.shared_inter if shared else s.inter
+    d = s.d
+    t_gu, t_gu_s, t_dn, t_dn_s, t_gu_sp, t_dn_sp = _SHARED_TIDS if shared else _ROUTED_TIDS
+    if fmt not in (FMT_INT8_ROW, FMT_INT4_B32):
+        raise ValueError(f"expert_slice: format {fmt} is drawn whole only")
+    n = len(experts)
+    lo, hi = (-127, 127) if fmt == FMT_INT8_ROW else (-8, 7)
+    gu = np.empty((n, 2 * inter, d), np.int8)
+    dn = np.empty((n, d, inter), np.int8)
+    if fmt == FMT_INT8_ROW:
+        gu_s = np.empty((n, 2 * inter), np.float32)
+        dn_s = np.empty((n, d), np.float32)
+    else:
+        gu_s = np.empty((n, 2 * inter, d // 32), np.float32)
+        dn_s = np.empty((n, d, inter // 32), np.float32)
+    c_gu = 1.0 / ((127.0 if fmt == FMT_INT8_ROW else 8.0) * math.sqrt(d))
+    c_dn = 1.0 / ((127.0 if fmt == FMT_INT8_ROW else 8.0) * math.sqrt(inter))
+    sp_gu, sp_dn = (0, 0) if fmt == FMT_INT8_ROW else (t_gu_sp, t_dn_sp)
+    for q, e in enumerate(experts):
+        e = int(e)
+        gu[q] = randint8(s.wseed, t_gu, gu[q].shape, lo, hi, start=e * gu[q].size)
+        dn[q] = randint8(s.wseed, t_dn, dn[q].shape, lo, hi, start=e * dn[q].size)
+        gu_s[q] = scales(s.wseed, t_gu_s, gu_s[q].shape, c_gu, sp_gu, start=e * gu_s[q].size)
+        dn_s[q] = scales(s.wseed, t_dn_s, dn_s[q].shape, c_dn, sp_dn, start=e * dn_s[q].size)
+    w = ExpertWeights(fmt, n, d, inter, gu, dn, gu_s, dn_s)
+    if fmt == FMT_INT4_B32:
+        w.gu_packed, w.dn_packed = pack_int4(gu), pack_int4(dn)
+    return w
+
+
+def dev_int8_experts(s: LayerSpec, device, shared: bool = False, stream=None):
+    """Codes and scales of the layer's routed experts (or its shared expert)
+    drawn on the GPU, row-major, bit-identical to make_experts():
+    (gu [E,2I,d] int8, gu_s [E,2I] fp32, dn [E,d,I] int8, dn_s [E,d] fp32)."""
+    import torch
+    fmt = s.shared if shared else s.fmt
+    if fmt != FMT_INT8_ROW:
+        raise ValueError("dev_int8_experts draws int8 per-row experts only")
+    E = 1 if shared else s.E
+    inter = s.shared_inter if shared else s.inter
+    d = s.d
+    t_gu, t_gu_s, t_dn, t_dn_s, _, _ = _SHARED_TIDS if shared else _ROUTED_TIDS
+    gu = torch.empty((E, 2 * inter, d), dtype=torch.int8, device=device)
+    dn = torch.empty((E, d, inter), dtype=torch.int8, device=device)
+    gu_s = torch.empty((E, 2 * inter), dtype=torch.float32, device=device)
+    dn_s = torch.empty((E, d), dtype=torch.float32, device=device)
+    dev_randint8(s.wseed, t_gu, gu, -127, 127, stream=stream)
+    dev_randint8(s.wseed, t_dn, dn, -127, 127, stream=stream)
+    dev_scales(s.wseed, t_gu_s, gu_s, 1.0 / (127.0 * math.sqrt(d)), stream=stream)
+    dev_scales(s.wseed, t_dn_s, dn_s, 1.0 / (127.0 * math.sqrt(inter)), stream=stream)
+    return gu, gu_s, dn, dn_s
+
+
+# --------------------------------------------------------------------------
+# the 26-layer Kimi-shaped stack with Zipf-skewed routing
+# --------------------------------------------------------------------------
+#
+# Layer l has its own weights (seed 0x4D6F4400 + l) and a selection bias
+#     b_l[e] = fp32( u_l[e] + alpha * r_l(e)^-1.1 ),   u_l ~ U(-0.1, 0.1)
+# where r_l is a seeded permutation of the ranks 1..E.  alpha is chosen once
+# (tests/golden/make_stack_zipf.py, by bisection with the oracle's router on
+# layer 0 at T=4096) so that the 64 most-selected experts take about 73% of
+# the selections, the concentration the code-corpus routing statistics of
+# the Kimi-Linear-48B-A3B-Code-CMF listing ("How it was made") report.  The
+# stack is x_{l+1} = x_l + MoE_l(x_l): the residual sits outside the layer
+# (Qwen3-30B-A3B model card, "Conversion Notes") and no norm is given.
+
+STACK_LAYERS = 26
+ZIPF_S = 1.1
+TID_ZIPF_RANK = 16
+STACK_X_SEED = _seed(4)
+ZIPF_FILE = os.path.join(os.path.dirname(os.path.dirname(_HERE)), "tests", "golden",
+                         "kimi_stack_zipf.json")
+
+
+def stack_wseed(l: int) -> int:
+    return 0x4D6F4400 + l
+
+
+def zipf_ranks(seed: int, E: int) -> np.ndarray:
+    """A seeded permutation of 1..E: expert e gets rank r[e] (1 = most favoured)."""
+    order = np.argsort(hashes(seed, TID_ZIPF_RANK, E), kind="stable")
+    r = np.empty(E, np.int64)
+    r[order] = np.arange(1, E + 1)
+    return r
+
+
+def zipf_bias(seed: int, E: int, alpha: float) -> np.ndarray:
+    u = uniform(seed, TID_BIAS, (E,), -0.1, 0.1).astype(np.float64)
+    r = zipf_ranks(seed, E).astype(np.float64)
+    return (u + alpha * r ** -ZIPF_S).astype(np.float32)
+
+
+def stack_alpha() -> float:
+    import json
+    with open(ZIPF_FILE) as f:
+        return float(json.load(f)["alpha"])
+
+
+@dataclass(frozen=True)
+class StackSpec:
+    name: str
+    layers: int
+    T: int
+    alpha: float
+    base: LayerSpec
+
+    def layer(self, l: int) -> LayerSpec:
+        return replace(self.base, name=f"{self.name}[{l}]", T=self.T, wseed=stack_wseed(l),
+                       xseed=STACK_X_SEED)
+
+
+def stack_spec(T: int, layers: int = STACK_LAYERS, alpha: Optional[float] = None,
+               name: Optional[str] = None) -> StackSpec:
+    a = stack_alpha() if alpha is None else float(alpha)
+    return StackSpec(name or f"kimi_stack_T{T}", layers, T, a, SPECS["kimi_decode"])
+
+
+def stack_router(st: StackSpec, l: int):
+    """(w_router [E,d] fp32, bias [E] fp32) of layer l."""
+    s = st.layer(l)
+    wr = normal(s.wseed, TID_WR, (s.E, s.d), 1.0 / math.sqrt(s.d))
+    return wr, zipf_bias(s.wseed, s.E, st.alpha)
+
+
+def stack_x(st: StackSpec) -> np.ndarray:
+    """x_0 [T, d]: the first T rows of one N(0,1) tensor (T=1 is row 0 of T=4096)."""
+    return normal(STACK_X_SEED, TID_X, (st.T, st.base.d), 1.0)

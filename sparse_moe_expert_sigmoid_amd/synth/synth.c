@@ -85,15 +85,21 @@ void synth_normal(uint64_t seed, uint64_t tid, int64_t n, double std, float* out
     }
 }
 
-/* Uniform integers on [lo, hi] (inclusive), stored as int8. */
-void synth_randint8(uint64_t seed, uint64_t tid, int64_t n, int lo, int hi, int8_t* out) {
+/* Uniform integers on [lo, hi] (inclusive), stored as int8: elements
+ * start .. start+n-1 of the tensor (out[i] is element start + i). */
+void synth_randint8_at(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, int lo, int hi,
+                       int8_t* out) {
     uint64_t key = synth_key(seed, tid);
     uint64_t span = (uint64_t)(hi - lo + 1);
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        uint64_t h = hash_at(key, (uint64_t)i);
+        uint64_t h = hash_at(key, start + (uint64_t)i);
         out[i] = (int8_t)(lo + (int)(((h >> 32) * span) >> 32));
     }
+}
+
+void synth_randint8(uint64_t seed, uint64_t tid, int64_t n, int lo, int hi, int8_t* out) {
+    synth_randint8_at(seed, tid, 0, n, lo, hi, out);
 }
 
 /*
@@ -102,23 +108,30 @@ void synth_randint8(uint64_t seed, uint64_t tid, int64_t n, int lo, int hi, int8
  * takes one of `n_special` listed values (chosen by the hash) and about 1 in
  * 1024 others takes `exact_value`.  This is how inputs exercise a clamp.
  */
-void synth_scale(uint64_t seed, uint64_t tid, int64_t n, float c,
-                 uint64_t special_tid, const float* special, int n_special,
-                 float exact_value, float* out) {
+void synth_scale_at(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, float c,
+                    uint64_t special_tid, const float* special, int n_special,
+                    float exact_value, float* out) {
     uint64_t key = synth_key(seed, tid);
     uint64_t skey = synth_key(seed, special_tid);
     #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i) {
-        float u = uniform24(hash_at(key, (uint64_t)i));
+    for (int64_t j = 0; j < n; ++j) {
+        uint64_t i = start + (uint64_t)j;
+        float u = uniform24(hash_at(key, i));
         float v = (0.5f + u) * c;
         if (special_tid != 0) {
-            uint64_t hs = hash_at(skey, (uint64_t)i);
+            uint64_t hs = hash_at(skey, i);
             uint64_t sel = hs >> 54;                 /* 10 bits */
             if (sel == 0 && n_special > 0) v = special[(hs >> 20) % (uint64_t)n_special];
             else if (sel == 1) v = exact_value;
         }
-        out[i] = v;
+        out[j] = v;
     }
+}
+
+void synth_scale(uint64_t seed, uint64_t tid, int64_t n, float c,
+                 uint64_t special_tid, const float* special, int n_special,
+                 float exact_value, float* out) {
+    synth_scale_at(seed, tid, 0, n, c, special_tid, special, n_special, exact_value, out);
 }
 
 /*

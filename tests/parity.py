@@ -12,6 +12,9 @@
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 GAP_TOL = 1e-6
@@ -66,3 +69,12 @@ def compare_outputs(gy, oy, keep=None, tol=Y_TOL):
     ratio = err / scale
     assert ratio <= tol, f"max|err| = {err:.3e} = {ratio:.3e} x max|y| (bound {tol})"
     return ratio
+
+
+def log_result(**kw):
+    """Print one result record and append it to $MOE_PARITY_LOG (JSON lines)."""
+    path = os.environ.get("MOE_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(kw) + "\n")
+    print(kw, flush=True)

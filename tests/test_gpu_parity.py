@@ -6,28 +6,19 @@ prefill, Qwen3-shaped int4 decode and prefill) plus edge cases: T = 0 and 1,
 ragged expert row counts, every token on the same experts (many tiles per
 expert), E = k, and int4 scales at, below and far below 2^-14.
 """
-import json
-import math
-import os
-
 import numpy as np
 import pytest
 
 import oracle
 from sparse_moe_expert_sigmoid_amd import synth as S
-from tests.parity import compare_outputs, compare_route, oracle_keys
+from tests.parity import compare_outputs, compare_route, log_result, oracle_keys
 
 pytestmark = pytest.mark.gpu
 
 _CACHE = {}
 
 
-def _log(**kw):
-    path = os.environ.get("MOE_PARITY_LOG")
-    if path:
-        with open(path, "a") as f:
-            f.write(json.dumps(kw) + "\n")
-    print(kw, flush=True)
+_log = log_result
 
 
 def inputs(name, **kw):

@@ -1,0 +1,203 @@
+"""GPU: the generator's device twin, and the 26-layer Kimi-shaped stack
+against the oracle.
+
+The stack (26 distinct layers, d=2304, E=256, top 8, I=2048, int8 per-row
+experts and shared expert, Zipf-skewed selection bias) holds about 95 GB of
+weights, drawn on the GPU.  It is checked layer by layer with teacher
+forcing on sampled tokens: before layer l the sampled rows of the GPU's
+x_l are overwritten with the oracle's x_l, and the GPU's layer-l routing and
+output rows are compared with the oracle's.  Tokens are independent (no
+capacity limit, no cross-token step), so the other T - S rows only provide
+the real load: expert row counts, tile shapes and kernel choices at T=4096.
+The oracle draws only the experts the sampled tokens select.  The
+free-running 26-layer difference is reported but not asserted: one excused
+near-tie flip legitimately changes everything downstream.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_moe_expert_sigmoid_amd import synth as S
+from tests.parity import Y_TOL, compare_route, log_result as _log, oracle_keys
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx(gpu):
+    from sparse_moe_expert_sigmoid_amd import Context
+    return Context(0)
+
+
+# ------------------------------------------------------------ device generator
+
+def test_device_generator_bit_exact(ctx):
+    import torch
+    s = S.spec("kimi_decode")
+    gu, gu_s, dn, dn_s = S.dev_int8_experts(s, "cuda:0")
+    sh = S.dev_int8_experts(s, "cuda:0", shared=True)
+    torch.cuda.synchronize()
+    for e in (0, 77, 255):
+        h = S.expert_slice(s, [e])
+        assert np.array_equal(gu[e].cpu().numpy(), h.gu[0])
+        assert np.array_equal(dn[e].cpu().numpy(), h.dn[0])
+        assert np.array_equal(gu_s[e].cpu().numpy(), h.gu_s[0])
+        assert np.array_equal(dn_s[e].cpu().numpy(), h.dn_s[0])
+    hs = S.expert_slice(s, [0], shared=True)
+    for a, b in zip(sh, (hs.gu, hs.gu_s, hs.dn, hs.dn_s)):
+        assert np.array_equal(a.cpu().numpy(), b)
+    del gu, gu_s, dn, dn_s, sh
+    # ragged length, offset start, and the clamp specials of int4 block scales
+    t = torch.empty(1000003, dtype=torch.int8, device="cuda:0")
+    S.dev_randint8(11, 4, t, -8, 7, start=12345)
+    sc = torch.empty(300001, dtype=torch.float32, device="cuda:0")
+    S.dev_scales(11, 5, sc, 1.0 / (8 * 48.0), special_tid=12, start=999)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), S.randint8(11, 4, (1000003,), -8, 7, start=12345))
+    hsc = S.scales(11, 5, (300001,), 1.0 / (8 * 48.0), special_tid=12, start=999)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), hsc.view(np.uint32))
+    assert (hsc < 2.0 ** -14).sum() > 0 and (hsc == np.float32(2.0 ** -14)).sum() > 0
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ the stack
+
+@pytest.fixture(scope="module")
+def stack(ctx):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import MoEStack
+    st = S.stack_spec(4096)
+    print(f"[stack] building {st.layers} layers on the GPU", flush=True)
+    stk = MoEStack.from_synth(ctx, st, log=lambda m: print(m, flush=True))
+    print(f"[stack] {stk.weight_bytes / 1e9:.1f} GB of weights", flush=True)
+    yield st, stk
+    del stk
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+class _OracleStack:
+    """The oracle's trajectory x_0 .. x_L for a few tokens: per layer its
+    router on all E experts, then only the selected experts (drawn by
+    element offset) through the staged oracle calls.  Renumbering the
+    selected experts to 0..n-1 is the slice of the experts that the
+    mask-equals-slice pin covers."""
+
+    def __init__(self, st, x0):
+        self.st = st
+        self.x = [np.ascontiguousarray(x0, dtype=np.float32)]
+        self.route, self.y = [], []
+
+    def layer(self, l, x):
+        st = self.st
+        s = st.layer(l)
+        wr, bias = S.stack_router(st, l)
+        idx, w, gap, logits = oracle.route(s.router, x, wr, bias, s.k, s.scale,
+                                           want_logits=True)
+        uniq = np.unique(idx)
+        remap = np.full(s.E, -1, np.int64)
+        remap[uniq] = np.arange(len(uniq))
+        idx_c = remap[idx].astype(np.int32)
+        ex = oracle.Experts.of(S.expert_slice(s, uniq))
+        sh = oracle.Experts.of(S.expert_slice(s, [0], shared=True))
+        offsets, row_token, token_row = oracle.permute(idx_c, len(uniq))
+        rows = oracle.expert_rows(ex, x, row_token, offsets)
+        n = x.shape[0]
+        shr = oracle.expert_rows(sh, x, None, np.array([0, n], np.int32))
+        y = oracle.combine(rows, token_row, w, shared=shr)
+        keys = oracle_keys(s.router, logits, bias)
+        return idx, w, gap, keys, y
+
+    def run(self):
+        for l in range(self.st.layers):
+            r = self.layer(l, self.x[-1])
+            self.route.append(r[:4])
+            self.y.append(r[4])
+            self.x.append((self.x[-1].astype(np.float64) + r[4]).astype(np.float32))
+        return self
+
+
+def _stack_teacher_forced(st, stk, T, sample):
+    import torch
+    x0 = S.stack_x(S.stack_spec(4096))[:T]
+    sample = np.asarray(sample)
+    orc = _OracleStack(st, x0[sample]).run()
+    xd = torch.from_numpy(np.ascontiguousarray(x0)).to("cuda:0")
+    sel = torch.from_numpy(sample).to("cuda:0")
+    results = []
+
+    def before(l, xl):
+        xl[sel] = torch.from_numpy(orc.x[l]).to("cuda:0")
+
+    def after(l, xin, xout):
+        torch.cuda.synchronize()
+        s = st.layer(l)
+        gidx = stk.idx[l][sel].cpu().numpy()
+        gw = stk.w[l][sel].cpu().numpy()
+        oidx, ow, ogap, keys = orc.route[l]
+        exc = compare_route(gidx, gw, oidx, ow, ogap, keys, s.scale)
+        keep = np.setdiff1d(np.arange(len(sample)), exc)
+        gy = xout[sel].cpu().numpy().astype(np.float64) - orc.x[l].astype(np.float64)
+        oy = orc.y[l]
+        scale = float(np.abs(oy).max())
+        err = float(np.abs(gy[keep] - oy[keep]).max()) if keep.size else 0.0
+        # fp32 rounding of the residual add is below ulp(|x_{l+1}|)
+        bound = Y_TOL * scale + 2.0 ** -23 * float(np.abs(orc.x[l + 1]).max())
+        assert err <= bound, f"layer {l}: max|err| {err:.3e} > {bound:.3e}"
+        counts = np.bincount(stk.idx[l].cpu().numpy().ravel(), minlength=s.E)
+        mass = float(np.sort(counts)[::-1][:64].sum()) / counts.sum()
+        results.append((l, len(exc), err / scale, mass, int(counts.max())))
+
+    with torch.no_grad():
+        stk.forward(xd, before_layer=before, after_layer=after)
+    torch.cuda.synchronize()
+    for l, exc, ratio, mass, cmax in results:
+        _log(test="stack_teacher_forced", T=T, layer=l, checked_tokens=len(sample), excused=exc,
+             err_over_max=ratio, top64_mass=round(mass, 4), max_rows_per_expert=cmax)
+    # free-running: reported only
+    xf = stk.forward(xd)
+    torch.cuda.synchronize()
+    diff = np.abs(xf[sel].cpu().numpy().astype(np.float64) - orc.x[-1]).max()
+    _log(test="stack_free_running", T=T, layers=st.layers,
+         max_abs_diff_final=float(diff), max_abs_final=float(np.abs(orc.x[-1]).max()))
+    return results
+
+
+def test_stack_prefill_T4096_teacher_forced(stack):
+    st, stk = stack
+    res = _stack_teacher_forced(st, stk, 4096, [0, 1717, 4095])
+    assert len(res) == st.layers
+    assert 0.70 <= res[0][3] <= 0.76     # the calibrated skew on layer 0
+
+
+def test_stack_decode_T1_teacher_forced(stack):
+    st, stk = stack
+    res = _stack_teacher_forced(st, stk, 1, [0])
+    assert len(res) == st.layers
+
+
+def test_stack_decode_graph_replays_match_eager(stack):
+    """The T=1 stack captured in a HIP graph: every replay, with eager work
+    and synchronisations between replays, equals the eager run bit-exactly."""
+    import torch
+    st, stk = stack
+    x0 = torch.from_numpy(S.stack_x(S.stack_spec(1))).to("cuda:0")
+    eager = stk.forward(x0).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stk.forward(x0)                       # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        out = stk.forward(x0)
+    for rep in range(4):
+        stk.buf[0].fill_(float("nan"))          # eager work between replays
+        stk.buf[1].fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+    del g
