@@ -183,6 +183,8 @@ def run_stack(args):
     steps = args.steps or (50 if decode else 5)
     warmup = args.warmup if args.warmup is not None else (5 if decode else 1)
     st = S.stack_spec(T)
+    if args.layers is not None:
+        st = S.StackSpec(st.name, args.layers, st.T, st.alpha, st.base)
     dev = torch.device("cuda:0")
     ctx = Context(0)
     log(f"[bench] workload {args.workload}: drawing {st.layers} layers on the GPU")
@@ -320,6 +322,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="kimi_decode",
                     choices=sorted(WORKLOADS) + sorted(STACK_WORKLOADS))
+    ap.add_argument("--layers", type=int, default=None,
+                    help="stack workloads: run only the first N of the 26 layers")
     ap.add_argument("--no-graph", action="store_true",
                     help="stack decode: launch the layers eagerly instead of replaying a HIP graph")
     ap.add_argument("--copies", type=int, default=None)

@@ -193,6 +193,11 @@ __device__ inline v4i i8_load(const int8_t* base, int step) {
   return __builtin_nontemporal_load(
       reinterpret_cast<const v4i*>(base + (LAY == kRows ? 64 : 1024) * step));
 }
+// Ordinary (cached) load: for weights that several tiles of one expert read.
+template <int LAY>
+__device__ inline v4i i8_load_cached(const int8_t* base, int step) {
+  return *reinterpret_cast<const v4i*>(base + (LAY == kRows ? 64 : 1024) * step);
+}
 
 template <int LAY>
 __device__ inline const uint8_t* i4_operand_base(const uint8_t* W, size_t row0, int K, int i,
@@ -594,247 +599,456 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 }
 
 // ------------------------------------------------------------------ prefill GEMM
-// Many rows per expert: a tile is up to 64 rows (4 groups of 16); a
-// workgroup of 8 wavefronts owns 128 output columns (16 per wavefront) of one
-// tile.  The tile's activation digits are staged in LDS 256 inputs at a time
-// (double-buffered) and shared by the 8 wavefronts; each wavefront streams its
-// weight rows and runs 4 row groups x 2 digits MFMAs per weight fragment, so
-// every weight byte read from HBM feeds up to 64 rows.  Software pipeline per
-// chunk c: weight fragments of chunk c+1 and the activation digits of chunk
-// c+1 are loaded into registers, chunk c is computed, the digits go to the
-// other LDS buffer, one barrier.
-constexpr int kGemmRows = 64, kGemmChunk = 256, kGemmWaves = 8;
-constexpr int kGemmLdr = 2 * kGemmChunk + 16;              // LDS bytes per staged row
-constexpr int kGemmStage = kGemmRows * 32 / (kGemmWaves * kWave);  // 16-B pieces per thread
+// Many rows per expert: a tile is up to 128 rows of one expert.  A workgroup
+// of 8 wavefronts covers the tile and 128 output columns (gate/up: 256 weight
+// rows) or 256 (down); wavefront w takes tile rows [64 (w / 4), +64) and the
+// weight row groups of its 32 (gate/up) or 64 (down) columns.  Per 64-wide
+// K-step a wavefront runs 4 weight fragments x 4 row groups x 2 digits = 32
+// MFMAs, all operands read from LDS.
+//
+// Both operands reach LDS by direct global-to-LDS loads (no registers): per
+// K-step 16 weight blocks (each an MFMA A operand of 1 KB, contiguous in the
+// tiled layout) and 16 digit blocks (row group x digit, gathered by row), 4
+// loads per wavefront.  A ring of four K-step slots keeps three K-steps in
+// flight.  Every wavefront issues the same loads in the same order on every
+// K-step (rows past the tile re-read row 0, K-steps past the end re-read the
+// last one), so before the barrier of K-step s each wavefront waits until at
+// most the 8 (down: 10) loads of K-steps s+1, s+2 are still in flight: its own
+// part of slot s has landed, and after the barrier every part has.  The
+// barrier is a bare s_barrier between compiler fences: no wait on the loads
+// still in flight.  The slots are separate LDS arrays so that the compiler
+// can tell the loads into one slot from the reads of another.
+constexpr int kPTok = 128, kPWaves = 8, kPSlots = 4;
+constexpr int kPBlk = 1024;                 // one MFMA operand
+constexpr int kPSlotBytes = 32 * kPBlk;     // 16 weight blocks + 16 digit blocks
 
-// Loads (into registers) this thread's pieces of the digit rows of one chunk:
-// piece q = tid + 512 u covers row q/32, digit (q%32)/16, bytes 16*(q%16).
-struct StageRegs {
-  v4i v[kGemmStage];
-};
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
+#define MOE_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | ((((n) >> 4) & 3) << 14))
 
-__device__ inline void stage_load(StageRegs& st, const int8_t* __restrict__ base, int rowbytes,
-                                  int plane, const int* rows, int nr, int k0, int nst) {
-#pragma unroll
-  for (int u = 0; u < kGemmStage; ++u) {
-    const int q = threadIdx.x + u * kGemmWaves * kWave;
-    const int j = q >> 5, c = q & 31;
-    st.v[u] = v4i{0, 0, 0, 0};
-    if (j < nr && 16 * (c & 15) < nst * kKStep)
-      st.v[u] = *reinterpret_cast<const v4i*>(base + (size_t)rows[j] * rowbytes +
-                                              (c < 16 ? 0 : plane) + k0 + 16 * (c & 15));
-  }
+__device__ inline void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-__device__ inline void stage_store(const StageRegs& st, int8_t* buf) {
-#pragma unroll
-  for (int u = 0; u < kGemmStage; ++u) {
-    const int q = threadIdx.x + u * kGemmWaves * kWave;
-    const int j = q >> 5, c = q & 31;
-    *reinterpret_cast<v4i*>(buf + j * kGemmLdr + (c < 16 ? 0 : kGemmChunk) + 16 * (c & 15)) =
-        st.v[u];
-  }
+// Direct global-to-LDS loads: lane l's 16 (4) bytes land at dst + 16 l (4 l).
+__device__ inline void lds_load16(const void* src, int8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
+__device__ inline void lds_load4(const void* src, int8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+__device__ inline v4i lds_frag(const int8_t* blk, int lane) {
+  return *reinterpret_cast<const v4i*>(blk + 16 * lane);
+}
+
+// Source of weight block "row group rg (16 rows from row0), K-step s" for this
+// lane: tiled = the block itself; rows = the lane's row and 16 bytes.
+template <int LAY>
+__device__ inline const int8_t* wblock_src(const int8_t* W, size_t row0, int K, int lane) {
+  return LAY == kRows ? W + (row0 + (lane & 15)) * K + 16 * (lane >> 4)
+                      : W + row0 * K + 16 * lane;
+}
+template <int LAY>
+constexpr int wblock_step() {
+  return LAY == kRows ? kKStep : kPBlk;
+}
+
+#define RING_SLOT(q) ((q) == 0 ? ring0 : (q) == 1 ? ring1 : (q) == 2 ? ring2 : ring3)
 
 template <int LAY>
 __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, int d,
                                                            const int8_t* __restrict__ xq,
                                                            const float* __restrict__ xs) {
-  __shared__ __attribute__((aligned(16))) int8_t bsm[2][kGemmRows * kGemmLdr];
-  __shared__ float red_max[kGemmWaves][kGemmRows];
-  __shared__ int tok_sm[kGemmRows];
+  __shared__ __attribute__((aligned(16))) int8_t ring0[kPSlotBytes];
+  __shared__ __attribute__((aligned(16))) int8_t ring1[kPSlotBytes];
+  __shared__ __attribute__((aligned(16))) int8_t ring2[kPSlotBytes];
+  __shared__ __attribute__((aligned(16))) int8_t ring3[kPSlotBytes];
+  __shared__ float red_max[4][kPTok];
+  __shared__ int tok_sm[kPTok];
   Job job;
-  if (!find_job(g0, g1, kGemmRows, blockIdx.y, job)) return;
+  if (!find_job(g0, g1, kPTok, blockIdx.y, job)) return;
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
-  if ((int)blockIdx.x * 128 >= I) return;
+  const int cb = blockIdx.x * 128;
+  if (cb >= I) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int c0 = blockIdx.x * 128 + wave * 16;
-  const bool active = c0 < I;  // every wavefront stays for the barriers
+  const int wc = wave & 3, wt = wave >> 2;
+  const int c0 = cb + wc * 32;
   const int i = lane & 15, g = lane >> 4;
-  const int ntg = (job.nr + 15) / 16;
-  for (int j = threadIdx.x; j < kGemmRows; j += blockDim.x)
-    tok_sm[j] = j < job.nr ? (G.row_token ? G.row_token[job.r0 + j] : job.r0 + j) : 0;
+  const int ntg = min(4, max(0, (job.nr - 64 * wt + 15) / 16));
+  const bool active = c0 < I && ntg > 0;  // every wavefront issues loads and meets the barriers
+  for (int j = threadIdx.x; j < kPTok; j += blockDim.x)
+    tok_sm[j] = j < job.nr ? (G.row_token ? G.row_token[job.r0 + j] : job.r0 + j) : -1;
   __syncthreads();
 
-  const size_t row0 = (size_t)job.e * 2 * I + (active ? c0 : 0);
-  const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wgu), row0, d, i, g, lane);
-  const int8_t* wb = wa + (size_t)I * d;
-  v4i acc[4][4];  // [row group][gate d0, gate d1, up d0, up d1]
+  // this wavefront's loads per K-step: weight blocks 2w, 2w+1 (blocks 0..7 =
+  // gate row groups of columns cb.., 8..15 = the same up rows) and digit
+  // blocks 2w, 2w+1 (block q = row group q/2, digit q%2)
+  const int8_t* W = static_cast<const int8_t*>(G.wgu);
+  const int8_t* asrc[2];
+  const int8_t* bsrc[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[t][q] = v4i{0, 0, 0, 0};
-
-  const int nchunk = (d + kGemmChunk - 1) / kGemmChunk;
-  v4i ra[4], rb[4];
-  {
-    const int nst = min(kGemmChunk, d) / kKStep;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = i8_load<LAY>(wa, min(u, nst - 1));
-      rb[u] = i8_load<LAY>(wb, min(u, nst - 1));
-    }
-    StageRegs st;
-    stage_load(st, xq, 2 * d, d, tok_sm, job.nr, 0, nst);
-    stage_store(st, bsm[0]);
+  for (int u = 0; u < 2; ++u) {
+    const int blk = 2 * wave + u;
+    const int col = cb + 16 * (blk & 7);
+    const size_t row0 = (size_t)job.e * 2 * I + (col < I ? col + (blk >= 8 ? I : 0) : 0);
+    asrc[u] = wblock_src<LAY>(W, row0, d, lane);
+    const int j = 16 * (blk >> 1) + i;
+    const int tok = tok_sm[j] >= 0 ? tok_sm[j] : tok_sm[0];
+    bsrc[u] = xq + (size_t)tok * 2 * d + (blk & 1) * d + 16 * g;
   }
-  __syncthreads();
+  const int nsteps = d / kKStep;
+  const int last = nsteps - 1;
+  auto issue = [&](int8_t* slot, int step) {
+    const int st = min(step, last);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      lds_load16(asrc[u] + (size_t)st * wblock_step<LAY>(), slot + (2 * wave + u) * kPBlk);
+      lds_load16(bsrc[u] + st * kKStep, slot + 16 * kPBlk + (2 * wave + u) * kPBlk);
+    }
+  };
 
-  for (int c = 0; c < nchunk; ++c) {
-    const int k0 = c * kGemmChunk;
-    const int nst = min(kGemmChunk, d - k0) / kKStep;
-    const bool more = c + 1 < nchunk;
-    const int k1 = k0 + kGemmChunk;
-    const int nst1 = more ? min(kGemmChunk, d - k1) / kKStep : 1;
-    v4i na[4], nb[4];
-    StageRegs st;
-    if (more) {
+  v4i acc[4][4][2];  // [weight fragment][row group][digit]
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        na[u] = i8_load<LAY>(wa, k1 / kKStep + min(u, nst1 - 1));
-        nb[u] = i8_load<LAY>(wb, k1 / kKStep + min(u, nst1 - 1));
-      }
-      stage_load(st, xq, 2 * d, d, tok_sm, job.nr, k1, nst1);
-    }
-    const int8_t* buf = bsm[c & 1];
-    if (active) {
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u < nst) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            if (t < ntg) {
-              const int8_t* brow = buf + (16 * t + i) * kGemmLdr;
-              const v4i x0 = *reinterpret_cast<const v4i*>(brow + 64 * u + 16 * g);
-              const v4i x1 = *reinterpret_cast<const v4i*>(brow + kGemmChunk + 64 * u + 16 * g);
-              acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0, acc[t][0], 0, 0, 0);
-              acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1, acc[t][1], 0, 0, 0);
-              acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0, acc[t][2], 0, 0, 0);
-              acc[t][3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1, acc[t][3], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-    if (more) {
-      stage_store(st, bsm[(c + 1) & 1]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ra[u] = na[u];
-        rb[u] = nb[u];
-      }
-    }
-    __syncthreads();
+    for (int t = 0; t < 4; ++t) acc[f][t][0] = acc[f][t][1] = v4i{0, 0, 0, 0};
+  // weight blocks of this wavefront's fragments: gate 2wc, 2wc+1, up 8+2wc, 9+2wc
+  const int ablk[4] = {2 * wc, 2 * wc + 1, 8 + 2 * wc, 9 + 2 * wc};
+
+  issue(ring0, 0);
+  issue(ring1, 1);
+  issue(ring2, 2);
+
+#define GU_STEP(S, Q)                                                                         \
+  {                                                                                           \
+    MOE_WAIT_VM(8);                                                                           \
+    ring_barrier();                                                                           \
+    if (active) {                                                                             \
+      const int8_t* slot = RING_SLOT(Q);                                                      \
+      v4i a[4];                                                                               \
+      _Pragma("unroll") for (int f = 0; f < 4; ++f) a[f] = lds_frag(slot + ablk[f] * kPBlk, lane); \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        if (t < ntg) {                                                                        \
+          const int8_t* bb = slot + 16 * kPBlk + 2 * (4 * wt + t) * kPBlk;                    \
+          const v4i b0 = lds_frag(bb, lane);                                                  \
+          const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
+          _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                     \
+            acc[f][t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b0, acc[f][t][0], 0, 0, 0); \
+            acc[f][t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b1, acc[f][t][1], 0, 0, 0); \
+          }                                                                                   \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    issue(RING_SLOT(((Q) + 3) & 3), (S) + 3);                                                 \
   }
+  int s0 = 0;
+  for (; s0 + 4 <= nsteps; s0 += 4) {
+    GU_STEP(s0, 0)
+    GU_STEP(s0 + 1, 1)
+    GU_STEP(s0 + 2, 2)
+    GU_STEP(s0 + 3, 3)
+  }
+  if (s0 < nsteps) GU_STEP(s0, 0)
+  if (s0 + 1 < nsteps) GU_STEP(s0 + 1, 1)
+  if (s0 + 2 < nsteps) GU_STEP(s0 + 2, 2)
+#undef GU_STEP
+  MOE_WAIT_VM(0);
 
-  // epilogue: h per row group, one scale per row and 64-column half
+  // epilogue: h per row, one scale per row and 64-column block (two wavefronts)
   const float* se = G.sgu + (size_t)job.e * 2 * I;
-  float h[4][4];
+  float h[2][4][4];  // [column half][row group][c]
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int j = 16 * t + i;
+    const int j = 64 * wt + 16 * t + i;
     const bool rv = active && t < ntg && j < job.nr;
     const float sig = rv ? xs[tok_sm[j]] : 0.0f;
     float mx = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int n = c0 + 4 * g + c;
-      const float gt = rv ? se[n] * sig * ((float)acc[t][0][c] + (float)acc[t][1][c] * (1.0f / 256.0f)) : 0.0f;
-      const float upv = rv ? se[I + n] * sig * ((float)acc[t][2][c] + (float)acc[t][3][c] * (1.0f / 256.0f)) : 0.0f;
-      h[t][c] = silu_f(gt) * upv;
-      mx = fmaxf(mx, fabsf(h[t][c]));
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = c0 + 16 * q + 4 * g + c;
+        const float gt = rv ? se[n] * sig *
+                                  ((float)acc[q][t][0][c] + (float)acc[q][t][1][c] * (1.0f / 256.0f))
+                            : 0.0f;
+        const float upv = rv ? se[I + n] * sig *
+                                   ((float)acc[2 + q][t][0][c] +
+                                    (float)acc[2 + q][t][1][c] * (1.0f / 256.0f))
+                             : 0.0f;
+        h[q][t][c] = silu_f(gt) * upv;
+        mx = fmaxf(mx, fabsf(h[q][t][c]));
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (g == 0) red_max[wave][j] = mx;
+    if (g == 0) red_max[wc][j] = mx;
   }
   __syncthreads();
   if (!active) return;
-  const int half = wave >> 2;  // 64-column scale block inside the 128 columns
+  const int pair = wc >> 1;  // 64-column scale block inside the 128 columns
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int j = 16 * t + i;
+    const int j = 64 * wt + 16 * t + i;
     if (t >= ntg || j >= job.nr) continue;
-    float mx = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_max[4 * half + w][j]);
+    const float mx = fmaxf(red_max[2 * pair][j], red_max[2 * pair + 1][j]);
     const int p = digit_exponent(mx);
-    int d0[4], d1[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) two_digits(h[t][c], p, d0[c], d1[c]);
     const int r = job.r0 + j;
     int8_t* hrow = G.hq + (size_t)r * 2 * I;
-    const int col = c0 + 4 * g;
-    *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
-    *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
-    if ((wave & 3) == 0 && g == 0)
-      G.hs[(size_t)r * (I / 64) + blockIdx.x * 2 + half] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int d0[4], d1[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) two_digits(h[q][t][c], p, d0[c], d1[c]);
+      const int col = c0 + 16 * q + 4 * g;
+      *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
+      *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
+    }
+    if ((wc & 1) == 0 && g == 0)
+      G.hs[(size_t)r * (I / 64) + blockIdx.x * 2 + pair] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
   }
 }
 
 template <int LAY>
 __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int d) {
-  __shared__ __attribute__((aligned(16))) int8_t bsm[2][kGemmRows * kGemmLdr];
-  __shared__ float ssm[2][kGemmRows][kGemmChunk / kKStep];
-  __shared__ int row_sm[kGemmRows];
+  // each slot: weight and digit blocks, then per wavefront 64 block scales
+  // (wavefronts 0 and 1 hold tile rows 0..63 and 64..127; the others load the
+  // same values again so that every wavefront issues the same loads)
+  constexpr int kSlot = kPSlotBytes + kPWaves * kWave * 4;
+  __shared__ __attribute__((aligned(16))) int8_t ring0[kSlot];
+  __shared__ __attribute__((aligned(16))) int8_t ring1[kSlot];
+  __shared__ __attribute__((aligned(16))) int8_t ring2[kSlot];
+  __shared__ __attribute__((aligned(16))) int8_t ring3[kSlot];
   Job job;
-  if (!find_job(g0, g1, kGemmRows, blockIdx.y, job)) return;
+  if (!find_job(g0, g1, kPTok, blockIdx.y, job)) return;
+  const Group G = job.g == 0 ? g0 : g1;
+  const int I = G.inter;
+  const int cb = blockIdx.x * 256;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int wc = wave & 3, wt = wave >> 2;
+  const int c0 = cb + wc * 64;
+  const int i = lane & 15, g = lane >> 4;
+  const int r0 = job.r0, nr = job.nr;
+  const int ntg = min(4, max(0, (nr - 64 * wt + 15) / 16));
+  const bool active = c0 < d && ntg > 0;
+  const int nhb = I / 64;
+
+  const int8_t* W = static_cast<const int8_t*>(G.wdn);
+  const int8_t* asrc[2];
+  const int8_t* bsrc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int blk = 2 * wave + u;
+    const int col = cb + 16 * blk;
+    const size_t row0 = (size_t)job.e * d + (col < d ? col : 0);
+    asrc[u] = wblock_src<LAY>(W, row0, I, lane);
+    const int j = 16 * (blk >> 1) + i;
+    bsrc[u] = G.hq + (size_t)(r0 + (j < nr ? j : 0)) * 2 * I + (blk & 1) * I + 16 * g;
+  }
+  const int srow = 64 * (wave & 1) + lane;
+  const float* ssrc = G.hs + (size_t)(r0 + (srow < nr ? srow : 0)) * nhb;
+  const int nsteps = I / kKStep;
+  const int last = nsteps - 1;
+  auto issue = [&](int8_t* slot, int step) {
+    const int st = min(step, last);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      lds_load16(asrc[u] + (size_t)st * wblock_step<LAY>(), slot + (2 * wave + u) * kPBlk);
+      lds_load16(bsrc[u] + st * kKStep, slot + 16 * kPBlk + (2 * wave + u) * kPBlk);
+    }
+    lds_load4(ssrc + st, slot + kPSlotBytes + wave * kWave * 4);
+  };
+
+  float acc[4][4][4];  // [weight fragment][row group][c]
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[f][t][c] = 0.0f;
+  const v4i zero = {0, 0, 0, 0};
+
+  issue(ring0, 0);
+  issue(ring1, 1);
+  issue(ring2, 2);
+
+#define DN_STEP(S, Q)                                                                         \
+  {                                                                                           \
+    MOE_WAIT_VM(10);                                                                          \
+    ring_barrier();                                                                           \
+    if (active) {                                                                             \
+      const int8_t* slot = RING_SLOT(Q);                                                      \
+      v4i a[4];                                                                               \
+      _Pragma("unroll") for (int f = 0; f < 4; ++f) a[f] = lds_frag(slot + (4 * wc + f) * kPBlk, lane); \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        if (t < ntg) {                                                                        \
+          const int8_t* bb = slot + 16 * kPBlk + 2 * (4 * wt + t) * kPBlk;                    \
+          const v4i b0 = lds_frag(bb, lane);                                                  \
+          const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
+          const float sg = reinterpret_cast<const float*>(slot + kPSlotBytes)[wt * kWave + 16 * t + i]; \
+          _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                     \
+            const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b0, zero, 0, 0, 0);    \
+            const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b1, zero, 0, 0, 0);    \
+            _Pragma("unroll") for (int c = 0; c < 4; ++c) acc[f][t][c] =                     \
+                fmaf(sg, fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[f][t][c]);      \
+          }                                                                                   \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    issue(RING_SLOT(((Q) + 3) & 3), (S) + 3);                                                 \
+  }
+  int s0 = 0;
+  for (; s0 + 4 <= nsteps; s0 += 4) {
+    DN_STEP(s0, 0)
+    DN_STEP(s0 + 1, 1)
+    DN_STEP(s0 + 2, 2)
+    DN_STEP(s0 + 3, 3)
+  }
+  if (s0 < nsteps) DN_STEP(s0, 0)
+  if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1)
+  if (s0 + 2 < nsteps) DN_STEP(s0 + 2, 2)
+#undef DN_STEP
+  MOE_WAIT_VM(0);
+  if (!active) return;
+  const float* sd = G.sdn + (size_t)job.e * d;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = 64 * wt + 16 * t + i;
+    if (t >= ntg || j >= nr) continue;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int n = c0 + 16 * f + 4 * g;
+      *reinterpret_cast<float4*>(G.out + (size_t)(r0 + j) * d + n) =
+          make_float4(sd[n] * acc[f][t][0], sd[n + 1] * acc[f][t][1], sd[n + 2] * acc[f][t][2],
+                      sd[n + 3] * acc[f][t][3]);
+    }
+  }
+}
+#undef RING_SLOT
+
+// The down projection uses smaller tiles: up to 64 rows, a workgroup of 8
+// wavefronts owning 128 output columns (16 per wavefront).  Its block scales
+// change every 64 inputs, so its K loop folds int32 products into fp32 per
+// K-step and holds 64 fp32 sums per lane; the smaller tile keeps registers low
+// enough for two workgroups per CU.  The tile's h digits are staged in LDS 256
+// inputs at a time (double-buffered); weight fragments and digits of chunk
+// c+1 are loaded into registers while chunk c is computed.  All loads are
+// unconditional (clamped addresses, masked values) so the compiler waits only
+// for the loads a chunk consumes.
+constexpr int kDRows = 64, kDChunk = 256;
+constexpr int kDLdr = 2 * kDChunk + 16;           // LDS bytes per staged row
+constexpr int kDStage = kDRows * 32 / (kPWaves * kWave);  // 16-byte pieces per thread
+
+// Piece q = tid + 512 u of a chunk: row q / 32, digit (q % 32) / 16, bytes
+// 16 (q % 16) of the chunk.  Source offsets are fixed per thread; rows past
+// the tile and bytes past the end of the row are masked to zero.
+struct DSrc {
+  const int8_t* p[kDStage];
+  int row_ok[kDStage];
+  int col[kDStage];  // byte offset inside the chunk
+};
+
+__device__ inline DSrc dsrc_init(const int8_t* __restrict__ base, int rowbytes, int plane,
+                                 int r0, int nr) {
+  DSrc src;
+#pragma unroll
+  for (int u = 0; u < kDStage; ++u) {
+    const int q = threadIdx.x + u * kPWaves * kWave;
+    const int j = q >> 5, c = q & 31;
+    src.row_ok[u] = j < nr;
+    src.col[u] = 16 * (c & 15);
+    src.p[u] = base + (size_t)(r0 + (j < nr ? j : 0)) * rowbytes + (c < 16 ? 0 : plane) + 16 * (c & 15);
+  }
+  return src;
+}
+
+struct DStage {
+  v4i v[kDStage];
+};
+
+// chunk starting at input k0 with `valid` bytes (a multiple of 64) per digit row
+__device__ inline void dstage_load(DStage& st, const DSrc& src, int k0, int valid) {
+#pragma unroll
+  for (int u = 0; u < kDStage; ++u) {
+    const int off = src.col[u] < valid ? k0 : k0 - src.col[u];  // stay inside the row
+    st.v[u] = *reinterpret_cast<const v4i*>(src.p[u] + off);
+  }
+}
+
+__device__ inline void dstage_store(const DStage& st, const DSrc& src, int valid, int8_t* buf) {
+#pragma unroll
+  for (int u = 0; u < kDStage; ++u) {
+    const int q = threadIdx.x + u * kPWaves * kWave;
+    const int j = q >> 5, c = q & 31;
+    const int m = (src.row_ok[u] && src.col[u] < valid) ? -1 : 0;
+    *reinterpret_cast<v4i*>(buf + j * kDLdr + (c < 16 ? 0 : kDChunk) + 16 * (c & 15)) =
+        st.v[u] & m;
+  }
+}
+
+template <int LAY>
+__global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, int d) {
+  __shared__ __attribute__((aligned(16))) int8_t bsm[2][kDRows * kDLdr];
+  __shared__ float ssm[2][kDRows][kDChunk / kKStep];
+  Job job;
+  if (!find_job(g0, g1, kDRows, blockIdx.y, job)) return;
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int c0 = blockIdx.x * 128 + wave * 16;
   const bool active = c0 < d;
   const int i = lane & 15, g = lane >> 4;
-  const int ntg = (job.nr + 15) / 16;
+  const int r0 = job.r0, nr = job.nr;
+  const int ntg = (nr + 15) / 16;
   const int nhb = I / 64;
-  for (int j = threadIdx.x; j < kGemmRows; j += blockDim.x) row_sm[j] = job.r0 + j;
   const size_t row0 = (size_t)job.e * d + (active ? c0 : 0);
   const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g, lane);
+  const DSrc src = dsrc_init(G.hq, 2 * I, I, r0, nr);
+  // block scales: thread tid < 256 reads row tid / 4, block tid % 4 of a chunk
+  const int sj = (threadIdx.x >> 2) & (kDRows - 1), sb = threadIdx.x & 3;
+  const bool s_ok = sj < nr;
+  const float* sp = G.hs + (size_t)(r0 + (s_ok ? sj : 0)) * nhb;
   float acc[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[t][c] = 0.0f;
   const v4i zero = {0, 0, 0, 0};
-  __syncthreads();
+  const int nchunk = (I + kDChunk - 1) / kDChunk;
+  const int lastc = nchunk - 1;
+  auto valid_of = [&](int c) { return min(kDChunk, I - c * kDChunk); };
+  auto scale_of = [&](int c) {  // clamp the block index inside the row
+    const int b = c * (kDChunk / kKStep) + sb;
+    return sp[b < nhb ? b : nhb - 1];
+  };
 
-  // per-chunk block scales: thread q < nr*4 holds row q/4, block q%4
-  const float* hs_base = G.hs;
-  const int r0 = job.r0, nr = job.nr;
-#define SCALE_LOAD(K0, NST)                                                          \
-  ((threadIdx.x < (unsigned)(nr * 4) && (int)(threadIdx.x & 3) < (NST))              \
-       ? hs_base[(size_t)(r0 + (threadIdx.x >> 2)) * nhb + (K0) / kKStep + (threadIdx.x & 3)] \
-       : 0.0f)
-  const int nchunk = (I + kGemmChunk - 1) / kGemmChunk;
   v4i ra[4];
   {
-    const int nst = min(kGemmChunk, I) / kKStep;
+    const int nst = valid_of(0) / kKStep;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ra[u] = i8_load<LAY>(wa, min(u, nst - 1));
-    StageRegs st;
-    stage_load(st, G.hq, 2 * I, I, row_sm, job.nr, 0, nst);
-    const float sv = SCALE_LOAD(0, nst);
-    stage_store(st, bsm[0]);
-    if (threadIdx.x < kGemmRows * 4) ssm[0][threadIdx.x >> 2][threadIdx.x & 3] = sv;
+    for (int u = 0; u < 4; ++u) ra[u] = i8_load_cached<LAY>(wa, min(u, nst - 1));
+    DStage st;
+    dstage_load(st, src, 0, valid_of(0));
+    const float sv = scale_of(0);
+    dstage_store(st, src, valid_of(0), bsm[0]);
+    if (threadIdx.x < kDRows * 4)
+      ssm[0][sj][sb] = (s_ok && sb < nst) ? sv : 0.0f;
   }
   __syncthreads();
 
   for (int c = 0; c < nchunk; ++c) {
-    const int k0 = c * kGemmChunk;
-    const int nst = min(kGemmChunk, I - k0) / kKStep;
-    const bool more = c + 1 < nchunk;
-    const int k1 = k0 + kGemmChunk;
-    const int nst1 = more ? min(kGemmChunk, I - k1) / kKStep : 1;
+    const int nst = valid_of(c) / kKStep;
+    const int c1 = min(c + 1, lastc);
+    const int val1 = valid_of(c1), nst1 = val1 / kKStep;
     v4i na[4];
-    StageRegs st;
-    float sv = 0.0f;
-    if (more) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) na[u] = i8_load<LAY>(wa, k1 / kKStep + min(u, nst1 - 1));
-      stage_load(st, G.hq, 2 * I, I, row_sm, job.nr, k1, nst1);
-      sv = SCALE_LOAD(k1, nst1);
-    }
+    for (int u = 0; u < 4; ++u) na[u] = i8_load_cached<LAY>(wa, c1 * (kDChunk / kKStep) + min(u, nst1 - 1));
+    DStage st;
+    dstage_load(st, src, c1 * kDChunk, val1);
+    const float sv = scale_of(c1);
     const int8_t* buf = bsm[c & 1];
     if (active) {
 #pragma unroll
@@ -843,9 +1057,9 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             if (t < ntg) {
-              const int8_t* brow = buf + (16 * t + i) * kGemmLdr;
+              const int8_t* brow = buf + (16 * t + i) * kDLdr;
               const v4i x0 = *reinterpret_cast<const v4i*>(brow + 64 * u + 16 * g);
-              const v4i x1 = *reinterpret_cast<const v4i*>(brow + kGemmChunk + 64 * u + 16 * g);
+              const v4i x1 = *reinterpret_cast<const v4i*>(brow + kDChunk + 64 * u + 16 * g);
               const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0, zero, 0, 0, 0);
               const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1, zero, 0, 0, 0);
               const float sg = ssm[c & 1][16 * t + i][u];
@@ -857,22 +1071,22 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
         }
       }
     }
-    if (more) {
-      stage_store(st, bsm[(c + 1) & 1]);
-      if (threadIdx.x < kGemmRows * 4) ssm[(c + 1) & 1][threadIdx.x >> 2][threadIdx.x & 3] = sv;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ra[u] = na[u];
+    if (c + 1 < nchunk) {
+      dstage_store(st, src, val1, bsm[(c + 1) & 1]);
+      if (threadIdx.x < kDRows * 4)
+        ssm[(c + 1) & 1][sj][sb] = (s_ok && sb < nst1) ? sv : 0.0f;
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ra[u] = na[u];
     __syncthreads();
   }
-#undef SCALE_LOAD
   if (!active) return;
+  const float* sd = G.sdn + (size_t)job.e * d + c0 + 4 * g;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = 16 * t + i;
-    if (t >= ntg || j >= job.nr) continue;
-    const float* sd = G.sdn + (size_t)job.e * d + c0 + 4 * g;
-    *reinterpret_cast<float4*>(G.out + (size_t)(job.r0 + j) * d + c0 + 4 * g) =
+    if (t >= ntg || j >= nr) continue;
+    *reinterpret_cast<float4*>(G.out + (size_t)(r0 + j) * d + c0 + 4 * g) =
         make_float4(sd[0] * acc[t][0], sd[1] * acc[t][1], sd[2] * acc[t][2], sd[3] * acc[t][3]);
   }
 }
@@ -1022,20 +1236,28 @@ hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nr
 }
 
 template <int LAY>
-hipError_t launch_gemm_pair(const Group& a, const Group& b, int d, const int8_t* xq,
-                            const float* xs, hipStream_t s) {
-  const int tiles = a.tiles + b.tiles;
+hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const float* xs,
+                            hipStream_t s) {
+  // tiles of kPTok rows for gate/up, kDRows rows for down
+  auto tiles_of = [](const Group& G, int mt) {
+    if (G.R <= 0) return 0;
+    return G.offsets ? max_tiles(G.R, G.E, mt) : (G.R + mt - 1) / mt;
+  };
   const int imax = a.inter > b.inter ? a.inter : b.inter;
+  a.tiles = tiles_of(a, kPTok);
+  b.tiles = tiles_of(b, kPTok);
   {
     TimedLaunch tl(K_FFN_I8_GATE_UP_GEMM, s);
-    hipLaunchKernelGGL(gate_up_gemm_kernel<LAY>, dim3((imax + 127) / 128, tiles), dim3(512), 0, s,
-                       a, b, d, xq, xs);
+    hipLaunchKernelGGL(gate_up_gemm_kernel<LAY>, dim3((imax + 127) / 128, a.tiles + b.tiles),
+                       dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  a.tiles = tiles_of(a, kDRows);
+  b.tiles = tiles_of(b, kDRows);
   TimedLaunch tl(K_FFN_I8_DOWN_GEMM, s);
-  hipLaunchKernelGGL(down_gemm_kernel<LAY>, dim3((d + 127) / 128, tiles), dim3(512), 0, s, a, b,
-                     d);
+  hipLaunchKernelGGL(down_gemm64_kernel<LAY>, dim3((d + 127) / 128, a.tiles + b.tiles),
+                     dim3(kPWaves * kWave), 0, s, a, b, d);
   return hipGetLastError();
 }
 
@@ -1046,14 +1268,14 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     err = launch_encode_rows(x, T, d, ws.xq, ws.xs, s);
     if (err != hipSuccess) return err;
   }
-  // int8 with many rows per expert: grouped GEMM tiles of 64 rows
+  // int8 with many rows per expert: grouped GEMM tiles of 128 rows
   if (sets[0].fmt == 1 && sets[0].pairs_idx == nullptr && sets[0].R >= 16LL * sets[0].E) {
     Group grp[2] = {};
     for (int q = 0; q < nsets; ++q) {
       const FfnSet& f = sets[q];
       Group& G = grp[q];
       G.E = f.E; G.inter = f.inter; G.R = f.R;
-      G.tiles = f.offsets ? max_tiles(f.R, f.E, kGemmRows) : (f.R + kGemmRows - 1) / kGemmRows;
+      G.tiles = f.offsets ? max_tiles(f.R, f.E, kPTok) : (f.R + kPTok - 1) / kPTok;
       G.wgu = f.wgu; G.sgu = f.sgu; G.wdn = f.wdn; G.sdn = f.sdn;
       G.row_token = f.row_token; G.offsets = f.offsets;
       G.hq = f.hq; G.hs = f.hs; G.out = f.out;
