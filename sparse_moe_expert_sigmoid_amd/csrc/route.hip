@@ -119,12 +119,29 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
   const int lane = gtid & (kWave - 1), wave = gtid / kWave;
   float sc[EPT];
   unsigned long long key[EPT];
+  float bv[EPT];
 #pragma unroll
   for (int m = 0; m < EPT; ++m) {
     const int e = gtid + 256 * m;
+    bv[m] = (bias && e < E) ? bias[e] : 0.0f;
+  }
+  // all slices are loaded before the first add (one trip to memory), then
+  // added in ascending order
+  constexpr int kMaxChunks = 16;
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) {
+    const int e = gtid + 256 * m;
+    const bool ok = active && e < E;
     float l = 0.0f;
-    if (active && e < E) {
-#pragma unroll 4
+    if (nchunk <= kMaxChunks) {
+      float pv[kMaxChunks];
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c)
+        pv[c] = (ok && c < nchunk) ? partial[((size_t)c * T + t) * E + e] : 0.0f;
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c)
+        if (c < nchunk) l += pv[c];
+    } else if (ok) {
       for (int c = 0; c < nchunk; ++c) l += partial[((size_t)c * T + t) * E + e];
     }
     sc[m] = l;
@@ -135,7 +152,7 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
       const int e = gtid + 256 * m;
       const float s = 1.0f / (1.0f + expf(-sc[m]));
       sc[m] = s;
-      const float kap = s + (bias && e < E ? bias[e] : 0.0f);
+      const float kap = s + bv[m];
       key[m] = ((unsigned long long)ordered_bits(kap) << 32) | (0xffffffffu - (unsigned)e);
     }
   } else {
@@ -228,16 +245,54 @@ __global__ __launch_bounds__(256) void router_tail_kernel(
     float* __restrict__ xs) {
   __shared__ unsigned long long keys[256 * EPT];
   __shared__ float red[4];
+  __shared__ float xred[4];
   __shared__ float sel_s[kMaxK];
   const int t = blockIdx.x;
-  // the row of x is read into L1/L2 while the selection's loads are in flight
-  if (threadIdx.x < kWave) {
-    const float* row = x + (size_t)t * d;
-    for (int c = threadIdx.x; c < d / 4; c += kWave) __builtin_prefetch(row + 4 * c, 0, 3);
+  const float* row = x + (size_t)t * d;
+  // the token's row of x (up to 4096 values) goes into registers first, so its
+  // loads are in flight during the selection
+  constexpr int kXPer = 4;
+  const int nq = d / 4;
+  const bool in_regs = nq <= kXPer * 256;
+  float4 xv[kXPer];
+#pragma unroll
+  for (int m = 0; m < kXPer; ++m) {
+    const int c = threadIdx.x + 256 * m;
+    xv[m] = (in_regs && c < nq) ? *reinterpret_cast<const float4*>(row + 4 * c)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, t, true, threadIdx.x, keys,
                     red, sel_s, idx, w, nullptr);
-  if (threadIdx.x < kWave) encode_row(x + (size_t)t * d, d, xq + (size_t)t * 2 * d, xs + t);
+  if (!in_regs) {
+    if (threadIdx.x < kWave) encode_row(row, d, xq + (size_t)t * 2 * d, xs + t);
+    return;
+  }
+  // two-digit encoding of the row with one scale (as encode_row), by all threads
+  float mx = 0.0f;
+#pragma unroll
+  for (int m = 0; m < kXPer; ++m)
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m].x), fabsf(xv[m].y)),
+                         fmaxf(fabsf(xv[m].z), fabsf(xv[m].w))));
+  mx = wave_max_f(mx);
+  if ((threadIdx.x & (kWave - 1)) == 0) xred[threadIdx.x / kWave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(xred[0], xred[1]), fmaxf(xred[2], xred[3]));
+  const int p = digit_exponent(mx);
+  unsigned* q0 = reinterpret_cast<unsigned*>(xq + (size_t)t * 2 * d);
+  unsigned* q1 = reinterpret_cast<unsigned*>(xq + (size_t)t * 2 * d + d);
+#pragma unroll
+  for (int m = 0; m < kXPer; ++m) {
+    const int c = threadIdx.x + 256 * m;
+    if (c >= nq) continue;
+    int a0, b0, a1, b1, a2, b2, a3, b3;
+    two_digits(xv[m].x, p, a0, b0);
+    two_digits(xv[m].y, p, a1, b1);
+    two_digits(xv[m].z, p, a2, b2);
+    two_digits(xv[m].w, p, a3, b3);
+    q0[c] = pack4(a0, a1, a2, a3);
+    q1[c] = pack4(b0, b1, b2, b3);
+  }
+  if (threadIdx.x == 0) xs[t] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
 }
 
 template <int EPT>
