@@ -93,24 +93,23 @@ def expert_bytes(ew, e_list):
 
 def counter_traffic(workload: str, kernel_prefix: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary (profiles/<workload>.md), or None when that summary is
-    missing or was taken from a different version of the kernel source."""
+    counter summary (profiles/<workload>__*.md, FETCH_SIZE + WRITE_SIZE
+    calibrated), or None when no summary matches or it was taken from a
+    different version of the kernel source."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload}.md")
     src = os.path.join(ROOT, "sparse_moe_expert_sigmoid_amd", "csrc", "ffn.hip")
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if ":" in line and not line.startswith(("|", "#", "`")):
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha:
-        return None
-    if not fields.get("dominant_kernel", "").startswith(kernel_prefix):
-        return None
-    return int(fields["traffic_bytes_per_launch"])
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"{workload}__*.md"))):
+        fields = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(("|", "#", "`")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        if (fields.get("kernel_source_sha256") == sha
+                and fields.get("dominant_kernel", "").startswith(kernel_prefix)):
+            return int(fields["traffic_bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(inputs, budget_s: float):
@@ -261,7 +260,9 @@ def run_stack(args):
             roofline = {"bound": "mfma", "kernel": "ffn_i8_gate_up_gemm",
                         "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
-                        "traffic": None, "flops_per_launch": per_launch,
+                        "traffic": counter_traffic(args.workload, "gate_up_gemm_kernel"),
+                        "traffic_scope": "median launch of the first 2 layers (profiles/)",
+                        "flops_per_launch": per_launch,
                         "avg_launch_us": round(avg_s * 1e6, 2),
                         "frac_of_bf16_peak": round(achieved / BF16_PEAK_TFLOPS, 4)}
         elif "ffn_i8_gate_up" in kt:
@@ -273,7 +274,9 @@ def run_stack(args):
             achieved = per_launch / avg_s / 1e9
             roofline = {"bound": "hbm", "kernel": "ffn_i8_gate_up",
                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": counter_traffic(args.workload, "gate_up_kernel<"),
+                        "traffic_scope": "median launch of the first 2 layers (profiles/)",
                         "bytes_per_launch": int(per_launch),
                         "avg_launch_us": round(avg_s * 1e6, 2)}
 
@@ -445,6 +448,9 @@ def main():
         ctx.moe_timing(0)
         kernels = {n: {"launches": int(c), "avg_us": t / c * 1e3} for n, (c, t) in kt.items()}
         dom = "ffn_i4_gate_up" if spec.fmt == "int4_b32" else "ffn_i8_gate_up"
+        gemm = "ffn_i8_gate_up_gemm" in kt
+        if gemm:
+            dom = "ffn_i8_gate_up_gemm"
         if dom in kt:
             launches, tot_ms = kt[dom]
             # algorithmic bytes of the gate/up launches of one step: codes + scales of
@@ -458,12 +464,17 @@ def main():
             bytes_per_launch = per_step / launches_per_step
             avg_s = tot_ms / launches / 1e3
             achieved = bytes_per_launch / avg_s / 1e9
-            traffic = counter_traffic(args.workload, "gate_up_kernel")
+            traffic = counter_traffic(args.workload,
+                                      "gate_up_gemm_kernel" if gemm else "gate_up_kernel<")
             roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "bytes_per_launch": int(bytes_per_launch),
                         "avg_launch_us": round(avg_s * 1e6, 2)}
+            if gemm:  # the grouped GEMM's matrix-core rate beside its HBM rate
+                gflops = 2.0 * (R * 2 * I * d + spec.T * 2 * Is * d) / launches_per_step
+                roofline["mfma_tflops"] = round(gflops / avg_s / 1e12, 1)
+                roofline["mfma_frac_int8"] = round(gflops / avg_s / 1e12 / INT8_PEAK_TOPS, 4)
 
     if args.copy_probe > 0:
         # a fill kernel (writes N bytes) and an elementwise kernel (reads N, writes N)
