@@ -39,11 +39,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
   const int kbeg = c * kRouterChunk;
   const int kend = min(d, kbeg + kRouterChunk);
   for (int k0 = kbeg; k0 < kend; k0 += kSub) {
+    const int kn = min(kSub, kend - k0);  // the last slice of a row can be short
     for (int q = threadIdx.x; q < TE * (kSub / 4); q += 256) {
       const int r = q / (kSub / 4), c4 = q % (kSub / 4);
       const int e = e0 + r;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E) v = *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + 4 * c4);
+      if (e < E && 4 * c4 < kn)
+        v = *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + 4 * c4);
       ws[r][4 * c4 + 0] = v.x;
       ws[r][4 * c4 + 1] = v.y;
       ws[r][4 * c4 + 2] = v.z;
@@ -53,7 +55,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
       const int r = q / (kSub / 4), c4 = q % (kSub / 4);
       const int t = t0 + r;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < T) v = *reinterpret_cast<const float4*>(x + (size_t)t * d + k0 + 4 * c4);
+      if (t < T && 4 * c4 < kn)
+        v = *reinterpret_cast<const float4*>(x + (size_t)t * d + k0 + 4 * c4);
       xs[r][4 * c4 + 0] = v.x;
       xs[r][4 * c4 + 1] = v.y;
       xs[r][4 * c4 + 2] = v.z;
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
     }
     __syncthreads();
 #pragma unroll 8
-    for (int kk = 0; kk < kSub; ++kk) {
+    for (int kk = 0; kk < kn; ++kk) {
       float wv[PE], xv[PT];
 #pragma unroll
       for (int a = 0; a < PE; ++a) wv[a] = ws[ti + 16 * a][kk];

@@ -96,6 +96,29 @@ def test_route_batch_invariance(ctx):
         assert np.array_equal(idx_1[0], idx_full[t]) and np.array_equal(w_1[0], w_full[t])
 
 
+@pytest.mark.parametrize("d", [64, 320])
+def test_route_short_last_slice(ctx, d):
+    # d not a multiple of the 256-wide logit slice: the last slice is short.
+    # Small T (16x16 tiles, one 256 step) and T > 32 (64x64 tiles, 64 steps)
+    # must both match the oracle and each other bit for bit.
+    got = {}
+    for T in (1, 8, 40):
+        inp = inputs("tiny", d=d, T=T, E=24, k=4, xseed=0x4D6F45A0)
+        s = inp.spec
+        L = device_layer(ctx, "tiny", d=d, T=T, E=24, k=4, xseed=0x4D6F45A0)
+        gidx, gw = run_route(ctx, L, inp.x)
+        oidx, ow, ogap, logits = oracle.route(s.router, inp.x, inp.wr, inp.bias, s.k, s.scale,
+                                              want_logits=True)
+        exc = compare_route(gidx, gw, oidx, ow, ogap, oracle_keys(s.router, logits, inp.bias),
+                            s.scale)
+        assert np.isfinite(gw).all()
+        got[T] = (gidx, gw)
+        _log(test="route_short_slice", d=d, T=T, excused=len(exc))
+    for T in (1, 8):
+        assert np.array_equal(got[T][0], got[40][0][:T])
+        assert np.array_equal(got[T][1], got[40][1][:T])
+
+
 # ------------------------------------------------------------------ permute
 
 def _check_permute(ctx, idx, E):
@@ -341,10 +364,11 @@ def test_layer_every_token_on_same_experts(ctx):
 
 
 def test_layer_gemm_path_edges(ctx):
-    # >= 16 rows per expert selects the 64-row GEMM tiles; d = 320 and I = 192
-    # leave short K chunks and half-empty column blocks; experts with more than
-    # 64 rows take several tiles; the int8 shared expert (I = 128) rides along.
-    kw = dict(T=200, d=320, E=8, k=2, inter=192, shared="int8_row", shared_inter=128,
+    # >= 16 rows per expert selects the GEMM tiles (128 rows for gate/up, 64
+    # for down); d = 320 and I = 192 leave short K tails and half-empty column
+    # blocks; about 150 rows per expert take two gate/up tiles and three down
+    # tiles, the last ones partial; the int8 shared expert (I = 128) rides along.
+    kw = dict(T=600, d=320, E=8, k=2, inter=192, shared="int8_row", shared_inter=128,
               xseed=0x4D6F4595)
     _layer_vs_oracle(ctx, "tiny", **kw)
     _forward_vs_oracle(ctx, "tiny", **kw)
