@@ -94,8 +94,9 @@ typedef enum {
  *   fmt        one of moe_wfmt
  *   layout     one of moe_layout (MOE_LAYOUT_ROWS for fp32)
  *   n_experts  E >= 1
- *   d          model width; a multiple of 64 (int4: of 128)
- *   inter      expert intermediate width I; a multiple of 64 (int4: of 128)
+ *   d          model width; a multiple of 64 (int4: of 128), at most 16384
+ *   inter      expert intermediate width I; a multiple of 64 (int4: of 128), at
+ *              most 16384
  *   w_gate_up  [E][2I][d]: rows 0..I-1 are the gate projection, rows I..2I-1 the
  *              up projection, input axis contiguous.  int8: int8_t; int4: uint8_t
  *              with d/2 bytes per row; fp32: float

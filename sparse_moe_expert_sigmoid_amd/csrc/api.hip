@@ -386,6 +386,9 @@ moe_status check_weights(moe_ctx* ctx, const char* fn, const char* which, const 
   if (w->n_experts < 1 || w->d < 1 || w->inter < 1)
     return fail(ctx, MOE_E_INVALID, "%s: %s: n_experts=%d d=%d inter=%d", fn, which,
                 w->n_experts, w->d, w->inter);
+  if (w->d > moe::kMaxWidth || w->inter > moe::kMaxWidth)
+    return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: d=%d and inter=%d must be at most %d", fn,
+                which, w->d, w->inter, moe::kMaxWidth);
   const int mult = w->fmt == MOE_W_INT4_B32 ? 128 : 64;
   if (w->d % mult != 0 || w->inter % mult != 0)
     return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: d=%d and inter=%d must be multiples of %d", fn,

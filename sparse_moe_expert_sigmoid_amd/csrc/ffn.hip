@@ -1285,8 +1285,21 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
                                : launch_gemm_pair<kRows>(grp[0], grp[1], d, ws.xq, ws.xs, s);
   }
   // rows per tile: at most 16 (the MFMA N side); small batches use fewer so
-  // that the staged activation rows take less LDS
-  const int mt = T < kTileRows ? (T > 0 ? T : 1) : kTileRows;
+  // that the staged activation rows take less LDS; wide rows use fewer so that
+  // a tile's staged rows (x digits for gate/up, h digits and block scales for
+  // down) fit the LDS beside the kernels' largest static arrays (the K-slice
+  // partials, under 50 KB)
+  int mt = T < kTileRows ? (T > 0 ? T : 1) : kTileRows;
+  {
+    size_t per_row = (size_t)2 * d + 16;
+    for (int q = 0; q < nsets; ++q) {
+      const size_t dn = (size_t)2 * sets[q].inter + 16 + (size_t)(sets[q].inter / 64) * 4;
+      if (dn > per_row) per_row = dn;
+    }
+    const size_t cap = (kLdsBytes - 50 * 1024) / per_row;
+    if (cap < 1) return hipErrorInvalidValue;
+    if ((size_t)mt > cap) mt = (int)cap;
+  }
   Group grp[2] = {};
   for (int q = 0; q < nsets; ++q) {
     const FfnSet& f = sets[q];

@@ -13,6 +13,8 @@ constexpr int kWave = 64;              // CDNA wavefront width
 constexpr int kRouterChunk = 256;      // router logits are summed in fixed 256-input chunks
 constexpr int kMaxK = 16;              // top-k limit
 constexpr int kMaxE = 1024;            // experts per layer limit
+constexpr int kMaxWidth = 16384;       // d and inter limit
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup (gfx950)
 constexpr int kKStep = 64;             // K of one int8 MFMA (16x16x64)
 constexpr int kTileRows = 16;          // routed rows per FFN tile (MFMA N)
 

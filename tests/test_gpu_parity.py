@@ -119,6 +119,17 @@ def test_route_short_last_slice(ctx, d):
         assert np.array_equal(got[T][1], got[40][1][:T])
 
 
+@pytest.mark.parametrize("E,k,d", [(300, 16, 512), (1024, 16, 256), (40, 8, 4096), (40, 8, 4160)])
+def test_layer_router_edges(ctx, E, k, d):
+    # E > 256 (2 and 4 experts per selecting thread), k = 16, and d at and past
+    # the small-batch tail's limits (16 logit slices, 4096 inputs held in
+    # registers); both the small-batch path (T = 5) and the permuted one (T = 40)
+    for T in (5, 40):
+        kw = dict(E=E, k=k, d=d, T=T, inter=64, shared=None, shared_inter=0,
+                  xseed=0x4D6F45B0 + T)
+        _forward_vs_oracle(ctx, "tiny", **kw)
+
+
 # ------------------------------------------------------------------ permute
 
 def _check_permute(ctx, idx, E):
@@ -519,3 +530,10 @@ def test_abi_errors(ctx):
     with pytest.raises(B.MoeError) as e:
         ctx.moe_combine(L.rows, L.token_row, L.w, None, None, 4, 8, 510, L.y)
     assert e.value.status == B.MOE_E_UNSUPPORTED
+    # widths past the supported maximum are refused before any launch
+    wide = B.DeviceExperts(L.experts.fmt, L.experts.n_experts, 16448, L.experts.inter,
+                           L.experts.w_gate_up, L.experts.w_down, L.experts.s_gate_up,
+                           L.experts.s_down, L.experts.layout)
+    with pytest.raises(B.MoeError) as e:
+        ctx.moe_expert_ffn(wide, 0, x, 4, L.row_token, L.offsets, 32, L.rows, L.ws)
+    assert e.value.status == B.MOE_E_UNSUPPORTED and "16384" in str(e.value)
