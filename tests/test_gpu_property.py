@@ -28,13 +28,16 @@ def ctx(gpu):
 def layer_shapes(draw):
     fmt = draw(st.sampled_from(["int8_row", "int8_row", "int4_b32"]))
     step = 128 if fmt == "int4_b32" else 64
-    d = step * draw(st.integers(1, 4))
+    wide = draw(st.integers(0, 5)) == 0      # now and then a wide layer, few tokens
+    d = step * (draw(st.integers(16, 96)) if wide else draw(st.integers(1, 4)))
     inter = step * draw(st.integers(1, 3))
     k = draw(st.integers(1, 8))
     E = draw(st.integers(k, 40))
     # small batches, 16-row tiles, or enough rows per expert for the GEMM tiles
     T = draw(st.one_of(st.integers(1, 16), st.integers(17, 64),
                        st.integers(max(17, (16 * E + k - 1) // k), 16 * E // k + 64)))
+    if wide:
+        T = min(T, 40)
     router = draw(st.sampled_from(["sigmoid_bias", "softmax"]))
     shared = draw(st.sampled_from([None, "fp32", fmt if fmt == "int8_row" else None]))
     shared_inter = step * draw(st.integers(1, 2)) if shared else 0
@@ -46,7 +49,7 @@ def layer_shapes(draw):
                 tiled=tiled)
 
 
-@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
           suppress_health_check=[HealthCheck.function_scoped_fixture,
                                  HealthCheck.too_slow])
 @given(case=layer_shapes())
