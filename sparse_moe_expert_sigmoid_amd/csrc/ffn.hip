@@ -17,10 +17,10 @@
 //   sum_k q_k v_k = 2^-p (sum_k q_k d0_k + 2^-8 sum_k q_k d1_k)
 // is two exact int32 MFMA accumulations.  The encoding error is at most
 // 2^-16 of the largest |v| sharing the scale.  x uses one scale per row; h
-// uses one scale per row and 64-column block, chosen in the gate/up epilogue
-// (so h never exists in fp32 memory and no separate pass is needed); the
-// down projection folds each 64-column block's int32 sums into fp32 with
-// that block's scale.
+// uses one scale per row and 64-column block (128-column block on the
+// prefill GEMM path), chosen in the gate/up epilogue (so h never exists in
+// fp32 memory and no separate pass is needed); the down projection folds each
+// block's int32 sums into fp32 with that block's scale.
 //
 // Work split: a tile is up to 16 rows of one expert (the MFMA N side); a
 // workgroup owns 64 output columns of one tile, one wavefront per 16 columns
@@ -789,12 +789,12 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
   }
   __syncthreads();
   if (!active) return;
-  const int pair = wc >> 1;  // 64-column scale block inside the 128 columns
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = 64 * wt + 16 * t + i;
     if (t >= ntg || j >= job.nr) continue;
-    const float mx = fmaxf(red_max[2 * pair][j], red_max[2 * pair + 1][j]);
+    // one scale per row and 128-column block (this workgroup's columns)
+    const float mx = fmaxf(fmaxf(red_max[0][j], red_max[1][j]), fmaxf(red_max[2][j], red_max[3][j]));
     const int p = digit_exponent(mx);
     const int r = job.r0 + j;
     int8_t* hrow = G.hq + (size_t)r * 2 * I;
@@ -807,133 +807,20 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
       *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
       *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
     }
-    if ((wc & 1) == 0 && g == 0)
-      G.hs[(size_t)r * (I / 64) + blockIdx.x * 2 + pair] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+    if (wc == 0 && g == 0)
+      G.hs[(size_t)r * ((I + 127) / 128) + blockIdx.x] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
   }
 }
 
-template <int LAY>
-__global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int d) {
-  // each slot: weight and digit blocks, then per wavefront 64 block scales
-  // (wavefronts 0 and 1 hold tile rows 0..63 and 64..127; the others load the
-  // same values again so that every wavefront issues the same loads)
-  constexpr int kSlot = kPSlotBytes + kPWaves * kWave * 4;
-  __shared__ __attribute__((aligned(16))) int8_t ring0[kSlot];
-  __shared__ __attribute__((aligned(16))) int8_t ring1[kSlot];
-  __shared__ __attribute__((aligned(16))) int8_t ring2[kSlot];
-  __shared__ __attribute__((aligned(16))) int8_t ring3[kSlot];
-  Job job;
-  if (!find_job(g0, g1, kPTok, blockIdx.y, job)) return;
-  const Group G = job.g == 0 ? g0 : g1;
-  const int I = G.inter;
-  const int cb = blockIdx.x * 256;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int wc = wave & 3, wt = wave >> 2;
-  const int c0 = cb + wc * 64;
-  const int i = lane & 15, g = lane >> 4;
-  const int r0 = job.r0, nr = job.nr;
-  const int ntg = min(4, max(0, (nr - 64 * wt + 15) / 16));
-  const bool active = c0 < d && ntg > 0;
-  const int nhb = I / 64;
-
-  const int8_t* W = static_cast<const int8_t*>(G.wdn);
-  const int8_t* asrc[2];
-  const int8_t* bsrc[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int blk = 2 * wave + u;
-    const int col = cb + 16 * blk;
-    const size_t row0 = (size_t)job.e * d + (col < d ? col : 0);
-    asrc[u] = wblock_src<LAY>(W, row0, I, lane);
-    const int j = 16 * (blk >> 1) + i;
-    bsrc[u] = G.hq + (size_t)(r0 + (j < nr ? j : 0)) * 2 * I + (blk & 1) * I + 16 * g;
-  }
-  const int srow = 64 * (wave & 1) + lane;
-  const float* ssrc = G.hs + (size_t)(r0 + (srow < nr ? srow : 0)) * nhb;
-  const int nsteps = I / kKStep;
-  const int last = nsteps - 1;
-  auto issue = [&](int8_t* slot, int step) {
-    const int st = min(step, last);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      lds_load16(asrc[u] + (size_t)st * wblock_step<LAY>(), slot + (2 * wave + u) * kPBlk);
-      lds_load16(bsrc[u] + st * kKStep, slot + 16 * kPBlk + (2 * wave + u) * kPBlk);
-    }
-    lds_load4(ssrc + st, slot + kPSlotBytes + wave * kWave * 4);
-  };
-
-  float acc[4][4][4];  // [weight fragment][row group][c]
-#pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[f][t][c] = 0.0f;
-  const v4i zero = {0, 0, 0, 0};
-
-  issue(ring0, 0);
-  issue(ring1, 1);
-  issue(ring2, 2);
-
-#define DN_STEP(S, Q)                                                                         \
-  {                                                                                           \
-    MOE_WAIT_VM(10);                                                                          \
-    ring_barrier();                                                                           \
-    if (active) {                                                                             \
-      const int8_t* slot = RING_SLOT(Q);                                                      \
-      v4i a[4];                                                                               \
-      _Pragma("unroll") for (int f = 0; f < 4; ++f) a[f] = lds_frag(slot + (4 * wc + f) * kPBlk, lane); \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
-        if (t < ntg) {                                                                        \
-          const int8_t* bb = slot + 16 * kPBlk + 2 * (4 * wt + t) * kPBlk;                    \
-          const v4i b0 = lds_frag(bb, lane);                                                  \
-          const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
-          const float sg = reinterpret_cast<const float*>(slot + kPSlotBytes)[wt * kWave + 16 * t + i]; \
-          _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                     \
-            const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b0, zero, 0, 0, 0);    \
-            const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b1, zero, 0, 0, 0);    \
-            _Pragma("unroll") for (int c = 0; c < 4; ++c) acc[f][t][c] =                     \
-                fmaf(sg, fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[f][t][c]);      \
-          }                                                                                   \
-        }                                                                                     \
-      }                                                                                       \
-    }                                                                                         \
-    issue(RING_SLOT(((Q) + 3) & 3), (S) + 3);                                                 \
-  }
-  int s0 = 0;
-  for (; s0 + 4 <= nsteps; s0 += 4) {
-    DN_STEP(s0, 0)
-    DN_STEP(s0 + 1, 1)
-    DN_STEP(s0 + 2, 2)
-    DN_STEP(s0 + 3, 3)
-  }
-  if (s0 < nsteps) DN_STEP(s0, 0)
-  if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1)
-  if (s0 + 2 < nsteps) DN_STEP(s0 + 2, 2)
-#undef DN_STEP
-  MOE_WAIT_VM(0);
-  if (!active) return;
-  const float* sd = G.sdn + (size_t)job.e * d;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int j = 64 * wt + 16 * t + i;
-    if (t >= ntg || j >= nr) continue;
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int n = c0 + 16 * f + 4 * g;
-      *reinterpret_cast<float4*>(G.out + (size_t)(r0 + j) * d + n) =
-          make_float4(sd[n] * acc[f][t][0], sd[n + 1] * acc[f][t][1], sd[n + 2] * acc[f][t][2],
-                      sd[n + 3] * acc[f][t][3]);
-    }
-  }
-}
 #undef RING_SLOT
 
 // The down projection uses smaller tiles: up to 64 rows, a workgroup of 8
-// wavefronts owning 128 output columns (16 per wavefront).  Its block scales
-// change every 64 inputs, so its K loop folds int32 products into fp32 per
-// K-step and holds 64 fp32 sums per lane; the smaller tile keeps registers low
-// enough for two workgroups per CU.  The tile's h digits are staged in LDS 256
+// wavefronts owning 128 output columns (16 per wavefront).  Its h scales
+// change every 128 inputs (the gate/up GEMM writes one per row and 128-column
+// block), so its K loop accumulates two K-steps of each digit in int32 on the
+// matrix cores, joins the digits as 256 d0 + d1 (exact in int32) and folds
+// that into fp32 with one multiply-add per output, holding 16 fp32 sums per
+// lane; the smaller tile keeps registers low enough for two workgroups per CU.  The tile's h digits are staged in LDS 256
 // inputs at a time (double-buffered); weight fragments and digits of chunk
 // c+1 are loaded into registers while chunk c is computed.  All loads are
 // unconditional (clamped addresses, masked values) so the compiler waits only
@@ -992,7 +879,7 @@ __device__ inline void dstage_store(const DStage& st, const DSrc& src, int valid
 template <int LAY>
 __global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, int d) {
   __shared__ __attribute__((aligned(16))) int8_t bsm[2][kDRows * kDLdr];
-  __shared__ float ssm[2][kDRows][kDChunk / kKStep];
+  __shared__ float ssm[2][kDRows][kDChunk / 128];
   Job job;
   if (!find_job(g0, g1, kDRows, blockIdx.y, job)) return;
   const Group G = job.g == 0 ? g0 : g1;
@@ -1003,12 +890,13 @@ __global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, in
   const int i = lane & 15, g = lane >> 4;
   const int r0 = job.r0, nr = job.nr;
   const int ntg = (nr + 15) / 16;
-  const int nhb = I / 64;
+  const int nhb = (I + 127) / 128;  // h scale blocks per row
   const size_t row0 = (size_t)job.e * d + (active ? c0 : 0);
   const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g, lane);
   const DSrc src = dsrc_init(G.hq, 2 * I, I, r0, nr);
-  // block scales: thread tid < 256 reads row tid / 4, block tid % 4 of a chunk
-  const int sj = (threadIdx.x >> 2) & (kDRows - 1), sb = threadIdx.x & 3;
+  // h scales: thread tid < 128 reads row tid / 2, block tid % 2 of a chunk
+  // (divided by 256, exactly, for the joined digits)
+  const int sj = (threadIdx.x >> 1) & (kDRows - 1), sb = threadIdx.x & 1;
   const bool s_ok = sj < nr;
   const float* sp = G.hs + (size_t)(r0 + (s_ok ? sj : 0)) * nhb;
   float acc[4][4];
@@ -1021,8 +909,8 @@ __global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, in
   const int lastc = nchunk - 1;
   auto valid_of = [&](int c) { return min(kDChunk, I - c * kDChunk); };
   auto scale_of = [&](int c) {  // clamp the block index inside the row
-    const int b = c * (kDChunk / kKStep) + sb;
-    return sp[b < nhb ? b : nhb - 1];
+    const int b = c * (kDChunk / 128) + sb;
+    return sp[b < nhb ? b : nhb - 1] * (1.0f / 256.0f);
   };
 
   v4i ra[4];
@@ -1034,8 +922,8 @@ __global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, in
     dstage_load(st, src, 0, valid_of(0));
     const float sv = scale_of(0);
     dstage_store(st, src, valid_of(0), bsm[0]);
-    if (threadIdx.x < kDRows * 4)
-      ssm[0][sj][sb] = (s_ok && sb < nst) ? sv : 0.0f;
+    if (threadIdx.x < kDRows * 2)
+      ssm[0][sj][sb] = (s_ok && 2 * sb < nst) ? sv : 0.0f;
   }
   __syncthreads();
 
@@ -1052,20 +940,31 @@ __global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, in
     const int8_t* buf = bsm[c & 1];
     if (active) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u < nst) {
+      for (int pr = 0; pr < 2; ++pr) {  // the chunk's two 128-input scale blocks
+        const int u0 = 2 * pr;
+        if (u0 < nst) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             if (t < ntg) {
               const int8_t* brow = buf + (16 * t + i) * kDLdr;
-              const v4i x0 = *reinterpret_cast<const v4i*>(brow + 64 * u + 16 * g);
-              const v4i x1 = *reinterpret_cast<const v4i*>(brow + kDChunk + 64 * u + 16 * g);
-              const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0, zero, 0, 0, 0);
-              const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1, zero, 0, 0, 0);
-              const float sg = ssm[c & 1][16 * t + i][u];
+              v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  ra[u0], *reinterpret_cast<const v4i*>(brow + 64 * u0 + 16 * g), zero, 0, 0, 0);
+              v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  ra[u0], *reinterpret_cast<const v4i*>(brow + kDChunk + 64 * u0 + 16 * g), zero,
+                  0, 0, 0);
+              if (u0 + 1 < nst) {
+                p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    ra[u0 + 1], *reinterpret_cast<const v4i*>(brow + 64 * (u0 + 1) + 16 * g), p0,
+                    0, 0, 0);
+                p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    ra[u0 + 1],
+                    *reinterpret_cast<const v4i*>(brow + kDChunk + 64 * (u0 + 1) + 16 * g), p1,
+                    0, 0, 0);
+              }
+              const float sg = ssm[c & 1][16 * t + i][pr];
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                acc[t][q] = fmaf(sg, fmaf((float)p1[q], 1.0f / 256.0f, (float)p0[q]), acc[t][q]);
+                acc[t][q] = fmaf(sg, (float)(p0[q] * 256 + p1[q]), acc[t][q]);
             }
           }
         }
@@ -1073,8 +972,8 @@ __global__ __launch_bounds__(512) void down_gemm64_kernel(Group g0, Group g1, in
     }
     if (c + 1 < nchunk) {
       dstage_store(st, src, val1, bsm[(c + 1) & 1]);
-      if (threadIdx.x < kDRows * 4)
-        ssm[(c + 1) & 1][sj][sb] = (s_ok && sb < nst1) ? sv : 0.0f;
+      if (threadIdx.x < kDRows * 2)
+        ssm[(c + 1) & 1][sj][sb] = (s_ok && 2 * sb < nst1) ? sv : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) ra[u] = na[u];
