@@ -599,28 +599,31 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 }
 
 // ------------------------------------------------------------------ prefill GEMM
-// Many rows per expert: a tile is up to 128 rows of one expert.  A workgroup
-// of 8 wavefronts covers the tile and 128 output columns (gate/up: 256 weight
-// rows) or 256 (down); wavefront w takes tile rows [64 (w / 4), +64) and the
-// weight row groups of its 32 (gate/up) or 64 (down) columns.  Per 64-wide
-// K-step a wavefront runs 4 weight fragments x 4 row groups x 2 digits = 32
-// MFMAs, all operands read from LDS.
+// Many rows per expert: gate/up runs as a grouped GEMM over tiles of one
+// expert's rows.  A workgroup of 8 wavefronts covers a tile and a block of
+// output columns; each wavefront owns 32 columns (16 gate and 16 up rows,
+// twice) and 64 tile rows, so per 64-wide K-step it runs 4 weight fragments x
+// 4 row groups x 2 digits = 32 MFMAs with every operand read from LDS.  Two
+// shapes (WT = wavefront rows): WT = 2 takes 128-row tiles and 128 columns
+// (many rows per expert, so weights are re-read for fewer tiles); WT = 1
+// takes 64-row tiles and 256 columns (few rows per expert, so fewer digit
+// bytes move per weight byte).
 //
 // Both operands reach LDS by direct global-to-LDS loads (no registers): per
-// K-step 16 weight blocks (each an MFMA A operand of 1 KB, contiguous in the
-// tiled layout) and 16 digit blocks (row group x digit, gathered by row), 4
-// loads per wavefront.  A ring of four K-step slots keeps three K-steps in
-// flight.  Every wavefront issues the same loads in the same order on every
-// K-step (rows past the tile re-read row 0, K-steps past the end re-read the
-// last one), so before the barrier of K-step s each wavefront waits until at
-// most the 8 (down: 10) loads of K-steps s+1, s+2 are still in flight: its own
-// part of slot s has landed, and after the barrier every part has.  The
-// barrier is a bare s_barrier between compiler fences: no wait on the loads
-// still in flight.  The slots are separate LDS arrays so that the compiler
-// can tell the loads into one slot from the reads of another.
-constexpr int kPTok = 128, kPWaves = 8, kPSlots = 4;
+// K-step 4 weight blocks per 16-column group (each an MFMA A operand of 1 KB,
+// contiguous in the tiled layout) and 2 digit blocks per row group (gathered
+// by row), the same number of loads for every wavefront.  A ring of K-step
+// slots (4 for WT = 2, 3 for WT = 1) keeps 3 or 2 K-steps in flight.  Every
+// wavefront issues the same loads in the same order on every K-step (rows
+// past the tile re-read row 0, K-steps past the end re-read the last one), so
+// before the barrier of K-step s each wavefront waits until only the loads of
+// the K-steps after s are still in flight: its own part of slot s has landed,
+// and after the barrier every part has.  The barrier is a bare s_barrier
+// between compiler fences: no wait on the loads still in flight.  The slots
+// are separate LDS arrays so that the compiler can tell the loads into one
+// slot from the reads of another.
+constexpr int kPWaves = 8;
 constexpr int kPBlk = 1024;                 // one MFMA operand
-constexpr int kPSlotBytes = 32 * kPBlk;     // 16 weight blocks + 16 digit blocks
 
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
 #define MOE_WAIT_VM(n) \
@@ -656,46 +659,67 @@ constexpr int wblock_step() {
   return LAY == kRows ? kKStep : kPBlk;
 }
 
+// Tile geometry of the gate/up GEMM for WT wavefront rows.
+template <int WT>
+struct GuShape {
+  static constexpr int CW = kPWaves / WT;          // column wavefronts
+  static constexpr int ROWS = 64 * WT;             // tile rows
+  static constexpr int COLS = 32 * CW;             // output columns per workgroup
+  static constexpr int NA = 4 * CW;                // weight blocks per K-step
+  static constexpr int NB = 2 * ROWS / 16;         // digit blocks per K-step
+  static constexpr int A_PER = NA / kPWaves;       // per wavefront
+  static constexpr int B_PER = NB / kPWaves;
+  static constexpr int SLOT = (NA + NB) * kPBlk;   // LDS bytes per K-step slot
+  static constexpr int NS = WT == 2 ? 4 : 3;       // slots in the ring
+  static constexpr int WAIT = (NS - 2) * (A_PER + B_PER);  // loads left in flight
+};
+
 #define RING_SLOT(q) ((q) == 0 ? ring0 : (q) == 1 ? ring1 : (q) == 2 ? ring2 : ring3)
 
-template <int LAY>
+template <int LAY, int WT>
 __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, int d,
                                                            const int8_t* __restrict__ xq,
                                                            const float* __restrict__ xs) {
-  __shared__ __attribute__((aligned(16))) int8_t ring0[kPSlotBytes];
-  __shared__ __attribute__((aligned(16))) int8_t ring1[kPSlotBytes];
-  __shared__ __attribute__((aligned(16))) int8_t ring2[kPSlotBytes];
-  __shared__ __attribute__((aligned(16))) int8_t ring3[kPSlotBytes];
-  __shared__ float red_max[4][kPTok];
-  __shared__ int tok_sm[kPTok];
+  using S = GuShape<WT>;
+  __shared__ __attribute__((aligned(16))) int8_t ring0[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring1[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring2[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring3[S::NS == 4 ? S::SLOT : 16];
+  __shared__ float red_max[S::CW][S::ROWS];
+  __shared__ int tok_sm[S::ROWS];
   Job job;
-  if (!find_job(g0, g1, kPTok, blockIdx.y, job)) return;
+  if (!find_job(g0, g1, S::ROWS, blockIdx.y, job)) return;
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
-  const int cb = blockIdx.x * 128;
+  const int cb = blockIdx.x * S::COLS;
   if (cb >= I) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int wc = wave & 3, wt = wave >> 2;
+  const int wc = wave % S::CW, wt = wave / S::CW;
   const int c0 = cb + wc * 32;
   const int i = lane & 15, g = lane >> 4;
   const int ntg = min(4, max(0, (job.nr - 64 * wt + 15) / 16));
   const bool active = c0 < I && ntg > 0;  // every wavefront issues loads and meets the barriers
-  for (int j = threadIdx.x; j < kPTok; j += blockDim.x)
+  for (int j = threadIdx.x; j < S::ROWS; j += blockDim.x)
     tok_sm[j] = j < job.nr ? (G.row_token ? G.row_token[job.r0 + j] : job.r0 + j) : -1;
   __syncthreads();
 
-  // this wavefront's loads per K-step: weight blocks 2w, 2w+1 (blocks 0..7 =
-  // gate row groups of columns cb.., 8..15 = the same up rows) and digit
-  // blocks 2w, 2w+1 (block q = row group q/2, digit q%2)
+  // this wavefront's loads per K-step: weight blocks A_PER w .. (blocks
+  // 0 .. 2CW-1 = gate row groups of columns cb.., then the same up rows) and
+  // digit blocks B_PER w .. (block q = row group q/2, digit q%2)
   const int8_t* W = static_cast<const int8_t*>(G.wgu);
-  const int8_t* asrc[2];
-  const int8_t* bsrc[2];
+  const int8_t* asrc[S::A_PER];
+  const int8_t* bsrc[S::B_PER];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int blk = 2 * wave + u;
-    const int col = cb + 16 * (blk & 7);
-    const size_t row0 = (size_t)job.e * 2 * I + (col < I ? col + (blk >= 8 ? I : 0) : 0);
+  for (int u = 0; u < S::A_PER; ++u) {
+    const int blk = S::A_PER * wave + u;
+    const bool up = blk >= 2 * S::CW;
+    const int col = cb + 16 * (up ? blk - 2 * S::CW : blk);
+    const size_t row0 = (size_t)job.e * 2 * I + (col < I ? col + (up ? I : 0) : 0);
     asrc[u] = wblock_src<LAY>(W, row0, d, lane);
+  }
+#pragma unroll
+  for (int u = 0; u < S::B_PER; ++u) {
+    const int blk = S::B_PER * wave + u;
     const int j = 16 * (blk >> 1) + i;
     const int tok = tok_sm[j] >= 0 ? tok_sm[j] : tok_sm[0];
     bsrc[u] = xq + (size_t)tok * 2 * d + (blk & 1) * d + 16 * g;
@@ -705,10 +729,12 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
   auto issue = [&](int8_t* slot, int step) {
     const int st = min(step, last);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      lds_load16(asrc[u] + (size_t)st * wblock_step<LAY>(), slot + (2 * wave + u) * kPBlk);
-      lds_load16(bsrc[u] + st * kKStep, slot + 16 * kPBlk + (2 * wave + u) * kPBlk);
-    }
+    for (int u = 0; u < S::A_PER; ++u)
+      lds_load16(asrc[u] + (size_t)st * wblock_step<LAY>(),
+                 slot + (S::A_PER * wave + u) * kPBlk);
+#pragma unroll
+    for (int u = 0; u < S::B_PER; ++u)
+      lds_load16(bsrc[u] + st * kKStep, slot + (S::NA + S::B_PER * wave + u) * kPBlk);
   };
 
   v4i acc[4][4][2];  // [weight fragment][row group][digit]
@@ -716,16 +742,15 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[f][t][0] = acc[f][t][1] = v4i{0, 0, 0, 0};
-  // weight blocks of this wavefront's fragments: gate 2wc, 2wc+1, up 8+2wc, 9+2wc
-  const int ablk[4] = {2 * wc, 2 * wc + 1, 8 + 2 * wc, 9 + 2 * wc};
+  // weight blocks of this wavefront's fragments: gate 2wc, 2wc+1, up 2CW+2wc, 2CW+2wc+1
+  const int ablk[4] = {2 * wc, 2 * wc + 1, 2 * S::CW + 2 * wc, 2 * S::CW + 2 * wc + 1};
 
-  issue(ring0, 0);
-  issue(ring1, 1);
-  issue(ring2, 2);
+#pragma unroll
+  for (int q = 0; q < S::NS - 1; ++q) issue(RING_SLOT(q), q);
 
-#define GU_STEP(S, Q)                                                                         \
+#define GU_STEP(STEP, Q)                                                                      \
   {                                                                                           \
-    MOE_WAIT_VM(8);                                                                           \
+    MOE_WAIT_VM(S::WAIT);                                                                     \
     ring_barrier();                                                                           \
     if (active) {                                                                             \
       const int8_t* slot = RING_SLOT(Q);                                                      \
@@ -733,7 +758,7 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
       _Pragma("unroll") for (int f = 0; f < 4; ++f) a[f] = lds_frag(slot + ablk[f] * kPBlk, lane); \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
         if (t < ntg) {                                                                        \
-          const int8_t* bb = slot + 16 * kPBlk + 2 * (4 * wt + t) * kPBlk;                    \
+          const int8_t* bb = slot + (S::NA + 2 * (4 * wt + t)) * kPBlk;                       \
           const v4i b0 = lds_frag(bb, lane);                                                  \
           const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
           _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                     \
@@ -743,22 +768,32 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
         }                                                                                     \
       }                                                                                       \
     }                                                                                         \
-    issue(RING_SLOT(((Q) + 3) & 3), (S) + 3);                                                 \
+    issue(RING_SLOT(((Q) + S::NS - 1) % S::NS), (STEP) + S::NS - 1);                          \
   }
   int s0 = 0;
-  for (; s0 + 4 <= nsteps; s0 += 4) {
-    GU_STEP(s0, 0)
-    GU_STEP(s0 + 1, 1)
-    GU_STEP(s0 + 2, 2)
-    GU_STEP(s0 + 3, 3)
+  if constexpr (S::NS == 4) {
+    for (; s0 + 4 <= nsteps; s0 += 4) {
+      GU_STEP(s0, 0)
+      GU_STEP(s0 + 1, 1)
+      GU_STEP(s0 + 2, 2)
+      GU_STEP(s0 + 3, 3)
+    }
+    if (s0 < nsteps) GU_STEP(s0, 0)
+    if (s0 + 1 < nsteps) GU_STEP(s0 + 1, 1)
+    if (s0 + 2 < nsteps) GU_STEP(s0 + 2, 2)
+  } else {
+    for (; s0 + 3 <= nsteps; s0 += 3) {
+      GU_STEP(s0, 0)
+      GU_STEP(s0 + 1, 1)
+      GU_STEP(s0 + 2, 2)
+    }
+    if (s0 < nsteps) GU_STEP(s0, 0)
+    if (s0 + 1 < nsteps) GU_STEP(s0 + 1, 1)
   }
-  if (s0 < nsteps) GU_STEP(s0, 0)
-  if (s0 + 1 < nsteps) GU_STEP(s0 + 1, 1)
-  if (s0 + 2 < nsteps) GU_STEP(s0 + 2, 2)
 #undef GU_STEP
   MOE_WAIT_VM(0);
 
-  // epilogue: h per row, one scale per row and 64-column block (two wavefronts)
+  // epilogue: h per row, one scale per row and 128-column block (4 wavefronts)
   const float* se = G.sgu + (size_t)job.e * 2 * I;
   float h[2][4][4];  // [column half][row group][c]
 #pragma unroll
@@ -789,12 +824,13 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
   }
   __syncthreads();
   if (!active) return;
+  const int grp = wc >> 2;  // 128-column scale block of this wavefront
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = 64 * wt + 16 * t + i;
     if (t >= ntg || j >= job.nr) continue;
-    // one scale per row and 128-column block (this workgroup's columns)
-    const float mx = fmaxf(fmaxf(red_max[0][j], red_max[1][j]), fmaxf(red_max[2][j], red_max[3][j]));
+    const float mx = fmaxf(fmaxf(red_max[4 * grp][j], red_max[4 * grp + 1][j]),
+                           fmaxf(red_max[4 * grp + 2][j], red_max[4 * grp + 3][j]));
     const int p = digit_exponent(mx);
     const int r = job.r0 + j;
     int8_t* hrow = G.hq + (size_t)r * 2 * I;
@@ -807,11 +843,10 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
       *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
       *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
     }
-    if (wc == 0 && g == 0)
-      G.hs[(size_t)r * ((I + 127) / 128) + blockIdx.x] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+    if ((wc & 3) == 0 && g == 0)
+      G.hs[(size_t)r * ((I + 127) / 128) + (cb >> 7) + grp] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
   }
 }
-
 #undef RING_SLOT
 
 // The down projection uses smaller tiles: up to 64 rows, a workgroup of 8
@@ -1137,18 +1172,29 @@ hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nr
 template <int LAY>
 hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const float* xs,
                             hipStream_t s) {
-  // tiles of kPTok rows for gate/up, kDRows rows for down
   auto tiles_of = [](const Group& G, int mt) {
     if (G.R <= 0) return 0;
     return G.offsets ? max_tiles(G.R, G.E, mt) : (G.R + mt - 1) / mt;
   };
   const int imax = a.inter > b.inter ? a.inter : b.inter;
-  a.tiles = tiles_of(a, kPTok);
-  b.tiles = tiles_of(b, kPTok);
+  // gate/up: 64-row tiles x 256 columns below 96 rows per expert on average,
+  // else 128-row tiles x 128 columns
+  const bool tall = a.R >= 96LL * a.E;
   {
     TimedLaunch tl(K_FFN_I8_GATE_UP_GEMM, s);
-    hipLaunchKernelGGL(gate_up_gemm_kernel<LAY>, dim3((imax + 127) / 128, a.tiles + b.tiles),
-                       dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+    if (tall) {
+      using S = GuShape<2>;
+      a.tiles = tiles_of(a, S::ROWS);
+      b.tiles = tiles_of(b, S::ROWS);
+      hipLaunchKernelGGL((gate_up_gemm_kernel<LAY, 2>), dim3((imax + S::COLS - 1) / S::COLS,
+                         a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+    } else {
+      using S = GuShape<1>;
+      a.tiles = tiles_of(a, S::ROWS);
+      b.tiles = tiles_of(b, S::ROWS);
+      hipLaunchKernelGGL((gate_up_gemm_kernel<LAY, 1>), dim3((imax + S::COLS - 1) / S::COLS,
+                         a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1167,14 +1213,13 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     err = launch_encode_rows(x, T, d, ws.xq, ws.xs, s);
     if (err != hipSuccess) return err;
   }
-  // int8 with many rows per expert: grouped GEMM tiles of 128 rows
+  // int8 with many rows per expert: grouped GEMM
   if (sets[0].fmt == 1 && sets[0].pairs_idx == nullptr && sets[0].R >= 16LL * sets[0].E) {
     Group grp[2] = {};
     for (int q = 0; q < nsets; ++q) {
       const FfnSet& f = sets[q];
       Group& G = grp[q];
       G.E = f.E; G.inter = f.inter; G.R = f.R;
-      G.tiles = f.offsets ? max_tiles(f.R, f.E, kPTok) : (f.R + kPTok - 1) / kPTok;
       G.wgu = f.wgu; G.sgu = f.sgu; G.wdn = f.wdn; G.sdn = f.sdn;
       G.row_token = f.row_token; G.offsets = f.offsets;
       G.hq = f.hq; G.hs = f.hs; G.out = f.out;
