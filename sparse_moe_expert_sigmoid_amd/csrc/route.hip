@@ -26,8 +26,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
                                                             int T, int d, int E,
                                                             float* __restrict__ partial) {
   constexpr int PE = TE / 16, PT = TT / 16;
-  __shared__ float ws[TE][kSub + 1];
-  __shared__ float xs[TT][kSub + 1];
+  constexpr int kLd = kSub + 4;  // row stride: 16-byte aligned, rows 4 banks apart
+  __shared__ __attribute__((aligned(16))) float ws[TE][kLd];
+  __shared__ __attribute__((aligned(16))) float xs[TT][kLd];
   const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, c = blockIdx.z;
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
   float acc[PE][PT];
@@ -46,10 +47,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < E && 4 * c4 < kn)
         v = *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + 4 * c4);
-      ws[r][4 * c4 + 0] = v.x;
-      ws[r][4 * c4 + 1] = v.y;
-      ws[r][4 * c4 + 2] = v.z;
-      ws[r][4 * c4 + 3] = v.w;
+      *reinterpret_cast<float4*>(&ws[r][4 * c4]) = v;
     }
     for (int q = threadIdx.x; q < TT * (kSub / 4); q += 256) {
       const int r = q / (kSub / 4), c4 = q % (kSub / 4);
@@ -57,23 +55,26 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float* __restr
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (t < T && 4 * c4 < kn)
         v = *reinterpret_cast<const float4*>(x + (size_t)t * d + k0 + 4 * c4);
-      xs[r][4 * c4 + 0] = v.x;
-      xs[r][4 * c4 + 1] = v.y;
-      xs[r][4 * c4 + 2] = v.z;
-      xs[r][4 * c4 + 3] = v.w;
+      *reinterpret_cast<float4*>(&xs[r][4 * c4]) = v;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kn; ++kk) {
-      float wv[PE], xv[PT];
+    // four inputs per LDS read; the fmaf chain still runs in ascending i
+#pragma unroll 2
+    for (int kk = 0; kk < kn; kk += 4) {
+      float4 wv[PE], xv[PT];
 #pragma unroll
-      for (int a = 0; a < PE; ++a) wv[a] = ws[ti + 16 * a][kk];
+      for (int a = 0; a < PE; ++a) wv[a] = *reinterpret_cast<const float4*>(&ws[ti + 16 * a][kk]);
 #pragma unroll
-      for (int b = 0; b < PT; ++b) xv[b] = xs[tj + 16 * b][kk];
+      for (int b = 0; b < PT; ++b) xv[b] = *reinterpret_cast<const float4*>(&xs[tj + 16 * b][kk]);
 #pragma unroll
       for (int a = 0; a < PE; ++a)
 #pragma unroll
-        for (int b = 0; b < PT; ++b) acc[a][b] = fmaf(wv[a], xv[b], acc[a][b]);
+        for (int b = 0; b < PT; ++b) {
+          acc[a][b] = fmaf(wv[a].x, xv[b].x, acc[a][b]);
+          acc[a][b] = fmaf(wv[a].y, xv[b].y, acc[a][b]);
+          acc[a][b] = fmaf(wv[a].z, xv[b].z, acc[a][b]);
+          acc[a][b] = fmaf(wv[a].w, xv[b].w, acc[a][b]);
+        }
     }
     __syncthreads();
   }
