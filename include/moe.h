@@ -160,6 +160,32 @@ moe_status moe_route(moe_ctx* ctx, int router, const float* x, const float* w_ro
                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Router restricted to a subset of the experts.  Restricting a model to an
+ * expert subset is the same as masking the others at run time
+ * (Kimi-Linear-48B-A3B-Code-CMF listing, "How it was made", step 3): the
+ * result equals moe_route on the allowed experts alone (router rows and bias
+ * sliced, ids mapped back), bit for bit.
+ *   mask  [E] uint8 device array: nonzero = the expert may be selected, 0 =
+ *         never; NULL = all allowed (then this is moe_route).  At least k experts
+ *         should be allowed: with fewer, the remaining slots hold masked experts
+ *         (lowest id first, ids still in [0, E)) with weight 0, and with none
+ *         allowed every weight is NaN.  Sigmoid router: masked experts drop out
+ *         of the selection and their scores never enter a weight.  Softmax
+ *         router: the softmax runs over the allowed experts only.
+ * Other arguments, checks and errors as for moe_route. */
+moe_status moe_route_masked(moe_ctx* ctx, int router, const float* x, const float* w_router,
+                            const float* bias, const uint8_t* mask, int T, int d, int E,
+                            int k, float scale, int32_t* topk_idx, float* topk_w, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Routing statistics (the per-expert routing frequencies of the
+ * Kimi-Linear-48B-A3B-Code-CMF listing, "How it was made", step 2):
+ *   counts[e] += #{(t, j) : topk_idx[t][j] == e}   for e < E
+ *   topk_idx [T][k] int32 device; counts [E] uint64 device, accumulated (the
+ *   caller zeroes it once).  Entries outside [0, E) are not counted. */
+moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
+                             unsigned long long* counts, void* stream);
+
 /* Group the T*k (token, slot) pairs by expert (Qwen3 card, Conversion Notes:
  * only the routed experts are computed for each token).  Stable: within an
  * expert, rows follow (t, j) order.
@@ -203,7 +229,9 @@ moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row
  *   router, k, scale, w_router [E][d], bias [E] or NULL: as for moe_route
  *   experts: the routed experts (E = experts.n_experts)
  *   shared:  the shared expert (shared.n_experts == 1), or shared.n_experts == 0
- *            for none; same d as the routed experts                              */
+ *            for none; same d as the routed experts
+ *   expert_mask: [E] uint8 device, or NULL; restricts the routed experts as in
+ *            moe_route_masked                                                   */
 typedef struct {
     int router;
     int k;
@@ -212,6 +240,7 @@ typedef struct {
     const float* bias;
     moe_weights experts;
     moe_weights shared;
+    const uint8_t* expert_mask;  /* [E] device, or NULL: see moe_route_masked */
 } moe_layer;
 
 /* Workspace for moe_forward on T tokens.  [host] *bytes. */

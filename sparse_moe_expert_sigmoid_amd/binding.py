@@ -30,7 +30,7 @@ FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B3
 EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
-           "moe_tile_weights")
+           "moe_tile_weights", "moe_route_masked", "moe_expert_counts")
 
 
 class MoeError(RuntimeError):
@@ -50,7 +50,8 @@ class moe_weights(ctypes.Structure):
 class moe_layer(ctypes.Structure):
     _fields_ = [("router", ctypes.c_int), ("k", ctypes.c_int), ("scale", ctypes.c_float),
                 ("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
-                ("experts", moe_weights), ("shared", moe_weights)]
+                ("experts", moe_weights), ("shared", moe_weights),
+                ("expert_mask", ctypes.c_void_p)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -81,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_workspace_size.argtypes = [vp, ci, ci, ci, ci, ci, ci, ctypes.POINTER(sz)]
     lib.moe_route.argtypes = [vp, ci, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, vp, vp, vp, sz,
                               vp]
+    lib.moe_route_masked.argtypes = [vp, ci, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, vp,
+                                     vp, vp, sz, vp]
+    lib.moe_expert_counts.argtypes = [vp, vp, ci, ci, ci, vp, vp]
     lib.moe_permute.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp]
     lib.moe_expert_ffn.argtypes = [vp, ctypes.POINTER(moe_weights), ci, vp, ci, vp, vp, ci, vp,
                                    vp, sz, vp]
@@ -95,7 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ci)]
     for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
               "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
-              "moe_forward", "moe_tile_weights"):
+              "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -155,6 +159,17 @@ class Context:
             self.handle, router, _p(x), _p(w_router), _p(bias), T, d, E, k, scale, _p(topk_idx),
             _p(topk_w), _p(ws), ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
             _stream(stream)))
+
+    def moe_route_masked(self, router, x, w_router, bias, mask, T, d, E, k, scale, topk_idx,
+                         topk_w, ws, stream=None, ws_bytes=None):
+        self._check(self.lib.moe_route_masked(
+            self.handle, router, _p(x), _p(w_router), _p(bias), _p(mask), T, d, E, k, scale,
+            _p(topk_idx), _p(topk_w), _p(ws),
+            ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes, _stream(stream)))
+
+    def moe_expert_counts(self, topk_idx, T, k, E, counts, stream=None):
+        self._check(self.lib.moe_expert_counts(self.handle, _p(topk_idx), T, k, E, _p(counts),
+                                               _stream(stream)))
 
     def moe_permute(self, topk_idx, T, k, E, offsets, row_token, token_row, stream=None):
         self._check(self.lib.moe_permute(self.handle, _p(topk_idx), T, k, E, _p(offsets),

@@ -317,6 +317,14 @@ moe_status moe_route(moe_ctx* ctx, int router, const float* x, const float* w_ro
                      const float* bias, int T, int d, int E, int k, float scale,
                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
                      void* stream) {
+  return moe_route_masked(ctx, router, x, w_router, bias, nullptr, T, d, E, k, scale, topk_idx,
+                          topk_w, ws, ws_bytes, stream);
+}
+
+moe_status moe_route_masked(moe_ctx* ctx, int router, const float* x, const float* w_router,
+                            const float* bias, const uint8_t* mask, int T, int d, int E,
+                            int k, float scale, int32_t* topk_idx, float* topk_w, void* ws,
+                            size_t ws_bytes, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
   if (router != MOE_ROUTER_SIGMOID_BIAS && router != MOE_ROUTER_SOFTMAX)
     return fail(ctx, MOE_E_INVALID, "moe_route: unknown router %d", router);
@@ -346,9 +354,31 @@ moe_status moe_route(moe_ctx* ctx, int router, const float* x, const float* w_ro
                 need, ws_bytes);
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_route: hipSetDevice(%d) failed", ctx->device);
-  hipError_t e = moe::launch_router(router, x, w_router, bias, T, d, E, k, scale, topk_idx,
-                                    topk_w, static_cast<float*>(ws), (hipStream_t)stream);
+  hipError_t e = moe::launch_router(router, x, w_router, bias, mask, T, d, E, k, scale,
+                                    topk_idx, topk_w, static_cast<float*>(ws),
+                                    (hipStream_t)stream);
   return device_result(ctx, e, "moe_route");
+}
+
+moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
+                             unsigned long long* counts, void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  if (T < 0 || k < 1 || (long long)T * k > 0x7fffffffLL)
+    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: T=%d k=%d", T, k);
+  if (E < 1 || E > moe::kMaxE)
+    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: E=%d outside [1, %d]", E, moe::kMaxE);
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !counts)
+    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: %s is NULL",
+                !topk_idx ? "topk_idx" : "counts");
+  if (!aligned16(topk_idx) || (reinterpret_cast<uintptr_t>(counts) & 7) != 0)
+    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: a pointer is misaligned");
+  DeviceGuard g(ctx->device);
+  if (!g.ok)
+    return fail(ctx, MOE_E_DEVICE, "moe_expert_counts: hipSetDevice(%d) failed", ctx->device);
+  hipError_t e = moe::launch_expert_counts(topk_idx, (long long)T * k, E, counts,
+                                           (hipStream_t)stream);
+  return device_result(ctx, e, "moe_expert_counts");
 }
 
 moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
@@ -542,11 +572,11 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
   if (small) {
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, fused ? 2 : 1, Rs, Is, true);
-    e = moe::launch_router_small(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale, idx,
-                                 w, f.partial, lay.xq, lay.xs, s);
+    e = moe::launch_router_small(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
+                                 k, L->scale, idx, w, f.partial, lay.xq, lay.xs, s);
   } else {
-    e = moe::launch_router(L->router, x, L->w_router, L->bias, T, d, E, k, L->scale, idx, w,
-                           f.partial, s);
+    e = moe::launch_router(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E, k,
+                           L->scale, idx, w, f.partial, s);
     if (e == hipSuccess)
       e = moe::launch_permute(idx, T, k, E, f.offsets, f.row_token, f.token_row, s);
   }

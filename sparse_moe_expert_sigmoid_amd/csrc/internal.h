@@ -121,7 +121,9 @@ struct TimedLaunch {
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.
-hipError_t launch_router(int router, const float* x, const float* wr, const float* bias, int T,
+// mask: [E] uint8 device array (nonzero = the expert may be selected) or NULL
+hipError_t launch_router(int router, const float* x, const float* wr, const float* bias,
+                         const uint8_t* mask, int T,
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s);
 // Up to kSmallT tokens: logits, then one launch for selection and the x
@@ -129,8 +131,12 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
 // pairs itself, FfnSet::pairs_idx).
 constexpr int kSmallT = 16;
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
+                               const uint8_t* mask,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
                                float* partial, int8_t* xq, float* xs, hipStream_t s);
+// counts[e] += number of topk_idx entries equal to e (entries outside [0, E) skipped)
+hipError_t launch_expert_counts(const int32_t* idx, long long n, int E, unsigned long long* counts,
+                                hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);

@@ -120,6 +120,34 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Routing statistics: per-expert counts of the selections, accumulated into a
+// 64-bit histogram (integer atomics, so the totals do not depend on order).
+__global__ __launch_bounds__(256) void expert_counts_kernel(const int32_t* __restrict__ idx,
+                                                            long long n, int E,
+                                                            unsigned long long* counts) {
+  extern __shared__ unsigned int hist_u32[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist_u32[e] = 0u;
+  __syncthreads();
+  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < n;
+       q += (long long)gridDim.x * blockDim.x) {
+    const int e = idx[q];
+    if (e >= 0 && e < E) atomicAdd(&hist_u32[e], 1u);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (hist_u32[e]) atomicAdd(&counts[e], (unsigned long long)hist_u32[e]);
+}
+
+hipError_t launch_expert_counts(const int32_t* idx, long long n, int E,
+                                unsigned long long* counts, hipStream_t s) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(expert_counts_kernel, dim3((unsigned)blocks), dim3(256),
+                     (size_t)E * sizeof(unsigned int), s, idx, n, E, counts);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t s) {
   const long long n = (long long)T * k;

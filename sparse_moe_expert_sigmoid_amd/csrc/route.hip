@@ -115,7 +115,8 @@ __device__ inline unsigned ordered_bits(float f) {
 // scale * s_j / sum_j s_j with the sum taken in slot order.
 template <int EPT>
 __device__ inline void select_token(const float* __restrict__ partial, int nchunk,
-                                    const float* __restrict__ bias, int T, int E, int k,
+                                    const float* __restrict__ bias,
+                                    const uint8_t* __restrict__ mask, int T, int E, int k,
                                     int router, float scale, int t, bool active, int gtid,
                                     unsigned long long* keys, float* red, float* sel_s,
                                     int32_t* __restrict__ idx, float* __restrict__ w,
@@ -124,10 +125,12 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
   float sc[EPT];
   unsigned long long key[EPT];
   float bv[EPT];
+  bool ok[EPT];  // allowed by the expert mask (and inside E)
 #pragma unroll
   for (int m = 0; m < EPT; ++m) {
     const int e = gtid + 256 * m;
     bv[m] = (bias && e < E) ? bias[e] : 0.0f;
+    ok[m] = e < E && (mask == nullptr || mask[e] != 0);
   }
   // all slices are loaded before the first add (one trip to memory), then
   // added in ascending order
@@ -155,15 +158,19 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
     for (int m = 0; m < EPT; ++m) {
       const int e = gtid + 256 * m;
       const float s = 1.0f / (1.0f + expf(-sc[m]));
-      sc[m] = s;
+      sc[m] = ok[m] ? s : 0.0f;
       const float kap = s + bv[m];
-      key[m] = ((unsigned long long)ordered_bits(kap) << 32) | (0xffffffffu - (unsigned)e);
+      // A masked expert's key has a zero high word, below every real key (the
+      // ordered bits of a non-NaN float are nonzero), and stays distinct by id.
+      key[m] = ((unsigned long long)(ok[m] ? ordered_bits(kap) : 0u) << 32) |
+               (0xffffffffu - (unsigned)e);
     }
   } else {
+    // the softmax runs over the allowed experts only (masked logits removed)
     float mx = -INFINITY;
 #pragma unroll
     for (int m = 0; m < EPT; ++m)
-      if (gtid + 256 * m < E) mx = fmaxf(mx, sc[m]);
+      if (ok[m]) mx = fmaxf(mx, sc[m]);
     mx = wave_max_f(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
@@ -172,7 +179,7 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
     float z = 0.0f;
 #pragma unroll
     for (int m = 0; m < EPT; ++m) {
-      const float p = gtid + 256 * m < E ? expf(sc[m] - mx) : 0.0f;
+      const float p = ok[m] ? expf(sc[m] - mx) : 0.0f;
       sc[m] = p;
       z += p;
     }
@@ -185,7 +192,8 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
       const int e = gtid + 256 * m;
       const float p = sc[m] / z;
       sc[m] = p;
-      key[m] = ((unsigned long long)ordered_bits(p) << 32) | (0xffffffffu - (unsigned)e);
+      key[m] = ((unsigned long long)(ok[m] ? ordered_bits(p) : 0u) << 32) |
+               (0xffffffffu - (unsigned)e);
     }
   }
 #pragma unroll
@@ -217,6 +225,7 @@ template <int EPT>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ partial,
                                                             int nchunk,
                                                             const float* __restrict__ bias,
+                                                            const uint8_t* __restrict__ mask,
                                                             int T, int E, int k, int router,
                                                             float scale,
                                                             int32_t* __restrict__ idx,
@@ -224,15 +233,18 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   __shared__ unsigned long long keys[256 * EPT];
   __shared__ float red[4];
   __shared__ float sel_s[kMaxK];
-  select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, blockIdx.x, true, threadIdx.x,
+  select_token<EPT>(partial, nchunk, bias, mask, T, E, k, router, scale, blockIdx.x, true,
+                    threadIdx.x,
                     keys, red, sel_s, idx, w, nullptr);
 }
 
 template <int EPT>
-hipError_t launch_select(const float* partial, int nchunk, const float* bias, int T, int E, int k,
+hipError_t launch_select(const float* partial, int nchunk, const float* bias,
+                         const uint8_t* mask, int T, int E, int k,
                          int router, float scale, int32_t* idx, float* w, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TOPK, s);
   hipLaunchKernelGGL(router_select_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, bias,
+                     mask,
                      T, E, k, router, scale, idx, w);
   return hipGetLastError();
 }
@@ -244,7 +256,8 @@ hipError_t launch_select(const float* partial, int nchunk, const float* bias, in
 template <int EPT>
 __global__ __launch_bounds__(256) void router_tail_kernel(
     const float* __restrict__ partial, int nchunk, const float* __restrict__ x, int d,
-    const float* __restrict__ bias, int T, int E, int k, int router, float scale,
+    const float* __restrict__ bias, const uint8_t* __restrict__ mask, int T, int E, int k,
+    int router, float scale,
     int32_t* __restrict__ idx, float* __restrict__ w, int8_t* __restrict__ xq,
     float* __restrict__ xs) {
   __shared__ unsigned long long keys[256 * EPT];
@@ -265,7 +278,8 @@ __global__ __launch_bounds__(256) void router_tail_kernel(
     xv[m] = (in_regs && c < nq) ? *reinterpret_cast<const float4*>(row + 4 * c)
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  select_token<EPT>(partial, nchunk, bias, T, E, k, router, scale, t, true, threadIdx.x, keys,
+  select_token<EPT>(partial, nchunk, bias, mask, T, E, k, router, scale, t, true, threadIdx.x,
+                    keys,
                     red, sel_s, idx, w, nullptr);
   if (!in_regs) {
     if (threadIdx.x < kWave) encode_row(row, d, xq + (size_t)t * 2 * d, xs + t);
@@ -301,17 +315,19 @@ __global__ __launch_bounds__(256) void router_tail_kernel(
 
 template <int EPT>
 hipError_t launch_tail(const float* partial, int nchunk, const float* x, int d, const float* bias,
+                       const uint8_t* mask,
                        int T, int E, int k, int router, float scale, int32_t* idx, float* w,
                        int8_t* xq, float* xs, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TAIL, s);
   hipLaunchKernelGGL(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
-                     bias, T, E, k, router, scale, idx, w, xq, xs);
+                     bias, mask, T, E, k, router, scale, idx, w, xq, xs);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router(int router, const float* x, const float* wr, const float* bias, int T,
+hipError_t launch_router(int router, const float* x, const float* wr, const float* bias,
+                         const uint8_t* mask, int T,
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
@@ -329,12 +345,15 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (E <= 256) return launch_select<1>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
-  if (E <= 512) return launch_select<2>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
-  return launch_select<4>(partial, nchunk, bias, T, E, k, router, scale, idx, w, s);
+  if (E <= 256)
+    return launch_select<1>(partial, nchunk, bias, mask, T, E, k, router, scale, idx, w, s);
+  if (E <= 512)
+    return launch_select<2>(partial, nchunk, bias, mask, T, E, k, router, scale, idx, w, s);
+  return launch_select<4>(partial, nchunk, bias, mask, T, E, k, router, scale, idx, w, s);
 }
 
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
+                               const uint8_t* mask,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
                                float* partial, int8_t* xq, float* xs, hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
@@ -347,10 +366,13 @@ hipError_t launch_router_small(int router, const float* x, const float* wr, cons
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (E <= 256)
-    return launch_tail<1>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs, s);
+    return launch_tail<1>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
+                          xs, s);
   if (E <= 512)
-    return launch_tail<2>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs, s);
-  return launch_tail<4>(partial, nchunk, x, d, bias, T, E, k, router, scale, idx, w, xq, xs, s);
+    return launch_tail<2>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
+                          xs, s);
+  return launch_tail<4>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
+                          xs, s);
 }
 
 }  // namespace moe

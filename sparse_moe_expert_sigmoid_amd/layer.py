@@ -19,7 +19,8 @@ from .binding import (Context, DeviceExperts, MOE_ACT_SILU, ROUTER, moe_layer, m
 class MoELayer:
     def __init__(self, ctx: Context, router: str, k: int, scale: float, w_router: torch.Tensor,
                  bias: Optional[torch.Tensor], experts: DeviceExperts,
-                 shared: Optional[DeviceExperts] = None):
+                 shared: Optional[DeviceExperts] = None,
+                 expert_mask: Optional[torch.Tensor] = None):
         self.ctx = ctx
         self.router = ROUTER[router]
         self.k, self.scale = k, float(scale)
@@ -29,9 +30,11 @@ class MoELayer:
         self.device = w_router.device
         self._T = None
         self._fused_T = None
+        self.expert_mask = expert_mask  # [E] uint8 on the device, nonzero = allowed
         self.desc = moe_layer(self.router, k, self.scale, w_router.data_ptr(),
                               bias.data_ptr() if bias is not None else None, experts.struct(),
-                              shared.struct() if shared is not None else moe_weights())
+                              shared.struct() if shared is not None else moe_weights(),
+                              expert_mask.data_ptr() if expert_mask is not None else None)
 
     @staticmethod
     def from_inputs(ctx: Context, inputs, device="cuda:0", tiled: bool = True) -> "MoELayer":
@@ -50,7 +53,13 @@ class MoELayer:
     def with_weights(self, experts: DeviceExperts, shared: Optional[DeviceExperts]) -> "MoELayer":
         """Same router, other expert weights (e.g. a copy in other HBM pages)."""
         return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
-                        self.scale, self.w_router, self.bias, experts, shared)
+                        self.scale, self.w_router, self.bias, experts, shared, self.expert_mask)
+
+    def with_mask(self, expert_mask: Optional[torch.Tensor]) -> "MoELayer":
+        """Same layer restricted to the experts whose mask entry is nonzero."""
+        return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
+                        self.scale, self.w_router, self.bias, self.experts, self.shared,
+                        expert_mask)
 
     def alloc(self, T: int):
         if self._T == T:
@@ -79,8 +88,8 @@ class MoELayer:
         T, d = x.shape
         self.alloc(T)
         c, k, E = self.ctx, self.k, self.E
-        c.moe_route(self.router, x, self.w_router, self.bias, T, d, E, k, self.scale, self.idx,
-                    self.w, self.ws, stream)
+        c.moe_route_masked(self.router, x, self.w_router, self.bias, self.expert_mask, T, d, E, k,
+                           self.scale, self.idx, self.w, self.ws, stream)
         c.moe_permute(self.idx, T, k, E, self.offsets, self.row_token, self.token_row, stream)
         c.moe_expert_ffn(self.experts, MOE_ACT_SILU, x, T, self.row_token, self.offsets, T * k,
                          self.rows, self.ws, stream)
