@@ -75,6 +75,8 @@ def _load():
     lib.oracle_combine.restype = None
     lib.oracle_layer.argtypes = [ctypes.POINTER(_Layer), vp, i64, vp, vp, vp, vp]
     lib.oracle_layer.restype = ci
+    lib.oracle_coverage_set.argtypes = [vp, ci, ctypes.c_double, ci, vp]
+    lib.oracle_coverage_set.restype = ci
     _lib = lib
     return lib
 
@@ -239,3 +241,15 @@ def layer_of(inputs, tokens=None):
                  Experts.of(inputs.experts),
                  Experts.of(inputs.shared) if inputs.shared is not None else None,
                  tokens=tokens)
+
+
+def coverage_set(counts, cover: float, k: int) -> np.ndarray:
+    """Experts kept by the restriction: the smallest set reaching `cover` of
+    the selection counts, padded to k; ascending ids (int32)."""
+    counts = np.ascontiguousarray(counts, dtype=np.uint64)
+    E = counts.shape[0]
+    keep = np.empty(E, np.int32)
+    n = _load().oracle_coverage_set(_p(counts), E, float(cover), k, _p(keep))
+    if n < 0:
+        raise ValueError(f"oracle_coverage_set failed ({n})")
+    return keep[:n].copy()

@@ -346,3 +346,37 @@ int oracle_layer(const oracle_layer_args* L, const float* x, int64_t T, int32_t*
     }
     return err;
 }
+
+/* Expert restriction (Kimi-Linear-48B-A3B-Code-CMF listing, "How it was made",
+ * steps 2 and 3): per layer, keep the smallest set of experts whose recorded
+ * selection counts reach the fraction `cover` of all selections.  Taking
+ * experts by descending count (equal counts: lower id first) until the running
+ * sum reaches cover * total gives a smallest such set.  The set is padded in
+ * the same order to at least k experts (min(k, E)), so that every token can
+ * still select k, and is written to keep[] in ascending id order (the dense
+ * renumbering keeps the original order).  Returns its size, or -1 for bad
+ * arguments (E < 1, k < 1, cover outside [0, 1]). */
+int oracle_coverage_set(const uint64_t* counts, int E, double cover, int k, int32_t* keep) {
+    if (E < 1 || k < 1 || !(cover >= 0.0 && cover <= 1.0)) return -1;
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    if (!taken) return -2;
+    uint64_t total = 0;
+    for (int e = 0; e < E; ++e) total += counts[e];
+    const double need = cover * (double)total;
+    const int kmin = k < E ? k : E;
+    uint64_t sum = 0;
+    int n = 0;
+    while (n < E && ((double)sum < need || n < kmin)) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (!taken[e] && (best < 0 || counts[e] > counts[best])) best = e;
+        taken[best] = 1;
+        sum += counts[best];
+        ++n;
+    }
+    int m = 0;
+    for (int e = 0; e < E; ++e)
+        if (taken[e]) keep[m++] = e;
+    free(taken);
+    return n;
+}

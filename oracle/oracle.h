@@ -50,6 +50,7 @@ void oracle_combine(const float* rows, const int32_t* token_row, const float* w,
                     double* y);
 int oracle_layer(const oracle_layer_args* L, const float* x, int64_t T, int32_t* idx,
                  double* w, double* gap, double* y);
+int oracle_coverage_set(const uint64_t* counts, int E, double cover, int k, int32_t* keep);
 
 #ifdef __cplusplus
 }

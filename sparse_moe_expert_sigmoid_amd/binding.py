@@ -263,6 +263,18 @@ class DeviceExperts:
         t = lambda a: None if a is None else torch.from_numpy(a).to(device)
         return DeviceExperts(fmt, w.E, w.d, w.inter, t(gu), t(dn), t(w.gu_s), t(w.dn_s))
 
+    def select(self, ids) -> "DeviceExperts":
+        """Experts `ids` (in that order) as a new dense set, gathered whole on
+        the device; both code layouts keep each expert's bytes contiguous, so
+        format and layout carry over."""
+        dev = self.w_gate_up.device
+        ix = torch.as_tensor([int(i) for i in ids], dtype=torch.long, device=dev)
+        if ix.numel() == 0 or int(ix.min()) < 0 or int(ix.max()) >= self.n_experts:
+            raise ValueError(f"expert ids must be in [0, {self.n_experts})")
+        g = lambda a: None if a is None else a.index_select(0, ix)
+        return DeviceExperts(self.fmt, int(ix.numel()), self.d, self.inter, g(self.w_gate_up),
+                             g(self.w_down), g(self.s_gate_up), g(self.s_down), self.layout)
+
     def clone(self) -> "DeviceExperts":
         c = lambda a: None if a is None else a.clone()
         return DeviceExperts(self.fmt, self.n_experts, self.d, self.inter, c(self.w_gate_up),

@@ -61,6 +61,21 @@ class MoELayer:
                         self.scale, self.w_router, self.bias, self.experts, self.shared,
                         expert_mask)
 
+    def restricted(self, keep) -> "MoELayer":
+        """The layer cut to the experts `keep` (ascending ids), renumbered
+        0..n-1: router rows, selection bias and expert weights sliced, the
+        shared expert unchanged.  Equal to with_mask() of the same set, with
+        ids mapped through keep (Kimi-Linear-48B-A3B-Code-CMF listing, "How it
+        was made", step 3)."""
+        keep = [int(e) for e in keep]
+        if sorted(set(keep)) != keep:
+            raise ValueError("keep must be strictly ascending expert ids")
+        ix = torch.as_tensor(keep, dtype=torch.long, device=self.device)
+        wr = self.w_router.index_select(0, ix).contiguous()
+        bias = self.bias.index_select(0, ix).contiguous() if self.bias is not None else None
+        return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
+                        self.scale, wr, bias, self.experts.select(keep), self.shared)
+
     def alloc(self, T: int):
         if self._T == T:
             return

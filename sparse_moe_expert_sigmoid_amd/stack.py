@@ -49,14 +49,17 @@ class MoEStack:
 
     def forward(self, x0: torch.Tensor, stream=None,
                 before_layer: Optional[Callable[[int, torch.Tensor], None]] = None,
-                after_layer: Optional[Callable[[int, torch.Tensor, torch.Tensor], None]] = None
-                ) -> torch.Tensor:
+                after_layer: Optional[Callable[[int, torch.Tensor, torch.Tensor], None]] = None,
+                counts: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Runs every layer on x0 [T, d]; returns x_L (one of the two buffers).
 
         before_layer(l, x_l) may modify x_l in place before layer l reads it
         (x_0 itself is passed for l = 0); after_layer(l, x_l, x_{l+1}) sees
         each layer's input and output.  Both run on the host between the
-        enqueues, so they are for tests, not for timed or captured runs."""
+        enqueues, so they are for tests, not for timed or captured runs.
+        counts: optional [layers, E] int64 device tensor; each layer's expert
+        selections are added to its row (the routing statistics of a
+        calibration run)."""
         T, d = x0.shape
         assert d == self.d and x0.dtype == torch.float32 and x0.is_contiguous()
         self.alloc(T)
@@ -67,12 +70,31 @@ class MoEStack:
             out = self.buf[l % 2]
             self.ctx.moe_forward(L.desc, MOE_ACT_SILU, cur, T, cur, out, self.idx[l], self.w[l],
                                  self.ws, stream)
+            if counts is not None:
+                self.ctx.moe_expert_counts(self.idx[l], T, L.k, L.E, counts[l], stream)
             if after_layer is not None:
                 after_layer(l, cur, out)
             cur = out
         return cur
 
     __call__ = forward
+
+    def restricted(self, counts, cover: float = 0.95, masked: bool = False):
+        """Per layer, the smallest expert set carrying `cover` of the recorded
+        selections (counts: [layers, E], host or device), as a new stack of
+        sliced layers, or of masked full layers with masked=True.  Returns
+        (stack, [kept ids per layer])."""
+        from .restrict import coverage_set, expert_mask
+        c = counts.cpu().numpy() if isinstance(counts, torch.Tensor) else counts
+        if len(c) != len(self.layers):
+            raise ValueError("counts needs one row per layer")
+        keeps, layers = [], []
+        for l, L in enumerate(self.layers):
+            keep = coverage_set(c[l][:L.E], cover, L.k)
+            keeps.append(keep)
+            layers.append(L.with_mask(expert_mask(keep, L.E, L.device)) if masked
+                          else L.restricted(keep))
+        return MoEStack(self.ctx, layers), keeps
 
     # ------------------------------------------------------------------
     @staticmethod

@@ -213,3 +213,70 @@ def test_expert_counts_of_a_routed_batch(ctx):
     if (ogap < 1e-6).any():
         pytest.skip("oracle near-tie in this draw")
     assert np.array_equal(counts.cpu().numpy(), np.bincount(oidx.ravel(), minlength=64))
+
+
+def _tiny_stack(ctx, layers=3, T=256, d=256, E=64, k=6, inter=128):
+    from sparse_moe_expert_sigmoid_amd import MoELayer, MoEStack
+    out, inps = [], []
+    for l in range(layers):
+        spec = S.spec("tiny", T=T, d=d, E=E, k=k, inter=inter, shared="int8_row",
+                      shared_inter=inter, wseed=0x4D615300 + l, xseed=0x4D6153F0)
+        inp = S.make_layer(spec)
+        # skewed selection bias, as the calibration statistics of a real model
+        bias = S.zipf_bias(spec.wseed, E, 1.0)
+        inp = S.LayerInputs(spec, inp.x, inp.wr, bias, inp.experts, inp.shared)
+        inps.append(inp)
+        out.append(MoELayer.from_inputs(ctx, inp))
+    return MoEStack(ctx, out), inps
+
+
+def test_restriction_from_recorded_counts(ctx):
+    # Calibrate: run a batch through a 3-layer stack recording per-layer
+    # counts; restrict each layer to the smallest set carrying 95% of its
+    # selections; the sliced stack and the masked full stack then agree on
+    # another batch (ids through the renumbering, outputs within the bound),
+    # and layer 0 of the sliced stack matches the oracle on the slice.
+    import torch
+    stk, inps = _tiny_stack(ctx)
+    E, k, T = 64, 6, 256
+    x_cal = _dev(inps[0].x)
+    counts = torch.zeros((3, E), dtype=torch.int64, device="cuda:0")
+    stk.forward(x_cal, counts=counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    for l in range(3):
+        assert np.array_equal(c[l], np.bincount(stk.idx[l].cpu().numpy().ravel(), minlength=E))
+    cut, keeps = stk.restricted(counts, 0.95)
+    masked, keeps_m = stk.restricted(counts, 0.95, masked=True)
+    for l in range(3):
+        assert np.array_equal(keeps[l], oracle.coverage_set(c[l], 0.95, k))
+        assert np.array_equal(keeps[l], keeps_m[l])
+        assert k <= len(keeps[l]) < E
+    x = S.normal(0x4D6153F1, 1, (T, 256), 1.0)
+    xd = _dev(x)
+    y_cut = cut.forward(xd).clone()
+    idx_cut = [i.cpu().numpy() for i in cut.idx]
+    y_mask = masked.forward(xd).clone()
+    torch.cuda.synchronize()
+    assert np.array_equal(keeps[0][idx_cut[0]], masked.idx[0].cpu().numpy())
+    a, b = y_cut.cpu().numpy(), y_mask.cpu().numpy()
+    err = float(np.abs(a - b).max()) / float(np.abs(b).max())
+    assert err <= 2e-3
+    # layer 0 of the cut stack against the oracle on the slice
+    inp = inps[0]
+    keep = keeps[0]
+    exs = oracle.Experts(inp.experts.fmt, inp.experts.gu[keep], inp.experts.dn[keep],
+                         inp.experts.gu_s[keep], inp.experts.dn_s[keep])
+    wr_s, b_s = np.ascontiguousarray(inp.wr[keep]), np.ascontiguousarray(inp.bias[keep])
+    oy, oidx, ow, ogap = oracle.layer("sigmoid_bias", k, inp.spec.scale, x, wr_s, b_s, exs,
+                                      oracle.Experts.of(inp.shared))
+    _, _, _, logits = oracle.route("sigmoid_bias", x, wr_s, b_s, k, inp.spec.scale,
+                                   want_logits=True)
+    cut0 = cut.layers[0]
+    y0 = cut0.forward_fused(xd)
+    torch.cuda.synchronize()
+    exc = compare_route(cut0.idx.cpu().numpy(), cut0.w.cpu().numpy(), oidx, ow, ogap,
+                        oracle_keys("sigmoid_bias", logits, b_s), inp.spec.scale)
+    ratio = compare_outputs(y0.cpu().numpy(), oy, np.setdiff1d(np.arange(T), exc))
+    log_result(test="restriction", kept=[len(kp) for kp in keeps], cut_vs_masked=err,
+               bit_identical=bool(np.array_equal(a, b)), layer0_err_over_max=ratio)

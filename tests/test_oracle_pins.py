@@ -441,3 +441,57 @@ def test_combine_one_hot_and_linear():
     ref2 = np.einsum("tk,tkd->td", w2.astype(np.float64),
                      rows.astype(np.float64)[token_row].reshape(T, k, d))
     assert np.allclose(y2, ref2, rtol=1e-14)
+
+
+# ------------------------------------------------------------ expert restriction
+
+def _min_cover_size_bruteforce(counts, cover):
+    import itertools
+    E = len(counts)
+    total = int(counts.sum())
+    need = cover * float(total)
+    for n in range(0, E + 1):
+        for sub in itertools.combinations(range(E), n):
+            if float(int(counts[list(sub)].sum())) >= need:
+                return n
+    return E
+
+
+def test_coverage_set_is_a_smallest_cover_bruteforce():
+    # CMF listing, step 3: the smallest expert set reaching the covered share
+    # of the recorded routing mass.  Every subset of tiny layers is tried.
+    for trial in range(60):
+        E = 3 + trial % 7
+        counts = S.randint8(0xC0FE, trial, (E,), 0, 20).astype(np.uint64)
+        if trial % 5 == 0:
+            counts[:] = counts[0]                        # all equal
+        for cover in (0.0, 0.5, 0.73, 0.95, 1.0):
+            for k in (1, 2, 4):
+                keep = oracle.coverage_set(counts, cover, k)
+                n_min = _min_cover_size_bruteforce(counts, cover)
+                assert len(keep) == max(n_min, min(k, E)), (counts, cover, k, keep)
+                assert np.all(np.diff(keep) > 0)         # ascending, distinct
+                assert float(counts[keep].sum()) >= cover * float(counts.sum())
+                # greedy by count: no expert left out has more selections than
+                # one kept (ties go to the lower id)
+                out = np.setdiff1d(np.arange(E), keep)
+                if len(out):
+                    c_in = counts[keep].astype(np.int64)
+                    assert counts[out].max() <= c_in.min()
+                    tie_out = out[counts[out] == c_in.min()]
+                    tie_in = keep[c_in == c_in.min()]
+                    if len(tie_out):
+                        assert tie_in.max() < tie_out.min()
+
+
+def test_coverage_set_worked_example_and_edges():
+    c = np.array([5, 1, 9, 0, 9, 3], np.uint64)      # total 27
+    assert list(oracle.coverage_set(c, 0.80, 2)) == [0, 2, 4]      # 9+9+5 = 23 >= 21.6
+    assert list(oracle.coverage_set(c, 18 / 27, 1)) == [2, 4]      # exactly the share
+    assert list(oracle.coverage_set(c, 1.0, 1)) == [0, 1, 2, 4, 5]  # every expert ever chosen
+    assert list(oracle.coverage_set(c, 0.0, 3)) == [0, 2, 4]      # only the k floor
+    assert list(oracle.coverage_set(np.zeros(4, np.uint64), 0.95, 2)) == [0, 1]
+    assert list(oracle.coverage_set(c, 0.5, 9)) == [0, 1, 2, 3, 4, 5]   # k > E: all
+    for bad in (-0.1, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.coverage_set(c, bad, 2)
