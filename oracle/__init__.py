@@ -77,6 +77,10 @@ def _load():
     lib.oracle_layer.restype = ci
     lib.oracle_coverage_set.argtypes = [vp, ci, ctypes.c_double, ci, vp]
     lib.oracle_coverage_set.restype = ci
+    lib.oracle_quantize_int8_rows.argtypes = [vp, i64, ci, vp, vp]
+    lib.oracle_quantize_int8_rows.restype = ci
+    lib.oracle_quantize_int4_blocks.argtypes = [vp, i64, ci, vp, vp]
+    lib.oracle_quantize_int4_blocks.restype = ci
     _lib = lib
     return lib
 
@@ -253,3 +257,29 @@ def coverage_set(counts, cover: float, k: int) -> np.ndarray:
     if n < 0:
         raise ValueError(f"oracle_coverage_set failed ({n})")
     return keep[:n].copy()
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) as the fp32 values they denote (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize(fmt: str, w) -> tuple:
+    """Float weights [rows, K] -> (codes int8 [rows, K], scales fp32).
+    fmt "int8_row": scales [rows]; "int4_b32": scales [rows, K/32], codes
+    unpacked (one int8 per code, in [-8, 7])."""
+    w = _f32(w)
+    rows, K = w.shape
+    q = np.empty((rows, K), np.int8)
+    if fmt == "int8_row":
+        s = np.empty(rows, np.float32)
+        rc = _load().oracle_quantize_int8_rows(_p(w), rows, K, _p(q), _p(s))
+    elif fmt == "int4_b32":
+        s = np.empty((rows, K // 32), np.float32)
+        rc = _load().oracle_quantize_int4_blocks(_p(w), rows, K, _p(q), _p(s))
+    else:
+        raise ValueError(f"no quantizer for {fmt}")
+    if rc != 0:
+        raise ValueError(f"oracle quantizer failed ({rc})")
+    return q, s

@@ -380,3 +380,68 @@ int oracle_coverage_set(const uint64_t* counts, int E, double cover, int k, int3
     free(taken);
     return n;
 }
+
+/* Weight quantizers: the step that produces the expert formats from float
+ * weights.
+ *
+ * int8 per output row (Kimi-Linear-48B-A3B-Instruct LiteRT-LM details,
+ * "Conversion notes", quantization of the int8 file: one scale per output row
+ * and expert, symmetric min-max): s = max_k |w[k]| / 127, q[k] = round(w[k] / s),
+ * so the largest magnitude maps to +-127.  An all-zero row gets s = 0 and
+ * codes 0.
+ *
+ * int4 per block of 32 inputs (Qwen3-30B-A3B model card, file table: int4
+ * blockwise, block 32, fp32 scales; "Conversion notes": block scales below
+ * 2^-14 are raised to 2^-14): s = max(max_b |w| / 7, 2^-14) over the block,
+ * q = round(w / s) in [-8, 7] (symmetric: at most 7 in magnitude).  Raising
+ * the scale here, before dividing, makes the stored scale the one the layer
+ * dequantises with.
+ *
+ * The pages fix no precision for the scale and the quotient.  A code is an
+ * integer decided by floating point, so both are taken in fp32, each
+ * correctly rounded (computed here in fp64 and rounded once to fp32, which
+ * equals the correctly rounded fp32 quotient of two fp32 values), and the
+ * quotient is rounded to the nearest integer with halves away from zero (C's
+ * round).  Inputs must be finite. */
+static inline float div_f32(float a, float b) { return (float)((double)a / (double)b); }
+
+int oracle_quantize_int8_rows(const float* w, int64_t rows, int K, int8_t* q, float* s) {
+    if (rows < 0 || K < 1) return -1;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* wr = w + r * K;
+        float m = 0.0f;
+        for (int k = 0; k < K; ++k) m = fabsf(wr[k]) > m ? fabsf(wr[k]) : m;
+        const float sc = div_f32(m, 127.0f);
+        s[r] = sc;
+        for (int k = 0; k < K; ++k) {
+            double c = sc > 0.0f ? round((double)div_f32(wr[k], sc)) : 0.0;
+            c = c > 127.0 ? 127.0 : (c < -127.0 ? -127.0 : c);
+            q[r * K + k] = (int8_t)c;
+        }
+    }
+    return 0;
+}
+
+int oracle_quantize_int4_blocks(const float* w, int64_t rows, int K, int8_t* q, float* s) {
+    if (rows < 0 || K < 32 || K % 32 != 0) return -1;
+    const int nb = K / 32;
+    const float floor_s = 1.0f / 16384.0f;  /* 2^-14 */
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const float* wb = w + r * K + 32 * b;
+            float m = 0.0f;
+            for (int i = 0; i < 32; ++i) m = fabsf(wb[i]) > m ? fabsf(wb[i]) : m;
+            float sc = div_f32(m, 7.0f);
+            if (sc < floor_s) sc = floor_s;
+            s[r * nb + b] = sc;
+            for (int i = 0; i < 32; ++i) {
+                double c = round((double)div_f32(wb[i], sc));
+                c = c > 7.0 ? 7.0 : (c < -8.0 ? -8.0 : c);
+                q[r * K + 32 * b + i] = (int8_t)c;
+            }
+        }
+    }
+    return 0;
+}

@@ -51,6 +51,8 @@ void oracle_combine(const float* rows, const int32_t* token_row, const float* w,
 int oracle_layer(const oracle_layer_args* L, const float* x, int64_t T, int32_t* idx,
                  double* w, double* gap, double* y);
 int oracle_coverage_set(const uint64_t* counts, int E, double cover, int k, int32_t* keep);
+int oracle_quantize_int8_rows(const float* w, int64_t rows, int K, int8_t* q, float* s);
+int oracle_quantize_int4_blocks(const float* w, int64_t rows, int K, int8_t* q, float* s);
 
 #ifdef __cplusplus
 }

@@ -495,3 +495,104 @@ def test_coverage_set_worked_example_and_edges():
     for bad in (-0.1, 1.5, float("nan")):
         with pytest.raises(ValueError):
             oracle.coverage_set(c, bad, 2)
+
+
+# ------------------------------------------------------------ weight quantizers
+
+def test_quantize_int8_worked_example():
+    # The row's largest magnitude is 127 * 2^-7, so s = 2^-7 exactly and every
+    # quotient below is exact: codes are the quotients rounded, halves away
+    # from zero (2.5 -> 3, -63.5 -> -64, 1.5 -> 2).
+    u = 2.0 ** -7
+    row = np.array([[127 * u, 0.5, 2.5 * u, -2.5 * u, 1.5 * u, -63.5 * u, 0.0, 0.49 * u,
+                     -127 * u, 0.51 * u]], np.float32)
+    q, s = oracle.quantize("int8_row", row)
+    assert s[0] == np.float32(u)
+    assert list(q[0]) == [127, 64, 3, -3, 2, -64, 0, 0, -127, 1]
+    z, sz = oracle.quantize("int8_row", np.zeros((2, 16), np.float32))
+    assert (z == 0).all() and (sz == 0).all()
+
+
+def test_quantize_int4_worked_example_and_clamp():
+    # block 0: max 7 * 2^-3 -> s = 2^-3, quotients exact: 3.5 -> 4, -0.5 -> -1
+    # block 1: max 3 * 2^-15 -> max/7 < 2^-14, so s = 2^-14: codes w * 2^14
+    #          (1.5 -> 2, 0.25 -> 0, -1.5 -> -2)
+    # block 2: zero -> s = 2^-14, codes 0
+    b0 = np.zeros(32, np.float32)
+    b0[:4] = [7 * 0.125, 3.5 * 0.125, -0.5 * 0.125, -7 * 0.125]
+    b1 = np.zeros(32, np.float32)
+    b1[:3] = [3 * 2.0 ** -15, 2.0 ** -16, -3 * 2.0 ** -15]
+    row = np.concatenate([b0, b1, np.zeros(32, np.float32)])[None, :]
+    q, s = oracle.quantize("int4_b32", row)
+    assert list(s[0]) == [0.125, 2.0 ** -14, 2.0 ** -14]
+    assert list(q[0, :4]) == [7, 4, -1, -7] and (q[0, 4:32] == 0).all()
+    assert list(q[0, 32:35]) == [2, 0, -2] and (q[0, 35:] == 0).all()
+
+
+@pytest.mark.parametrize("fmt", ["int8_row", "int4_b32"])
+def test_quantize_round_trip_range_and_extremes(fmt):
+    # |q s - w| <= s/2 (plus the fp32 rounding of the quotient), codes in range,
+    # each row's (block's) largest magnitude on the end code, and codes
+    # non-decreasing in w within a row (block).
+    w = S.normal(0x5151, 1, (64, 256), 0.02)
+    w[3] *= 1e-4                                  # int4: every block below the floor
+    w[5, :40] = 0.0
+    q, s = oracle.quantize(fmt, w)
+    qmax = 127 if fmt == "int8_row" else 7
+    B = 256 if fmt == "int8_row" else 32
+    sb = np.repeat(s.reshape(64, -1), B, axis=1).astype(np.float64)
+    err = np.abs(q * sb - w.astype(np.float64))
+    assert (err <= sb * (0.5 + 2.0 ** -20)).all()
+    assert q.min() >= -qmax and q.max() <= qmax
+    for r in range(64):
+        for b in range(256 // B):
+            wb, qb = w[r, b * B:(b + 1) * B], q[r, b * B:(b + 1) * B]
+            o = np.argsort(wb, kind="stable")
+            assert (np.diff(qb[o].astype(int)) >= 0).all()
+            if sb[r, b * B] > 2.0 ** -14:
+                assert np.abs(qb).max() == qmax
+                assert qb[np.argmax(np.abs(wb))] == qmax * np.sign(wb[np.argmax(np.abs(wb))])
+    if fmt == "int4_b32":
+        assert (s[3] == np.float32(2.0 ** -14)).all()
+
+
+@pytest.mark.parametrize("fmt", ["int8_row", "int4_b32"])
+def test_quantize_power_of_two_scaling(fmt):
+    # scaling a row by 2^j scales s by 2^j and keeps the codes (exact in fp32)
+    w = S.normal(0x5152, 1, (8, 128), 1.0)
+    q, s = oracle.quantize(fmt, w)
+    for j in (-3, 5):
+        q2, s2 = oracle.quantize(fmt, w * np.float32(2.0 ** j))
+        assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(2.0 ** j))
+
+
+def test_quantized_experts_reproduce_the_float_layer():
+    # Format wiring: fp32 experts quantized by the oracle and read back as
+    # int8 per-row / int4 block-32 experts give nearly the fp32 layer (a
+    # transposed scale or a wrong block index would not).
+    T, d, E, k, I = 12, 128, 6, 2, 64
+    x = S.normal(0x5153, 1, (T, d), 1.0)
+    wr = S.normal(0x5153, 2, (E, d), 1.0 / math.sqrt(d))
+    bias = S.uniform(0x5153, 3, (E,), -0.1, 0.1)
+    gu = S.normal(0x5153, 4, (E, 2 * I, d), 1.0 / math.sqrt(d))
+    dn = S.normal(0x5153, 5, (E, d, I), 1.0 / math.sqrt(I))
+    yf, idxf, _, _ = oracle.layer("sigmoid_bias", k, K_SCALE, x, wr, bias,
+                                  oracle.Experts("fp32", gu, dn))
+    for fmt, tol in (("int8_row", 0.02), ("int4_b32", 0.25)):
+        qg, sg = oracle.quantize(fmt, gu.reshape(E * 2 * I, d))
+        qd, sd = oracle.quantize(fmt, dn.reshape(E * d, I))
+        shp = (lambda a, n: a.reshape(E, n)) if fmt == "int8_row" else \
+              (lambda a, n: a.reshape(E, n, -1))
+        ex = oracle.Experts(fmt, qg.reshape(E, 2 * I, d), qd.reshape(E, d, I),
+                            shp(sg, 2 * I), shp(sd, d))
+        yq, idxq, _, _ = oracle.layer("sigmoid_bias", k, K_SCALE, x, wr, bias, ex)
+        assert np.array_equal(idxq, idxf)
+        rel = np.abs(yq - yf).max() / np.abs(yf).max()
+        assert rel < tol, (fmt, rel)
+
+
+def test_bf16_bits_to_f32():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F7F, 0x0001], np.uint16)
+    v = oracle.bf16_to_f32(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 0.0 and np.signbit(v[3])
+    assert v[4] == np.float32(3.3895314e38) and v[5] == np.float32(2.0 ** -133)
