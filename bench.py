@@ -18,6 +18,10 @@ distinct Kimi-shaped layers (about 95 GB of weights, drawn on the GPU, so cold
 by size) with the residual between layers and a Zipf-skewed selection bias; a
 step is one pass through all 26 layers, replayed as one HIP graph at T=1.
 
+Quantizer workloads (--workload kimi_quantize | qwen_quantize): a step
+quantizes a whole routed expert set from bf16 (moe_quantize, gate/up and
+down); value = weights per second.
+
 Output: one JSON line (metric, value = tokens/s, ms_per_step, roofline of the
 dominant kernel measured with HIP events on its own stream in a second,
 separately timed pass, and the CPU oracle timed on a bounded sample).
@@ -73,6 +77,18 @@ STACK_WORKLOADS = {
 }
 
 
+QUANT_WORKLOADS = {
+    # name: (layer spec whose routed expert set is quantized, format, description)
+    "kimi_quantize": ("kimi_decode", "int8_row",
+                      "weight quantizer: the Kimi-shaped routed expert set (E=256, d=2304, "
+                      "I=2048; 3.62e9 weights) from bf16 to int8 per output row, "
+                      "gate/up and down in one launch each"),
+    "qwen_quantize": ("qwen_decode", "int4_b32",
+                      "weight quantizer: the Qwen3-shaped routed expert set (E=128, d=2048, "
+                      "I=768; 6.04e8 weights) from bf16 to int4 block-32"),
+}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -91,14 +107,14 @@ def expert_bytes(ew, e_list):
     return gu * n, dn * n
 
 
-def counter_traffic(workload: str, kernel_prefix: str):
+def counter_traffic(workload: str, kernel_prefix: str, source: str = "ffn.hip"):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary (profiles/<workload>__*.md, FETCH_SIZE + WRITE_SIZE
     calibrated), or None when no summary matches or it was taken from a
     different version of the kernel source."""
     import glob
     import hashlib
-    src = os.path.join(ROOT, "sparse_moe_expert_sigmoid_amd", "csrc", "ffn.hip")
+    src = os.path.join(ROOT, "sparse_moe_expert_sigmoid_amd", "csrc", source)
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"{workload}__*.md"))):
         fields = {}
@@ -318,13 +334,140 @@ def run_stack(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_quant(spec, fmt, budget_s: float):
+    """The oracle's quantizer on whole experts of the same workload (host copies of
+    the same bf16 values), bounded repeat count."""
+    import oracle
+    from sparse_moe_expert_sigmoid_amd import synth as S
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    w = [oracle.bf16_to_f32(S.bf16_bits(S.float_expert(spec, e, p)))
+         for e in range(2) for p in ("gu", "dn")]
+    n = sum(a.size for a in w)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for a in w:
+            oracle.quantize(fmt, a)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    return {"value": n * reps / el, "unit": "weights/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x oracle quantizer on experts 0 and 1 (gate/up and down, "
+                      f"{n} weights) of this workload (C, OpenMP over rows), {el:.1f} s"}
+
+
+def run_quant(args):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import Context, binding as B, synth as S
+
+    spec_name, fmt, desc = QUANT_WORKLOADS[args.workload]
+    spec = S.spec(spec_name)
+    E, d, I = spec.E, spec.d, spec.inter
+    steps = args.steps or 10
+    warmup = args.warmup if args.warmup is not None else 2
+    dev = torch.device("cuda:0")
+    ctx = Context(0)
+    log(f"[bench] workload {args.workload}: uploading bf16 weights of {E} experts")
+    gu = torch.empty((E * 2 * I, d), dtype=torch.bfloat16, device=dev)
+    dn = torch.empty((E * d, I), dtype=torch.bfloat16, device=dev)
+    for e in range(E):
+        gu[e * 2 * I:(e + 1) * 2 * I] = torch.from_numpy(
+            S.bf16_bits(S.float_expert(spec, e, "gu")).view(np.int16)).view(torch.bfloat16)
+        dn[e * d:(e + 1) * d] = torch.from_numpy(
+            S.bf16_bits(S.float_expert(spec, e, "dn")).view(np.int16)).view(torch.bfloat16)
+    per = 1 if fmt == "int8_row" else 2
+    f = B.MOE_W_INT8_ROW if fmt == "int8_row" else B.MOE_W_INT4_B32
+    cdt = torch.int8 if per == 1 else torch.uint8
+    cg = torch.empty((E * 2 * I, d // per), dtype=cdt, device=dev)
+    cd = torch.empty((E * d, I // per), dtype=cdt, device=dev)
+    sg = torch.empty((E * 2 * I) * (1 if per == 1 else d // 32), dtype=torch.float32, device=dev)
+    sd = torch.empty((E * d) * (1 if per == 1 else I // 32), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ctx.moe_quantize(f, gu, cg, sg, stream)
+        ctx.moe_quantize(f, dn, cd, sd, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    n_w = gu.numel() + dn.numel()
+    w_s = n_w / (ms_per_step / 1e3)
+    step_bytes = (n_w * 2 + cg.numel() + cd.numel() + (sg.numel() + sd.numel()) * 4)
+    gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    log(f"[bench] {ms_per_step:.3f} ms/step, {w_s / 1e9:.1f} G weights/s, {gbs:.0f} GB/s "
+        f"(wall {wall:.3f} s)")
+
+    kernels, roofline = {}, None
+    if not args.no_kernel_timing:
+        ctx.moe_timing(4 * steps)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        kt = ctx.moe_timing_read()
+        ctx.moe_timing(0)
+        kernels = {n: {"launches": int(c), "avg_us": t / c * 1e3} for n, (c, t) in kt.items()}
+        name = "quant_i8_rows" if per == 1 else "quant_i4_blocks"
+        if name in kt:
+            launches, tot_ms = kt[name]
+            per_launch = step_bytes / (launches / steps)
+            avg_s = tot_ms / launches / 1e3
+            achieved = per_launch / avg_s / 1e9
+            roofline = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": counter_traffic(args.workload, "quant_", "quant.hip"),
+                        "bytes_per_launch": int(per_launch),
+                        "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_quant(spec, fmt, args.cpu_budget)
+
+    out = {
+        "metric": "weights quantized per second (bf16 -> expert format), % HBM roofline",
+        "value": round(w_s, 1),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0, 0.02^2) weights rounded to bf16)",
+        "config": {"workload": desc, "E": E, "d": d, "inter": I, "format": fmt,
+                   "input": "bf16", "entry_point": "moe_quantize x2",
+                   "parallelism": "single GPU"},
+        "hbm_gbps_algorithmic": round(gbs, 1),
+        "step_bytes_algorithmic": int(step_bytes),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="kimi_decode",
-                    choices=sorted(WORKLOADS) + sorted(STACK_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(STACK_WORKLOADS) +
+                    sorted(QUANT_WORKLOADS))
     ap.add_argument("--layers", type=int, default=None,
                     help="stack workloads: run only the first N of the 26 layers")
     ap.add_argument("--no-graph", action="store_true",
@@ -348,6 +491,8 @@ def main():
 
     if args.workload in STACK_WORKLOADS:
         return run_stack(args)
+    if args.workload in QUANT_WORKLOADS:
+        return run_quant(args)
 
     import torch
     from sparse_moe_expert_sigmoid_amd import Context, MoELayer, synth as S

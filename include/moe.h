@@ -115,6 +115,36 @@ typedef struct {
     const float* s_down;
 } moe_weights;
 
+/* Element type of float weights handed to moe_quantize. */
+typedef enum {
+    MOE_IN_F32 = 0,   /* fp32                                        */
+    MOE_IN_BF16 = 1   /* bf16 (the upper 16 bits of an fp32), widened exactly */
+} moe_in_type;
+
+/* Quantize float weights on the device into one of the expert formats, row
+ * layout (MOE_LAYOUT_ROWS; moe_tile_weights converts afterwards).  w is a
+ * [rows][K] matrix with the input axis contiguous: for an expert set, the
+ * gate/up codes are rows = E*2I, K = d and the down codes rows = E*d, K = I.
+ *   MOE_W_INT8_ROW (Kimi-Linear-48B-A3B-Instruct LiteRT-LM details,
+ *     "Conversion notes", quantization of the int8 file: symmetric min-max,
+ *     one scale per output row):  scales[r] = max_k |w[r][k]| / 127,
+ *     codes[r][k] = round(w[r][k] / scales[r]) as int8 in [-127, 127]; an
+ *     all-zero row gets scale 0 and codes 0.  K a multiple of 8.
+ *   MOE_W_INT4_B32 (Qwen3-30B-A3B model card: int4 blockwise, block 32, fp32
+ *     scales; block scales below 2^-14 raised to 2^-14):
+ *     scales[r][b] = max(max_{k in block b} |w[r][k]| / 7, 2^-14),
+ *     codes in [-7, 7], two per byte ([rows][K/2] bytes, low nibble = even k).
+ *     K a multiple of 32.
+ * Both divisions are correctly rounded fp32; the quotient is rounded to the
+ * nearest integer, halves away from zero.  Inputs must be finite.
+ *   in_type  one of moe_in_type
+ *   codes    int8 [rows][K] or uint8 [rows][K/2]; scales fp32 [rows] or
+ *            [rows][K/32]; caller-owned, 16-byte aligned, not overlapping w.
+ * K above 2^24, rows above 2^32 or rows*K above 2^40 returns MOE_E_UNSUPPORTED.  Enqueued on
+ * `stream`; one read of w and one write of the codes and scales. */
+moe_status moe_quantize(moe_ctx* ctx, int fmt, int in_type, const void* w, long long rows,
+                        int K, void* codes, float* scales, void* stream);
+
 /* Copy row-major int8/int4 codes into MOE_LAYOUT_TILED order (a byte
  * permutation; scales are not touched).  src: weights with layout
  * MOE_LAYOUT_ROWS; dst_gate_up / dst_down: device buffers of the same byte

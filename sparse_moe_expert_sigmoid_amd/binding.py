@@ -23,6 +23,7 @@ MOE_ROUTER_SIGMOID_BIAS, MOE_ROUTER_SOFTMAX = 0, 1
 MOE_W_FP32, MOE_W_INT8_ROW, MOE_W_INT4_B32 = 0, 1, 2
 MOE_ACT_SILU = 0
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
+MOE_IN_F32, MOE_IN_BF16 = 0, 1
 
 ROUTER = {"sigmoid_bias": MOE_ROUTER_SIGMOID_BIAS, "softmax": MOE_ROUTER_SOFTMAX}
 FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B32}
@@ -30,7 +31,7 @@ FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B3
 EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
-           "moe_tile_weights", "moe_route_masked", "moe_expert_counts")
+           "moe_tile_weights", "moe_route_masked", "moe_expert_counts", "moe_quantize")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route_masked.argtypes = [vp, ci, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, vp,
                                      vp, vp, sz, vp]
     lib.moe_expert_counts.argtypes = [vp, vp, ci, ci, ci, vp, vp]
+    lib.moe_quantize.argtypes = [vp, ci, ci, vp, ctypes.c_longlong, ci, vp, vp, vp]
     lib.moe_permute.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp]
     lib.moe_expert_ffn.argtypes = [vp, ctypes.POINTER(moe_weights), ci, vp, ci, vp, vp, ci, vp,
                                    vp, sz, vp]
@@ -99,7 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ci)]
     for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
               "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
-              "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts"):
+              "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts",
+              "moe_quantize"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -170,6 +173,19 @@ class Context:
     def moe_expert_counts(self, topk_idx, T, k, E, counts, stream=None):
         self._check(self.lib.moe_expert_counts(self.handle, _p(topk_idx), T, k, E, _p(counts),
                                                _stream(stream)))
+
+    def moe_quantize(self, fmt, w, codes, scales, stream=None):
+        """w: [rows, K] fp32 or bf16 device tensor; fmt MOE_W_INT8_ROW or
+        MOE_W_INT4_B32; codes / scales preallocated (see moe.h)."""
+        if w.dtype == torch.float32:
+            in_type = MOE_IN_F32
+        elif w.dtype == torch.bfloat16:
+            in_type = MOE_IN_BF16
+        else:
+            raise TypeError(f"moe_quantize takes fp32 or bf16 weights, not {w.dtype}")
+        rows, K = w.shape
+        self._check(self.lib.moe_quantize(self.handle, fmt, in_type, _p(w), rows, K, _p(codes),
+                                          _p(scales), _stream(stream)))
 
     def moe_permute(self, topk_idx, T, k, E, offsets, row_token, token_row, stream=None):
         self._check(self.lib.moe_permute(self.handle, _p(topk_idx), T, k, E, _p(offsets),

@@ -18,7 +18,8 @@ const char* const kKernelNames[K_COUNT] = {
     "router_logits", "router_topk",     "permute",         "fill",
     "encode_rows",   "ffn_i8_gate_up",  "ffn_i8_down",     "ffn_i4_gate_up",
     "ffn_i4_down",   "ffn_f32_gate_up", "ffn_f32_down",    "combine",
-    "router_tail",   "ffn_i8_gate_up_gemm", "ffn_i8_down_gemm"};
+    "router_tail",   "ffn_i8_gate_up_gemm", "ffn_i8_down_gemm", "quant_i8_rows",
+    "quant_i4_blocks"};
 
 // Event pairs recorded around launches while a context has timing on.
 struct KernelTimer {
@@ -379,6 +380,33 @@ moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k
   hipError_t e = moe::launch_expert_counts(topk_idx, (long long)T * k, E, counts,
                                            (hipStream_t)stream);
   return device_result(ctx, e, "moe_expert_counts");
+}
+
+moe_status moe_quantize(moe_ctx* ctx, int fmt, int in_type, const void* w, long long rows,
+                        int K, void* codes, float* scales, void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  if (fmt != MOE_W_INT8_ROW && fmt != MOE_W_INT4_B32)
+    return fail(ctx, MOE_E_UNSUPPORTED, "moe_quantize: format %d has no quantizer", fmt);
+  if (in_type != MOE_IN_F32 && in_type != MOE_IN_BF16)
+    return fail(ctx, MOE_E_INVALID, "moe_quantize: unknown input type %d", in_type);
+  if (rows < 0) return fail(ctx, MOE_E_INVALID, "moe_quantize: rows=%lld is negative", rows);
+  const int kmul = fmt == MOE_W_INT8_ROW ? 8 : 32;
+  if (K < kmul || K % kmul != 0 || K > (1 << 24))
+    return fail(ctx, MOE_E_UNSUPPORTED,
+                "moe_quantize: K=%d must be a positive multiple of %d, at most 2^24", K, kmul);
+  if (rows > (1LL << 32) || rows > (1LL << 40) / K)
+    return fail(ctx, MOE_E_UNSUPPORTED, "moe_quantize: rows above 2^32 or rows*K above 2^40");
+  if (rows == 0) return MOE_OK;
+  if (!w || !codes || !scales)
+    return fail(ctx, MOE_E_INVALID, "moe_quantize: %s is NULL",
+                !w ? "w" : !codes ? "codes" : "scales");
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales))
+    return fail(ctx, MOE_E_INVALID, "moe_quantize: a pointer is not 16-byte aligned");
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_quantize: hipSetDevice(%d) failed", ctx->device);
+  hipError_t e = moe::launch_quantize(fmt, in_type, w, rows, K, codes, scales,
+                                      (hipStream_t)stream);
+  return device_result(ctx, e, "moe_quantize");
 }
 
 moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,

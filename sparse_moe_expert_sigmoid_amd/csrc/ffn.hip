@@ -635,12 +635,9 @@ __device__ inline void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Direct global-to-LDS loads: lane l's 16 (4) bytes land at dst + 16 l (4 l).
+// Direct global-to-LDS load: lane l's 16 bytes land at dst + 16 l.
 __device__ inline void lds_load16(const void* src, int8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-__device__ inline void lds_load4(const void* src, int8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
 }
 
 __device__ inline v4i lds_frag(const int8_t* blk, int lane) {

@@ -100,7 +100,7 @@ enum KernelId {
   K_ROUTER_LOGITS, K_ROUTER_TOPK, K_PERMUTE, K_FILL, K_ENCODE_ROWS,
   K_FFN_I8_GATE_UP, K_FFN_I8_DOWN, K_FFN_I4_GATE_UP, K_FFN_I4_DOWN,
   K_FFN_F32_GATE_UP, K_FFN_F32_DOWN, K_COMBINE, K_ROUTER_TAIL, K_FFN_I8_GATE_UP_GEMM,
-  K_FFN_I8_DOWN_GEMM, K_COUNT
+  K_FFN_I8_DOWN_GEMM, K_QUANT_I8, K_QUANT_I4, K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];
 
@@ -269,5 +269,10 @@ __device__ inline void encode_row(const float* __restrict__ row, int K, int8_t* 
 }
 
 #endif
+
+// ---------------------------------------------------------------- weight quantizers (quant.hip)
+// fmt 1 = int8 per row, 2 = int4 blocks of 32; in_type 0 = fp32, 1 = bf16.
+hipError_t launch_quantize(int fmt, int in_type, const void* w, long long rows, int K,
+                           void* codes, float* scales, hipStream_t st);
 
 }  // namespace moe

@@ -504,3 +504,25 @@ def stack_router(st: StackSpec, l: int):
 def stack_x(st: StackSpec) -> np.ndarray:
     """x_0 [T, d]: the first T rows of one N(0,1) tensor (T=1 is row 0 of T=4096)."""
     return normal(STACK_X_SEED, TID_X, (st.T, st.base.d), 1.0)
+
+
+# ------------------------------------------------------------ float weights for the quantizer
+# Expert e's float gate/up [2I, d] and down [d, I] matrices, N(0, QUANT_STD^2)
+# (the spread of trained projection weights), one tensor id per (expert, part)
+# so that any expert can be drawn alone.
+TID_FLOAT_BASE = 0x100
+QUANT_STD = 0.02
+
+
+def float_expert(s: LayerSpec, e: int, part: str) -> np.ndarray:
+    if part not in ("gu", "dn"):
+        raise ValueError(part)
+    shape = (2 * s.inter, s.d) if part == "gu" else (s.d, s.inter)
+    return normal(s.wseed, TID_FLOAT_BASE + 2 * e + (part == "dn"), shape, QUANT_STD)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 (round to nearest even), as uint16 bit patterns."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
