@@ -60,6 +60,12 @@ WORKLOADS = {
                     "Qwen3-shaped MoE layer decode: T=1, d=2048, E=128, top-8 softmax, "
                     "I=768 SwiGLU, int4 block-32 experts, no shared expert"),
     "qwen_prefill": ("qwen_prefill", 1, "Qwen3-shaped MoE layer, T=128"),
+    "qwen_decode_b128": ("qwen_decode", 1,
+                         "Qwen3-shaped MoE layer decode as qwen_decode, int4 experts with one "
+                         "scale per block of 128 inputs", {"fmt": "int4_b128"}),
+    "qwen_prefill_b128": ("qwen_prefill", 1,
+                          "Qwen3-shaped MoE layer, T=128, int4 block-128 experts",
+                          {"fmt": "int4_b128"}),
     "tiny": ("tiny", 1, "tiny MoE layer: T=32, d=512, E=32, top-8, I=256"),
 }
 
@@ -95,7 +101,7 @@ def log(*a):
 
 def expert_bytes(ew, e_list):
     """Codes + scales of the listed experts (host arrays), gate_up and down separately."""
-    if ew.fmt == "int4_b32":
+    if ew.fmt in ("int4_b32", "int4_b128"):
         gu = ew.gu_packed[0].nbytes + ew.gu_s[0].nbytes
         dn = ew.dn_packed[0].nbytes + ew.dn_s[0].nbytes
     elif ew.fmt == "int8_row":
@@ -128,17 +134,20 @@ def counter_traffic(workload: str, kernel_prefix: str, source: str = "ffn.hip"):
     return None
 
 
-def cpu_baseline(inputs, budget_s: float):
+def cpu_baseline(inputs, budget_s: float, act: str = "silu"):
     """The oracle, as it stands, on the same layer and tokens; bounded repeat count."""
     import oracle
     s = inputs.spec
+    ex = oracle.Experts.of(inputs.experts, act)
+    sh = oracle.Experts.of(inputs.shared, act) if inputs.shared is not None else None
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     T_sample = min(s.T, 8)
     tokens = np.arange(T_sample)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.layer_of(inputs, tokens=tokens)
+        oracle.layer(s.router, s.k, s.scale, inputs.x, inputs.wr, inputs.bias, ex, sh,
+                     tokens=tokens)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
@@ -476,6 +485,8 @@ def main():
     ap.add_argument("--path", default="fused", choices=["fused", "staged"],
                     help="fused: one moe_forward call per step; staged: moe_route, "
                          "moe_permute, moe_expert_ffn (routed, shared), moe_combine")
+    ap.add_argument("--act", default="silu", choices=["silu", "gelu_tanh"],
+                    help="gate activation of the layer workloads")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -497,8 +508,8 @@ def main():
     import torch
     from sparse_moe_expert_sigmoid_amd import Context, MoELayer, synth as S
 
-    spec_name, chunks, desc = WORKLOADS[args.workload]
-    spec = S.spec(spec_name)
+    spec_name, chunks, desc, *spec_kw = WORKLOADS[args.workload]
+    spec = S.spec(spec_name, **(spec_kw[0] if spec_kw else {}))
     decode = spec.T <= 16
     steps = args.steps or (200 if decode else 40)
     warmup = args.warmup if args.warmup is not None else (20 if decode else 5)
@@ -507,7 +518,7 @@ def main():
     inputs = S.make_layer(spec)
     dev = torch.device("cuda:0")
     ctx = Context(0)
-    base = MoELayer.from_inputs(ctx, inputs, dev)
+    base = MoELayer.from_inputs(ctx, inputs, dev, act=args.act)
     layer_bytes = base.experts.nbytes + (base.shared.nbytes if base.shared else 0)
     # enough copies that one step's weights are never cache-resident from the last
     copies = args.copies or max(2, min(32, math.ceil(2.0e9 / layer_bytes) + 1))
@@ -592,7 +603,7 @@ def main():
         kt = ctx.moe_timing_read()
         ctx.moe_timing(0)
         kernels = {n: {"launches": int(c), "avg_us": t / c * 1e3} for n, (c, t) in kt.items()}
-        dom = "ffn_i4_gate_up" if spec.fmt == "int4_b32" else "ffn_i8_gate_up"
+        dom = "ffn_i4_gate_up" if spec.fmt.startswith("int4") else "ffn_i8_gate_up"
         gemm = "ffn_i8_gate_up_gemm" in kt
         if gemm:
             dom = "ffn_i8_gate_up_gemm"
@@ -633,7 +644,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(inputs, args.cpu_budget)
+        cpu = cpu_baseline(inputs, args.cpu_budget, args.act)
 
     out = {
         "metric": METRIC,
@@ -651,6 +662,7 @@ def main():
         "config": {"workload": desc, "T": spec.T, "chunks": chunks, "d": d, "E": E, "k": k,
                    "inter": I, "router": spec.router, "expert_format": spec.fmt,
                    "shared_expert": spec.shared, "weight_copies": copies,
+                   "activation": args.act,
                    "entry_point": "moe_forward" if args.path == "fused" else
                    "moe_route+moe_permute+moe_expert_ffn x2+moe_combine",
                    "parallelism": "single GPU"},

@@ -65,15 +65,23 @@ typedef enum {
     MOE_W_FP32 = 0,      /* plain fp32 weights, no scales                              */
     MOE_W_INT8_ROW = 1,  /* int8 codes, one fp32 scale per output row and expert:
                             w = q * s[row] (DETAILS.md, quantization of the int8 file) */
-    MOE_W_INT4_B32 = 2   /* int4 codes in blocks of 32 along the input axis with fp32
+    MOE_W_INT4_B32 = 2,  /* int4 codes in blocks of 32 along the input axis with fp32
                             scales raised to 2^-14: w = q * max(s[row][i/32], 2^-14)
                             (Qwen3 card, Available Artifacts and Conversion Notes).
                             Two codes per byte, two's complement: input element 2i in
                             the low nibble of byte i, element 2i+1 in the high nibble */
+    MOE_W_INT4_B128 = 3  /* the same codes with one scale per block of 128 inputs:
+                            w = q * max(s[row][i/128], 2^-14) (the 128-wide blocks the
+                            Kimi-Linear LiteRT-LM model card measures beside 32-wide
+                            ones; the 2^-14 floor read as applying to any block) */
 } moe_wfmt;
 
 typedef enum {
-    MOE_ACT_SILU = 0     /* h = silu(gate x) * (up x), silu(z) = z / (1 + exp(-z)) */
+    MOE_ACT_SILU = 0,     /* h = silu(gate x) * (up x), silu(z) = z / (1 + exp(-z)) */
+    MOE_ACT_GELU_TANH = 1 /* h = gelu(gate x) * (up x) with the tanh form
+                             gelu(z) = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+                             (DETAILS.md, Runtime: the moe op's activation attribute
+                             is 'silu' or 'gelu_tanh', legacy spelling 'gelu') */
 } moe_act;
 
 /* Byte order of the int8/int4 codes in HBM (scales are always row-major).
@@ -94,15 +102,18 @@ typedef enum {
  *   fmt        one of moe_wfmt
  *   layout     one of moe_layout (MOE_LAYOUT_ROWS for fp32)
  *   n_experts  E >= 1
- *   d          model width; a multiple of 64 (int4: of 128), at most 16384
+ *   d          model width; a multiple of 64 (int4, either block: of 128), at
+ *              most 16384
  *   inter      expert intermediate width I; a multiple of 64 (int4: of 128), at
  *              most 16384
  *   w_gate_up  [E][2I][d]: rows 0..I-1 are the gate projection, rows I..2I-1 the
  *              up projection, input axis contiguous.  int8: int8_t; int4: uint8_t
  *              with d/2 bytes per row; fp32: float
- *   s_gate_up  int8: [E][2I]; int4: [E][2I][d/32]; fp32: NULL
+ *   s_gate_up  int8: [E][2I]; int4: [E][2I][d/32] (block 128: [E][2I][d/128]);
+ *              fp32: NULL
  *   w_down     [E][d][I] (int4: [E][d][I/2] bytes)
- *   s_down     int8: [E][d]; int4: [E][d][I/32]; fp32: NULL                         */
+ *   s_down     int8: [E][d]; int4: [E][d][I/32] (block 128: [E][d][I/128]); fp32:
+ *              NULL                                                                  */
 typedef struct {
     int fmt;
     int layout;
@@ -135,6 +146,8 @@ typedef enum {
  *     scales[r][b] = max(max_{k in block b} |w[r][k]| / 7, 2^-14),
  *     codes in [-7, 7], two per byte ([rows][K/2] bytes, low nibble = even k).
  *     K a multiple of 32.
+ *   MOE_W_INT4_B128: the same per block of 128 (scales [rows][K/128]); K a
+ *     multiple of 128.
  * Both divisions are correctly rounded fp32; the quotient is rounded to the
  * nearest integer, halves away from zero.  Inputs must be finite.
  *   in_type  one of moe_in_type
@@ -229,9 +242,10 @@ moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int 
 
 /* Expert SwiGLU FFNs over grouped rows (DETAILS.md, mixture-of-experts bullet:
  * the routed experts with SiLU; Qwen3 card, Accuracy: activation 'silu').
- *   rows_out[r] = W_down[e] (silu(W_gate[e] x[row_token[r]]) * W_up[e] x[row_token[r]])
+ *   rows_out[r] = W_down[e] (act(W_gate[e] x[row_token[r]]) * W_up[e] x[row_token[r]])
  * for every row r of every expert e, with weights dequantised in-kernel.
- *   act        MOE_ACT_SILU; anything else returns MOE_E_UNSUPPORTED with a message
+ *   act        MOE_ACT_SILU or MOE_ACT_GELU_TANH; anything else returns
+ *              MOE_E_UNSUPPORTED with a message
  *   x          [T][d] fp32
  *   row_token  [R] or NULL (row r reads token r)
  *   offsets    [E+1] device, as written by moe_permute; NULL only when E == 1,
@@ -287,6 +301,7 @@ moe_status moe_layer_workspace_size(const moe_ctx* ctx, const moe_layer* layer, 
  * routed experts' launches.
  *   x [T][d], residual [T][d] or NULL, y [T][d] out (may alias residual)
  *   topk_idx [T][k], topk_w [T][k]: outputs, or NULL to keep them internal
+ *   act: the gate activation of the routed and the shared experts alike
  * Checks and errors as for the separate calls. */
 moe_status moe_forward(moe_ctx* ctx, const moe_layer* layer, int act, const float* x, int T,
                        const float* residual, float* y, int32_t* topk_idx, float* topk_w,

@@ -23,7 +23,9 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 ROUTER = {"sigmoid_bias": 0, "softmax": 1}
-FMT = {"fp32": 0, "int8_row": 1, "int4_b32": 2}
+FMT = {"fp32": 0, "int8_row": 1, "int4_b32": 2, "int4_b128": 3}
+ACT = {"silu": 0, "gelu_tanh": 1}
+INT4_BLOCK = {"int4_b32": 32, "int4_b128": 128}
 
 
 def build(verbose: bool = False) -> str:
@@ -42,7 +44,7 @@ def build(verbose: bool = False) -> str:
 class _Experts(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int), ("E", ctypes.c_int), ("d", ctypes.c_int),
                 ("inter", ctypes.c_int), ("gu", ctypes.c_void_p), ("gu_s", ctypes.c_void_p),
-                ("dn", ctypes.c_void_p), ("dn_s", ctypes.c_void_p)]
+                ("dn", ctypes.c_void_p), ("dn_s", ctypes.c_void_p), ("act", ctypes.c_int)]
 
 
 class _Layer(ctypes.Structure):
@@ -63,6 +65,8 @@ def _load():
     lib.oracle_sigmoid.restype = ctypes.c_double
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
+    lib.oracle_gelu_tanh.restype = ctypes.c_double
     lib.oracle_route.argtypes = [ci, vp, vp, vp, i64, ci, ci, ci, ctypes.c_float, vp, vp, vp, vp]
     lib.oracle_route.restype = ci
     lib.oracle_permute.argtypes = [vp, i64, ci, ci, vp, vp, vp]
@@ -79,7 +83,7 @@ def _load():
     lib.oracle_coverage_set.restype = ci
     lib.oracle_quantize_int8_rows.argtypes = [vp, i64, ci, vp, vp]
     lib.oracle_quantize_int8_rows.restype = ci
-    lib.oracle_quantize_int4_blocks.argtypes = [vp, i64, ci, vp, vp]
+    lib.oracle_quantize_int4_blocks.argtypes = [vp, i64, ci, ci, vp, vp]
     lib.oracle_quantize_int4_blocks.restype = ci
     _lib = lib
     return lib
@@ -104,6 +108,7 @@ class Experts:
     dn: np.ndarray
     gu_s: Optional[np.ndarray] = None
     dn_s: Optional[np.ndarray] = None
+    act: str = "silu"
 
     def _struct(self):
         E, n2, d = self.gu.shape
@@ -116,19 +121,20 @@ class Experts:
             if self.fmt == "int8_row":
                 assert self.gu_s.shape == (E, n2) and self.dn_s.shape == (E, d)
             else:
-                assert d % 32 == 0 and inter % 32 == 0
-                assert self.gu_s.shape == (E, n2, d // 32)
-                assert self.dn_s.shape == (E, d, inter // 32)
+                B = INT4_BLOCK[self.fmt]
+                assert d % B == 0 and inter % B == 0
+                assert self.gu_s.shape == (E, n2, d // B)
+                assert self.dn_s.shape == (E, d, inter // B)
         keep = [np.ascontiguousarray(self.gu), np.ascontiguousarray(self.dn),
                 _f32(self.gu_s), _f32(self.dn_s)]
         s = _Experts(FMT[self.fmt], E, d, inter, _p(keep[0]), _p(keep[2]), _p(keep[1]),
-                     _p(keep[3]))
+                     _p(keep[3]), ACT[self.act])
         return s, keep
 
     @staticmethod
-    def of(w) -> "Experts":
+    def of(w, act: str = "silu") -> "Experts":
         """From a synth.ExpertWeights."""
-        return Experts(w.fmt, w.gu, w.dn, w.gu_s, w.dn_s)
+        return Experts(w.fmt, w.gu, w.dn, w.gu_s, w.dn_s, act)
 
 
 def sigmoid(z: float) -> float:
@@ -137,6 +143,10 @@ def sigmoid(z: float) -> float:
 
 def silu(z: float) -> float:
     return _load().oracle_silu(z)
+
+
+def gelu_tanh(z: float) -> float:
+    return _load().oracle_gelu_tanh(z)
 
 
 def route(router: str, x, wr, bias, k: int, scale: float, want_logits: bool = False):
@@ -267,17 +277,19 @@ def bf16_to_f32(bits) -> np.ndarray:
 
 def quantize(fmt: str, w) -> tuple:
     """Float weights [rows, K] -> (codes int8 [rows, K], scales fp32).
-    fmt "int8_row": scales [rows]; "int4_b32": scales [rows, K/32], codes
-    unpacked (one int8 per code, in [-8, 7])."""
+    fmt "int8_row": scales [rows]; "int4_b32" / "int4_b128": scales
+    [rows, K/32] / [rows, K/128], codes unpacked (one int8 per code, in
+    [-8, 7])."""
     w = _f32(w)
     rows, K = w.shape
     q = np.empty((rows, K), np.int8)
     if fmt == "int8_row":
         s = np.empty(rows, np.float32)
         rc = _load().oracle_quantize_int8_rows(_p(w), rows, K, _p(q), _p(s))
-    elif fmt == "int4_b32":
-        s = np.empty((rows, K // 32), np.float32)
-        rc = _load().oracle_quantize_int4_blocks(_p(w), rows, K, _p(q), _p(s))
+    elif fmt in INT4_BLOCK:
+        B = INT4_BLOCK[fmt]
+        s = np.empty((rows, K // B), np.float32)
+        rc = _load().oracle_quantize_int4_blocks(_p(w), rows, K, B, _p(q), _p(s))
     else:
         raise ValueError(f"no quantizer for {fmt}")
     if rc != 0:

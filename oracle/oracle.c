@@ -25,8 +25,9 @@
  * weights use sigmoid(l) without the bias; renormalise, then multiply by the
  * scale; no epsilon in the renormalisation; flat top-k; ties go to the lower
  * expert index; the softmax router selects on the probabilities; the FFN is
- * down(silu(gate x) * (up x)); the int4 block runs along the input axis; the
- * clamp is max(s, 2^-14); the shared expert is added unweighted.
+ * down(act(gate x) * (up x)) with act = silu unless gelu_tanh is asked for; the
+ * int4 block runs along the input axis; the clamp is max(s, 2^-14) for either
+ * int4 block width; the shared expert is added unweighted.
  *
  * The top-k decision is taken on keys rounded to fp32, the precision the
  * pages give the router (fp32 router in [Q]; fp32 activations in [K]), so
@@ -50,6 +51,14 @@ double oracle_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 /* SiLU(z) = z * sigmoid(z)  ([K] "the 256 routed experts ... with SiLU";
  * [Q] "Accuracy": activation='silu', the source's hidden_act) */
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* GELU in its tanh form, z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))): the
+ * other activation the moe op's attribute names (LiteRT-LM details, "Runtime":
+ * 'gelu_tanh', legacy spelling 'gelu'). */
+double oracle_gelu_tanh(double z) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
 
 /* ------------------------------------------------------------------ */
 /* router                                                              */
@@ -201,6 +210,10 @@ int oracle_permute(const int32_t* idx, int64_t T, int k, int E, int32_t* offsets
  *                                              output row and expert, symmetric)
  *   int4_b32:  q * max(s[e][n][i/32], 2^-14)  ([Q] int4 blockwise, block 32, fp32
  *                                              scales; scales below 2^-14 raised)
+ *   int4_b128: q * max(s[e][n][i/128], 2^-14) (the same with blocks of 128, the
+ *                                              block width the Kimi model card
+ *                                              measures against 32; the clamp
+ *                                              read as applying to any block)
  * int4 codes are read unpacked, one int8 per element.
  */
 static inline double weight_at(const oracle_experts* W, int m, int e, int64_t n, int64_t i) {
@@ -212,9 +225,10 @@ static inline double weight_at(const oracle_experts* W, int m, int e, int64_t n,
     if (W->fmt == ORACLE_W_FP32) return (double)((const float*)q)[at];
     double code = (double)((const int8_t*)q)[at];
     if (W->fmt == ORACLE_W_INT8_ROW) return code * (double)s[(int64_t)e * rows + n];
-    /* int4, block of 32 along the input axis */
-    int64_t nblk = cols / 32;
-    double sc = (double)s[((int64_t)e * rows + n) * nblk + i / 32];
+    /* int4, blocks of B along the input axis */
+    const int64_t B = W->fmt == ORACLE_W_INT4_B128 ? 128 : 32;
+    int64_t nblk = cols / B;
+    double sc = (double)s[((int64_t)e * rows + n) * nblk + i / B];
     const double floor_scale = 1.0 / 16384.0; /* 2^-14 */
     if (!(sc >= floor_scale)) sc = floor_scale;
     return code * sc;
@@ -222,8 +236,9 @@ static inline double weight_at(const oracle_experts* W, int m, int e, int64_t n,
 
 /*
  * out[0..d) = FFN_e(x):  g_n = sum_i Wg[n][i] x_i,  u_n = sum_i Wu[n][i] x_i,
- *                        h_n = silu(g_n) * u_n,      out_m = sum_n Wd[m][n] h_n
- * Rows 0..I-1 of the gate/up matrix are the gate, rows I..2I-1 the up.
+ *                        h_n = act(g_n) * u_n,       out_m = sum_n Wd[m][n] h_n
+ * with act = silu (the default) or gelu_tanh.  Rows 0..I-1 of the gate/up
+ * matrix are the gate, rows I..2I-1 the up.
  */
 void oracle_ffn(const oracle_experts* W, int e, const float* x, double* out, double* h) {
     int64_t I = W->inter, d = W->d;
@@ -231,7 +246,7 @@ void oracle_ffn(const oracle_experts* W, int e, const float* x, double* out, dou
         double g = 0.0, u = 0.0;
         for (int64_t i = 0; i < d; ++i) g += weight_at(W, 0, e, n, i) * (double)x[i];
         for (int64_t i = 0; i < d; ++i) u += weight_at(W, 0, e, I + n, i) * (double)x[i];
-        h[n] = oracle_silu(g) * u;
+        h[n] = (W->act == ORACLE_ACT_GELU_TANH ? oracle_gelu_tanh(g) : oracle_silu(g)) * u;
     }
     for (int64_t m = 0; m < d; ++m) {
         double acc = 0.0;
@@ -390,9 +405,10 @@ int oracle_coverage_set(const uint64_t* counts, int E, double cover, int k, int3
  * so the largest magnitude maps to +-127.  An all-zero row gets s = 0 and
  * codes 0.
  *
- * int4 per block of 32 inputs (Qwen3-30B-A3B model card, file table: int4
- * blockwise, block 32, fp32 scales; "Conversion notes": block scales below
- * 2^-14 are raised to 2^-14): s = max(max_b |w| / 7, 2^-14) over the block,
+ * int4 per block of B = 32 inputs (Qwen3-30B-A3B model card, file table:
+ * int4 blockwise, block 32, fp32 scales; "Conversion notes": block scales below
+ * 2^-14 are raised to 2^-14), or B = 128: s = max(max_b |w| / 7, 2^-14) over
+ * the block,
  * q = round(w / s) in [-8, 7] (symmetric: at most 7 in magnitude).  Raising
  * the scale here, before dividing, makes the stored scale the one the layer
  * dequantises with.
@@ -423,23 +439,24 @@ int oracle_quantize_int8_rows(const float* w, int64_t rows, int K, int8_t* q, fl
     return 0;
 }
 
-int oracle_quantize_int4_blocks(const float* w, int64_t rows, int K, int8_t* q, float* s) {
-    if (rows < 0 || K < 32 || K % 32 != 0) return -1;
-    const int nb = K / 32;
+int oracle_quantize_int4_blocks(const float* w, int64_t rows, int K, int B, int8_t* q,
+                                float* s) {
+    if (rows < 0 || (B != 32 && B != 128) || K < B || K % B != 0) return -1;
+    const int nb = K / B;
     const float floor_s = 1.0f / 16384.0f;  /* 2^-14 */
     #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         for (int b = 0; b < nb; ++b) {
-            const float* wb = w + r * K + 32 * b;
+            const float* wb = w + r * K + (int64_t)B * b;
             float m = 0.0f;
-            for (int i = 0; i < 32; ++i) m = fabsf(wb[i]) > m ? fabsf(wb[i]) : m;
+            for (int i = 0; i < B; ++i) m = fabsf(wb[i]) > m ? fabsf(wb[i]) : m;
             float sc = div_f32(m, 7.0f);
             if (sc < floor_s) sc = floor_s;
             s[r * nb + b] = sc;
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < B; ++i) {
                 double c = round((double)div_f32(wb[i], sc));
                 c = c > 7.0 ? 7.0 : (c < -8.0 ? -8.0 : c);
-                q[r * K + 32 * b + i] = (int8_t)c;
+                q[r * K + (int64_t)B * b + i] = (int8_t)c;
             }
         }
     }

@@ -20,13 +20,15 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = range(5)
 MOE_ROUTER_SIGMOID_BIAS, MOE_ROUTER_SOFTMAX = 0, 1
-MOE_W_FP32, MOE_W_INT8_ROW, MOE_W_INT4_B32 = 0, 1, 2
-MOE_ACT_SILU = 0
+MOE_W_FP32, MOE_W_INT8_ROW, MOE_W_INT4_B32, MOE_W_INT4_B128 = 0, 1, 2, 3
+MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
+ACT = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_IN_F32, MOE_IN_BF16 = 0, 1
 
 ROUTER = {"sigmoid_bias": MOE_ROUTER_SIGMOID_BIAS, "softmax": MOE_ROUTER_SOFTMAX}
-FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B32}
+FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B32,
+       "int4_b128": MOE_W_INT4_B128}
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
@@ -272,7 +274,7 @@ class DeviceExperts:
     def upload(w, device) -> "DeviceExperts":
         """From a synth.ExpertWeights (host numpy)."""
         fmt = FMT[w.fmt]
-        if w.fmt == "int4_b32":
+        if w.fmt in ("int4_b32", "int4_b128"):
             gu, dn = w.gu_packed, w.dn_packed
         else:
             gu, dn = w.gu, w.dn

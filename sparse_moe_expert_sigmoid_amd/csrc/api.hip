@@ -304,7 +304,7 @@ moe_status moe_workspace_size(const moe_ctx* cctx, int T, int k, int E, int d, i
     return fail(ctx, MOE_E_INVALID,
                 "moe_workspace_size: need T >= 0, k >= 1, E >= 1, d >= 1, inter >= 1 "
                 "(got T=%d k=%d E=%d d=%d inter=%d)", T, k, E, d, inter);
-  if (fmt < MOE_W_FP32 || fmt > MOE_W_INT4_B32)
+  if (fmt < MOE_W_FP32 || fmt > MOE_W_INT4_B128)
     return fail(ctx, MOE_E_INVALID, "moe_workspace_size: unknown weight format %d", fmt);
   const long long R = (long long)T * k;
   if (R > 0x7fffffffLL) return fail(ctx, MOE_E_INVALID, "moe_workspace_size: T*k overflows");
@@ -385,12 +385,12 @@ moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k
 moe_status moe_quantize(moe_ctx* ctx, int fmt, int in_type, const void* w, long long rows,
                         int K, void* codes, float* scales, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (fmt != MOE_W_INT8_ROW && fmt != MOE_W_INT4_B32)
+  if (fmt != MOE_W_INT8_ROW && fmt != MOE_W_INT4_B32 && fmt != MOE_W_INT4_B128)
     return fail(ctx, MOE_E_UNSUPPORTED, "moe_quantize: format %d has no quantizer", fmt);
   if (in_type != MOE_IN_F32 && in_type != MOE_IN_BF16)
     return fail(ctx, MOE_E_INVALID, "moe_quantize: unknown input type %d", in_type);
   if (rows < 0) return fail(ctx, MOE_E_INVALID, "moe_quantize: rows=%lld is negative", rows);
-  const int kmul = fmt == MOE_W_INT8_ROW ? 8 : 32;
+  const int kmul = fmt == MOE_W_INT8_ROW ? 8 : (fmt == MOE_W_INT4_B32 ? 32 : 128);
   if (K < kmul || K % kmul != 0 || K > (1 << 24))
     return fail(ctx, MOE_E_UNSUPPORTED,
                 "moe_quantize: K=%d must be a positive multiple of %d, at most 2^24", K, kmul);
@@ -439,7 +439,7 @@ moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int 
 
 namespace {
 moe_status check_weights(moe_ctx* ctx, const char* fn, const char* which, const moe_weights* w) {
-  if (w->fmt < MOE_W_FP32 || w->fmt > MOE_W_INT4_B32)
+  if (w->fmt < MOE_W_FP32 || w->fmt > MOE_W_INT4_B128)
     return fail(ctx, MOE_E_INVALID, "%s: %s: unknown weight format %d", fn, which, w->fmt);
   if (w->n_experts < 1 || w->d < 1 || w->inter < 1)
     return fail(ctx, MOE_E_INVALID, "%s: %s: n_experts=%d d=%d inter=%d", fn, which,
@@ -447,7 +447,7 @@ moe_status check_weights(moe_ctx* ctx, const char* fn, const char* which, const 
   if (w->d > moe::kMaxWidth || w->inter > moe::kMaxWidth)
     return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: d=%d and inter=%d must be at most %d", fn,
                 which, w->d, w->inter, moe::kMaxWidth);
-  const int mult = w->fmt == MOE_W_INT4_B32 ? 128 : 64;
+  const int mult = w->fmt == MOE_W_INT4_B32 || w->fmt == MOE_W_INT4_B128 ? 128 : 64;
   if (w->d % mult != 0 || w->inter % mult != 0)
     return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: d=%d and inter=%d must be multiples of %d", fn,
                 which, w->d, w->inter, mult);
@@ -472,9 +472,10 @@ moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const flo
                           float* rows_out, void* ws, size_t ws_bytes, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
   if (!w) return fail(ctx, MOE_E_INVALID, "moe_expert_ffn: weights is NULL");
-  if (act != MOE_ACT_SILU)
+  if (act != MOE_ACT_SILU && act != MOE_ACT_GELU_TANH)
     return fail(ctx, MOE_E_UNSUPPORTED,
-                "moe_expert_ffn: unsupported activation=%d (only MOE_ACT_SILU=0)", act);
+                "moe_expert_ffn: unsupported activation=%d (MOE_ACT_SILU=0 or "
+                "MOE_ACT_GELU_TANH=1)", act);
   {
     moe_status st = check_weights(ctx, "moe_expert_ffn", "weights", w);
     if (st != MOE_OK) return st;
@@ -505,13 +506,13 @@ moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const flo
     moe::FfnWs lay = moe::ffn_ws_layout(ws, T, w->d, 1, &R_max, &inter, false);
     e = moe::launch_ffn_f32(static_cast<const float*>(w->w_gate_up),
                             static_cast<const float*>(w->w_down), w->n_experts, w->d, w->inter,
-                            x, T, row_token, offsets, R_max, rows_out, lay.h,
+                            x, T, row_token, offsets, R_max, rows_out, lay.h, act,
                             (hipStream_t)stream);
   } else {
     moe::FfnWs lay = moe::ffn_ws_layout(ws, T, w->d, 1, &R_max, &inter, true);
     moe::FfnSet set{w->fmt, w->layout, w->n_experts, w->inter, R_max, w->w_gate_up, w->s_gate_up,
                     w->w_down, w->s_down, row_token, offsets, lay.hq[0], lay.hs[0], rows_out,
-                    nullptr, 1};
+                    nullptr, 1, act};
     e = moe::launch_ffn_quant(&set, 1, w->d, x, T, lay, false, (hipStream_t)stream);
   }
   return device_result(ctx, e, "moe_expert_ffn");
@@ -568,9 +569,10 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
   moe_status st = check_layer(ctx, "moe_forward", L);
   if (st != MOE_OK) return st;
-  if (act != MOE_ACT_SILU)
+  if (act != MOE_ACT_SILU && act != MOE_ACT_GELU_TANH)
     return fail(ctx, MOE_E_UNSUPPORTED,
-                "moe_forward: unsupported activation=%d (only MOE_ACT_SILU=0)", act);
+                "moe_forward: unsupported activation=%d (MOE_ACT_SILU=0 or MOE_ACT_GELU_TANH=1)",
+                act);
   if (T < 0 || (long long)T * L->k > 0x7fffffffLL)
     return fail(ctx, MOE_E_INVALID, "moe_forward: T=%d", T);
   if (T == 0) return MOE_OK;
@@ -614,9 +616,9 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, 2, Rs, Is, true);
     moe::FfnSet sets[2] = {
         {X.fmt, X.layout, E, X.inter, R, X.w_gate_up, X.s_gate_up, X.w_down, X.s_down, f.row_token,
-         f.offsets, lay.hq[0], lay.hs[0], f.rows, small ? idx : nullptr, k},
+         f.offsets, lay.hq[0], lay.hs[0], f.rows, small ? idx : nullptr, k, act},
         {S.fmt, S.layout, 1, S.inter, T, S.w_gate_up, S.s_gate_up, S.w_down, S.s_down, nullptr,
-         nullptr, lay.hq[1], lay.hs[1], f.sh_rows, nullptr, 1}};
+         nullptr, lay.hq[1], lay.hs[1], f.sh_rows, nullptr, 1, act}};
     e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, small, s);
   } else {
     auto run = [&](const moe_weights& W, int Ew, int Rw, const int32_t* rt, const int32_t* of,
@@ -626,12 +628,13 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
         moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, 1, &Rw, &Iw, false);
         return moe::launch_ffn_f32(static_cast<const float*>(W.w_gate_up),
                                    static_cast<const float*>(W.w_down), Ew, d, W.inter, x, T, rt,
-                                   of, Rw, out, lay.h, s);
+                                   of, Rw, out, lay.h, act, s);
       }
       moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, 1, &Rw, &Iw, true);
       const bool pairs = small && &W == &X;
       moe::FfnSet set{W.fmt, W.layout, Ew, W.inter, Rw, W.w_gate_up, W.s_gate_up, W.w_down,
-                      W.s_down, rt, of, lay.hq[0], lay.hs[0], out, pairs ? idx : nullptr, k};
+                      W.s_down, rt, of, lay.hq[0], lay.hs[0], out, pairs ? idx : nullptr, k,
+                      act};
       // x was encoded by the small-batch router when only routed experts run here
       return moe::launch_ffn_quant(&set, 1, d, x, T, lay, small && &W == &X, s);
     };
@@ -657,7 +660,7 @@ moe_status moe_tile_weights(moe_ctx* ctx, const moe_weights* src, void* dst_gate
   if (!dst_gate_up || !dst_down || !aligned16(dst_gate_up) || !aligned16(dst_down))
     return fail(ctx, MOE_E_INVALID, "moe_tile_weights: a destination is NULL or misaligned");
   const long long E = src->n_experts, d = src->d, I = src->inter;
-  const long long half = src->fmt == MOE_W_INT4_B32 ? 2 : 1;
+  const long long half = src->fmt == MOE_W_INT8_ROW ? 1 : 2;
   const long long gu_bytes = E * 2 * I * d / half, dn_bytes = E * d * I / half;
   auto overlap = [](const void* a, long long na, const void* b, long long nb) {
     const char* pa = static_cast<const char*>(a);

@@ -66,6 +66,7 @@ struct Group {
   float* out;                // [R][d]
   const int32_t* pairs_idx;  // non-NULL: group the R = T*k pairs of topk_idx [T][k] on the fly
   int k;
+  int act;                   // gate activation: 0 silu, 1 gelu (tanh form)
 };
 
 struct Job {
@@ -348,10 +349,12 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
         up[c] = se[I + n] * sigx * ((float)b0[c] + (float)b1[c] * (1.0f / 256.0f));
       }
     } else {
-      // int4: one 16x16x32 MFMA pair per block of 32 inputs; each block's int32
-      // sum (256*d0-part + d1-part, exact in fp32 since |.| < 2^24) is scaled by
-      // max(s, 2^-14) into the fp32 accumulator.
-      const int nb = d / 32, nspan = d / 128;
+      // int4: one 16x16x32 MFMA pair per 32 inputs.  Blocks of 32 (FMT 2):
+      // each block's int32 sum (256*d0-part + d1-part, exact in fp32 since
+      // |.| < 2^24) is scaled by max(s, 2^-14) into the fp32 accumulator.
+      // Blocks of 128 (FMT 3) are the 128-input spans: the span's four MFMA
+      // pairs accumulate in int32 and the digits join once per span.
+      const int nb = d / (FMT == 3 ? 128 : 32), nspan = d / 128;
       const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
       const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wgu), row0, d, i,
                                                g, lane);
@@ -373,21 +376,41 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
             x1[q] = *reinterpret_cast<const long*>(xb1 + 128 * m + 32 * q + 8 * g);
           }
         }
+        if constexpr (FMT == 2) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int b = 4 * m + q;
-          const long qa = unpack8_int4((unsigned)wa4[q]);
-          const long qb = unpack8_int4((unsigned)wb4[q]);
-          const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], zero, 0, 0, 0);
-          const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], zero, 0, 0, 0);
-          const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], zero, 0, 0, 0);
-          const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], zero, 0, 0, 0);
+          for (int q = 0; q < 4; ++q) {
+            const int b = 4 * m + q;
+            const long qa = unpack8_int4((unsigned)wa4[q]);
+            const long qb = unpack8_int4((unsigned)wb4[q]);
+            const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], zero, 0, 0, 0);
+            const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], zero, 0, 0, 0);
+            const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], zero, 0, 0, 0);
+            const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], zero, 0, 0, 0);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float s1 = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
-            const float s2 = fmaxf(sb[(size_t)c * nb + b], kScaleFloor);
-            fa[c] = fmaf(s1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
-            fb[c] = fmaf(s2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+            for (int c = 0; c < 4; ++c) {
+              const float s1 = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
+              const float s2 = fmaxf(sb[(size_t)c * nb + b], kScaleFloor);
+              fa[c] = fmaf(s1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
+              fb[c] = fmaf(s2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+            }
+          }
+        } else {
+          v4i pa0 = zero, pa1 = zero, pb0 = zero, pb1 = zero;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const long qa = unpack8_int4((unsigned)wa4[q]);
+            const long qb = unpack8_int4((unsigned)wb4[q]);
+            pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], pa0, 0, 0, 0);
+            pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], pa1, 0, 0, 0);
+            pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], pb0, 0, 0, 0);
+            pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], pb1, 0, 0, 0);
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {  // |p0| < 2^17: each digit sum exact in fp32
+            const float s1 = fmaxf(sa[(size_t)c * nb + m], kScaleFloor);
+            const float s2 = fmaxf(sb[(size_t)c * nb + m], kScaleFloor);
+            fa[c] = fmaf(s1, fmaf((float)pa0[c], 256.0f, (float)pa1[c]), fa[c]);
+            fb[c] = fmaf(s2, fmaf((float)pb0[c], 256.0f, (float)pb1[c]), fb[c]);
           }
         }
       }
@@ -419,7 +442,7 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
     float mx = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      h[c] = silu_f(gate[c]) * up[c];
+      h[c] = act_f(G.act, gate[c]) * up[c];
       mx = fmaxf(mx, fabsf(h[c]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -536,7 +559,9 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
       }
     }
   } else {
-    const int nb = I / 32, nspan = I / 128;
+    // int4 blocks of 32 (FMT 2) or 128 (FMT 3, the span: its MFMA pairs
+    // accumulate in int32 per 64-column half, since h has one scale per 64)
+    const int nb = I / (FMT == 3 ? 128 : 32), nspan = I / 128;
     const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
     const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wdn), row0, I, i, g,
                                              lane);
@@ -556,16 +581,33 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
       }
       sg[0] = jv ? hsr[2 * m] * (1.0f / 256.0f) : 0.0f;
       sg[1] = jv ? hsr[2 * m + 1] * (1.0f / 256.0f) : 0.0f;
+      if constexpr (FMT == 2) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int b = 4 * m + q;
-        const long wq = unpack8_int4((unsigned)w4[q]);
-        const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], zero, 0, 0, 0);
-        const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], zero, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const int b = 4 * m + q;
+          const long wq = unpack8_int4((unsigned)w4[q]);
+          const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], zero, 0, 0, 0);
+          const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], zero, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float sw = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
+            acc[0][c] = fmaf(sw * sg[q >> 1], (float)(p0[c] * 256 + p1[c]), acc[0][c]);
+          }
+        }
+      } else {
+        v4i p0[2] = {zero, zero}, p1[2] = {zero, zero};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const long wq = unpack8_int4((unsigned)w4[q]);
+          p0[q >> 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], p0[q >> 1], 0, 0, 0);
+          p1[q >> 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], p1[q >> 1], 0, 0, 0);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float sw = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
-          acc[0][c] = fmaf(sw * sg[q >> 1], (float)(p0[c] * 256 + p1[c]), acc[0][c]);
+          const float sw = fmaxf(sa[(size_t)c * nb + m], kScaleFloor);
+          const float v = fmaf(sg[0], fmaf((float)p0[0][c], 256.0f, (float)p1[0][c]),
+                               sg[1] * fmaf((float)p0[1][c], 256.0f, (float)p1[1][c]));
+          acc[0][c] = fmaf(sw, v, acc[0][c]);
         }
       }
     }
@@ -811,7 +853,7 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
                                    ((float)acc[2 + q][t][0][c] +
                                     (float)acc[2 + q][t][1][c] * (1.0f / 256.0f))
                              : 0.0f;
-        h[q][t][c] = silu_f(gt) * upv;
+        h[q][t][c] = act_f(G.act, gt) * upv;
         mx = fmaxf(mx, fabsf(h[q][t][c]));
       }
     }
@@ -1058,7 +1100,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ act,
                                                       const int32_t* __restrict__ row_token,
                                                       const int32_t* __restrict__ offsets, int E,
-                                                      int K, int N_out, int R,
+                                                      int K, int N_out, int R, int actf,
                                                       float* __restrict__ out) {
   Tile tl;
   if (!find_tile(offsets, E, R, kTileRows, blockIdx.y, tl)) return;
@@ -1089,7 +1131,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
       sa += __shfl_xor(sa, o, kWave);
       sb += __shfl_xor(sb, o, kWave);
     }
-    if (lane == 0) out[(size_t)r * N_out + n] = MODE == 0 ? silu_f(sa) * sb : sa;
+    if (lane == 0) out[(size_t)r * N_out + n] = MODE == 0 ? act_f(actf, sa) * sb : sa;
   }
 }
 
@@ -1219,7 +1261,7 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
       G.E = f.E; G.inter = f.inter; G.R = f.R;
       G.wgu = f.wgu; G.sgu = f.sgu; G.wdn = f.wdn; G.sdn = f.sdn;
       G.row_token = f.row_token; G.offsets = f.offsets;
-      G.hq = f.hq; G.hs = f.hs; G.out = f.out;
+      G.hq = f.hq; G.hs = f.hs; G.out = f.out; G.act = f.act;
     }
     if (nsets < 2) grp[1].inter = grp[0].inter;
     return sets[0].layout == 1 ? launch_gemm_pair<kTiled>(grp[0], grp[1], d, ws.xq, ws.xs, s)
@@ -1260,6 +1302,7 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     G.out = f.out;
     G.pairs_idx = f.pairs_idx;
     G.k = f.k;
+    G.act = f.act;
   }
   if (nsets < 2) grp[1].inter = grp[0].inter;
   const bool tiled = sets[0].layout == 1;
@@ -1268,26 +1311,27 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
   (pairs ? launch_pair<F, L, true>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)           \
          : launch_pair<F, L, false>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s))
   if (sets[0].fmt == 1) return tiled ? MOE_PAIR(1, kTiled) : MOE_PAIR(1, kRows);
+  if (sets[0].fmt == 3) return tiled ? MOE_PAIR(3, kTiled) : MOE_PAIR(3, kRows);
   return tiled ? MOE_PAIR(2, kTiled) : MOE_PAIR(2, kRows);
 #undef MOE_PAIR
 }
 
 hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int inter,
                           const float* x, int T, const int32_t* row_token,
-                          const int32_t* offsets, int R, float* rows_out, float* h,
+                          const int32_t* offsets, int R, float* rows_out, float* h, int act,
                           hipStream_t s) {
   (void)T;
   const int tiles = offsets ? max_tiles(R, E, kTileRows) : (R + kTileRows - 1) / kTileRows;
   {
     TimedLaunch tl(K_FFN_F32_GATE_UP, s);
     hipLaunchKernelGGL(ffn_f32_kernel<0>, dim3((inter + 3) / 4, tiles), dim3(256), 0, s, wgu,
-                       x, row_token, offsets, E, d, inter, R, h);
+                       x, row_token, offsets, E, d, inter, R, act, h);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   TimedLaunch tl(K_FFN_F32_DOWN, s);
   hipLaunchKernelGGL(ffn_f32_kernel<1>, dim3((d + 3) / 4, tiles), dim3(256), 0, s, wdn, h,
-                     row_token, offsets, E, inter, d, R, rows_out);
+                     row_token, offsets, E, inter, d, R, 0, rows_out);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ inline FfnWs ffn_ws_layout(void* base, int T, int d, int nsets, const int* R, co
 
 // One expert set for the quantised FFN launchers.
 struct FfnSet {
-  int fmt;                   // 1 = int8 rows, 2 = int4 blocks of 32
+  int fmt;                   // 1 = int8 rows, 2 = int4 blocks of 32, 3 = int4 blocks of 128
   int layout;                // 0 = rows, 1 = tiled (both sets of one launch alike)
   int E, inter, R;
   const void* wgu;
@@ -83,6 +83,7 @@ struct FfnSet {
   float* out;                // [R][d]
   const int32_t* pairs_idx;  // non-NULL: rows are the R = T*k pairs of topk_idx, grouped in-kernel
   int k;
+  int act;                   // gate activation: 0 silu, 1 gelu_tanh
 };
 
 // Upper bound on the number of FFN tiles (kTileRows rows of one expert each)
@@ -152,7 +153,7 @@ hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nr
                                hipStream_t s);
 hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int inter,
                           const float* x, int T, const int32_t* row_token,
-                          const int32_t* offsets, int R, float* rows_out, float* h,
+                          const int32_t* offsets, int R, float* rows_out, float* h, int act,
                           hipStream_t s);
 hipError_t launch_combine(const float* rows, const int32_t* token_row, const float* w,
                           const float* shared, const float* residual, int T, int k, int d,
@@ -213,6 +214,13 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
 }
 
 __device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
+// GELU, tanh form: z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ inline float gelu_tanh_f(float z) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+// Gate activation of the SwiGLU-style FFN: 0 = silu, 1 = gelu_tanh.
+__device__ inline float act_f(int act, float z) { return act == 1 ? gelu_tanh_f(z) : silu_f(z); }
 
 // ---- two-digit int8 encoding of fp32 activations (used by the FFN kernels)
 // v = 2^-p (d0 + d1/256) + e, |e| <= 2^-p / 512, d0, d1 in [-127, 127], with p

@@ -8,7 +8,8 @@
 //   int4 per block of 32 inputs: Qwen3-30B-A3B model card, file table (int4
 //     blockwise, block 32, fp32 scales) and "Conversion Notes" (block scales
 //     below 2^-14 raised to 2^-14): s = max(max|w_block| / 7, 2^-14),
-//     q = round(w / s) in [-7, 7], two codes per byte, low nibble first.
+//     q = round(w / s) in [-7, 7], two codes per byte, low nibble first; or
+//     the same per block of 128 inputs.
 //
 // Arithmetic: the scale is an IEEE fp32 division (correctly rounded; the
 // library is built without fast-math).  The quotient w / s must be the
@@ -252,13 +253,13 @@ __global__ __launch_bounds__(256) void quant_i8_long_rows_kernel(const void* __r
 
 // ---------------------------------------------------------------- int4 blocks
 // Flat over all pairs of 8-input units of all rows: a lane owns 16 inputs
-// (two units), a block of 32 is the lane pair (2i, 2i+1), its maximum one
-// swizzle away.  A workgroup codes 256 * kI4Pairs pairs (kI4Pairs per lane,
-// strided by 256 so that each load instruction reads contiguous bytes), all
-// loaded before any is coded; the grid covers every pair.  Lane pairs past
-// the end load the last block again (pair count even, lane parity kept) and
-// store its identical codes and scale again, so no load or store is
-// conditional.
+// (two units), a block of 32 (128) is LPB = 2 (8) neighbouring lanes, its
+// maximum one (three) swizzles away.  A workgroup codes 256 * kI4Pairs pairs
+// (kI4Pairs per lane, strided by 256 so that each load instruction reads
+// contiguous bytes), all loaded before any is coded; the grid covers every
+// pair.  Lanes past the end load the last block again (the pair count is a
+// multiple of LPB; the lane's place in its block is kept) and store its
+// identical codes and scale again, so no load or store is conditional.
 constexpr int kI4Pairs = 8;
 
 template <int IN>
@@ -266,7 +267,7 @@ struct Pair16 {
   Raw8<IN> lo, hi;
 };
 
-template <int IN>
+template <int IN, int LPB>
 __global__ __launch_bounds__(256) void quant_i4_blocks_kernel(const void* __restrict__ w,
                                                               long long pairs,
                                                               uint8_t* __restrict__ q,
@@ -277,17 +278,18 @@ __global__ __launch_bounds__(256) void quant_i4_blocks_kernel(const void* __rest
 #pragma unroll
   for (int n = 0; n < kI4Pairs; ++n) {
     const long long x = (long long)blockIdx.x * (256 * kI4Pairs) + 256 * n + threadIdx.x;
-    g[n] = x < pairs ? x : pairs - 2 + (x & 1);  // the last block, lane parity kept
+    g[n] = x < pairs ? x : pairs - LPB + (x & (LPB - 1));  // the last block
     b[n].lo.load(w, 16 * (size_t)g[n]);
     b[n].hi.load(w, 16 * (size_t)g[n] + 8);
   }
 #pragma unroll
   for (int n = 0; n < kI4Pairs; ++n) {
     float m = fmaxf(absmax8(b[n].lo), absmax8(b[n].hi));
-    m = fmaxf(m, __shfl_xor(m, 1, kWave));
+#pragma unroll
+    for (int o = 1; o < LPB; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     const float sc = fmaxf(div7(m), floor_s);
     const float y = 1.0f / sc;
-    s[g[n] >> 1] = sc;  // both lanes of the block write the same value
+    s[g[n] / LPB] = sc;  // every lane of the block writes the same value
     __builtin_nontemporal_store(v2u{codes_i4(b[n].lo, sc, y), codes_i4(b[n].hi, sc, y)},
                                 reinterpret_cast<v2u*>(q) + g[n]);
   }
@@ -340,12 +342,13 @@ hipError_t launch_i8(const void* w, long long rows, int K, int8_t* q, float* s,
   }
 }
 
-template <int IN>
+template <int IN, int LPB>
 hipError_t launch_i4(const void* w, long long rows, int K, uint8_t* q, float* s,
                      hipStream_t st) {
-  const long long pairs = rows * (long long)(K / 16);   // even: K is a multiple of 32
+  const long long pairs = rows * (long long)(K / 16);  // a multiple of LPB: K % (16 LPB) == 0
   const long long blocks = (pairs + 256 * kI4Pairs - 1) / (256 * kI4Pairs);
-  quant_i4_blocks_kernel<IN><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, pairs, q, s);
+  quant_i4_blocks_kernel<IN, LPB><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, pairs, q,
+                                                                               s);
   return hipGetLastError();
 }
 
@@ -361,9 +364,12 @@ hipError_t launch_quantize(int fmt, int in_type, const void* w, long long rows, 
                : launch_i8<kInBf16>(w, rows, K, static_cast<int8_t*>(codes), scales, st);
   }
   TimedLaunch t(K_QUANT_I4, st);
-  return in_type == kInF32
-             ? launch_i4<kInF32>(w, rows, K, static_cast<uint8_t*>(codes), scales, st)
-             : launch_i4<kInBf16>(w, rows, K, static_cast<uint8_t*>(codes), scales, st);
+  uint8_t* c = static_cast<uint8_t*>(codes);
+  if (fmt == 3)
+    return in_type == kInF32 ? launch_i4<kInF32, 8>(w, rows, K, c, scales, st)
+                             : launch_i4<kInBf16, 8>(w, rows, K, c, scales, st);
+  return in_type == kInF32 ? launch_i4<kInF32, 2>(w, rows, K, c, scales, st)
+                           : launch_i4<kInBf16, 2>(w, rows, K, c, scales, st);
 }
 
 }  // namespace moe

@@ -13,15 +13,17 @@ from typing import Optional
 
 import torch
 
-from .binding import (Context, DeviceExperts, MOE_ACT_SILU, ROUTER, moe_layer, moe_weights)
+from .binding import ACT, Context, DeviceExperts, ROUTER, moe_layer, moe_weights
 
 
 class MoELayer:
     def __init__(self, ctx: Context, router: str, k: int, scale: float, w_router: torch.Tensor,
                  bias: Optional[torch.Tensor], experts: DeviceExperts,
                  shared: Optional[DeviceExperts] = None,
-                 expert_mask: Optional[torch.Tensor] = None):
+                 expert_mask: Optional[torch.Tensor] = None, act: str = "silu"):
         self.ctx = ctx
+        self.act_name = act
+        self.act = ACT[act]  # gate activation of the routed and shared experts
         self.router = ROUTER[router]
         self.k, self.scale = k, float(scale)
         self.w_router, self.bias = w_router, bias
@@ -37,7 +39,8 @@ class MoELayer:
                               expert_mask.data_ptr() if expert_mask is not None else None)
 
     @staticmethod
-    def from_inputs(ctx: Context, inputs, device="cuda:0", tiled: bool = True) -> "MoELayer":
+    def from_inputs(ctx: Context, inputs, device="cuda:0", tiled: bool = True,
+                    act: str = "silu") -> "MoELayer":
         """Upload a synth.LayerInputs; quantised codes go to the tiled layout unless
         tiled=False."""
         s = inputs.spec
@@ -48,18 +51,20 @@ class MoELayer:
         if tiled:
             ex = ex.tiled(ctx)
             sh = sh.tiled(ctx) if sh is not None else None
-        return MoELayer(ctx, s.router, s.k, s.scale, wr, bias, ex, sh)
+        return MoELayer(ctx, s.router, s.k, s.scale, wr, bias, ex, sh, act=act)
 
     def with_weights(self, experts: DeviceExperts, shared: Optional[DeviceExperts]) -> "MoELayer":
         """Same router, other expert weights (e.g. a copy in other HBM pages)."""
-        return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
-                        self.scale, self.w_router, self.bias, experts, shared, self.expert_mask)
+        return MoELayer(self.ctx, self._router_name(), self.k, self.scale, self.w_router,
+                        self.bias, experts, shared, self.expert_mask, self.act_name)
+
+    def _router_name(self) -> str:
+        return [k for k, v in ROUTER.items() if v == self.router][0]
 
     def with_mask(self, expert_mask: Optional[torch.Tensor]) -> "MoELayer":
         """Same layer restricted to the experts whose mask entry is nonzero."""
-        return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
-                        self.scale, self.w_router, self.bias, self.experts, self.shared,
-                        expert_mask)
+        return MoELayer(self.ctx, self._router_name(), self.k, self.scale, self.w_router,
+                        self.bias, self.experts, self.shared, expert_mask, self.act_name)
 
     def restricted(self, keep) -> "MoELayer":
         """The layer cut to the experts `keep` (ascending ids), renumbered
@@ -73,8 +78,8 @@ class MoELayer:
         ix = torch.as_tensor(keep, dtype=torch.long, device=self.device)
         wr = self.w_router.index_select(0, ix).contiguous()
         bias = self.bias.index_select(0, ix).contiguous() if self.bias is not None else None
-        return MoELayer(self.ctx, [k for k, v in ROUTER.items() if v == self.router][0], self.k,
-                        self.scale, wr, bias, self.experts.select(keep), self.shared)
+        return MoELayer(self.ctx, self._router_name(), self.k, self.scale, wr, bias,
+                        self.experts.select(keep), self.shared, act=self.act_name)
 
     def alloc(self, T: int):
         if self._T == T:
@@ -106,10 +111,10 @@ class MoELayer:
         c.moe_route_masked(self.router, x, self.w_router, self.bias, self.expert_mask, T, d, E, k,
                            self.scale, self.idx, self.w, self.ws, stream)
         c.moe_permute(self.idx, T, k, E, self.offsets, self.row_token, self.token_row, stream)
-        c.moe_expert_ffn(self.experts, MOE_ACT_SILU, x, T, self.row_token, self.offsets, T * k,
+        c.moe_expert_ffn(self.experts, self.act, x, T, self.row_token, self.offsets, T * k,
                          self.rows, self.ws, stream)
         if self.shared is not None:
-            c.moe_expert_ffn(self.shared, MOE_ACT_SILU, x, T, None, None, T, self.sh_out,
+            c.moe_expert_ffn(self.shared, self.act, x, T, None, None, T, self.sh_out,
                              self.ws, stream)
         y = self.y if out is None else out
         c.moe_combine(self.rows, self.token_row, self.w, self.sh_out, residual, T, k, d, y,
@@ -126,7 +131,7 @@ class MoELayer:
             self.fws = torch.empty(need, dtype=torch.uint8, device=self.device)
             self._fused_T = T
         y = self.y if out is None else out
-        self.ctx.moe_forward(self.desc, MOE_ACT_SILU, x, T, residual, y, self.idx, self.w,
+        self.ctx.moe_forward(self.desc, self.act, x, T, residual, y, self.idx, self.w,
                              self.fws, stream)
         return y
 

@@ -15,7 +15,7 @@ from typing import Callable, List, Optional
 
 import torch
 
-from .binding import MOE_ACT_SILU, Context, DeviceExperts, MOE_W_INT8_ROW
+from .binding import Context, DeviceExperts, MOE_W_INT8_ROW
 from .layer import MoELayer
 
 
@@ -68,7 +68,7 @@ class MoEStack:
             if before_layer is not None:
                 before_layer(l, cur)
             out = self.buf[l % 2]
-            self.ctx.moe_forward(L.desc, MOE_ACT_SILU, cur, T, cur, out, self.idx[l], self.w[l],
+            self.ctx.moe_forward(L.desc, L.act, cur, T, cur, out, self.idx[l], self.w[l],
                                  self.ws, stream)
             if counts is not None:
                 self.ctx.moe_expert_counts(self.idx[l], T, L.k, L.E, counts[l], stream)

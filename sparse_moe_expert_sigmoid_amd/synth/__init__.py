@@ -223,6 +223,8 @@ ROUTER_SOFTMAX = "softmax"
 FMT_FP32 = "fp32"
 FMT_INT8_ROW = "int8_row"
 FMT_INT4_B32 = "int4_b32"
+FMT_INT4_B128 = "int4_b128"
+INT4_BLOCK = {FMT_INT4_B32: 32, FMT_INT4_B128: 128}
 
 KIMI_ROUTED_SCALE = float(np.float32(2.446))
 
@@ -292,6 +294,7 @@ class ExpertWeights:
     fmt == int4_b32: gu [E, 2I, d] int8 codes in [-8, 7], gu_s [E, 2I, d/32]
                      dn [E, d, I] int8 codes,               dn_s [E, d, I/32]
                      (gu_packed / dn_packed hold the nibble-packed copies)
+    fmt == int4_b128: as int4_b32 with scales [E, 2I, d/128] and [E, d, I/128]
     fmt == fp32:     gu [E, 2I, d] fp32, dn [E, d, I] fp32, no scales
     Rows 0..I-1 of gu are the gate projection, rows I..2I-1 the up projection.
     """
@@ -330,13 +333,14 @@ def make_experts(fmt: str, E: int, d: int, inter: int, seed: int, tids) -> Exper
         gu_s = scales(seed, t_gu_s, (E, 2 * inter), 1.0 / (127.0 * math.sqrt(d)))
         dn_s = scales(seed, t_dn_s, (E, d), 1.0 / (127.0 * math.sqrt(inter)))
         return ExpertWeights(fmt, E, d, inter, gu, dn, gu_s, dn_s)
-    if fmt == FMT_INT4_B32:
-        assert d % 32 == 0 and inter % 32 == 0
+    if fmt in INT4_BLOCK:
+        B = INT4_BLOCK[fmt]
+        assert d % B == 0 and inter % B == 0
         gu = randint8(seed, t_gu, (E, 2 * inter, d), -8, 7)
         dn = randint8(seed, t_dn, (E, d, inter), -8, 7)
-        gu_s = scales(seed, t_gu_s, (E, 2 * inter, d // 32), 1.0 / (8.0 * math.sqrt(d)),
+        gu_s = scales(seed, t_gu_s, (E, 2 * inter, d // B), 1.0 / (8.0 * math.sqrt(d)),
                       special_tid=t_gu_sp)
-        dn_s = scales(seed, t_dn_s, (E, d, inter // 32), 1.0 / (8.0 * math.sqrt(inter)),
+        dn_s = scales(seed, t_dn_s, (E, d, inter // B), 1.0 / (8.0 * math.sqrt(inter)),
                       special_tid=t_dn_sp)
         return ExpertWeights(fmt, E, d, inter, gu, dn, gu_s, dn_s,
                              pack_int4(gu), pack_int4(dn))
@@ -379,7 +383,7 @@ def expert_slice(s: LayerSpec, experts, shared: bool = False) -> ExpertWeights:
     inter = s.shared_inter if shared else s.inter
     d = s.d
     t_gu, t_gu_s, t_dn, t_dn_s, t_gu_sp, t_dn_sp = _SHARED_TIDS if shared else _ROUTED_TIDS
-    if fmt not in (FMT_INT8_ROW, FMT_INT4_B32):
+    if fmt not in (FMT_INT8_ROW, FMT_INT4_B32, FMT_INT4_B128):
         raise ValueError(f"expert_slice: format {fmt} is drawn whole only")
     n = len(experts)
     lo, hi = (-127, 127) if fmt == FMT_INT8_ROW else (-8, 7)
@@ -389,8 +393,9 @@ def expert_slice(s: LayerSpec, experts, shared: bool = False) -> ExpertWeights:
         gu_s = np.empty((n, 2 * inter), np.float32)
         dn_s = np.empty((n, d), np.float32)
     else:
-        gu_s = np.empty((n, 2 * inter, d // 32), np.float32)
-        dn_s = np.empty((n, d, inter // 32), np.float32)
+        B = INT4_BLOCK[fmt]
+        gu_s = np.empty((n, 2 * inter, d // B), np.float32)
+        dn_s = np.empty((n, d, inter // B), np.float32)
     c_gu = 1.0 / ((127.0 if fmt == FMT_INT8_ROW else 8.0) * math.sqrt(d))
     c_dn = 1.0 / ((127.0 if fmt == FMT_INT8_ROW else 8.0) * math.sqrt(inter))
     sp_gu, sp_dn = (0, 0) if fmt == FMT_INT8_ROW else (t_gu_sp, t_dn_sp)
@@ -401,7 +406,7 @@ def expert_slice(s: LayerSpec, experts, shared: bool = False) -> ExpertWeights:
         gu_s[q] = scales(s.wseed, t_gu_s, gu_s[q].shape, c_gu, sp_gu, start=e * gu_s[q].size)
         dn_s[q] = scales(s.wseed, t_dn_s, dn_s[q].shape, c_dn, sp_dn, start=e * dn_s[q].size)
     w = ExpertWeights(fmt, n, d, inter, gu, dn, gu_s, dn_s)
-    if fmt == FMT_INT4_B32:
+    if fmt in INT4_BLOCK:
         w.gu_packed, w.dn_packed = pack_int4(gu), pack_int4(dn)
     return w
 

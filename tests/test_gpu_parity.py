@@ -525,7 +525,7 @@ def test_abi_errors(ctx):
                       ws_bytes=16)
     assert e.value.status == B.MOE_E_WORKSPACE
     with pytest.raises(B.MoeError) as e:
-        ctx.moe_expert_ffn(L.experts, 1, x, 4, L.row_token, L.offsets, 32, L.rows, L.ws)
+        ctx.moe_expert_ffn(L.experts, 7, x, 4, L.row_token, L.offsets, 32, L.rows, L.ws)
     assert e.value.status == B.MOE_E_UNSUPPORTED and "activation" in str(e.value)
     with pytest.raises(B.MoeError) as e:
         ctx.moe_combine(L.rows, L.token_row, L.w, None, None, 4, 8, 510, L.y)

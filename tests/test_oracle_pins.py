@@ -596,3 +596,77 @@ def test_bf16_bits_to_f32():
     v = oracle.bf16_to_f32(bits)
     assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 0.0 and np.signbit(v[3])
     assert v[4] == np.float32(3.3895314e38) and v[5] == np.float32(2.0 ** -133)
+
+
+# ------------------------------------------------------------ gelu_tanh, int4 block 128
+
+def test_gelu_tanh_identities_and_erf_form():
+    # odd part: f(z) - f(-z) = z exactly (tanh is odd); f(0) = 0; the tails go
+    # to z and 0; and the tanh form stays within 5e-4 of the erf form z Phi(z)
+    for z in (0.0, 0.3, 1.0, 2.5, 7.0):
+        assert abs(oracle.gelu_tanh(z) - oracle.gelu_tanh(-z) - z) <= 1e-15 * max(1.0, z)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert abs(oracle.gelu_tanh(12.0) - 12.0) < 1e-12 and abs(oracle.gelu_tanh(-12.0)) < 1e-12
+    zs = np.linspace(-8.0, 8.0, 4001)
+    gap = max(abs(oracle.gelu_tanh(z) - 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))))
+              for z in zs)
+    assert 1e-4 < gap < 5e-4                    # an approximation, and a close one
+    # slope 1/2 at 0 (central difference)
+    h = 1e-6
+    assert abs((oracle.gelu_tanh(h) - oracle.gelu_tanh(-h)) / (2 * h) - 0.5) < 1e-9
+
+
+def test_gelu_tanh_layer_uses_the_activation():
+    # A layer run with gelu_tanh equals the staged pipeline with h computed by
+    # gelu_tanh: checked through one expert, gate row n, by the oracle's FFN
+    # on a one-hot weight layout (down = identity rows pick h_n out).
+    d, I = 32, 32
+    x = S.normal(0x6E10, 1, (d,), 1.0)
+    gu = np.zeros((1, 2 * I, d), np.float32)
+    gu[0, :I] = np.eye(I, d, dtype=np.float32)            # gate_n = x_n
+    gu[0, I:] = np.eye(I, d, dtype=np.float32)            # up_n = x_n
+    dn = np.eye(d, I, dtype=np.float32)[None]             # out_m = h_m
+    for act, f in (("silu", oracle.silu), ("gelu_tanh", oracle.gelu_tanh)):
+        out = oracle.ffn(oracle.Experts("fp32", gu, dn, act=act), 0, x)
+        want = np.array([f(float(v)) * float(v) for v in x])
+        assert np.allclose(out, want, rtol=1e-15, atol=0)
+
+
+def test_int4_b128_equals_b32_with_repeated_scales():
+    # A block-128 scale is the block-32 scale of each of its four sub-blocks:
+    # the layer with block-128 experts equals the layer with block-32 experts
+    # whose scales repeat each block-128 scale four times (clamp included).
+    T, d, E, k, I = 9, 256, 6, 2, 128
+    x = S.normal(0x6E20, 1, (T, d), 1.0)
+    wr = S.normal(0x6E20, 2, (E, d), 1.0 / math.sqrt(d))
+    bias = S.uniform(0x6E20, 3, (E,), -0.1, 0.1)
+    gu = S.randint8(0x6E20, 4, (E, 2 * I, d), -8, 7)
+    dn = S.randint8(0x6E20, 5, (E, d, I), -8, 7)
+    sg = S.scales(0x6E20, 6, (E, 2 * I, d // 128), 0.02)
+    sd = S.scales(0x6E20, 7, (E, d, I // 128), 0.02)
+    sg[:, 3, 1] = 1e-6                                    # below the 2^-14 floor
+    sd[:, 5, 0] = 0.0
+    e128 = oracle.Experts("int4_b128", gu, dn, sg, sd)
+    e32 = oracle.Experts("int4_b32", gu, dn, np.repeat(sg, 4, axis=2), np.repeat(sd, 4, axis=2))
+    y1, i1, w1, _ = oracle.layer("sigmoid_bias", k, K_SCALE, x, wr, bias, e128)
+    y2, i2, w2, _ = oracle.layer("sigmoid_bias", k, K_SCALE, x, wr, bias, e32)
+    assert np.array_equal(i1, i2) and np.array_equal(y1, y2)
+    # and differs from reading the scales as block-32 (the first quarter)
+    e_wrong = oracle.Experts("int4_b32", gu, dn, np.repeat(sg, 4, axis=2)[:, :, ::-1].copy(),
+                             np.repeat(sd, 4, axis=2))
+    y3, _, _, _ = oracle.layer("sigmoid_bias", k, K_SCALE, x, wr, bias, e_wrong)
+    assert not np.allclose(y1, y3)
+
+
+def test_quantize_int4_b128_scale_is_max_of_b32_scales():
+    # RN(max/7) is monotone in the maximum, so a block-128 scale is the largest
+    # of its four block-32 scales (before and after the 2^-14 floor), and the
+    # round trip stays within half a scale.
+    w = S.normal(0x6E30, 1, (40, 512), 0.02)
+    w[7] *= 1e-5
+    q128, s128 = oracle.quantize("int4_b128", w)
+    q32, s32 = oracle.quantize("int4_b32", w)
+    assert np.array_equal(s128, s32.reshape(40, -1, 4).max(axis=2))
+    sb = np.repeat(s128, 128, axis=1).astype(np.float64)
+    assert (np.abs(q128 * sb - w) <= sb * (0.5 + 2.0 ** -20)).all()
+    assert q128.min() >= -7 and q128.max() <= 7 and (s128[7] == np.float32(2.0 ** -14)).all()
