@@ -80,6 +80,10 @@ STACK_WORKLOADS = {
     "kimi_stack_prefill": (4096, "stack of 26 distinct Kimi-shaped MoE layers with the residual "
                                  "between layers, T=4096 prefill, Zipf-skewed selection bias, "
                                  "int8 experts and shared expert, ~95 GB of weights"),
+    "qwen_stack_decode": (1, "stack of 48 distinct Qwen3-shaped MoE layers with the residual "
+                             "between layers, T=1 decode, d=2048, E=128, softmax top-8, I=768, "
+                             "int4 block-32 experts, no shared expert, ~18 GB of weights; the "
+                             "48 layers replayed as one HIP graph"),
 }
 
 
@@ -179,11 +183,13 @@ def cpu_baseline_stack(st, budget_s: float):
         remap = np.full(s.E, -1, np.int64)
         remap[uniq] = np.arange(len(uniq))
         ex = oracle.Experts.of(S.expert_slice(s, uniq))
-        sh = oracle.Experts.of(S.expert_slice(s, [0], shared=True))
+        sh = (oracle.Experts.of(S.expert_slice(s, [0], shared=True))
+              if s.shared is not None else None)
         t0 = time.perf_counter()
         offsets, row_token, token_row = oracle.permute(remap[idx].astype(np.int32), len(uniq))
         rows = oracle.expert_rows(ex, x, row_token, offsets)
-        shr = oracle.expert_rows(sh, x, None, np.array([0, n_tok], np.int32))
+        shr = (oracle.expert_rows(sh, x, None, np.array([0, n_tok], np.int32))
+               if sh is not None else None)
         y = oracle.combine(rows, token_row, w, shared=shr, residual=x)
         spent += time.perf_counter() - t0
         x = y.astype(np.float32)
@@ -206,7 +212,7 @@ def run_stack(args):
     decode = T <= 16
     steps = args.steps or (50 if decode else 5)
     warmup = args.warmup if args.warmup is not None else (5 if decode else 1)
-    st = S.stack_spec(T)
+    st = S.qwen_stack_spec(T) if args.workload.startswith("qwen") else S.stack_spec(T)
     if args.layers is not None:
         st = S.StackSpec(st.name, args.layers, st.T, st.alpha, st.base)
     dev = torch.device("cuda:0")
@@ -252,14 +258,19 @@ def run_stack(args):
     # ---- algorithmic work, from each layer's actual routing
     s0 = st.layer(0)
     d, I, Is, E, k = s0.d, s0.inter, s0.shared_inter, s0.E, s0.k
-    e_gu, e_dn = 2 * I * d + 2 * I * 4, d * I + d * 4          # codes + fp32 row scales
-    sh_gu, sh_dn = 2 * Is * d + 2 * Is * 4, d * Is + d * 4
+    int4 = s0.fmt in S.INT4_BLOCK
+    if int4:  # packed codes + one fp32 scale per block
+        B = S.INT4_BLOCK[s0.fmt]
+        e_gu, e_dn = I * d + 2 * I * (d // B) * 4, d * I // 2 + d * (I // B) * 4
+    else:     # codes + fp32 row scales
+        e_gu, e_dn = 2 * I * d + 2 * I * 4, d * I + d * 4
+    sh_gu, sh_dn = (2 * Is * d + 2 * Is * 4, d * Is + d * 4) if Is else (0, 0)
     touched, masses = [], []
     for l in range(st.layers):
         counts = np.bincount(stk.idx[l].cpu().numpy().ravel(), minlength=E)
         touched.append(int((counts > 0).sum()))
         masses.append(round(float(np.sort(counts)[::-1][:64].sum()) / counts.sum(), 4))
-    router_b = (E * d + E) * 4
+    router_b = (E * d + (E if s0.router == "sigmoid_bias" else 0)) * 4
     step_bytes = sum(n * (e_gu + e_dn) + sh_gu + sh_dn + router_b + T * d * 4 * 2
                      for n in touched)
     step_flops = st.layers * 2.0 * (T * k * 3 * d * I + T * 3 * d * Is + T * d * E)
@@ -290,14 +301,15 @@ def run_stack(args):
                         "flops_per_launch": per_launch,
                         "avg_launch_us": round(avg_s * 1e6, 2),
                         "frac_of_bf16_peak": round(achieved / BF16_PEAK_TFLOPS, 4)}
-        elif "ffn_i8_gate_up" in kt:
-            launches, tot_ms = kt["ffn_i8_gate_up"]
+        elif "ffn_i8_gate_up" in kt or "ffn_i4_gate_up" in kt:
+            kname = "ffn_i4_gate_up" if int4 else "ffn_i8_gate_up"
+            launches, tot_ms = kt[kname]
             per_step = sum(n * e_gu + sh_gu + T * d * 2 + (R * I + T * Is) * 2
                            + (R * I + T * Is) // 64 * 4 for n in touched)
             per_launch = per_step / (launches / steps)
             avg_s = tot_ms / launches / 1e3
             achieved = per_launch / avg_s / 1e9
-            roofline = {"bound": "hbm", "kernel": "ffn_i8_gate_up",
+            roofline = {"bound": "hbm", "kernel": kname,
                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4),
                         "traffic": counter_traffic(args.workload, "gate_up_kernel<"),
@@ -321,7 +333,7 @@ def run_stack(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "int4" if int4 else "int8",
         "data": "synthetic (seeded generator, weights drawn on the GPU; random weights of the "
                 "stated shapes)",
         "config": {"workload": desc, "T": T, "layers": st.layers, "d": d, "E": E, "k": k,

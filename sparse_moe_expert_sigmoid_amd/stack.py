@@ -100,27 +100,35 @@ class MoEStack:
     @staticmethod
     def from_synth(ctx: Context, st, device="cuda:0", layers: Optional[int] = None,
                    log: Optional[Callable[[str], None]] = None) -> "MoEStack":
-        """Builds the Kimi-shaped stack `st` (a synth.StackSpec): router weights
-        and biases drawn on the host, expert codes and scales drawn on the GPU
-        by the generator's device twin, codes converted to the tiled layout."""
+        """Builds the stack `st` (a synth.StackSpec: the Kimi-shaped int8 stack
+        or the Qwen3-shaped int4 one): router weights and biases drawn on the
+        host, expert codes and scales drawn on the GPU by the generator's
+        device twin, codes converted to the tiled layout."""
         from . import synth
+        from .binding import FMT
         n = st.layers if layers is None else layers
         out = []
         for l in range(n):
             s = st.layer(l)
             wr, bias = synth.stack_router(st, l)
-            parts = []
-            for shared in (False, True):
-                gu, gu_s, dn, dn_s = synth.dev_int8_experts(s, device, shared=shared)
-                E = 1 if shared else s.E
-                inter = s.shared_inter if shared else s.inter
-                rows = DeviceExperts(MOE_W_INT8_ROW, E, s.d, inter, gu, dn, gu_s, dn_s)
-                parts.append(rows.tiled(ctx))
+            if s.fmt == synth.FMT_INT8_ROW:
+                gu, gu_s, dn, dn_s = synth.dev_int8_experts(s, device)
+            else:
+                gu, gu_s, dn, dn_s = synth.dev_int4_experts(s, device)
+            rows = DeviceExperts(FMT[s.fmt], s.E, s.d, s.inter, gu, dn, gu_s, dn_s)
+            routed = rows.tiled(ctx)
+            del rows, gu, dn
+            shared = None
+            if s.shared is not None:
+                gu, gu_s, dn, dn_s = synth.dev_int8_experts(s, device, shared=True)
+                rows = DeviceExperts(MOE_W_INT8_ROW, 1, s.d, s.shared_inter, gu, dn, gu_s, dn_s)
+                shared = rows.tiled(ctx)
                 del rows, gu, dn
             L = MoELayer(ctx, s.router, s.k, s.scale, torch.from_numpy(wr).to(device),
-                         torch.from_numpy(bias).to(device), parts[0], parts[1])
+                         torch.from_numpy(bias).to(device) if bias is not None else None,
+                         routed, shared)
             out.append(L)
-            if log is not None and (l == 0 or (l + 1) % 5 == 0 or l + 1 == n):
+            if log is not None and (l == 0 or (l + 1) % 8 == 0 or l + 1 == n):
                 torch.cuda.synchronize()
                 log(f"[stack] layer {l + 1}/{n} built")
         torch.cuda.synchronize()

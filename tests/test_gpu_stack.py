@@ -1,5 +1,5 @@
-"""GPU: the generator's device twin, and the 26-layer Kimi-shaped stack
-against the oracle.
+"""GPU: the generator's device twin, the 26-layer Kimi-shaped stack and the
+48-layer Qwen3-shaped int4 stack against the oracle.
 
 The stack (26 distinct layers, d=2304, E=256, top 8, I=2048, int8 per-row
 experts and shared expert, Zipf-skewed selection bias) holds about 95 GB of
@@ -12,6 +12,11 @@ the real load: expert row counts, tile shapes and kernel choices at T=4096.
 The oracle draws only the experts the sampled tokens select.  The
 free-running 26-layer difference is reported but not asserted: one excused
 near-tie flip legitimately changes everything downstream.
+
+The Qwen3-shaped stack (48 distinct layers, d=2048, E=128, softmax top 8,
+I=768, int4 block-32 experts, no shared expert; about 18 GB drawn on the GPU)
+is checked the same way at decode (T=1 and a few tokens) and through a HIP
+graph of all 48 layers.
 """
 import numpy as np
 import pytest
@@ -99,11 +104,13 @@ class _OracleStack:
         remap[uniq] = np.arange(len(uniq))
         idx_c = remap[idx].astype(np.int32)
         ex = oracle.Experts.of(S.expert_slice(s, uniq))
-        sh = oracle.Experts.of(S.expert_slice(s, [0], shared=True))
         offsets, row_token, token_row = oracle.permute(idx_c, len(uniq))
         rows = oracle.expert_rows(ex, x, row_token, offsets)
-        n = x.shape[0]
-        shr = oracle.expert_rows(sh, x, None, np.array([0, n], np.int32))
+        shr = None
+        if s.shared is not None:
+            sh = oracle.Experts.of(S.expert_slice(s, [0], shared=True))
+            n = x.shape[0]
+            shr = oracle.expert_rows(sh, x, None, np.array([0, n], np.int32))
         y = oracle.combine(rows, token_row, w, shared=shr)
         keys = oracle_keys(s.router, logits, bias)
         return idx, w, gap, keys, y
@@ -117,9 +124,9 @@ class _OracleStack:
         return self
 
 
-def _stack_teacher_forced(st, stk, T, sample):
+def _stack_teacher_forced(st, stk, T, sample, x_all=None):
     import torch
-    x0 = S.stack_x(S.stack_spec(4096))[:T]
+    x0 = (S.stack_x(S.stack_spec(4096)) if x_all is None else x_all)[:T]
     sample = np.asarray(sample)
     orc = _OracleStack(st, x0[sample]).run()
     xd = torch.from_numpy(np.ascontiguousarray(x0)).to("cuda:0")
@@ -177,11 +184,14 @@ def test_stack_decode_T1_teacher_forced(stack):
 
 
 def test_stack_decode_graph_replays_match_eager(stack):
+    _graph_replays_match_eager(stack[1], S.stack_x(S.stack_spec(1)))
+
+
+def _graph_replays_match_eager(stk, x0_host):
     """The T=1 stack captured in a HIP graph: every replay, with eager work
     and synchronisations between replays, equals the eager run bit-exactly."""
     import torch
-    st, stk = stack
-    x0 = torch.from_numpy(S.stack_x(S.stack_spec(1))).to("cuda:0")
+    x0 = torch.from_numpy(x0_host).to("cuda:0")
     eager = stk.forward(x0).clone()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -201,3 +211,54 @@ def test_stack_decode_graph_replays_match_eager(stack):
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep}"
     del g
+
+
+# ------------------------------------------------------------ the Qwen3-shaped int4 stack
+
+def test_device_int4_generator_bit_exact(ctx):
+    import torch
+    s = S.spec("qwen_decode")
+    gu, gu_s, dn, dn_s = S.dev_int4_experts(s, "cuda:0")
+    torch.cuda.synchronize()
+    for e in (0, 63, 127):
+        h = S.expert_slice(s, [e])
+        assert np.array_equal(gu[e].cpu().numpy(), h.gu_packed[0])
+        assert np.array_equal(dn[e].cpu().numpy(), h.dn_packed[0])
+        assert np.array_equal(gu_s[e].cpu().numpy().view(np.uint32), h.gu_s[0].view(np.uint32))
+        assert np.array_equal(dn_s[e].cpu().numpy().view(np.uint32), h.dn_s[0].view(np.uint32))
+    del gu, gu_s, dn, dn_s
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def qwen_stack(ctx):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import MoEStack
+    st = S.qwen_stack_spec(1)
+    print(f"[qwen stack] building {st.layers} layers on the GPU", flush=True)
+    stk = MoEStack.from_synth(ctx, st, log=lambda m: print(m, flush=True))
+    print(f"[qwen stack] {stk.weight_bytes / 1e9:.1f} GB of weights", flush=True)
+    yield st, stk
+    del stk
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _qwen_x(T):
+    return S.stack_x(S.qwen_stack_spec(T))
+
+
+def test_qwen_stack_decode_T1_teacher_forced(qwen_stack):
+    st, stk = qwen_stack
+    res = _stack_teacher_forced(st, stk, 1, [0], x_all=_qwen_x(1))
+    assert len(res) == 48
+
+
+def test_qwen_stack_decode_T4_teacher_forced(qwen_stack):
+    st, stk = qwen_stack
+    res = _stack_teacher_forced(st, stk, 4, [0, 3], x_all=_qwen_x(4))
+    assert len(res) == 48
+
+
+def test_qwen_stack_decode_graph_replays_match_eager(qwen_stack):
+    _graph_replays_match_eager(qwen_stack[1], _qwen_x(1))

@@ -88,3 +88,19 @@ def test_stored_zipf_alpha_gives_target_mass():
     mass = np.sort(counts)[::-1][:64].sum() / idx.size
     assert abs(mass - 0.73) <= 0.01, mass
     assert abs(mass - rec["mass_layer0_T4096"]) < 1e-4
+
+
+def test_qwen_stack_spec_layers():
+    st = S.qwen_stack_spec(1)
+    assert st.layers == 48 and st.base.fmt == "int4_b32" and st.base.shared is None
+    seeds = {st.layer(l).wseed for l in range(48)}
+    assert len(seeds) == 48
+    s = st.layer(7)
+    assert (s.d, s.E, s.k, s.inter, s.router) == (2048, 128, 8, 768, "softmax")
+    wr, bias = S.stack_router(st, 7)
+    assert wr.shape == (128, 2048) and bias is None
+    # distinct from the Kimi stack's seeds
+    assert not seeds & {S.stack_spec(1).layer(l).wseed for l in range(26)}
+    x = S.stack_x(st)
+    assert x.shape == (1, 2048)
+    assert np.array_equal(S.stack_x(S.qwen_stack_spec(4))[:1], x)
