@@ -602,8 +602,10 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
   if (small) {
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, fused ? 2 : 1, Rs, Is, true);
+    // x digits in the order the routed experts' kernels read (int4: permuted)
+    const bool perm = X.fmt == MOE_W_INT4_B32 || X.fmt == MOE_W_INT4_B128;
     e = moe::launch_router_small(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
-                                 k, L->scale, idx, w, f.partial, lay.xq, lay.xs, s);
+                                 k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, s);
   } else {
     e = moe::launch_router(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E, k,
                            L->scale, idx, w, f.partial, s);

@@ -39,14 +39,29 @@ namespace moe {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef long v2l __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// A load through a pointer the compiler knows to be global.  Where a kernel
+// mixes LDS and global pointers the address-space inference can give up and
+// emit flat loads, which also count against the LDS wait counter: every wait
+// for an LDS read then waits for the weight stream as well.
+template <class T>
+__device__ inline T gload(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ inline T gload_nt(const void* p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)p);
+}
 
 // One wavefront per row (see encode_row).
 __global__ __launch_bounds__(256) void encode_rows_kernel(const float* __restrict__ v, int n,
                                                           int K, int8_t* __restrict__ q,
-                                                          float* __restrict__ sig) {
+                                                          float* __restrict__ sig, bool perm) {
   const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (r >= n) return;
-  encode_row(v + (size_t)r * K, K, q + (size_t)r * 2 * K, sig + r);
+  encode_row(v + (size_t)r * K, K, q + (size_t)r * 2 * K, sig + r, perm);
 }
 
 // ------------------------------------------------------------------ work items
@@ -108,6 +123,21 @@ __device__ inline bool find_rows(const Group& g0, const Group& g1, int mt, int t
     for (int j = threadIdx.x; j < tl.nr; j += blockDim.x) {
       rows[j] = tl.r0 + j;
       if (need_toks) toks[j] = G.row_token ? G.row_token[tl.r0 + j] : tl.r0 + j;
+    }
+    __syncthreads();
+    return true;
+  }
+  if (G.R == G.k && mt == 1) {
+    // one token: its k experts are distinct, so tile t is slot t alone (the
+    // same rows, in another tile order, as the histogram path below)
+    const int e = G.pairs_idx[t];
+    if (e < 0 || e >= G.E) return false;
+    job.e = e;
+    job.r0 = 0;
+    job.nr = 1;
+    if (threadIdx.x == 0) {
+      rows[0] = t;
+      if (need_toks) toks[0] = 0;
     }
     __syncthreads();
     return true;
@@ -191,13 +221,12 @@ __device__ inline const int8_t* i8_operand_base(const int8_t* W, size_t row0, in
 }
 template <int LAY>
 __device__ inline v4i i8_load(const int8_t* base, int step) {
-  return __builtin_nontemporal_load(
-      reinterpret_cast<const v4i*>(base + (LAY == kRows ? 64 : 1024) * step));
+  return gload_nt<v4i>(base + (LAY == kRows ? 64 : 1024) * step);
 }
 // Ordinary (cached) load: for weights that several tiles of one expert read.
 template <int LAY>
 __device__ inline v4i i8_load_cached(const int8_t* base, int step) {
-  return *reinterpret_cast<const v4i*>(base + (LAY == kRows ? 64 : 1024) * step);
+  return gload<v4i>(base + (LAY == kRows ? 64 : 1024) * step);
 }
 
 template <int LAY>
@@ -208,26 +237,27 @@ __device__ inline const uint8_t* i4_operand_base(const uint8_t* W, size_t row0, 
 // the 4 words (one per block of 32) of span m
 template <int LAY>
 __device__ inline v4i i4_load(const uint8_t* base, int m) {
-  if (LAY == kTiled)
-    return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(base + 1024 * m));
-  const unsigned* p = reinterpret_cast<const unsigned*>(base + 64 * m);
-  return v4i{(int)p[0], (int)p[4], (int)p[8], (int)p[12]};
+  if (LAY == kTiled) return gload_nt<v4i>(base + 1024 * m);
+  const uint8_t* p = base + 64 * m;
+  return v4i{gload<int>(p), gload<int>(p + 16), gload<int>(p + 32), gload<int>(p + 48)};
 }
 
 // ------------------------------------------------------------------ int4
-// 8 codes of one 4-byte word -> 8 sign-extended bytes in element order.
-__device__ inline long unpack8_int4(unsigned w) {
-  const unsigned lo = w & 0x0F0F0F0Fu;          // elements 0,2,4,6
-  const unsigned hi = (w >> 4) & 0x0F0F0F0Fu;   // elements 1,3,5,7
-  // nibble n -> byte n - 16*(n >= 8): ((n ^ 0x88) - 0x08) ^ 0x80, bytewise, no borrows
-  const unsigned slo = ((lo ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u;
-  const unsigned shi = ((hi ^ 0x88888888u) - 0x08080808u) ^ 0x80808080u;
-  const unsigned o0 = __builtin_amdgcn_perm(shi, slo, 0x05010400u);  // e0 e1 e2 e3
-  const unsigned o1 = __builtin_amdgcn_perm(shi, slo, 0x07030602u);  // e4 e5 e6 e7
-  return (long)(((unsigned long)o1 << 32) | o0);
+// 8 codes of one 4-byte word (code 2b in the low nibble of byte b, code 2b+1
+// in the high nibble) -> 8 bytes holding 16 * code, in the order
+// (0, 2, 4, 6, 1, 3, 5, 7): the low nibbles shifted into the high half of each
+// byte, the high nibbles masked in place.  A nibble in the high half of a byte
+// reads as the signed byte 16 * code (two's complement), so three operations
+// unpack 8 codes; the activation digits are stored in the same order (encode8)
+// and the factor 16 goes into the block scale.
+__device__ inline long unpack8_int4_x16(unsigned w) {
+  const unsigned even = (w << 4) & 0xF0F0F0F0u;  // codes 0, 2, 4, 6
+  const unsigned odd = w & 0xF0F0F0F0u;          // codes 1, 3, 5, 7
+  return (long)(((unsigned long)odd << 32) | even);
 }
 
 constexpr float kScaleFloor = 1.0f / 16384.0f;  // int4 block scales are raised to 2^-14
+constexpr float kInv16 = 1.0f / 16.0f;          // the unpacked codes carry a factor 16
 
 // ------------------------------------------------------------------ gate/up
 // FMT 1: int8 rows; FMT 2: int4 blocks of 32.  Block = 4*KS wavefronts:
@@ -258,27 +288,49 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
   }
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
-  const int ldr = 2 * d + 16;
-  {
-    const int per_row = (2 * d) / 16;
-    for (int q = threadIdx.x; q < job.nr * per_row; q += blockDim.x) {
-      const int j = q / per_row, c = q % per_row;
-      const int src = PAIRS ? toks_sm[j] : G.row_token ? G.row_token[job.r0 + j] : job.r0 + j;
-      *reinterpret_cast<v4i*>(lds + j * ldr + 16 * c) =
-          *reinterpret_cast<const v4i*>(xq + (size_t)src * 2 * d + 16 * c);
-    }
-    __syncthreads();
-  }
-
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
   const int i = lane & 15, g = lane >> 4;
-  const bool jv = i < job.nr;
-  const int r = !jv ? 0 : PAIRS ? rows_sm[i] : job.r0 + i;
-  const int tok = !jv ? 0 : PAIRS ? toks_sm[i] : (G.row_token ? G.row_token[r] : r);
-  const int8_t* xb0 = lds + i * ldr;
+  // x digits of the tile rows.  Small batches (PAIRS) read their few token
+  // rows straight from L2: no staging barrier before the weight loads, no LDS
+  // to limit how many workgroups a CU holds.  Tiles of up to 16 rows stage them
+  // in LDS (measured faster there).  A rows past the tile (i >= nr) read a real
+  // row again: their products land in accumulator rows that are never stored,
+  // and unconditional loads keep the compiler's count of loads in flight exact.
+  // (the lambdas capture scalars by value: a reference to the selected Group
+  // would keep the struct in private memory, with every pointer read from it
+  // losing its address space)
+  const int32_t* const row_token = G.row_token;
+  const int r0 = job.r0, nr = job.nr;
+  auto tile_tok = [=](int j) {
+    return PAIRS ? toks_sm[j] : row_token ? gload<int>(row_token + r0 + j) : r0 + j;
+  };
+  const int8_t* xb0;
+  if (PAIRS) {
+    xb0 = xq + (size_t)tile_tok(min(i, job.nr - 1)) * 2 * d;
+  } else {
+    const int ldr = 2 * d + 16;
+    const int per_row = (2 * d) / 16;
+    for (int q = threadIdx.x; q < job.nr * per_row; q += blockDim.x) {
+      const int j = q / per_row, c = q % per_row;
+      *reinterpret_cast<v4i*>(lds + j * ldr + 16 * c) =
+          *reinterpret_cast<const v4i*>(xq + (size_t)tile_tok(j) * 2 * d + 16 * c);
+    }
+    __syncthreads();
+    xb0 = lds + min(i, job.nr - 1) * ldr;
+  }
   const int8_t* xb1 = xb0 + d;
-  const float sigx = jv ? xs[tok] : 0.0f;
+  // x scale of tile rows 4g+c: loaded only after the main loop, unconditionally
+  // from clamped rows, so no load in front of the loop is conditional
+  auto x_scale = [=](int c) {
+    const float v = gload<float>(xs + tile_tok(min(4 * g + c, nr - 1)));
+    return 4 * g + c < nr ? v : 0.0f;
+  };
+
+  // Operands: A = the tile's activation digits (A row = tile row lane % 16),
+  // B = 16 weight rows as stored (B column = h column c0 + lane % 16).  A lane's
+  // accumulator c is tile row 4 g + c of h column c0 + i, so each lane needs
+  // the scale of one weight row only (one per int4 block).
 
 #pragma unroll 1
   for (int cbi = 0; cbi < NCB; ++cbi) {
@@ -303,21 +355,20 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
           const int ss = min(s + u, s_end - 1);
           ra[u] = i8_load<LAY>(wa, ss);
           rb[u] = i8_load<LAY>(wb, ss);
-          x0[u] = v4i{0, 0, 0, 0};
-          x1[u] = v4i{0, 0, 0, 0};
-          if (jv) {
-            x0[u] = *reinterpret_cast<const v4i*>(xb0 + ss * kKStep + 16 * g);
-            x1[u] = *reinterpret_cast<const v4i*>(xb1 + ss * kKStep + 16 * g);
-          }
+          x0[u] = *reinterpret_cast<const v4i*>(xb0 + ss * kKStep + 16 * g);
+          x1[u] = *reinterpret_cast<const v4i*>(xb1 + ss * kKStep + 16 * g);
         }
+        // steps past the slice (the last batch) multiply zero activations: no
+        // branch, so the compiler keeps every load of the batch in front
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (s + u < s_end) {
-            a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x0[u], a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[u], x1[u], a1, 0, 0, 0);
-            b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x0[u], b0, 0, 0, 0);
-            b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(rb[u], x1[u], b1, 0, 0, 0);
-          }
+          const bool ok = s + u < s_end;
+          const v4i z = {0, 0, 0, 0};
+          const v4i xa = ok ? x0[u] : z, xb = ok ? x1[u] : z;
+          a0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, ra[u], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb, ra[u], a1, 0, 0, 0);
+          b0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, rb[u], b0, 0, 0, 0);
+          b1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xb, rb[u], b1, 0, 0, 0);
         }
       }
       // exact int32 reduction of the K slices (order-free)
@@ -342,75 +393,100 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
         }
       }
       const float* se = G.sgu + (size_t)job.e * 2 * I;
+      const float sgate = gload<float>(se + c0 + i), sup = gload<float>(se + I + c0 + i);
+      float sx[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sx[c] = x_scale(c);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int n = c0 + 4 * g + c;
-        gate[c] = se[n] * sigx * ((float)a0[c] + (float)a1[c] * (1.0f / 256.0f));
-        up[c] = se[I + n] * sigx * ((float)b0[c] + (float)b1[c] * (1.0f / 256.0f));
+        gate[c] = sgate * sx[c] * ((float)a0[c] + (float)a1[c] * (1.0f / 256.0f));
+        up[c] = sup * sx[c] * ((float)b0[c] + (float)b1[c] * (1.0f / 256.0f));
       }
     } else {
-      // int4: one 16x16x32 MFMA pair per 32 inputs.  Blocks of 32 (FMT 2):
-      // each block's int32 sum (256*d0-part + d1-part, exact in fp32 since
-      // |.| < 2^24) is scaled by max(s, 2^-14) into the fp32 accumulator.
-      // Blocks of 128 (FMT 3) are the 128-input spans: the span's four MFMA
-      // pairs accumulate in int32 and the digits join once per span.
+      // int4: one 16x16x32 MFMA pair per 32 inputs on codes unpacked as
+      // 16 * code.  Blocks of 32 (FMT 2): each block's two int32 digit sums
+      // join as 256 p0 + p1 in int32 (below 2^28, rounded once to fp32) and are
+      // scaled by max(s, 2^-14) / 16 into the fp32 accumulator.  Blocks of 128
+      // (FMT 3) are the 128-input spans: the span's four MFMA pairs accumulate
+      // in int32 and join once per span.  U spans (codes and their scales) are
+      // loaded before any is used.
       const int nb = d / (FMT == 3 ? 128 : 32), nspan = d / 128;
       const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
       const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wgu), row0, d, i,
                                                g, lane);
       const uint8_t* wb = wa + (size_t)I * (d / 2);
-      const float* sa = G.sgu + ((size_t)job.e * 2 * I + c0 + 4 * g) * nb;
+      const float* sa = G.sgu + ((size_t)job.e * 2 * I + c0 + i) * nb;  // this lane's rows
       const float* sb = sa + (size_t)I * nb;
       float fa[4] = {0.f, 0.f, 0.f, 0.f}, fb[4] = {0.f, 0.f, 0.f, 0.f};
       const v4i zero = {0, 0, 0, 0};
-      for (int m = m_beg; m < m_end; ++m) {
-        const v4i wa4 = i4_load<LAY>(wa, m);
-        const v4i wb4 = i4_load<LAY>(wb, m);
-        long x0[4], x1[4];
+      constexpr int U = 2;
+      for (int m0 = m_beg; m0 < m_end; m0 += U) {
+        v4i wa4[U], wb4[U];
+        v4f s1[U], s2[U];
+        v2l xa[U][2], xc[U][2];  // digit 0 and 1 of the lane's 4 groups (span order)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          x0[q] = 0;
-          x1[q] = 0;
-          if (jv) {
-            x0[q] = *reinterpret_cast<const long*>(xb0 + 128 * m + 32 * q + 8 * g);
-            x1[q] = *reinterpret_cast<const long*>(xb1 + 128 * m + 32 * q + 8 * g);
+        for (int u = 0; u < U; ++u) {
+          const int m = min(m0 + u, m_end - 1);
+          wa4[u] = i4_load<LAY>(wa, m);
+          wb4[u] = i4_load<LAY>(wb, m);
+          if constexpr (FMT == 2) {
+            s1[u] = gload<v4f>(sa + 4 * m);
+            s2[u] = gload<v4f>(sb + 4 * m);
+          } else {
+            s1[u] = v4f{gload<float>(sa + m), 0.f, 0.f, 0.f};
+            s2[u] = v4f{gload<float>(sb + m), 0.f, 0.f, 0.f};
           }
+          const v2l* p0 = reinterpret_cast<const v2l*>(xb0 + 128 * m + 32 * g);
+          const v2l* p1 = reinterpret_cast<const v2l*>(xb1 + 128 * m + 32 * g);
+          xa[u][0] = p0[0];
+          xa[u][1] = p0[1];
+          xc[u][0] = p1[0];
+          xc[u][1] = p1[1];
         }
-        if constexpr (FMT == 2) {
+        // spans past the slice (the last batch) multiply zero activations: no
+        // branch, so the compiler keeps every load of the batch in front
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int b = 4 * m + q;
-            const long qa = unpack8_int4((unsigned)wa4[q]);
-            const long qb = unpack8_int4((unsigned)wb4[q]);
-            const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], zero, 0, 0, 0);
-            const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], zero, 0, 0, 0);
-            const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], zero, 0, 0, 0);
-            const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], zero, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+          const long on = m0 + u < m_end ? -1L : 0L;
+          const long x0[4] = {xa[u][0].x & on, xa[u][0].y & on, xa[u][1].x & on, xa[u][1].y & on};
+          const long x1[4] = {xc[u][0].x & on, xc[u][0].y & on, xc[u][1].x & on, xc[u][1].y & on};
+          if constexpr (FMT == 2) {
+            const float ss1[4] = {s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+            const float ss2[4] = {s2[u].x, s2[u].y, s2[u].z, s2[u].w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float s1 = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
-              const float s2 = fmaxf(sb[(size_t)c * nb + b], kScaleFloor);
-              fa[c] = fmaf(s1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
-              fb[c] = fmaf(s2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+            for (int q = 0; q < 4; ++q) {
+              const long qa = unpack8_int4_x16((unsigned)wa4[u][q]);
+              const long qb = unpack8_int4_x16((unsigned)wb4[u][q]);
+              const v4i pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[q], qa, zero, 0, 0, 0);
+              const v4i pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[q], qa, zero, 0, 0, 0);
+              const v4i pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[q], qb, zero, 0, 0, 0);
+              const v4i pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[q], qb, zero, 0, 0, 0);
+              const float t1 = fmaxf(ss1[q], kScaleFloor) * kInv16;
+              const float t2 = fmaxf(ss2[q], kScaleFloor) * kInv16;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                fa[c] = fmaf(t1, (float)(pa0[c] * 256 + pa1[c]), fa[c]);
+                fb[c] = fmaf(t2, (float)(pb0[c] * 256 + pb1[c]), fb[c]);
+              }
             }
-          }
-        } else {
-          v4i pa0 = zero, pa1 = zero, pb0 = zero, pb1 = zero;
+          } else {
+            v4i pa0 = zero, pa1 = zero, pb0 = zero, pb1 = zero;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const long qa = unpack8_int4((unsigned)wa4[q]);
-            const long qb = unpack8_int4((unsigned)wb4[q]);
-            pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x0[q], pa0, 0, 0, 0);
-            pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa, x1[q], pa1, 0, 0, 0);
-            pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x0[q], pb0, 0, 0, 0);
-            pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(qb, x1[q], pb1, 0, 0, 0);
-          }
+            for (int q = 0; q < 4; ++q) {
+              const long qa = unpack8_int4_x16((unsigned)wa4[u][q]);
+              const long qb = unpack8_int4_x16((unsigned)wb4[u][q]);
+              pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[q], qa, pa0, 0, 0, 0);
+              pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[q], qa, pa1, 0, 0, 0);
+              pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[q], qb, pb0, 0, 0, 0);
+              pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[q], qb, pb1, 0, 0, 0);
+            }
+            const float t1 = fmaxf(s1[u].x, kScaleFloor) * kInv16;
+            const float t2 = fmaxf(s2[u].x, kScaleFloor) * kInv16;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {  // |p0| < 2^17: each digit sum exact in fp32
-            const float s1 = fmaxf(sa[(size_t)c * nb + m], kScaleFloor);
-            const float s2 = fmaxf(sb[(size_t)c * nb + m], kScaleFloor);
-            fa[c] = fmaf(s1, fmaf((float)pa0[c], 256.0f, (float)pa1[c]), fa[c]);
-            fb[c] = fmaf(s2, fmaf((float)pb0[c], 256.0f, (float)pb1[c]), fb[c]);
+            for (int c = 0; c < 4; ++c) {  // |p0| < 2^22: each digit sum exact in fp32
+              fa[c] = fmaf(t1, fmaf((float)pa0[c], 256.0f, (float)pa1[c]), fa[c]);
+              fb[c] = fmaf(t2, fmaf((float)pb0[c], 256.0f, (float)pb1[c]), fb[c]);
+            }
           }
         }
       }
@@ -429,38 +505,50 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
           }
         }
       }
-      const float sig = sigx * (1.0f / 256.0f);
+      float sx[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sx[c] = x_scale(c);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        const float sig = sx[c] * (1.0f / 256.0f);
         gate[c] = fa[c] * sig;
         up[c] = fb[c] * sig;
       }
     }
 
-    // ---- epilogue: h = silu(gate) * up, encoded per (row, 64-column block)
-    float h[4];
-    float mx = 0.0f;
+    // ---- epilogue: h = act(gate) * up, encoded per (tile row, 64-column block).
+    // Lane (i, g) holds tile rows 4g+c of column c0+i: the row maximum runs over
+    // the 16 lanes of equal g, then over the 4 column groups through LDS.
+    float h[4], mx[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       h[c] = act_f(G.act, gate[c]) * up[c];
-      mx = fmaxf(mx, fabsf(h[c]));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (kp == 0 && g == 0) red_max[cg][i] = mx;
-    __syncthreads();
-    if (kp == 0 && jv) {
-      mx = fmaxf(fmaxf(red_max[0][i], red_max[1][i]), fmaxf(red_max[2][i], red_max[3][i]));
-      const int p = digit_exponent(mx);
-      int d0[4], d1[4];
+      mx[c] = fabsf(h[c]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) two_digits(h[c], p, d0[c], d1[c]);
-      int8_t* hrow = G.hq + (size_t)r * 2 * I;
-      const int col = c0 + 4 * g;
-      *reinterpret_cast<unsigned*>(hrow + col) = pack4(d0[0], d0[1], d0[2], d0[3]);
-      *reinterpret_cast<unsigned*>(hrow + I + col) = pack4(d1[0], d1[1], d1[2], d1[3]);
-      if (cg == 0 && g == 0)
-        G.hs[(size_t)r * (I / 64) + cb] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+      for (int o = 1; o < 16; o <<= 1) mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], o, kWave));
+    }
+    if (kp == 0 && i == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) red_max[cg][4 * g + c] = mx[c];
+    }
+    __syncthreads();
+    if (kp == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = 4 * g + c;
+        if (t >= job.nr) continue;
+        const float m = fmaxf(fmaxf(red_max[0][t], red_max[1][t]),
+                              fmaxf(red_max[2][t], red_max[3][t]));
+        const int p = digit_exponent(m);
+        int d0, d1;
+        two_digits(h[c], p, d0, d1);
+        const int r = PAIRS ? rows_sm[t] : job.r0 + t;
+        int8_t* hrow = G.hq + (size_t)r * 2 * I;
+        const int col = FMT == 1 ? c0 + i : int4_digit_pos(c0 + i);  // the down kernel's order
+        hrow[col] = (int8_t)d0;
+        hrow[I + col] = (int8_t)d1;
+        if (cg == 0 && i == 0) G.hs[(size_t)r * (I / 64) + cb] = m > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+      }
     }
     if (NCB > 1) __syncthreads();  // red_max is reused by the next column block
   }
@@ -575,8 +663,8 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
         x0[q] = 0;
         x1[q] = 0;
         if (jv) {
-          x0[q] = *reinterpret_cast<const long*>(hb0 + 128 * m + 32 * q + 8 * g);
-          x1[q] = *reinterpret_cast<const long*>(hb1 + 128 * m + 32 * q + 8 * g);
+          x0[q] = *reinterpret_cast<const long*>(hb0 + 128 * m + 32 * g + 8 * q);
+          x1[q] = *reinterpret_cast<const long*>(hb1 + 128 * m + 32 * g + 8 * q);
         }
       }
       sg[0] = jv ? hsr[2 * m] * (1.0f / 256.0f) : 0.0f;
@@ -585,12 +673,12 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int b = 4 * m + q;
-          const long wq = unpack8_int4((unsigned)w4[q]);
+          const long wq = unpack8_int4_x16((unsigned)w4[q]);
           const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], zero, 0, 0, 0);
           const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], zero, 0, 0, 0);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const float sw = fmaxf(sa[(size_t)c * nb + b], kScaleFloor);
+            const float sw = fmaxf(sa[(size_t)c * nb + b], kScaleFloor) * kInv16;
             acc[0][c] = fmaf(sw * sg[q >> 1], (float)(p0[c] * 256 + p1[c]), acc[0][c]);
           }
         }
@@ -598,13 +686,13 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
         v4i p0[2] = {zero, zero}, p1[2] = {zero, zero};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const long wq = unpack8_int4((unsigned)w4[q]);
+          const long wq = unpack8_int4_x16((unsigned)w4[q]);
           p0[q >> 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], p0[q >> 1], 0, 0, 0);
           p1[q >> 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], p1[q >> 1], 0, 0, 0);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float sw = fmaxf(sa[(size_t)c * nb + m], kScaleFloor);
+          const float sw = fmaxf(sa[(size_t)c * nb + m], kScaleFloor) * kInv16;
           const float v = fmaf(sg[0], fmaf((float)p0[0][c], 256.0f, (float)p1[0][c]),
                                sg[1] * fmaf((float)p0[1][c], 256.0f, (float)p1[1][c]));
           acc[0][c] = fmaf(sw, v, acc[0][c]);
@@ -1146,7 +1234,8 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   const long long blocks = (long long)tiles * (imax / 64);
   const int ks = blocks >= 2LL * g_cu_count ? 1 : (blocks >= g_cu_count / 2 ? 2 : 4);
   const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
-  const size_t lds_gu = std::max((size_t)mt * (2 * d + 16), emax);
+  // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
+  const size_t lds_gu = PAIRS ? emax : (size_t)mt * (2 * d + 16);
   {
     TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
     dim3 grid(imax / 64, tiles);
@@ -1186,11 +1275,12 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
 
 void set_device_info(int cu_count) { g_cu_count = cu_count > 0 ? cu_count : 256; }
 
-hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig,
+hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig, bool perm,
                               hipStream_t s) {
   if (n <= 0) return hipSuccess;
   TimedLaunch tl(K_ENCODE_ROWS, s);
-  hipLaunchKernelGGL(encode_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, v, n, K, q, sig);
+  hipLaunchKernelGGL(encode_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, v, n, K, q, sig,
+                     perm);
   return hipGetLastError();
 }
 
@@ -1249,7 +1339,8 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
                             const FfnWs& ws, bool x_encoded, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (!x_encoded) {
-    err = launch_encode_rows(x, T, d, ws.xq, ws.xs, s);
+    // int4 kernels read the digits in their permuted order (encode8)
+    err = launch_encode_rows(x, T, d, ws.xq, ws.xs, sets[0].fmt != 1, s);
     if (err != hipSuccess) return err;
   }
   // int8 with many rows per expert: grouped GEMM
@@ -1267,11 +1358,10 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     return sets[0].layout == 1 ? launch_gemm_pair<kTiled>(grp[0], grp[1], d, ws.xq, ws.xs, s)
                                : launch_gemm_pair<kRows>(grp[0], grp[1], d, ws.xq, ws.xs, s);
   }
-  // rows per tile: at most 16 (the MFMA N side); small batches use fewer so
-  // that the staged activation rows take less LDS; wide rows use fewer so that
-  // a tile's staged rows (x digits for gate/up, h digits and block scales for
-  // down) fit the LDS beside the kernels' largest static arrays (the K-slice
-  // partials, under 50 KB)
+  // rows per tile: at most 16 (the MFMA N side); small batches use fewer; wide
+  // rows use fewer so that a tile's staged rows (x digits for gate/up, h
+  // digits and block scales for down) fit the LDS beside the kernels' largest
+  // static arrays (the K-slice partials, under 50 KB)
   int mt = T < kTileRows ? (T > 0 ? T : 1) : kTileRows;
   {
     size_t per_row = (size_t)2 * d + 16;

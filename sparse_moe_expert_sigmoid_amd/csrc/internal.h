@@ -134,14 +134,14 @@ constexpr int kSmallT = 16;
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
                                const uint8_t* mask,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, hipStream_t s);
+                               float* partial, int8_t* xq, float* xs, bool perm, hipStream_t s);
 // counts[e] += number of topk_idx entries equal to e (entries outside [0, E) skipped)
 hipError_t launch_expert_counts(const int32_t* idx, long long n, int E, unsigned long long* counts,
                                 hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
-hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig,
+hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig, bool perm,
                               hipStream_t s);
 // Encodes x (unless x_encoded) and runs gate/up then down for 1 or 2 expert
 // sets (same format) in one pair of launches.
@@ -248,10 +248,51 @@ __device__ inline unsigned pack4(int a, int b, int c, int d) {
          ((unsigned)(d & 0xff) << 24);
 }
 
-// One wavefront encodes one row of K values (K % 4 == 0): q = [d0 x K | d1 x K],
-// *sig = 2^-p (0 for an all-zero row).
+// Digit bytes of 8 consecutive values v[0..7] (two float4), as two 8-byte
+// words (d0 digits, d1 digits).  perm = false: natural order.  perm = true:
+// (0, 2, 4, 6, 1, 3, 5, 7), the order within each group of 8 that the int4
+// FFN kernels read: their weight unpacking leaves even and odd codes in
+// separate words, and the activations must line up with them (ffn.hip,
+// int4).  The int4 order also moves the groups inside each 128-wide span
+// (int4_digit_chunk), so that a lane's four groups of a span are contiguous.
+__device__ inline void encode8(const float4& a, const float4& b, int p, bool perm, uint2& w0,
+                               uint2& w1) {
+  int x[8], y[8];
+  two_digits(a.x, p, x[0], y[0]);
+  two_digits(a.y, p, x[1], y[1]);
+  two_digits(a.z, p, x[2], y[2]);
+  two_digits(a.w, p, x[3], y[3]);
+  two_digits(b.x, p, x[4], y[4]);
+  two_digits(b.y, p, x[5], y[5]);
+  two_digits(b.z, p, x[6], y[6]);
+  two_digits(b.w, p, x[7], y[7]);
+  if (perm) {
+    w0 = make_uint2(pack4(x[0], x[2], x[4], x[6]), pack4(x[1], x[3], x[5], x[7]));
+    w1 = make_uint2(pack4(y[0], y[2], y[4], y[6]), pack4(y[1], y[3], y[5], y[7]));
+  } else {
+    w0 = make_uint2(pack4(x[0], x[1], x[2], x[3]), pack4(x[4], x[5], x[6], x[7]));
+    w1 = make_uint2(pack4(y[0], y[1], y[2], y[3]), pack4(y[4], y[5], y[6], y[7]));
+  }
+}
+
+// The int4 digit order of a row: group c (elements 8c..8c+7) of span c / 16
+// is group j = 4q + g of its span (q = block of 32, g = group within the
+// block); it moves to place 4g + q, so that lane group g of an MFMA finds its
+// four blocks' groups in 32 contiguous bytes; inside the group the order is
+// encode8's.  int4_digit_chunk gives the group's new index, int4_digit_pos an
+// element's new byte position.
+__device__ inline int int4_digit_chunk(int c) {
+  return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3);
+}
+__device__ inline int int4_digit_pos(int k) {
+  return 8 * int4_digit_chunk(k >> 3) | ((k & 7) >> 1) | ((k & 1) << 2);
+}
+
+// One wavefront encodes one row of K values (K % 8 == 0; K % 128 == 0 with
+// perm): q = [d0 x K | d1 x K], *sig = 2^-p (0 for an all-zero row); perm: the
+// int4 digit order (encode8, int4_digit_chunk).
 __device__ inline void encode_row(const float* __restrict__ row, int K, int8_t* __restrict__ q,
-                                  float* __restrict__ sig) {
+                                  float* __restrict__ sig, bool perm) {
   const int lane = threadIdx.x & (kWave - 1);
   float m = 0.0f;
   for (int c = lane; c < K / 4; c += kWave) {
@@ -261,17 +302,16 @@ __device__ inline void encode_row(const float* __restrict__ row, int K, int8_t* 
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
   const int p = digit_exponent(m);
-  unsigned* q0 = reinterpret_cast<unsigned*>(q);
-  unsigned* q1 = reinterpret_cast<unsigned*>(q + K);
-  for (int c = lane; c < K / 4; c += kWave) {
-    const float4 a = *reinterpret_cast<const float4*>(row + 4 * c);
-    int x0, y0, x1, y1, x2, y2, x3, y3;
-    two_digits(a.x, p, x0, y0);
-    two_digits(a.y, p, x1, y1);
-    two_digits(a.z, p, x2, y2);
-    two_digits(a.w, p, x3, y3);
-    q0[c] = pack4(x0, x1, x2, x3);
-    q1[c] = pack4(y0, y1, y2, y3);
+  uint2* q0 = reinterpret_cast<uint2*>(q);
+  uint2* q1 = reinterpret_cast<uint2*>(q + K);
+  for (int c = lane; c < K / 8; c += kWave) {
+    const float4 a = *reinterpret_cast<const float4*>(row + 8 * c);
+    const float4 b = *reinterpret_cast<const float4*>(row + 8 * c + 4);
+    uint2 w0, w1;
+    encode8(a, b, p, perm, w0, w1);
+    const int dst = perm ? int4_digit_chunk(c) : c;
+    q0[dst] = w0;
+    q1[dst] = w1;
   }
   if (lane == 0) *sig = m > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
 }

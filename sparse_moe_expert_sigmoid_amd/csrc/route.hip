@@ -259,56 +259,58 @@ __global__ __launch_bounds__(256) void router_tail_kernel(
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, int T, int E, int k,
     int router, float scale,
     int32_t* __restrict__ idx, float* __restrict__ w, int8_t* __restrict__ xq,
-    float* __restrict__ xs) {
+    float* __restrict__ xs, bool perm) {
   __shared__ unsigned long long keys[256 * EPT];
   __shared__ float red[4];
   __shared__ float xred[4];
   __shared__ float sel_s[kMaxK];
   const int t = blockIdx.x;
   const float* row = x + (size_t)t * d;
-  // the token's row of x (up to 4096 values) goes into registers first, so its
-  // loads are in flight during the selection
-  constexpr int kXPer = 4;
-  const int nq = d / 4;
-  const bool in_regs = nq <= kXPer * 256;
-  float4 xv[kXPer];
+  // the token's row of x (up to 4096 values, in groups of 8 per thread) goes
+  // into registers first, so its loads are in flight during the selection
+  constexpr int kXPer = 2;
+  const int n8 = d / 8;
+  const bool in_regs = n8 <= kXPer * 256;
+  float4 xv[kXPer][2];
 #pragma unroll
   for (int m = 0; m < kXPer; ++m) {
     const int c = threadIdx.x + 256 * m;
-    xv[m] = (in_regs && c < nq) ? *reinterpret_cast<const float4*>(row + 4 * c)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool ok = in_regs && c < n8;
+    xv[m][0] = ok ? *reinterpret_cast<const float4*>(row + 8 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    xv[m][1] = ok ? *reinterpret_cast<const float4*>(row + 8 * c + 4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   select_token<EPT>(partial, nchunk, bias, mask, T, E, k, router, scale, t, true, threadIdx.x,
                     keys,
                     red, sel_s, idx, w, nullptr);
   if (!in_regs) {
-    if (threadIdx.x < kWave) encode_row(row, d, xq + (size_t)t * 2 * d, xs + t);
+    if (threadIdx.x < kWave) encode_row(row, d, xq + (size_t)t * 2 * d, xs + t, perm);
     return;
   }
   // two-digit encoding of the row with one scale (as encode_row), by all threads
   float mx = 0.0f;
 #pragma unroll
   for (int m = 0; m < kXPer; ++m)
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m].x), fabsf(xv[m].y)),
-                         fmaxf(fabsf(xv[m].z), fabsf(xv[m].w))));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][h].x), fabsf(xv[m][h].y)),
+                           fmaxf(fabsf(xv[m][h].z), fabsf(xv[m][h].w))));
   mx = wave_max_f(mx);
   if ((threadIdx.x & (kWave - 1)) == 0) xred[threadIdx.x / kWave] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(xred[0], xred[1]), fmaxf(xred[2], xred[3]));
   const int p = digit_exponent(mx);
-  unsigned* q0 = reinterpret_cast<unsigned*>(xq + (size_t)t * 2 * d);
-  unsigned* q1 = reinterpret_cast<unsigned*>(xq + (size_t)t * 2 * d + d);
+  uint2* q0 = reinterpret_cast<uint2*>(xq + (size_t)t * 2 * d);
+  uint2* q1 = reinterpret_cast<uint2*>(xq + (size_t)t * 2 * d + d);
 #pragma unroll
   for (int m = 0; m < kXPer; ++m) {
     const int c = threadIdx.x + 256 * m;
-    if (c >= nq) continue;
-    int a0, b0, a1, b1, a2, b2, a3, b3;
-    two_digits(xv[m].x, p, a0, b0);
-    two_digits(xv[m].y, p, a1, b1);
-    two_digits(xv[m].z, p, a2, b2);
-    two_digits(xv[m].w, p, a3, b3);
-    q0[c] = pack4(a0, a1, a2, a3);
-    q1[c] = pack4(b0, b1, b2, b3);
+    if (c >= n8) continue;
+    uint2 w0, w1;
+    encode8(xv[m][0], xv[m][1], p, perm, w0, w1);
+    const int dst = perm ? int4_digit_chunk(c) : c;
+    q0[dst] = w0;
+    q1[dst] = w1;
   }
   if (threadIdx.x == 0) xs[t] = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
 }
@@ -317,10 +319,10 @@ template <int EPT>
 hipError_t launch_tail(const float* partial, int nchunk, const float* x, int d, const float* bias,
                        const uint8_t* mask,
                        int T, int E, int k, int router, float scale, int32_t* idx, float* w,
-                       int8_t* xq, float* xs, hipStream_t s) {
+                       int8_t* xq, float* xs, bool perm, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TAIL, s);
   hipLaunchKernelGGL(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
-                     bias, mask, T, E, k, router, scale, idx, w, xq, xs);
+                     bias, mask, T, E, k, router, scale, idx, w, xq, xs, perm);
   return hipGetLastError();
 }
 
@@ -355,7 +357,8 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
                                const uint8_t* mask,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, hipStream_t s) {
+                               float* partial, int8_t* xq, float* xs, bool perm,
+                               hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
   {
     TimedLaunch tl(K_ROUTER_LOGITS, s);
@@ -367,12 +370,12 @@ hipError_t launch_router_small(int router, const float* x, const float* wr, cons
   if (err != hipSuccess) return err;
   if (E <= 256)
     return launch_tail<1>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
-                          xs, s);
+                          xs, perm, s);
   if (E <= 512)
     return launch_tail<2>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
-                          xs, s);
+                          xs, perm, s);
   return launch_tail<4>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
-                          xs, s);
+                          xs, perm, s);
 }
 
 }  // namespace moe
