@@ -181,7 +181,11 @@ const char* moe_status_string(moe_status status);
    for a layer of T tokens, top k of E experts, width d, intermediate width
    `inter` and weight format `fmt` (the larger of the two calls; one buffer
    may serve all of them in turn on one stream).  [host] *bytes.
-   For the shared expert (one expert over T rows) pass k = 1, E = 1. */
+   For the shared expert (one expert over T rows) pass k = 1, E = 1.
+   For int8/int4 weights this includes about 16 MB where small decode
+   launches that split K across workgroups meet (partial sums and arrival
+   counts); the workspace needs no initialisation, each call clears the
+   counts it uses before its FFN kernels run. */
 moe_status moe_workspace_size(const moe_ctx* ctx, int T, int k, int E, int d, int inter,
                               int fmt, size_t* bytes);
 
@@ -287,7 +291,8 @@ typedef struct {
     const uint8_t* expert_mask;  /* [E] device, or NULL: see moe_route_masked */
 } moe_layer;
 
-/* Workspace for moe_forward on T tokens.  [host] *bytes. */
+/* Workspace for moe_forward on T tokens (as moe_workspace_size, including the
+   split-K area for int8/int4 layers).  [host] *bytes. */
 moe_status moe_layer_workspace_size(const moe_ctx* ctx, const moe_layer* layer, int T,
                                     size_t* bytes);
 

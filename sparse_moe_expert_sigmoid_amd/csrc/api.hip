@@ -605,7 +605,8 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
     // x digits in the order the routed experts' kernels read (int4: permuted)
     const bool perm = X.fmt == MOE_W_INT4_B32 || X.fmt == MOE_W_INT4_B128;
     e = moe::launch_router_small(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
-                                 k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, s);
+                                 k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, lay.cnt,
+                                 s);
   } else {
     e = moe::launch_router(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E, k,
                            L->scale, idx, w, f.partial, s);

@@ -58,7 +58,11 @@ __device__ inline T gload_nt(const void* p) {
 // One wavefront per row (see encode_row).
 __global__ __launch_bounds__(256) void encode_rows_kernel(const float* __restrict__ v, int n,
                                                           int K, int8_t* __restrict__ q,
-                                                          float* __restrict__ sig, bool perm) {
+                                                          float* __restrict__ sig, bool perm,
+                                                          int* __restrict__ split_cnt) {
+  if (split_cnt)  // the FFN launches that follow start from zero counters
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < kSplitSlots; c += gridDim.x * blockDim.x)
+      split_cnt[c] = 0;
   const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (r >= n) return;
   encode_row(v + (size_t)r * K, K, q + (size_t)r * 2 * K, sig + r, perm);
@@ -87,6 +91,62 @@ struct Group {
 struct Job {
   int g, e, r0, nr;
 };
+
+// K split across the n workgroups of one work unit (grid z = 0 .. n-1).  Each
+// writes its partial sums to its slot; the last to arrive (by an atomic count)
+// adds every slot in workgroup order, so the result does not depend on arrival
+// order, clears the count for the next launch and goes on to the epilogue.
+struct SplitK {
+  int n;       // 1: no split
+  int* cnt;    // one arrival count per unit, zero before the launch
+  float* part; // kSplitSlotBytes per (unit, workgroup)
+};
+
+// holder lanes carry N values of type V (int32 digit sums or fp32 partials);
+// grp is the wavefront's index among the holders.  Returns false in every workgroup but
+// the last of its unit (uniform over the workgroup); the last one returns
+// with the total in v.  The slots and the count are accessed with relaxed
+// device-scope atomics, which stay coherent across the XCDs' separate L2
+// caches without the whole-L2 write-back and invalidation that a device-scope
+// fence costs: each thread waits for its own slot stores to complete
+// (vmcnt 0) before the barrier, and the count is taken after the barrier.
+template <typename V, int N>
+__device__ inline bool split_join(const SplitK& sk, int unit, int kw, int grp, bool holder, V* v,
+                                  int* flag_sm) {
+  // slot layout [grp][c][lane]: each store and load of a value is 256
+  // contiguous bytes over the wavefront
+  V* base = reinterpret_cast<V*>(sk.part);
+  constexpr size_t kPer = kSplitSlotBytes / sizeof(V);
+  const int lane = threadIdx.x & (kWave - 1);
+  const size_t at = (size_t)grp * N * kWave + lane;
+  if (holder) {
+    V* dst = base + (size_t)(unit * sk.n + kw) * kPer + at;
+#pragma unroll
+    for (int c = 0; c < N; ++c)
+      __hip_atomic_store(dst + c * kWave, v[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F70u);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag_sm = __hip_atomic_fetch_add(sk.cnt + unit, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == sk.n - 1;
+  __syncthreads();
+  if (!*flag_sm) return false;
+  if (holder) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) v[c] = V(0);
+    for (int q = 0; q < sk.n; ++q) {
+      V* src = base + (size_t)(unit * sk.n + q) * kPer + at;
+#pragma unroll
+      for (int c = 0; c < N; ++c)
+        v[c] += __hip_atomic_load(src + c * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(sk.cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
 
 __device__ inline bool find_job(const Group& g0, const Group& g1, int mt, int tile, Job& j) {
   const Group& G = tile < g0.tiles ? g0 : g1;
@@ -265,15 +325,16 @@ constexpr float kInv16 = 1.0f / 16.0f;          // the unpacked codes carry a fa
 // PAIRS (small batches): rows are the (token, slot) pairs grouped in-kernel.
 // The tile's activation digit rows are staged in LDS (mt rows of 2d bytes); a
 // workgroup covers NCB column blocks of 64 in turn.
-template <int FMT, int LAY, int KS, bool PAIRS, int NCB>
+template <int FMT, int LAY, int KS, bool PAIRS, int NCB, bool SPLIT>
 __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, int d, int mt,
                                                            const int8_t* __restrict__ xq,
-                                                           const float* __restrict__ xs) {
+                                                           const float* __restrict__ xs,
+                                                           SplitK sk) {
   extern __shared__ int8_t lds[];
   __shared__ float red_max[4][16];
   // K-slice partials: int8 path 16 ints per lane, int4 path 8 floats per lane
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 16 : 1];
-  __shared__ int rows_sm[kTileRows], toks_sm[kTileRows], sh_sm[3];
+  __shared__ int rows_sm[kTileRows], toks_sm[kTileRows], sh_sm[3], last_sm;
   {
     const bool first = (int)blockIdx.y < g0.tiles;
     if ((int)blockIdx.x * 64 * NCB >= (first ? g0.inter : g1.inter)) return;
@@ -291,6 +352,9 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
   const int i = lane & 15, g = lane >> 4;
+  // K slice of this wavefront: slice kw * KS + kp of sk.n * KS (SPLIT), else kp of KS
+  const int ksl = SPLIT ? (int)blockIdx.z * KS + kp : kp, nsl = SPLIT ? sk.n * KS : KS;
+  const int unit = blockIdx.y * gridDim.x + blockIdx.x;  // (NCB == 1 when SPLIT)
   // x digits of the tile rows.  Small batches (PAIRS) read their few token
   // rows straight from L2: no staging barrier before the weight loads, no LDS
   // to limit how many workgroups a CU holds.  Tiles of up to 16 rows stage them
@@ -342,7 +406,7 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
     float gate[4], up[4];
     if (FMT == 1) {
       const int nsteps = d / kKStep;
-      const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
+      const int s_beg = ksl * nsteps / nsl, s_end = (ksl + 1) * nsteps / nsl;
       const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wgu), row0, d, i, g,
                                               lane);
       const int8_t* wb = wa + (size_t)I * d;
@@ -392,6 +456,19 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
           }
         }
       }
+      if constexpr (SPLIT) {  // exact int32 sums across the unit's workgroups
+        int v[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[c] = a0[c]; v[4 + c] = a1[c]; v[8 + c] = b0[c]; v[12 + c] = b1[c];
+        }
+        if (!split_join<int, 16>(sk, unit, blockIdx.z, cg, kp == 0, v, &last_sm))
+          return;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a0[c] = v[c]; a1[c] = v[4 + c]; b0[c] = v[8 + c]; b1[c] = v[12 + c];
+        }
+      }
       const float* se = G.sgu + (size_t)job.e * 2 * I;
       const float sgate = gload<float>(se + c0 + i), sup = gload<float>(se + I + c0 + i);
       float sx[4];
@@ -411,7 +488,7 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
       // in int32 and join once per span.  U spans (codes and their scales) are
       // loaded before any is used.
       const int nb = d / (FMT == 3 ? 128 : 32), nspan = d / 128;
-      const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
+      const int m_beg = ksl * nspan / nsl, m_end = (ksl + 1) * nspan / nsl;
       const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wgu), row0, d, i,
                                                g, lane);
       const uint8_t* wb = wa + (size_t)I * (d / 2);
@@ -505,6 +582,15 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
           }
         }
       }
+      if constexpr (SPLIT) {  // fp32 partials added in workgroup order
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { v[c] = fa[c]; v[4 + c] = fb[c]; }
+        if (!split_join<float, 8>(sk, unit, blockIdx.z, cg, kp == 0, v, &last_sm))
+          return;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { fa[c] = v[c]; fb[c] = v[4 + c]; }
+      }
       float sx[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) sx[c] = x_scale(c);
@@ -560,11 +646,12 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
 // NG: 16-row weight groups per wavefront (2 for int8 without K split, so each
 // workgroup streams 128 output rows and its prologue is amortised over more
 // bytes).
-template <int FMT, int LAY, int KS, bool PAIRS, int NG>
-__global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int d, int mt) {
+template <int FMT, int LAY, int KS, bool PAIRS, int NG, bool SPLIT>
+__global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int d, int mt,
+                                                        SplitK sk) {
   extern __shared__ int8_t lds[];
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 4 : 1];
-  __shared__ int rows_sm[kTileRows], sh_sm[3];
+  __shared__ int rows_sm[kTileRows], sh_sm[3], last_sm;
   Job job;
   if (PAIRS) {  // the expert histogram borrows the h staging area
     if (!find_rows(g0, g1, mt, blockIdx.y, job, rows_sm, nullptr, reinterpret_cast<int*>(lds),
@@ -593,6 +680,8 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
+  // K slice of this wavefront: slice kw * KS + kp of sk.n * KS (SPLIT), else kp of KS
+  const int ksl = SPLIT ? (int)blockIdx.z * KS + kp : kp, nsl = SPLIT ? sk.n * KS : KS;
   const int c0 = blockIdx.x * 64 * NG + cg * 16 * NG;  // output rows of this wavefront
   const int i = lane & 15, g = lane >> 4;
   const bool jv = i < job.nr;
@@ -610,7 +699,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 
   if (FMT == 1) {
     const int nsteps = I / kKStep;
-    const int s_beg = kp * nsteps / KS, s_end = (kp + 1) * nsteps / KS;
+    const int s_beg = ksl * nsteps / nsl, s_end = (ksl + 1) * nsteps / nsl;
     const int8_t* wa = i8_operand_base<LAY>(static_cast<const int8_t*>(G.wdn), row0, I, i, g,
                                             lane);
     // 8 KB of weights in flight per wavefront
@@ -650,7 +739,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
     // int4 blocks of 32 (FMT 2) or 128 (FMT 3, the span: its MFMA pairs
     // accumulate in int32 per 64-column half, since h has one scale per 64)
     const int nb = I / (FMT == 3 ? 128 : 32), nspan = I / 128;
-    const int m_beg = kp * nspan / KS, m_end = (kp + 1) * nspan / KS;
+    const int m_beg = ksl * nspan / nsl, m_end = (ksl + 1) * nspan / nsl;
     const uint8_t* wa = i4_operand_base<LAY>(static_cast<const uint8_t*>(G.wdn), row0, I, i, g,
                                              lane);
     const float* sa = G.sdn + ((size_t)job.e * d + c0 + 4 * g) * nb;
@@ -707,14 +796,21 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
       for (int c = 0; c < 4; ++c) dst[c] = acc[0][c];
     }
     __syncthreads();
-    if (kp != 0) return;
-    for (int q = 1; q < KS; ++q) {
-      const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 4;
+    if (!SPLIT && kp != 0) return;
+    if (kp == 0) {
+      for (int q = 1; q < KS; ++q) {
+        const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 4;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[0][c] += src[c];
+        for (int c = 0; c < 4; ++c) acc[0][c] += src[c];
+      }
     }
   }
-  if (!jv) return;
+  if constexpr (SPLIT) {  // fp32 partials added in workgroup order (NG == 1 when SPLIT)
+    const int unit = blockIdx.y * gridDim.x + blockIdx.x;
+    if (!split_join<float, 4>(sk, unit, blockIdx.z, cg, kp == 0, acc[0], &last_sm))
+      return;
+  }
+  if ((SPLIT && kp != 0) || !jv) return;  // (without SPLIT, kp > 0 left above)
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     float res[4];
@@ -1225,49 +1321,84 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 
 int g_cu_count = 256;
 
+// Workgroups per work unit (K split) for a launch of `units` units on the
+// chip: the time of a launch follows its busiest CU, ceil(units n / CUs)
+// workgroups of 1/n unit each plus a fixed cost per workgroup (tile lookup,
+// the first loads' latency, the join through device-coherent memory; about
+// half a unit's streaming at decode sizes, measured), so n = 1 unless CUs
+// would sit idle.  Each wavefront keeps at least min_steps K-steps.
+inline int split_ways(long long units, int ksteps_per_wave_at_1, int min_steps) {
+  const long long cus = g_cu_count;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int n = 1; n <= 8; ++n) {
+    if (n > 1 && (units * n > kSplitSlots || ksteps_per_wave_at_1 / n < min_steps)) break;
+    const double waves = (double)((units * n + cus - 1) / cus);
+    const double cost = waves * (1.0 / n + 0.5);
+    if (cost < best_cost * 0.97) {
+      best_cost = cost;
+      best = n;
+    }
+  }
+  return best;
+}
+
 template <int FMT, int LAY, bool PAIRS>
 hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8_t* xq,
-                       const float* xs, hipStream_t s) {
+                       const float* xs, const FfnWs& ws, hipStream_t s) {
   const int tiles = a.tiles + b.tiles;
   const int imax = a.inter > b.inter ? a.inter : b.inter;
   // split K across more wavefronts when the tiles alone cannot fill the chip
   const long long blocks = (long long)tiles * (imax / 64);
   const int ks = blocks >= 2LL * g_cu_count ? 1 : (blocks >= g_cu_count / 2 ? 2 : 4);
+  // and across workgroups when the units do not spread evenly over the CUs
+  const int ksteps = FMT == 1 ? d / kKStep : d / 128;  // K-steps (int4: spans) per unit
+  // (only the small-batch launches split: they are the ones that leave CUs idle)
+  SplitK sk{PAIRS ? split_ways(blocks, ksteps / ks, 2) : 1, ws.cnt, ws.part};
   const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
   // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
   const size_t lds_gu = PAIRS ? emax : (size_t)mt * (2 * d + 16);
+#define MOE_GU(KSV, SPL)                                                                 \
+  hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, KSV, PAIRS, 1, SPL>), grid, dim3(256 * KSV), \
+                     lds_gu, s, a, b, d, mt, xq, xs, sk)
   {
     TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
-    dim3 grid(imax / 64, tiles);
-    if (ks == 1)
-      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 1, PAIRS, 1>), grid, dim3(256), lds_gu, s, a, b,
-                         d, mt, xq, xs);
-    else if (ks == 2)
-      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 2, PAIRS, 1>), grid, dim3(512), lds_gu, s, a, b,
-                         d, mt, xq, xs);
-    else
-      hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, 4, PAIRS, 1>), grid, dim3(1024), lds_gu, s, a, b,
-                         d, mt, xq, xs);
+    dim3 grid(imax / 64, tiles, sk.n);
+    if (sk.n > 1) {
+      if (ks == 1) MOE_GU(1, PAIRS);
+      else if (ks == 2) MOE_GU(2, PAIRS);
+      else MOE_GU(4, PAIRS);
+    } else {
+      if (ks == 1) MOE_GU(1, false);
+      else if (ks == 2) MOE_GU(2, false);
+      else MOE_GU(4, false);
+    }
   }
+#undef MOE_GU
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long dblocks = (long long)tiles * (d / 64);
   const int dks = dblocks >= 2LL * g_cu_count ? 1 : (dblocks >= g_cu_count / 2 ? 2 : 4);
+  const int dsteps = FMT == 1 ? imax / kKStep : imax / 128;
+  const bool ng2 = FMT == 1 && dks == 1 && d % 128 == 0;
+  SplitK dsk{PAIRS && !ng2 ? split_ways(dblocks, dsteps / dks, 2) : 1, ws.cnt, ws.part};
   const size_t lds_dn =
       PAIRS ? emax : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
+#define MOE_DN(KSV, NGV, SPL)                                                               \
+  hipLaunchKernelGGL((down_kernel<FMT, LAY, KSV, PAIRS, NGV, SPL>),                         \
+                     dim3(d / (64 * NGV), tiles, dsk.n), dim3(256 * KSV), lds_dn, s, a, b, d, mt, dsk)
   TimedLaunch tl(FMT == 1 ? K_FFN_I8_DOWN : K_FFN_I4_DOWN, s);
-  if (FMT == 1 && dks == 1 && d % 128 == 0)
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 1, PAIRS, 2>), dim3(d / 128, tiles), dim3(256),
-                       lds_dn, s, a, b, d, mt);
-  else if (dks == 1)
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 1, PAIRS, 1>), dim3(d / 64, tiles), dim3(256),
-                       lds_dn, s, a, b, d, mt);
-  else if (dks == 2)
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 2, PAIRS, 1>), dim3(d / 64, tiles), dim3(512),
-                       lds_dn, s, a, b, d, mt);
-  else
-    hipLaunchKernelGGL((down_kernel<FMT, LAY, 4, PAIRS, 1>), dim3(d / 64, tiles), dim3(1024),
-                       lds_dn, s, a, b, d, mt);
+  if (ng2) MOE_DN(1, 2, false);
+  else if (dsk.n > 1) {
+    if (dks == 1) MOE_DN(1, 1, PAIRS);
+    else if (dks == 2) MOE_DN(2, 1, PAIRS);
+    else MOE_DN(4, 1, PAIRS);
+  } else {
+    if (dks == 1) MOE_DN(1, 1, false);
+    else if (dks == 2) MOE_DN(2, 1, false);
+    else MOE_DN(4, 1, false);
+  }
+#undef MOE_DN
   return hipGetLastError();
 }
 
@@ -1276,11 +1407,11 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
 void set_device_info(int cu_count) { g_cu_count = cu_count > 0 ? cu_count : 256; }
 
 hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig, bool perm,
-                              hipStream_t s) {
+                              int* split_cnt, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   TimedLaunch tl(K_ENCODE_ROWS, s);
   hipLaunchKernelGGL(encode_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, v, n, K, q, sig,
-                     perm);
+                     perm, split_cnt);
   return hipGetLastError();
 }
 
@@ -1340,7 +1471,7 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
   hipError_t err = hipSuccess;
   if (!x_encoded) {
     // int4 kernels read the digits in their permuted order (encode8)
-    err = launch_encode_rows(x, T, d, ws.xq, ws.xs, sets[0].fmt != 1, s);
+    err = launch_encode_rows(x, T, d, ws.xq, ws.xs, sets[0].fmt != 1, ws.cnt, s);
     if (err != hipSuccess) return err;
   }
   // int8 with many rows per expert: grouped GEMM
@@ -1398,8 +1529,8 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
   const bool tiled = sets[0].layout == 1;
   const bool pairs = sets[0].pairs_idx != nullptr || (nsets > 1 && sets[1].pairs_idx != nullptr);
 #define MOE_PAIR(F, L)                                                               \
-  (pairs ? launch_pair<F, L, true>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s)           \
-         : launch_pair<F, L, false>(grp[0], grp[1], d, mt, ws.xq, ws.xs, s))
+  (pairs ? launch_pair<F, L, true>(grp[0], grp[1], d, mt, ws.xq, ws.xs, ws, s)       \
+         : launch_pair<F, L, false>(grp[0], grp[1], d, mt, ws.xq, ws.xs, ws, s))
   if (sets[0].fmt == 1) return tiled ? MOE_PAIR(1, kTiled) : MOE_PAIR(1, kRows);
   if (sets[0].fmt == 3) return tiled ? MOE_PAIR(3, kTiled) : MOE_PAIR(3, kRows);
   return tiled ? MOE_PAIR(2, kTiled) : MOE_PAIR(2, kRows);

@@ -39,8 +39,16 @@ struct FfnWs {
   int8_t* hq[2];
   float* hs[2];
   float* h;
+  int* cnt;     // split-K arrival counters (kSplitSlots), zero between launches
+  float* part;  // split-K partial sums (kSplitSlots slots of kSplitSlotBytes)
   size_t bytes;
 };
+
+// Decode launches with fewer work units than the chip has CUs (or a few more)
+// split K across workgroups: unit u's n workgroups write partial sums into
+// slots u*n .. u*n+n-1 and the last to arrive adds them in slot order.
+constexpr int kSplitSlots = 1024;
+constexpr size_t kSplitSlotBytes = 16384;
 
 // rows/inter of up to two expert sets sharing one x
 inline FfnWs ffn_ws_layout(void* base, int T, int d, int nsets, const int* R, const int* inter,
@@ -60,6 +68,8 @@ inline FfnWs ffn_ws_layout(void* base, int T, int d, int nsets, const int* R, co
       w.hq[q] = reinterpret_cast<int8_t*>(take((size_t)R[q] * 2 * inter[q]));
       w.hs[q] = reinterpret_cast<float*>(take((size_t)R[q] * (inter[q] / 64) * sizeof(float)));
     }
+    w.cnt = reinterpret_cast<int*>(take((size_t)kSplitSlots * sizeof(int)));
+    w.part = reinterpret_cast<float*>(take((size_t)kSplitSlots * kSplitSlotBytes));
   } else {
     w.h = reinterpret_cast<float*>(take((size_t)R[0] * inter[0] * sizeof(float)));
   }
@@ -134,15 +144,18 @@ constexpr int kSmallT = 16;
 hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
                                const uint8_t* mask,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, bool perm, hipStream_t s);
+                               float* partial, int8_t* xq, float* xs, bool perm,
+                               int* split_cnt, hipStream_t s);
 // counts[e] += number of topk_idx entries equal to e (entries outside [0, E) skipped)
 hipError_t launch_expert_counts(const int32_t* idx, long long n, int E, unsigned long long* counts,
                                 hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets,
                           int32_t* row_token, int32_t* token_row, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// (split_cnt, if not NULL: the kSplitSlots split-K counters, cleared here so
+// that the FFN launches after this one find them zero)
 hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig, bool perm,
-                              hipStream_t s);
+                              int* split_cnt, hipStream_t s);
 // Encodes x (unless x_encoded) and runs gate/up then down for 1 or 2 expert
 // sets (same format) in one pair of launches.
 hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,

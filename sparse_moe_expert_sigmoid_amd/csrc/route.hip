@@ -259,8 +259,11 @@ __global__ __launch_bounds__(256) void router_tail_kernel(
     const float* __restrict__ bias, const uint8_t* __restrict__ mask, int T, int E, int k,
     int router, float scale,
     int32_t* __restrict__ idx, float* __restrict__ w, int8_t* __restrict__ xq,
-    float* __restrict__ xs, bool perm) {
+    float* __restrict__ xs, bool perm, int* __restrict__ split_cnt) {
   __shared__ unsigned long long keys[256 * EPT];
+  if (split_cnt)  // the FFN launches that follow start from zero counters
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < kSplitSlots; q += gridDim.x * blockDim.x)
+      split_cnt[q] = 0;
   __shared__ float red[4];
   __shared__ float xred[4];
   __shared__ float sel_s[kMaxK];
@@ -319,10 +322,10 @@ template <int EPT>
 hipError_t launch_tail(const float* partial, int nchunk, const float* x, int d, const float* bias,
                        const uint8_t* mask,
                        int T, int E, int k, int router, float scale, int32_t* idx, float* w,
-                       int8_t* xq, float* xs, bool perm, hipStream_t s) {
+                       int8_t* xq, float* xs, bool perm, int* split_cnt, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TAIL, s);
   hipLaunchKernelGGL(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
-                     bias, mask, T, E, k, router, scale, idx, w, xq, xs, perm);
+                     bias, mask, T, E, k, router, scale, idx, w, xq, xs, perm, split_cnt);
   return hipGetLastError();
 }
 
@@ -358,7 +361,7 @@ hipError_t launch_router_small(int router, const float* x, const float* wr, cons
                                const uint8_t* mask,
                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
                                float* partial, int8_t* xq, float* xs, bool perm,
-                               hipStream_t s) {
+                               int* split_cnt, hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
   {
     TimedLaunch tl(K_ROUTER_LOGITS, s);
@@ -370,12 +373,12 @@ hipError_t launch_router_small(int router, const float* x, const float* wr, cons
   if (err != hipSuccess) return err;
   if (E <= 256)
     return launch_tail<1>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
-                          xs, perm, s);
+                          xs, perm, split_cnt, s);
   if (E <= 512)
     return launch_tail<2>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
-                          xs, perm, s);
+                          xs, perm, split_cnt, s);
   return launch_tail<4>(partial, nchunk, x, d, bias, mask, T, E, k, router, scale, idx, w, xq,
-                          xs, perm, s);
+                          xs, perm, split_cnt, s);
 }
 
 }  // namespace moe

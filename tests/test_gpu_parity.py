@@ -537,3 +537,41 @@ def test_abi_errors(ctx):
     with pytest.raises(B.MoeError) as e:
         ctx.moe_expert_ffn(wide, 0, x, 4, L.row_token, L.offsets, 32, L.rows, L.ws)
     assert e.value.status == B.MOE_E_UNSUPPORTED and "16384" in str(e.value)
+
+
+# K split across workgroups (decode launches with fewer work units than CUs).
+# Each case is sized so the launcher splits; the comment gives the arithmetic.
+#  int8 gate/up: 9 tiles (8 slots + shared) x 512/64 column blocks = 72 units
+#    on 256 CUs, 36 K-steps: split 3 ways (integer partials, exact).
+#  int8 down: 9 tiles x 512/64 output blocks = 72 units, I = 2048: 3 ways
+#    (fp32 partials added in workgroup order).
+#  int4 down: 8 tiles x 512/64 = 64 units, I = 2048 (16 spans): 2 ways.
+_SPLIT_CASES = {
+    "i8_gate_up": dict(d=2304, E=64, k=8, inter=512, shared="int8_row", shared_inter=512),
+    "i8_down": dict(d=512, E=64, k=8, inter=2048, shared="int8_row", shared_inter=2048),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_SPLIT_CASES))
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_forward_split_k(ctx, case, T):
+    print(f"[split] {case} T={T}", flush=True)
+    _forward_vs_oracle(ctx, "tiny", T=T, xseed=0x4D6F4580 + T, **_SPLIT_CASES[case])
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_forward_split_k_int4_down(ctx, T):
+    print(f"[split] int4 down T={T}", flush=True)
+    _forward_vs_oracle(ctx, "qwen_decode", T=T, d=512, inter=2048, xseed=0x4D6F4590 + T)
+
+
+def test_forward_split_k_repeatable(ctx):
+    # the join adds partials in workgroup order: repeated calls agree bit for bit
+    import torch
+    for name, kw in (("tiny", _SPLIT_CASES["i8_down"]), ("qwen_decode", dict(d=512, inter=2048))):
+        inp = inputs(name, T=2, xseed=0x4D6F4577, **kw)
+        L = device_layer(ctx, name, T=2, xseed=0x4D6F4577, **kw)
+        xd = to_dev(inp.x)
+        ys = [L.forward_fused(xd).clone() for _ in range(3)]
+        torch.cuda.synchronize()
+        assert all(torch.equal(ys[0], y) for y in ys[1:])
