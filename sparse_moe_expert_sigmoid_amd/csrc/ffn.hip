@@ -1355,6 +1355,8 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   const int ksteps = FMT == 1 ? d / kKStep : d / 128;  // K-steps (int4: spans) per unit
   // (only the small-batch launches split: they are the ones that leave CUs idle)
   SplitK sk{PAIRS ? split_ways(blocks, ksteps / ks, 2) : 1, ws.cnt, ws.part};
+  // the join area holds kSplitSlots (unit, workgroup) slots and one count per unit
+  if (sk.n > 1 && blocks * sk.n > kSplitSlots) return hipErrorInvalidValue;
   const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
   // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
   const size_t lds_gu = PAIRS ? emax : (size_t)mt * (2 * d + 16);
@@ -1382,6 +1384,7 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   const int dsteps = FMT == 1 ? imax / kKStep : imax / 128;
   const bool ng2 = FMT == 1 && dks == 1 && d % 128 == 0;
   SplitK dsk{PAIRS && !ng2 ? split_ways(dblocks, dsteps / dks, 2) : 1, ws.cnt, ws.part};
+  if (dsk.n > 1 && dblocks * dsk.n > kSplitSlots) return hipErrorInvalidValue;
   const size_t lds_dn =
       PAIRS ? emax : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
 #define MOE_DN(KSV, NGV, SPL)                                                               \

@@ -540,15 +540,20 @@ def test_abi_errors(ctx):
 
 
 # K split across workgroups (decode launches with fewer work units than CUs).
-# Each case is sized so the launcher splits; the comment gives the arithmetic.
-#  int8 gate/up: 9 tiles (8 slots + shared) x 512/64 column blocks = 72 units
-#    on 256 CUs, 36 K-steps: split 3 ways (integer partials, exact).
+# The T = 1 cases are sized so the launcher splits (256 CUs); the arithmetic:
+#  int8 gate/up: 9 tiles (8 slots + shared) x 512/64 column blocks = 72 units,
+#    36 K-steps: split 3 ways (integer partials, exact).
 #  int8 down: 9 tiles x 512/64 output blocks = 72 units, I = 2048: 3 ways
 #    (fp32 partials added in workgroup order).
 #  int4 down: 8 tiles x 512/64 = 64 units, I = 2048 (16 spans): 2 ways.
+#  int8 gate/up at T = 2 (pairs grouped in-kernel): 17 tiles x 384/64 = 102
+#    units: 2 ways.
+# At T = 2 and 3 the other shapes have too many tiles to split: those cases
+# check the unsplit path of the same shapes.
 _SPLIT_CASES = {
     "i8_gate_up": dict(d=2304, E=64, k=8, inter=512, shared="int8_row", shared_inter=512),
     "i8_down": dict(d=512, E=64, k=8, inter=2048, shared="int8_row", shared_inter=2048),
+    "i8_gate_up_pairs": dict(d=2304, E=64, k=8, inter=384, shared="int8_row", shared_inter=384),
 }
 
 
