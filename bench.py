@@ -508,7 +508,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X and "
+        print("bench.py measures one GPU: the library runs the layer on a single MI355X and "
               "has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
