@@ -1072,6 +1072,186 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
 }
 #undef RING_SLOT
 
+// Down projection as a grouped GEMM on the gate/up kernel's scheme: tiles of
+// 64 WT rows of one expert, 8 wavefronts of 64 rows x 16 NF output columns (NF
+// weight fragments of 16 output rows), every operand a 1 KB MFMA block moved
+// straight into an LDS ring slot (weight blocks of the tiled layout, and h
+// digit blocks gathered by row), 3 K-steps in flight, one bare barrier per
+// K-step.  h carries one scale per row and 128 inputs: each 128-input block's
+// two K-steps accumulate in int32 on the matrix cores, then fold into fp32 as
+// (256 d0 + d1) times the block scale / 256.  The tile's block scales are
+// staged in LDS once, before the ring starts, so that the loads in the K loop
+// follow the ring's fixed pattern.
+constexpr int kDnMaxBlocks = 32;  // 128-input scale blocks staged per row (I <= 4096)
+constexpr int kDnFrags = 4;       // weight fragments (16 output columns each) per wavefront
+template <int WT, int NF>
+struct DnShape {
+  static constexpr int CW = kPWaves / WT;          // column wavefronts
+  static constexpr int ROWS = 64 * WT;             // tile rows
+  static constexpr int COLS = 16 * NF * CW;        // output columns per workgroup
+  static constexpr int NA = COLS / 16;             // weight blocks per K-step
+  static constexpr int NB = 2 * ROWS / 16;         // digit blocks per K-step
+  static constexpr int A_PER = NA / kPWaves;       // per wavefront
+  static constexpr int B_PER = NB / kPWaves;
+  static constexpr int SLOT = (NA + NB) * kPBlk;   // LDS bytes per K-step slot
+  // slots in the ring: 4 where they fit beside the staged scales
+  static constexpr int NS = 4 * SLOT + ROWS * kDnMaxBlocks * 4 <= 160 * 1024 - 1024 ? 4 : 3;
+  static constexpr int WAIT = (NS - 2) * (A_PER + B_PER);  // loads left in flight
+};
+
+#define RING_SLOT(q) ((q) == 0 ? ring0 : (q) == 1 ? ring1 : (q) == 2 ? ring2 : ring3)
+
+template <int LAY, int WT, int NF>
+__global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int d) {
+  using S = DnShape<WT, NF>;
+  __shared__ __attribute__((aligned(16))) int8_t ring0[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring1[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring2[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring3[S::NS == 4 ? S::SLOT : 16];
+  __shared__ float sc_sm[S::ROWS][kDnMaxBlocks];
+  Job job;
+  if (!find_job(g0, g1, S::ROWS, blockIdx.y, job)) return;
+  const Group G = job.g == 0 ? g0 : g1;
+  const int I = G.inter;
+  const int cb = blockIdx.x * S::COLS;
+  if (cb >= d) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int wc = wave % S::CW, wt = wave / S::CW;
+  const int c0 = cb + wc * 16 * NF;  // this wavefront's 16 NF output columns
+  const int i = lane & 15, g = lane >> 4;
+  const int r0 = job.r0, nr = job.nr;
+  const int ntg = min(4, max(0, (nr - 64 * wt + 15) / 16));
+  const bool active = c0 < d && ntg > 0;  // every wavefront issues loads and meets the barriers
+  const int nhb = I / 128 + (I % 128 != 0);  // h scale blocks per row
+  for (int q = threadIdx.x; q < S::ROWS * nhb; q += blockDim.x) {
+    const int j = q / nhb, b = q % nhb;
+    sc_sm[j][b] = j < nr ? G.hs[(size_t)(r0 + j) * nhb + b] * (1.0f / 256.0f) : 0.0f;
+  }
+  __syncthreads();
+
+  // this wavefront's loads per K-step: weight blocks A_PER w .. (block q =
+  // output rows cb + 16 q) and digit blocks B_PER w .. (block q = row group
+  // q / 2, digit q % 2; rows past the tile re-read the tile's first row)
+  const int8_t* W = static_cast<const int8_t*>(G.wdn);
+  const int8_t* asrc[S::A_PER];
+  const int8_t* bsrc[S::B_PER];
+#pragma unroll
+  for (int u = 0; u < S::A_PER; ++u) {
+    const int col = cb + 16 * (S::A_PER * wave + u);
+    const size_t row0 = (size_t)job.e * d + (col < d ? col : 0);
+    asrc[u] = wblock_src<LAY>(W, row0, I, lane);
+  }
+#pragma unroll
+  for (int u = 0; u < S::B_PER; ++u) {
+    const int blk = S::B_PER * wave + u;
+    const int j = 16 * (blk >> 1) + i;
+    bsrc[u] = G.hq + (size_t)(r0 + (j < nr ? j : 0)) * 2 * I + (blk & 1) * I + 16 * g;
+  }
+  const int nsteps = I / kKStep;
+  const int last = nsteps - 1;
+  auto issue = [=](int8_t* slot, int step) {
+    const int st = min(step, last);
+#pragma unroll
+    for (int u = 0; u < S::A_PER; ++u)
+      lds_load16(asrc[u] + (size_t)st * wblock_step<LAY>(),
+                 slot + (S::A_PER * wave + u) * kPBlk);
+#pragma unroll
+    for (int u = 0; u < S::B_PER; ++u)
+      lds_load16(bsrc[u] + st * kKStep, slot + (S::NA + S::B_PER * wave + u) * kPBlk);
+  };
+
+  v4i p[NF][4][2];      // [weight fragment][row group][digit]: int32 sums of a 128-input block
+  float acc[NF][4][4];  // fp32 sums over the blocks
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      p[f][t][0] = p[f][t][1] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[f][t][c] = 0.0f;
+    }
+
+#pragma unroll
+  for (int q = 0; q < S::NS - 1; ++q) issue(RING_SLOT(q), q);
+
+#define DN_STEP(STEP, Q)                                                                      \
+  {                                                                                           \
+    MOE_WAIT_VM(S::WAIT);                                                                     \
+    ring_barrier();                                                                           \
+    if (active) {                                                                             \
+      const int8_t* slot = RING_SLOT(Q);                                                      \
+      v4i a[NF];                                                                              \
+      _Pragma("unroll") for (int f = 0; f < NF; ++f)                                          \
+        a[f] = lds_frag(slot + (NF * wc + f) * kPBlk, lane);                                  \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        if (t < ntg) {                                                                        \
+          const int8_t* bb = slot + (S::NA + 2 * (4 * wt + t)) * kPBlk;                       \
+          const v4i b0 = lds_frag(bb, lane);                                                  \
+          const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
+          _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                    \
+            p[f][t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b0, p[f][t][0], 0, 0, 0); \
+            p[f][t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b1, p[f][t][1], 0, 0, 0); \
+          }                                                                                   \
+        }                                                                                     \
+      }                                                                                       \
+      if (((STEP) & 1) || (STEP) == last) { /* end of a 128-input scale block */             \
+        const int blk = (STEP) >> 1;                                                          \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                       \
+          if (t < ntg) {                                                                      \
+            const float sg = sc_sm[64 * wt + 16 * t + i][blk];                                \
+            _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                  \
+              _Pragma("unroll") for (int c = 0; c < 4; ++c)                                   \
+                acc[f][t][c] = fmaf(sg, (float)(p[f][t][0][c] * 256 + p[f][t][1][c]),         \
+                                    acc[f][t][c]);                                            \
+              p[f][t][0] = p[f][t][1] = v4i{0, 0, 0, 0};                                      \
+            }                                                                                 \
+          }                                                                                   \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    issue(RING_SLOT(((Q) + S::NS - 1) % S::NS), (STEP) + S::NS - 1);                          \
+  }
+  int s0 = 0;
+  if constexpr (S::NS == 4) {
+    for (; s0 + 4 <= nsteps; s0 += 4) {
+      DN_STEP(s0, 0)
+      DN_STEP(s0 + 1, 1)
+      DN_STEP(s0 + 2, 2)
+      DN_STEP(s0 + 3, 3)
+    }
+    if (s0 < nsteps) DN_STEP(s0, 0)
+    if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1)
+    if (s0 + 2 < nsteps) DN_STEP(s0 + 2, 2)
+  } else {
+    for (; s0 + 3 <= nsteps; s0 += 3) {
+      DN_STEP(s0, 0)
+      DN_STEP(s0 + 1, 1)
+      DN_STEP(s0 + 2, 2)
+    }
+    if (s0 < nsteps) DN_STEP(s0, 0)
+    if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1)
+  }
+#undef DN_STEP
+  MOE_WAIT_VM(0);
+  if (!active) return;
+  // lane (i, g) holds output columns c0 + 16 f + 4 g + c of tile row 64 wt + 16 t + i
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (c0 + 16 * f >= d) break;  // (d is a multiple of 16)
+    const float* sd = G.sdn + (size_t)job.e * d + c0 + 16 * f + 4 * g;
+    const float s0v = sd[0], s1v = sd[1], s2v = sd[2], s3v = sd[3];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = 64 * wt + 16 * t + i;
+      if (t >= ntg || j >= nr) continue;
+      *reinterpret_cast<float4*>(G.out + (size_t)(r0 + j) * d + c0 + 16 * f + 4 * g) =
+          make_float4(s0v * acc[f][t][0], s1v * acc[f][t][1], s2v * acc[f][t][2],
+                      s3v * acc[f][t][3]);
+    }
+  }
+}
+#undef RING_SLOT
+
 // The down projection uses smaller tiles: up to 64 rows, a workgroup of 8
 // wavefronts owning 128 output columns (16 per wavefront).  Its h scales
 // change every 128 inputs (the gate/up GEMM writes one per row and 128-column
@@ -1461,9 +1641,25 @@ hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const flo
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  TimedLaunch tl(K_FFN_I8_DOWN_GEMM, s);
+  if (imax <= 128 * kDnMaxBlocks) {  // block scales staged in LDS: I <= 4096
+    if (tall) {
+      using S = DnShape<2, kDnFrags>;
+      a.tiles = tiles_of(a, S::ROWS);
+      b.tiles = tiles_of(b, S::ROWS);
+      hipLaunchKernelGGL((down_gemm_kernel<LAY, 2, kDnFrags>), dim3((d + S::COLS - 1) / S::COLS,
+                         a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d);
+    } else {
+      using S = DnShape<1, kDnFrags>;
+      a.tiles = tiles_of(a, S::ROWS);
+      b.tiles = tiles_of(b, S::ROWS);
+      hipLaunchKernelGGL((down_gemm_kernel<LAY, 1, kDnFrags>), dim3((d + S::COLS - 1) / S::COLS,
+                         a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d);
+    }
+    return hipGetLastError();
+  }
   a.tiles = tiles_of(a, kDRows);
   b.tiles = tiles_of(b, kDRows);
-  TimedLaunch tl(K_FFN_I8_DOWN_GEMM, s);
   hipLaunchKernelGGL(down_gemm64_kernel<LAY>, dim3((d + 127) / 128, a.tiles + b.tiles),
                      dim3(kPWaves * kWave), 0, s, a, b, d);
   return hipGetLastError();
