@@ -580,3 +580,12 @@ def test_forward_split_k_repeatable(ctx):
         ys = [L.forward_fused(xd).clone() for _ in range(3)]
         torch.cuda.synchronize()
         assert all(torch.equal(ys[0], y) for y in ys[1:])
+
+
+def test_layer_gemm_path_wide_inter(ctx):
+    # I = 4224 (33 scale blocks of 128) is above what the ring down GEMM
+    # stages in LDS: the register-staged down GEMM runs; 64 rows per expert
+    # select the GEMM path
+    kw = dict(T=128, d=256, E=4, k=2, inter=4224, shared="int8_row", shared_inter=4224,
+              xseed=0x4D6F4594)
+    _forward_vs_oracle(ctx, "tiny", **kw)
