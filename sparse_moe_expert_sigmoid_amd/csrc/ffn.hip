@@ -685,10 +685,17 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   const int c0 = blockIdx.x * 64 * NG + cg * 16 * NG;  // output rows of this wavefront
   const int i = lane & 15, g = lane >> 4;
   const bool jv = i < job.nr;
-  const int r = !jv ? 0 : PAIRS ? rows_sm[i] : job.r0 + i;
-  const int8_t* hb0 = PAIRS ? G.hq + (size_t)r * 2 * I : lds + i * ldr;
+  // Small batches (PAIRS, h rows from L2): lanes of rows past the tile read
+  // the tile's first row.  They only feed MFMA output column i, which those
+  // lanes never store, and unconditional global loads keep the compiler's
+  // count of loads in flight exact.  Tiles read h from LDS, where skipping
+  // the rows past the tile is cheaper (measured).
+  const bool hv = PAIRS || jv;
+  const int ii = jv ? i : 0;
+  const int r = PAIRS ? rows_sm[ii] : job.r0 + ii;
+  const int8_t* hb0 = PAIRS ? G.hq + (size_t)r * 2 * I : lds + ii * ldr;
   const int8_t* hb1 = hb0 + I;
-  const float* hsr = PAIRS ? G.hs + (size_t)r * nhb : lds_s + i * nhb;
+  const float* hsr = PAIRS ? G.hs + (size_t)r * nhb : lds_s + ii * nhb;
   const size_t row0 = (size_t)job.e * d + c0;
   const v4i zero = {0, 0, 0, 0};
   float acc[NG][4];
@@ -715,23 +722,24 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
         x0[u] = zero;
         x1[u] = zero;
         sg[u] = 0.0f;
-        if (jv) {
+        if (hv) {
           x0[u] = *reinterpret_cast<const v4i*>(hb0 + ss * kKStep + 16 * g);
           x1[u] = *reinterpret_cast<const v4i*>(hb1 + ss * kKStep + 16 * g);
           sg[u] = hsr[ss];
         }
       }
+      // steps past the slice (the last batch) get a zero scale: their
+      // (finite) products add nothing, and no branch keeps loads in front
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (s + u < s_end) {
+        const float su = s + u < s_end ? sg[u] : 0.0f;
 #pragma unroll
-          for (int q = 0; q < NG; ++q) {
-            const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[q][u], x0[u], zero, 0, 0, 0);
-            const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[q][u], x1[u], zero, 0, 0, 0);
+        for (int q = 0; q < NG; ++q) {
+          const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[q][u], x0[u], zero, 0, 0, 0);
+          const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[q][u], x1[u], zero, 0, 0, 0);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              acc[q][c] = fmaf(sg[u], fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[q][c]);
-          }
+          for (int c = 0; c < 4; ++c)
+            acc[q][c] = fmaf(su, fmaf((float)p1[c], 1.0f / 256.0f, (float)p0[c]), acc[q][c]);
         }
       }
     }
@@ -751,13 +759,13 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
       for (int q = 0; q < 4; ++q) {
         x0[q] = 0;
         x1[q] = 0;
-        if (jv) {
+        if (hv) {
           x0[q] = *reinterpret_cast<const long*>(hb0 + 128 * m + 32 * g + 8 * q);
           x1[q] = *reinterpret_cast<const long*>(hb1 + 128 * m + 32 * g + 8 * q);
         }
       }
-      sg[0] = jv ? hsr[2 * m] * (1.0f / 256.0f) : 0.0f;
-      sg[1] = jv ? hsr[2 * m + 1] * (1.0f / 256.0f) : 0.0f;
+      sg[0] = hv ? hsr[2 * m] * (1.0f / 256.0f) : 0.0f;
+      sg[1] = hv ? hsr[2 * m + 1] * (1.0f / 256.0f) : 0.0f;
       if constexpr (FMT == 2) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
