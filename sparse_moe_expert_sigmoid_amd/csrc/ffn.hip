@@ -92,15 +92,41 @@ struct Job {
   int g, e, r0, nr;
 };
 
-// K split across the n workgroups of one work unit (grid z = 0 .. n-1).  Each
-// writes its partial sums to its slot; the last to arrive (by an atomic count)
-// adds every slot in workgroup order, so the result does not depend on arrival
-// order, clears the count for the next launch and goes on to the epilogue.
+// K split across the workgroups of one work unit.  Each writes its partial
+// sums to its slot; the last to arrive (by an atomic count) adds every slot in
+// workgroup order, so the result does not depend on arrival order, clears the
+// count for the next launch and goes on to the epilogue.  The two expert sets
+// of a launch split n0 and n1 ways: the grid's y range holds group 0's tiles
+// n0 times each, then group 1's n1 times each (virtual tiles).
 struct SplitK {
-  int n;       // 1: no split
+  int n0, n1;  // workgroups per unit of group 0 / group 1 (1: no split)
   int* cnt;    // one arrival count per unit, zero before the launch
-  float* part; // kSplitSlotBytes per (unit, workgroup)
+  float* part; // kSplitSlotBytes per (unit, workgroup) of the units that split
 };
+
+// Where virtual tile v (unit column x of gx) sits: its real tile, its K-split
+// index and count, and its unit's first join slot (group 0's units take slots
+// first when they split, then group 1's).
+struct SplitPos {
+  int tile, kw, n, slot0;
+};
+__device__ inline SplitPos split_pos(const SplitK& sk, int v, int t0, int gx, int x) {
+  SplitPos p;
+  const int v0 = t0 * sk.n0;
+  if (v < v0) {
+    p.tile = v / sk.n0;
+    p.kw = v % sk.n0;
+    p.n = sk.n0;
+    p.slot0 = (p.tile * gx + x) * sk.n0;
+  } else {
+    const int v1 = v - v0;
+    p.tile = t0 + v1 / sk.n1;
+    p.kw = v1 % sk.n1;
+    p.n = sk.n1;
+    p.slot0 = (sk.n0 > 1 ? t0 * gx * sk.n0 : 0) + ((p.tile - t0) * gx + x) * sk.n1;
+  }
+  return p;
+}
 
 // holder lanes carry N values of type V (int32 digit sums or fp32 partials);
 // grp is the wavefront's index among the holders.  Returns false in every workgroup but
@@ -111,8 +137,8 @@ struct SplitK {
 // fence costs: each thread waits for its own slot stores to complete
 // (vmcnt 0) before the barrier, and the count is taken after the barrier.
 template <typename V, int N>
-__device__ inline bool split_join(const SplitK& sk, int unit, int kw, int grp, bool holder, V* v,
-                                  int* flag_sm) {
+__device__ inline bool split_join(const SplitK& sk, int unit, int slot0, int kw, int n, int grp,
+                                  bool holder, V* v, int* flag_sm) {
   // slot layout [grp][c][lane]: each store and load of a value is 256
   // contiguous bytes over the wavefront
   V* base = reinterpret_cast<V*>(sk.part);
@@ -120,7 +146,7 @@ __device__ inline bool split_join(const SplitK& sk, int unit, int kw, int grp, b
   const int lane = threadIdx.x & (kWave - 1);
   const size_t at = (size_t)grp * N * kWave + lane;
   if (holder) {
-    V* dst = base + (size_t)(unit * sk.n + kw) * kPer + at;
+    V* dst = base + (size_t)(slot0 + kw) * kPer + at;
 #pragma unroll
     for (int c = 0; c < N; ++c)
       __hip_atomic_store(dst + c * kWave, v[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -130,14 +156,14 @@ __device__ inline bool split_join(const SplitK& sk, int unit, int kw, int grp, b
   __syncthreads();
   if (threadIdx.x == 0)
     *flag_sm = __hip_atomic_fetch_add(sk.cnt + unit, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == sk.n - 1;
+                                      __HIP_MEMORY_SCOPE_AGENT) == n - 1;
   __syncthreads();
   if (!*flag_sm) return false;
   if (holder) {
 #pragma unroll
     for (int c = 0; c < N; ++c) v[c] = V(0);
-    for (int q = 0; q < sk.n; ++q) {
-      V* src = base + (size_t)(unit * sk.n + q) * kPer + at;
+    for (int q = 0; q < n; ++q) {
+      V* src = base + (size_t)(slot0 + q) * kPer + at;
 #pragma unroll
       for (int c = 0; c < N; ++c)
         v[c] += __hip_atomic_load(src + c * kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -335,26 +361,34 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
   // K-slice partials: int8 path 16 ints per lane, int4 path 8 floats per lane
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 16 : 1];
   __shared__ int rows_sm[kTileRows], toks_sm[kTileRows], sh_sm[3], last_sm;
+  int vtile = blockIdx.y, kw = 0, nsplit = 1, slot0 = 0;  // (see SplitK)
+  if constexpr (SPLIT) {
+    const SplitPos sp = split_pos(sk, blockIdx.y, g0.tiles, gridDim.x, blockIdx.x);
+    vtile = sp.tile;
+    kw = sp.kw;
+    nsplit = sp.n;
+    slot0 = sp.slot0;
+  }
   {
-    const bool first = (int)blockIdx.y < g0.tiles;
+    const bool first = vtile < g0.tiles;
     if ((int)blockIdx.x * 64 * NCB >= (first ? g0.inter : g1.inter)) return;
   }
   Job job;
   if (PAIRS) {  // the expert histogram uses the dynamic LDS area
-    if (!find_rows(g0, g1, mt, blockIdx.y, job, rows_sm, toks_sm, reinterpret_cast<int*>(lds),
+    if (!find_rows(g0, g1, mt, vtile, job, rows_sm, toks_sm, reinterpret_cast<int*>(lds),
                    sh_sm, true))
       return;
   } else {
-    if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+    if (!find_job(g0, g1, mt, vtile, job)) return;
   }
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
   const int i = lane & 15, g = lane >> 4;
-  // K slice of this wavefront: slice kw * KS + kp of sk.n * KS (SPLIT), else kp of KS
-  const int ksl = SPLIT ? (int)blockIdx.z * KS + kp : kp, nsl = SPLIT ? sk.n * KS : KS;
-  const int unit = blockIdx.y * gridDim.x + blockIdx.x;  // (NCB == 1 when SPLIT)
+  // K slice of this wavefront: slice kw * KS + kp of nsplit * KS
+  const int ksl = kw * KS + kp, nsl = nsplit * KS;
+  const int unit = vtile * gridDim.x + blockIdx.x;  // (NCB == 1 when SPLIT)
   // x digits of the tile rows.  Small batches (PAIRS) read their few token
   // rows straight from L2: no staging barrier before the weight loads, no LDS
   // to limit how many workgroups a CU holds.  Tiles of up to 16 rows stage them
@@ -456,13 +490,13 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
           }
         }
       }
-      if constexpr (SPLIT) {  // exact int32 sums across the unit's workgroups
+      if (SPLIT && nsplit > 1) {  // exact int32 sums across the unit's workgroups
         int v[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           v[c] = a0[c]; v[4 + c] = a1[c]; v[8 + c] = b0[c]; v[12 + c] = b1[c];
         }
-        if (!split_join<int, 16>(sk, unit, blockIdx.z, cg, kp == 0, v, &last_sm))
+        if (!split_join<int, 16>(sk, unit, slot0, kw, nsplit, cg, kp == 0, v, &last_sm))
           return;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -582,11 +616,11 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
           }
         }
       }
-      if constexpr (SPLIT) {  // fp32 partials added in workgroup order
+      if (SPLIT && nsplit > 1) {  // fp32 partials added in workgroup order
         float v[8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) { v[c] = fa[c]; v[4 + c] = fb[c]; }
-        if (!split_join<float, 8>(sk, unit, blockIdx.z, cg, kp == 0, v, &last_sm))
+        if (!split_join<float, 8>(sk, unit, slot0, kw, nsplit, cg, kp == 0, v, &last_sm))
           return;
 #pragma unroll
         for (int c = 0; c < 4; ++c) { fa[c] = v[c]; fb[c] = v[4 + c]; }
@@ -652,13 +686,21 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   extern __shared__ int8_t lds[];
   __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 4 : 1];
   __shared__ int rows_sm[kTileRows], sh_sm[3], last_sm;
+  int vtile = blockIdx.y, kw = 0, nsplit = 1, slot0 = 0;  // (see SplitK)
+  if constexpr (SPLIT) {
+    const SplitPos sp = split_pos(sk, blockIdx.y, g0.tiles, gridDim.x, blockIdx.x);
+    vtile = sp.tile;
+    kw = sp.kw;
+    nsplit = sp.n;
+    slot0 = sp.slot0;
+  }
   Job job;
   if (PAIRS) {  // the expert histogram borrows the h staging area
-    if (!find_rows(g0, g1, mt, blockIdx.y, job, rows_sm, nullptr, reinterpret_cast<int*>(lds),
+    if (!find_rows(g0, g1, mt, vtile, job, rows_sm, nullptr, reinterpret_cast<int*>(lds),
                    sh_sm, false))
       return;
   } else {
-    if (!find_job(g0, g1, mt, blockIdx.y, job)) return;
+    if (!find_job(g0, g1, mt, vtile, job)) return;
   }
   const Group G = job.g == 0 ? g0 : g1;
   const int I = G.inter;
@@ -680,8 +722,8 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int cg = wave & 3, kp = wave >> 2;
-  // K slice of this wavefront: slice kw * KS + kp of sk.n * KS (SPLIT), else kp of KS
-  const int ksl = SPLIT ? (int)blockIdx.z * KS + kp : kp, nsl = SPLIT ? sk.n * KS : KS;
+  // K slice of this wavefront: slice kw * KS + kp of nsplit * KS
+  const int ksl = kw * KS + kp, nsl = nsplit * KS;
   const int c0 = blockIdx.x * 64 * NG + cg * 16 * NG;  // output rows of this wavefront
   const int i = lane & 15, g = lane >> 4;
   const bool jv = i < job.nr;
@@ -813,9 +855,9 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
       }
     }
   }
-  if constexpr (SPLIT) {  // fp32 partials added in workgroup order (NG == 1 when SPLIT)
-    const int unit = blockIdx.y * gridDim.x + blockIdx.x;
-    if (!split_join<float, 4>(sk, unit, blockIdx.z, cg, kp == 0, acc[0], &last_sm))
+  if (SPLIT && nsplit > 1) {  // fp32 partials added in workgroup order (NG == 1 when SPLIT)
+    const int unit = vtile * gridDim.x + blockIdx.x;
+    if (!split_join<float, 4>(sk, unit, slot0, kw, nsplit, cg, kp == 0, acc[0], &last_sm))
       return;
   }
   if ((SPLIT && kp != 0) || !jv) return;  // (without SPLIT, kp > 0 left above)
@@ -1531,6 +1573,28 @@ inline int split_ways(long long units, int ksteps_per_wave_at_1, int min_steps) 
   return best;
 }
 
+// Split plan for a launch of t0 + t1 tiles (groups 0 and 1) x gx column
+// units: every unit alike (n0 = n1 from split_ways) when CUs would otherwise
+// sit idle; else, when group 0's units fit the chip and group 1's spill over
+// it (e.g. 256 routed units and the shared expert's 32 at one token), group 1
+// alone splits into enough small workgroups that each CU takes one beside its
+// group-0 unit.  kpw: K-steps per wavefront unsplit.  Returns false when the
+// join area cannot hold the plan's slots and counts.
+inline bool plan_split(long long t0, long long t1, int gx, int kpw, int min_steps, int& n0,
+                       int& n1) {
+  const long long u0 = t0 * gx, u1 = t1 * gx, cus = g_cu_count;
+  n0 = n1 = split_ways(u0 + u1, kpw, min_steps);
+  if (n0 == 1 && u1 > 0 && u0 <= cus && u0 + u1 > cus) {
+    int n = (int)((cus + u1 - 1) / u1);
+    n = n < 8 ? n : 8;
+    while (n > 1 && (kpw / n < min_steps || u1 * n > kSplitSlots)) --n;
+    n1 = n;
+  }
+  if (n0 == 1 && n1 == 1) return true;
+  const long long slots = (n0 > 1 ? u0 * n0 : 0) + (n1 > 1 ? u1 * n1 : 0);
+  return slots <= kSplitSlots && u0 + u1 <= kSplitSlots;
+}
+
 template <int FMT, int LAY, bool PAIRS>
 hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8_t* xq,
                        const float* xs, const FfnWs& ws, hipStream_t s) {
@@ -1542,9 +1606,10 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   // and across workgroups when the units do not spread evenly over the CUs
   const int ksteps = FMT == 1 ? d / kKStep : d / 128;  // K-steps (int4: spans) per unit
   // (only the small-batch launches split: they are the ones that leave CUs idle)
-  SplitK sk{PAIRS ? split_ways(blocks, ksteps / ks, 2) : 1, ws.cnt, ws.part};
-  // the join area holds kSplitSlots (unit, workgroup) slots and one count per unit
-  if (sk.n > 1 && blocks * sk.n > kSplitSlots) return hipErrorInvalidValue;
+  SplitK sk{1, 1, ws.cnt, ws.part};
+  if (PAIRS && !plan_split(a.tiles, b.tiles, imax / 64, ksteps / ks, 2, sk.n0, sk.n1))
+    return hipErrorInvalidValue;  // beyond the join area (the plan keeps within it)
+  const bool gsplit = sk.n0 > 1 || sk.n1 > 1;
   const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
   // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
   const size_t lds_gu = PAIRS ? emax : (size_t)mt * (2 * d + 16);
@@ -1553,8 +1618,8 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
                      lds_gu, s, a, b, d, mt, xq, xs, sk)
   {
     TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
-    dim3 grid(imax / 64, tiles, sk.n);
-    if (sk.n > 1) {
+    dim3 grid(imax / 64, gsplit ? a.tiles * sk.n0 + b.tiles * sk.n1 : tiles);
+    if (gsplit) {
       if (ks == 1) MOE_GU(1, PAIRS);
       else if (ks == 2) MOE_GU(2, PAIRS);
       else MOE_GU(4, PAIRS);
@@ -1571,16 +1636,19 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   const int dks = dblocks >= 2LL * g_cu_count ? 1 : (dblocks >= g_cu_count / 2 ? 2 : 4);
   const int dsteps = FMT == 1 ? imax / kKStep : imax / 128;
   const bool ng2 = FMT == 1 && dks == 1 && d % 128 == 0;
-  SplitK dsk{PAIRS && !ng2 ? split_ways(dblocks, dsteps / dks, 2) : 1, ws.cnt, ws.part};
-  if (dsk.n > 1 && dblocks * dsk.n > kSplitSlots) return hipErrorInvalidValue;
+  SplitK dsk{1, 1, ws.cnt, ws.part};
+  if (PAIRS && !ng2 && !plan_split(a.tiles, b.tiles, d / 64, dsteps / dks, 2, dsk.n0, dsk.n1))
+    return hipErrorInvalidValue;
+  const bool dsplit = dsk.n0 > 1 || dsk.n1 > 1;
+  const int dgy = dsplit ? a.tiles * dsk.n0 + b.tiles * dsk.n1 : tiles;
   const size_t lds_dn =
       PAIRS ? emax : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
 #define MOE_DN(KSV, NGV, SPL)                                                               \
   hipLaunchKernelGGL((down_kernel<FMT, LAY, KSV, PAIRS, NGV, SPL>),                         \
-                     dim3(d / (64 * NGV), tiles, dsk.n), dim3(256 * KSV), lds_dn, s, a, b, d, mt, dsk)
+                     dim3(d / (64 * NGV), dgy), dim3(256 * KSV), lds_dn, s, a, b, d, mt, dsk)
   TimedLaunch tl(FMT == 1 ? K_FFN_I8_DOWN : K_FFN_I4_DOWN, s);
   if (ng2) MOE_DN(1, 2, false);
-  else if (dsk.n > 1) {
+  else if (dsplit) {
     if (dks == 1) MOE_DN(1, 1, PAIRS);
     else if (dks == 2) MOE_DN(2, 1, PAIRS);
     else MOE_DN(4, 1, PAIRS);
