@@ -975,6 +975,28 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
   for (int j = threadIdx.x; j < S::ROWS; j += blockDim.x)
     tok_sm[j] = j < job.nr ? (G.row_token ? G.row_token[job.r0 + j] : job.r0 + j) : -1;
   __syncthreads();
+  // the epilogue's scales, loaded now and unconditionally (clamped indices):
+  // this wavefront's gate and up row scales and the x scales of its tile
+  // rows.  They are older than every load of the ring, whose waits therefore
+  // cover them; loaded in the epilogue under the row conditions they cost a
+  // round trip each.
+  float sgate[2][4], sup[2][4], sig[4];
+  {
+    const float* se = G.sgu + (size_t)job.e * 2 * I;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = min(c0 + 16 * q + 4 * g + c, I - 1);
+        sgate[q][c] = se[n];
+        sup[q][c] = se[I + n];
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tj = tok_sm[64 * wt + 16 * t + i];
+      sig[t] = xs[tj >= 0 ? tj : tok_sm[0]];
+    }
+  }
 
   // this wavefront's loads per K-step: weight blocks A_PER w .. (blocks
   // 0 .. 2CW-1 = gate row groups of columns cb.., then the same up rows) and
@@ -1067,23 +1089,20 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
   MOE_WAIT_VM(0);
 
   // epilogue: h per row, one scale per row and 128-column block (4 wavefronts)
-  const float* se = G.sgu + (size_t)job.e * 2 * I;
   float h[2][4][4];  // [column half][row group][c]
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = 64 * wt + 16 * t + i;
     const bool rv = active && t < ntg && j < job.nr;
-    const float sig = rv ? xs[tok_sm[j]] : 0.0f;
     float mx = 0.0f;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int n = c0 + 16 * q + 4 * g + c;
-        const float gt = rv ? se[n] * sig *
+        const float gt = rv ? sgate[q][c] * sig[t] *
                                   ((float)acc[q][t][0][c] + (float)acc[q][t][1][c] * (1.0f / 256.0f))
                             : 0.0f;
-        const float upv = rv ? se[I + n] * sig *
+        const float upv = rv ? sup[q][c] * sig[t] *
                                    ((float)acc[2 + q][t][0][c] +
                                     (float)acc[2 + q][t][1][c] * (1.0f / 256.0f))
                              : 0.0f;
@@ -1284,12 +1303,20 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
 #undef DN_STEP
   MOE_WAIT_VM(0);
   if (!active) return;
-  // lane (i, g) holds output columns c0 + 16 f + 4 g + c of tile row 64 wt + 16 t + i
+  // lane (i, g) holds output columns c0 + 16 f + 4 g + c of tile row 64 wt + 16 t + i;
+  // the output-row scales are loaded together and unconditionally (clamped
+  // columns): conditional loads would each cost a round trip
+  float sdv[NF][4];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    if (c0 + 16 * f >= d) break;  // (d is a multiple of 16)
-    const float* sd = G.sdn + (size_t)job.e * d + c0 + 16 * f + 4 * g;
-    const float s0v = sd[0], s1v = sd[1], s2v = sd[2], s3v = sd[3];
+    const int col = min(c0 + 16 * f, d - 16) + 4 * g;  // (d is a multiple of 16)
+    const float4 v = *reinterpret_cast<const float4*>(G.sdn + (size_t)job.e * d + col);
+    sdv[f][0] = v.x; sdv[f][1] = v.y; sdv[f][2] = v.z; sdv[f][3] = v.w;
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (c0 + 16 * f >= d) break;
+    const float s0v = sdv[f][0], s1v = sdv[f][1], s2v = sdv[f][2], s3v = sdv[f][3];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j = 64 * wt + 16 * t + i;

@@ -226,11 +226,21 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
   return false;
 }
 
-__device__ inline float silu_f(float z) { return z / (1.0f + expf(-z)); }
-// GELU, tanh form: z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+// The activations use the hardware's single-instruction exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32, about 1 ulp each): a few instructions per value
+// where the library exp and an IEEE division take about thirty, which
+// dominated the epilogues of the FFN kernels.  Relative error about 3e-7.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ inline float exp_approx(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// SiLU: z / (1 + e^-z)
+__device__ inline float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp_approx(-z)); }
+// GELU, tanh form: z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), with
+// tanh u = 1 - 2 / (1 + e^(2u)) (exact at both tails: e^(2u) -> 0 or inf).
 __device__ inline float gelu_tanh_f(float z) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+  const float u = c * (z + 0.044715f * z * z * z);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + exp_approx(2.0f * u));
+  return 0.5f * z * (1.0f + t);
 }
 // Gate activation of the SwiGLU-style FFN: 0 = silu, 1 = gelu_tanh.
 __device__ inline float act_f(int act, float z) { return act == 1 ? gelu_tanh_f(z) : silu_f(z); }
