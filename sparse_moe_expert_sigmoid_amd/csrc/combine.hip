@@ -14,6 +14,12 @@
 namespace moe {
 namespace {
 
+// KMAX >= k is a compile-time bound, so that every row load of a thread is
+// issued before the first one is used: slots past k read a real row (the
+// token's first) with weight 0.  Whether rows are found through
+// token_row (TR) is a template parameter for the same reason: loads under a
+// run-time condition would cost a round trip each.
+template <int KMAX, bool TR>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
                                                       const int32_t* __restrict__ token_row,
                                                       const float* __restrict__ w,
@@ -26,26 +32,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(q / d4), c = (int)(q % d4);
   const size_t o = (size_t)t * d + 4 * c;
   // all loads are issued before any arithmetic: row ids and weights, then rows
-  int r[kMaxK];
-  float wj[kMaxK];
+  int r[KMAX];
+  float wj[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    r[j] = j < k ? (token_row ? token_row[(size_t)t * k + j] : t * k + j) : -1;
-    wj[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = j < k ? j : 0;
+    r[j] = TR ? token_row[(size_t)t * k + jj] : t * k + jj;
+    const float wv = w[(size_t)t * k + jj];
+    wj[j] = j < k ? wv : 0.0f;
   }
   const float4 sh = shared ? *reinterpret_cast<const float4*>(shared + o)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
   const float4 rs = residual ? *reinterpret_cast<const float4*>(residual + o)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 v[kMaxK];
+  float4 v[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    v[j] = r[j] >= 0 ? *reinterpret_cast<const float4*>(rows + (size_t)r[j] * d + 4 * c)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < KMAX; ++j) v[j] = *reinterpret_cast<const float4*>(rows + (size_t)r[j] * d + 4 * c);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // slots in order; those past k add 0 * (a finite row value), which leaves
+  // the sum unchanged, and keeps every load in front of the first use
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (r[j] < 0) continue;
+  for (int j = 0; j < KMAX; ++j) {
     acc.x = fmaf(wj[j], v[j].x, acc.x);
     acc.y = fmaf(wj[j], v[j].y, acc.y);
     acc.z = fmaf(wj[j], v[j].z, acc.z);
@@ -68,8 +75,17 @@ hipError_t launch_combine(const float* rows, const int32_t* token_row, const flo
   const long long n = (long long)T * (d / 4);
   const int blocks = (int)((n + 255) / 256);
   TimedLaunch tl(K_COMBINE, s);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, rows, token_row, w, shared,
-                     residual, T, k, d, y);
+#define MOE_COMBINE(KM, TRV)                                                                   \
+  hipLaunchKernelGGL((combine_kernel<KM, TRV>), dim3(blocks), dim3(256), 0, s, rows, token_row, w, \
+                     shared, residual, T, k, d, y)
+  if (k <= 8) {
+    if (token_row) MOE_COMBINE(8, true);
+    else MOE_COMBINE(8, false);
+  } else {
+    if (token_row) MOE_COMBINE(kMaxK, true);
+    else MOE_COMBINE(kMaxK, false);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

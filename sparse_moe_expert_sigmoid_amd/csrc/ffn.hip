@@ -202,7 +202,7 @@ __device__ inline bool find_rows(const Group& g0, const Group& g1, int mt, int t
   job.g = first ? 0 : 1;
   if (G.pairs_idx == nullptr) {
     Tile tl;
-    if (!find_tile(G.offsets, G.E, G.R, mt, t, tl)) return false;
+    if (!find_tile<false>(G.offsets, G.E, G.R, mt, t, tl)) return false;
     job.e = tl.e;
     job.r0 = tl.r0;
     job.nr = tl.nr;

@@ -181,6 +181,9 @@ struct Tile {
   int e, r0, nr;
 };
 
+// PREFETCH: load every offset (E <= 512) before the scan (see below); kernels
+// whose registers are tight and that rarely scan leave it off.
+template <bool PREFETCH = true>
 __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int R, int mt,
                                  int tile, Tile& out) {
   if (offsets == nullptr) {  // one expert over rows [0, R)
@@ -192,15 +195,39 @@ __device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int
     return true;
   }
   const int lane = threadIdx.x & (kWave - 1);
+  // Up to kFastChunks chunks of 64 experts, every offset is loaded before the
+  // scan starts (unconditionally, indices clamped to the E + 1 offsets): one
+  // trip to memory instead of one per chunk.
+  constexpr int kFastChunks = 8;
+  int pre_st[kFastChunks], pre_en[kFastChunks];
+  const bool fast = PREFETCH && E <= kFastChunks * kWave;
+  if (fast) {
+#pragma unroll
+    for (int c = 0; c < kFastChunks; ++c) {
+      const int e = c * kWave + lane;
+      pre_st[c] = offsets[e < E ? e : E];
+      pre_en[c] = offsets[e + 1 < E ? e + 1 : E];
+    }
+  }
   int base = 0;
   for (int c0 = 0; c0 < E; c0 += kWave) {
     const int e = c0 + lane;
     int start = 0, cnt = 0;
-    if (e < E) {
+    if (fast) {
+      int st = 0, en = 0;
+#pragma unroll
+      for (int c = 0; c < kFastChunks; ++c)
+        if (c * kWave == c0) {
+          st = pre_st[c];
+          en = pre_en[c];
+        }
+      start = st;
+      cnt = e < E ? en - st : 0;
+    } else if (e < E) {
       start = offsets[e];
       cnt = offsets[e + 1] - start;
-      if (cnt < 0) cnt = 0;
     }
+    if (cnt < 0) cnt = 0;
     const int nt = (cnt + mt - 1) / mt;
     int incl = nt;
 #pragma unroll
