@@ -126,29 +126,45 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
   unsigned long long key[EPT];
   float bv[EPT];
   bool ok[EPT];  // allowed by the expert mask (and inside E)
-#pragma unroll
-  for (int m = 0; m < EPT; ++m) {
-    const int e = gtid + 256 * m;
-    bv[m] = (bias && e < E) ? bias[e] : 0.0f;
-    ok[m] = e < E && (mask == nullptr || mask[e] != 0);
-  }
-  // all slices are loaded before the first add (one trip to memory), then
-  // added in ascending order
+  // Every load of the selection is issued here and unconditionally, so that
+  // one wait covers them all (a load under a condition makes the compiler
+  // wait for every load in flight, the caller's early x loads included):
+  // expert indices clamped into [0, E), slices clamped into [0, nchunk), and
+  // an absent bias or mask read from a valid stand-in whose value is dropped.
   constexpr int kMaxChunks = 16;
+  const float* bsrc = bias ? bias : partial;
+  const uint8_t* msrc = mask ? mask : reinterpret_cast<const uint8_t*>(partial);
+  float braw[EPT], pv[EPT][kMaxChunks];
+  uint8_t mraw[EPT];
+  const bool fast = nchunk <= kMaxChunks;
 #pragma unroll
   for (int m = 0; m < EPT; ++m) {
     const int e = gtid + 256 * m;
-    const bool ok = active && e < E;
+    const int ec = e < E ? e : E - 1;
+    braw[m] = bsrc[ec];
+    mraw[m] = msrc[ec];
+    if (fast) {
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c)
+        pv[m][c] = partial[((size_t)(c < nchunk ? c : nchunk - 1) * T + t) * E + ec];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) {
+    const int e = gtid + 256 * m;
+    bv[m] = (bias && e < E) ? braw[m] : 0.0f;
+    ok[m] = e < E && (mask == nullptr || mraw[m] != 0);
+  }
+  // the slices added in ascending order
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) {
+    const int e = gtid + 256 * m;
     float l = 0.0f;
-    if (nchunk <= kMaxChunks) {
-      float pv[kMaxChunks];
+    if (fast) {
 #pragma unroll
       for (int c = 0; c < kMaxChunks; ++c)
-        pv[c] = (ok && c < nchunk) ? partial[((size_t)c * T + t) * E + e] : 0.0f;
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c)
-        if (c < nchunk) l += pv[c];
-    } else if (ok) {
+        if (c < nchunk) l += pv[m][c];
+    } else if (active && e < E) {
       for (int c = 0; c < nchunk; ++c) l += partial[((size_t)c * T + t) * E + e];
     }
     sc[m] = l;
