@@ -155,8 +155,12 @@ def test_permute_parity(ctx, name):
 
 
 @pytest.mark.parametrize("T,k,E", [(1, 8, 256), (37, 8, 32), (4096, 8, 256), (300, 16, 1024),
-                                   (5, 3, 3), (70, 1, 7)])
+                                   (5, 3, 3), (70, 1, 7), (1000, 7, 13), (16384, 8, 256),
+                                   (70000, 16, 64)])
 def test_permute_synthetic(ctx, T, k, E):
+    # (the list is cut into chunks of up to 1024 pairs, one workgroup each, and
+    # past 512 chunks into longer segments: T = 70000, k = 16 takes 192-pair
+    # segments)
     # distinct experts per token drawn from the generator; includes skew
     u = S.uniform(77, T, (T, E), 0, 1).astype(np.float64)
     u[:, : min(E, 4)] += 0.5                       # four popular experts
