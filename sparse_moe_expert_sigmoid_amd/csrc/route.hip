@@ -6,8 +6,9 @@
 // Conversion Notes): p = softmax(l), top k on p, weights p / sum(p).
 //
 // Two kernels.  The first writes partial logits, each a sum over a fixed
-// 256-wide slice of the input in ascending order; the second adds the slices
-// in order, so a token's logits never depend on T or on the launch shape.
+// 256-wide slice of the input on the matrix cores in one fixed order; the
+// second adds the slices in order, so a token's logits never depend on T or on
+// the launch shape.
 // The second kernel runs one workgroup per token and ranks the selection keys
 // by counting (no sequential arg-max rounds).
 #include "internal.h"
@@ -15,75 +16,182 @@
 namespace moe {
 namespace {
 
-// partial[c][t][e] = sum over i in [256c, 256c + 256) of Wr[e][i] * x[t][i],
-// one fmaf chain per output in ascending i (the same chain in every variant).
-// Block: 256 threads as a 16 x 16 grid, each thread PE x PT outputs; kSub
-// inputs are staged in LDS per step (the whole 256-chunk for the small tile,
-// so a decode launch makes one trip to memory).
-template <int TE, int TT, int kSub>
-__global__ __launch_bounds__(256) void router_logits_kernel(const float* __restrict__ x,
-                                                            const float* __restrict__ wr,
-                                                            int T, int d, int E,
-                                                            float* __restrict__ partial) {
-  constexpr int PE = TE / 16, PT = TT / 16;
-  constexpr int kLd = kSub + 4;  // row stride: 16-byte aligned, rows 4 banks apart
-  __shared__ __attribute__((aligned(16))) float ws[TE][kLd];
-  __shared__ __attribute__((aligned(16))) float xs[TT][kLd];
-  const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, c = blockIdx.z;
-  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
-  float acc[PE][PT];
-#pragma unroll
-  for (int a = 0; a < PE; ++a)
-#pragma unroll
-    for (int b = 0; b < PT; ++b) acc[a][b] = 0.0f;
+typedef float v4f __attribute__((ext_vector_type(4)));
 
+// partial[c][t][e] = sum over i in [256c, 256c + 256) of Wr[e][i] * x[t][i] on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 16 experts x 16 tokens x 4
+// inputs per instruction).  Step s of a slice multiplies inputs 4s .. 4s + 3:
+// lane quarter q (lane / 16) carries input 4s + q of weight row lane % 16 (A)
+// and of token lane % 16 (B).  Step s goes to accumulator chain s % 4 and the
+// slice's value is (chain 0 + chain 1) + (chain 2 + chain 3).  Both kernels
+// below run exactly this sequence for every output, and a product of the
+// instruction depends only on its own row and column, so a token's logits do
+// not depend on T or on where its row and expert sit in a tile.  d is a
+// multiple of 64 (checked on the host), so a slice has a multiple of 16 steps.
+__device__ inline void logit_steps4(const float4& a, const float4& b, v4f acc[4]) {
+  acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[0], 0, 0, 0);
+  acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[1], 0, 0, 0);
+  acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[2], 0, 0, 0);
+  acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[3], 0, 0, 0);
+}
+
+// Store one 16x16 block: lane l holds experts eb + 4 (l / 16) + r (r = 0..3)
+// of token tb + l % 16.
+__device__ inline void logit_store(const v4f& v, int eb, int tb, int lane, int c, int T, int E,
+                                   float* __restrict__ partial) {
+  const int t = tb + (lane & 15);
+  const int e = eb + 4 * (lane >> 4);
+  if (t >= T) return;
+  float* dst = partial + ((size_t)c * T + t) * E + e;
+  if ((E & 3) == 0 && e + 3 < E) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (e + r < E) dst[r] = v[r];
+  }
+}
+
+// One chain of N steps on operands already in registers.
+template <int N>
+__device__ __forceinline__ v4f logit_chain(const float* a, const float* b) {
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int m = 0; m < N; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[m], acc, 0, 0, 0);
+  return acc;
+}
+
+// Small batches (T <= 32): one workgroup per 16 experts x 16 tokens x slice,
+// wavefront h running chain h (steps h, h + 4, ...), its operands loaded
+// straight into registers (one trip to memory); the chains meet in LDS.
+__global__ __launch_bounds__(256) void router_logits_small_kernel(const float* __restrict__ x,
+                                                                  const float* __restrict__ wr,
+                                                                  int T, int d, int E,
+                                                                  float* __restrict__ partial) {
+  constexpr int kChainSteps = kRouterChunk / 16;  // steps per chain in a whole slice
+  __shared__ v4f chain_sm[4][kWave];
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16, c = blockIdx.z;
   const int kbeg = c * kRouterChunk;
-  const int kend = min(d, kbeg + kRouterChunk);
-  for (int k0 = kbeg; k0 < kend; k0 += kSub) {
-    const int kn = min(kSub, kend - k0);  // the last slice of a row can be short
-    for (int q = threadIdx.x; q < TE * (kSub / 4); q += 256) {
-      const int r = q / (kSub / 4), c4 = q % (kSub / 4);
-      const int e = e0 + r;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E && 4 * c4 < kn)
-        v = *reinterpret_cast<const float4*>(wr + (size_t)e * d + k0 + 4 * c4);
-      *reinterpret_cast<float4*>(&ws[r][4 * c4]) = v;
-    }
-    for (int q = threadIdx.x; q < TT * (kSub / 4); q += 256) {
-      const int r = q / (kSub / 4), c4 = q % (kSub / 4);
-      const int t = t0 + r;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < T && 4 * c4 < kn)
-        v = *reinterpret_cast<const float4*>(x + (size_t)t * d + k0 + 4 * c4);
-      *reinterpret_cast<float4*>(&xs[r][4 * c4]) = v;
+  const int nm = min(kRouterChunk, d - kbeg) / 16;  // steps per chain in this slice
+  const int h = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, q = lane >> 4;
+  // step s = h + 4m multiplies input 4s + q = 4h + 16m + q
+  const float* wa = wr + (size_t)min(e0 + i, E - 1) * d + kbeg + 4 * h + q;
+  const float* xb = x + (size_t)min(t0 + i, T - 1) * d + kbeg + 4 * h + q;
+  float a[kChainSteps], b[kChainSteps];
+#pragma unroll
+  for (int m = 0; m < kChainSteps; ++m) {
+    const int mc = min(m, nm - 1);
+    a[m] = wa[16 * mc];
+    b[m] = xb[16 * mc];
+  }
+  // a slice holds 4, 8, 12 or 16 steps per chain (d is a multiple of 64)
+  const v4f acc = nm == 16  ? logit_chain<16>(a, b)
+                  : nm == 12 ? logit_chain<12>(a, b)
+                  : nm == 8  ? logit_chain<8>(a, b)
+                             : logit_chain<4>(a, b);
+  chain_sm[h][lane] = acc;
+  __syncthreads();
+  if (h != 0) return;
+  const v4f c0 = chain_sm[0][lane], c1 = chain_sm[1][lane];
+  const v4f c2 = chain_sm[2][lane], c3 = chain_sm[3][lane];
+  v4f v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = (c0[r] + c1[r]) + (c2[r] + c3[r]);
+  logit_store(v, e0, t0, lane, c, T, E, partial);
+}
+
+// Larger batches: 64 experts x 64 tokens per workgroup, wavefront w owning
+// experts 32 (w & 1) .. + 31 and tokens 32 (w >> 1) .. + 31 (2 x 2 blocks, 4
+// chains each).  The slice moves through LDS 16 steps (64 inputs) at a time
+// as planes [q][row][step]: one 16-byte read gives a lane 4 consecutive steps.
+// The next 64 inputs are loaded into registers while the current ones are
+// multiplied.
+constexpr int kLtSteps = 16;           // steps staged at a time
+constexpr int kLtLd = kLtSteps + 4;    // row stride in floats (16-byte aligned, conflict-free)
+
+__global__ __launch_bounds__(256) void router_logits_tile_kernel(const float* __restrict__ x,
+                                                                 const float* __restrict__ wr,
+                                                                 int T, int d, int E,
+                                                                 float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) float wl[4][64][kLtLd];
+  __shared__ __attribute__((aligned(16))) float xl[4][64][kLtLd];
+  const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64, c = blockIdx.z;
+  const int kbeg = c * kRouterChunk;
+  const int nsub = min(kRouterChunk, d - kbeg) / (4 * kLtSteps);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, q = lane >> 4;
+  const int er = 32 * (wave & 1), tr = 32 * (wave >> 1);
+  // this thread's loads: rows (threadIdx.x + 256 u) / 16, step (threadIdx.x % 16)
+  const float* wsrc[4];
+  const float* xsrc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int f = threadIdx.x + 256 * u, row = f >> 4, st = f & 15;
+    wsrc[u] = wr + (size_t)min(e0 + row, E - 1) * d + kbeg + 4 * st;
+    xsrc[u] = x + (size_t)min(t0 + row, T - 1) * d + kbeg + 4 * st;
+  }
+  float4 wv[4], xv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    wv[u] = *reinterpret_cast<const float4*>(wsrc[u]);
+    xv[u] = *reinterpret_cast<const float4*>(xsrc[u]);
+  }
+  v4f acc[2][2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc[a][b][h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int sub = 0; sub < nsub; ++sub) {
+    if (sub > 0) __syncthreads();  // every read of the previous 16 steps is done
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = threadIdx.x + 256 * u, row = f >> 4, st = f & 15;
+      wl[0][row][st] = wv[u].x;
+      wl[1][row][st] = wv[u].y;
+      wl[2][row][st] = wv[u].z;
+      wl[3][row][st] = wv[u].w;
+      xl[0][row][st] = xv[u].x;
+      xl[1][row][st] = xv[u].y;
+      xl[2][row][st] = xv[u].z;
+      xl[3][row][st] = xv[u].w;
     }
     __syncthreads();
-    // four inputs per LDS read; the fmaf chain still runs in ascending i
-#pragma unroll 2
-    for (int kk = 0; kk < kn; kk += 4) {
-      float4 wv[PE], xv[PT];
+    {  // the next 64 inputs (the last group re-reads its own: in bounds, unused)
+      const int nx = (sub + 1 < nsub ? sub + 1 : sub) * 4 * kLtSteps;
 #pragma unroll
-      for (int a = 0; a < PE; ++a) wv[a] = *reinterpret_cast<const float4*>(&ws[ti + 16 * a][kk]);
-#pragma unroll
-      for (int b = 0; b < PT; ++b) xv[b] = *reinterpret_cast<const float4*>(&xs[tj + 16 * b][kk]);
-#pragma unroll
-      for (int a = 0; a < PE; ++a)
-#pragma unroll
-        for (int b = 0; b < PT; ++b) {
-          acc[a][b] = fmaf(wv[a].x, xv[b].x, acc[a][b]);
-          acc[a][b] = fmaf(wv[a].y, xv[b].y, acc[a][b]);
-          acc[a][b] = fmaf(wv[a].z, xv[b].z, acc[a][b]);
-          acc[a][b] = fmaf(wv[a].w, xv[b].w, acc[a][b]);
-        }
+      for (int u = 0; u < 4; ++u) {
+        wv[u] = *reinterpret_cast<const float4*>(wsrc[u] + nx);
+        xv[u] = *reinterpret_cast<const float4*>(xsrc[u] + nx);
+      }
     }
-    __syncthreads();
+#pragma unroll
+    for (int s4 = 0; s4 < kLtSteps / 4; ++s4) {
+      float4 av[2], bv[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        av[a] = *reinterpret_cast<const float4*>(&wl[q][er + 16 * a + i][4 * s4]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bv[b] = *reinterpret_cast<const float4*>(&xl[q][tr + 16 * b + i][4 * s4]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) logit_steps4(av[a], bv[b], acc[a][b]);
+    }
   }
 #pragma unroll
-  for (int a = 0; a < PE; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < PT; ++b) {
-      const int e = e0 + ti + 16 * a, t = t0 + tj + 16 * b;
-      if (e < E && t < T) partial[((size_t)c * T + t) * E + e] = acc[a][b];
+    for (int b = 0; b < 2; ++b) {
+      v4f v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        v[r] = (acc[a][b][0][r] + acc[a][b][1][r]) + (acc[a][b][2][r] + acc[a][b][3][r]);
+      logit_store(v, e0 + er + 16 * a, t0 + tr + 16 * b, lane, c, T, E, partial);
     }
 }
 
@@ -356,12 +464,12 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
   TimedLaunch tl(K_ROUTER_LOGITS, s);
   if (T <= 32) {
     dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
-    hipLaunchKernelGGL((router_logits_kernel<16, 16, 256>), grid, dim3(256), 0, s, x, wr, T, d,
-                       E, partial);
+    hipLaunchKernelGGL(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+                       partial);
   } else {
     dim3 grid((E + 63) / 64, (T + 63) / 64, nchunk);
-    hipLaunchKernelGGL((router_logits_kernel<64, 64, 64>), grid, dim3(256), 0, s, x, wr, T, d,
-                       E, partial);
+    hipLaunchKernelGGL(router_logits_tile_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+                       partial);
   }
   }
   hipError_t err = hipGetLastError();
@@ -382,8 +490,8 @@ hipError_t launch_router_small(int router, const float* x, const float* wr, cons
   {
     TimedLaunch tl(K_ROUTER_LOGITS, s);
     dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
-    hipLaunchKernelGGL((router_logits_kernel<16, 16, 256>), grid, dim3(256), 0, s, x, wr, T, d,
-                       E, partial);
+    hipLaunchKernelGGL(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+                       partial);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
