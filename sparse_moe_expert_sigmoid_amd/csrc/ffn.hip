@@ -1231,11 +1231,12 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
 
   v4i p[NF][4][2];      // [weight fragment][row group][digit]: int32 sums of a 128-input block
   float acc[NF][4][4];  // fp32 sums over the blocks
+  const v4i zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      p[f][t][0] = p[f][t][1] = v4i{0, 0, 0, 0};
+      p[f][t][0] = p[f][t][1] = zero4;
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[f][t][c] = 0.0f;
     }
@@ -1243,7 +1244,12 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
 #pragma unroll
   for (int q = 0; q < S::NS - 1; ++q) issue(RING_SLOT(q), q);
 
-#define DN_STEP(STEP, Q)                                                                      \
+  // PAR = the K-step's parity when the unrolling fixes it (4 slots): an even
+  // step (0) opens a 128-input block, its MFMAs starting from zero so that the
+  // int32 sums need no clearing, and an odd step (1) closes it and folds it
+  // into fp32.  PAR = 2: parity known at run time only (3 slots; unrolling
+  // those by 6 spills), the sums cleared after each fold.
+#define DN_STEP(STEP, Q, PAR)                                                                 \
   {                                                                                           \
     MOE_WAIT_VM(S::WAIT);                                                                     \
     ring_barrier();                                                                           \
@@ -1258,12 +1264,14 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
           const v4i b0 = lds_frag(bb, lane);                                                  \
           const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
           _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                    \
-            p[f][t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b0, p[f][t][0], 0, 0, 0); \
-            p[f][t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b1, p[f][t][1], 0, 0, 0); \
+            p[f][t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b0,                      \
+                                                               PAR ? p[f][t][0] : zero4, 0, 0, 0); \
+            p[f][t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b1,                      \
+                                                               PAR ? p[f][t][1] : zero4, 0, 0, 0); \
           }                                                                                   \
         }                                                                                     \
       }                                                                                       \
-      if (((STEP) & 1) || (STEP) == last) { /* end of a 128-input scale block */             \
+      if ((PAR == 1) || (PAR == 2 && ((STEP) & 1)) || (STEP) == last) { /* block end */       \
         const int blk = (STEP) >> 1;                                                          \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                       \
           if (t < ntg) {                                                                      \
@@ -1272,7 +1280,7 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
               _Pragma("unroll") for (int c = 0; c < 4; ++c)                                   \
                 acc[f][t][c] = fmaf(sg, (float)(p[f][t][0][c] * 256 + p[f][t][1][c]),         \
                                     acc[f][t][c]);                                            \
-              p[f][t][0] = p[f][t][1] = v4i{0, 0, 0, 0};                                      \
+              if (PAR == 2) p[f][t][0] = p[f][t][1] = zero4;                                  \
             }                                                                                 \
           }                                                                                   \
         }                                                                                     \
@@ -1283,22 +1291,22 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
   int s0 = 0;
   if constexpr (S::NS == 4) {
     for (; s0 + 4 <= nsteps; s0 += 4) {
-      DN_STEP(s0, 0)
-      DN_STEP(s0 + 1, 1)
-      DN_STEP(s0 + 2, 2)
-      DN_STEP(s0 + 3, 3)
+      DN_STEP(s0, 0, 0)
+      DN_STEP(s0 + 1, 1, 1)
+      DN_STEP(s0 + 2, 2, 0)
+      DN_STEP(s0 + 3, 3, 1)
     }
-    if (s0 < nsteps) DN_STEP(s0, 0)
-    if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1)
-    if (s0 + 2 < nsteps) DN_STEP(s0 + 2, 2)
+    if (s0 < nsteps) DN_STEP(s0, 0, 0)
+    if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1, 1)
+    if (s0 + 2 < nsteps) DN_STEP(s0 + 2, 2, 0)
   } else {
     for (; s0 + 3 <= nsteps; s0 += 3) {
-      DN_STEP(s0, 0)
-      DN_STEP(s0 + 1, 1)
-      DN_STEP(s0 + 2, 2)
+      DN_STEP(s0, 0, 2)
+      DN_STEP(s0 + 1, 1, 2)
+      DN_STEP(s0 + 2, 2, 2)
     }
-    if (s0 < nsteps) DN_STEP(s0, 0)
-    if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1)
+    if (s0 < nsteps) DN_STEP(s0, 0, 2)
+    if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1, 2)
   }
 #undef DN_STEP
   MOE_WAIT_VM(0);
