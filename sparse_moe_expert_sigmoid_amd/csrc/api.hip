@@ -596,17 +596,22 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
                      L->shared.layout == L->experts.layout && L->experts.fmt != MOE_W_FP32;
   const moe_weights& X = L->experts;
   const moe_weights& S = L->shared;
-  // small batches: router, x encoding and grouping in one launch
-  const bool small = T <= moe::kSmallT && X.fmt != MOE_W_FP32 && (fused || !has_sh);
+  // When every expert set reads x as digits, the selection kernel encodes x
+  // too (its row loads overlap the selection); small batches also skip the
+  // permutation (the FFN groups the pairs itself).
+  const bool enc = X.fmt != MOE_W_FP32 && (fused || !has_sh);
+  const bool small = enc && T <= moe::kSmallT;
   hipError_t e;
-  if (small) {
+  if (enc) {
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, fused ? 2 : 1, Rs, Is, true);
     // x digits in the order the routed experts' kernels read (int4: permuted)
     const bool perm = X.fmt == MOE_W_INT4_B32 || X.fmt == MOE_W_INT4_B128;
-    e = moe::launch_router_small(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
-                                 k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, lay.cnt,
-                                 s);
+    e = moe::launch_router_encode(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
+                                  k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, lay.cnt,
+                                  s);
+    if (e == hipSuccess && !small)
+      e = moe::launch_permute(idx, T, k, E, f.offsets, f.row_token, f.token_row, s);
   } else {
     e = moe::launch_router(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E, k,
                            L->scale, idx, w, f.partial, s);
@@ -622,7 +627,7 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
          f.offsets, lay.hq[0], lay.hs[0], f.rows, small ? idx : nullptr, k, act},
         {S.fmt, S.layout, 1, S.inter, T, S.w_gate_up, S.s_gate_up, S.w_down, S.s_down, nullptr,
          nullptr, lay.hq[1], lay.hs[1], f.sh_rows, nullptr, 1, act}};
-    e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, small, s);
+    e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, enc, s);
   } else {
     auto run = [&](const moe_weights& W, int Ew, int Rw, const int32_t* rt, const int32_t* of,
                    float* out) -> hipError_t {
@@ -638,8 +643,8 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
       moe::FfnSet set{W.fmt, W.layout, Ew, W.inter, Rw, W.w_gate_up, W.s_gate_up, W.w_down,
                       W.s_down, rt, of, lay.hq[0], lay.hs[0], out, pairs ? idx : nullptr, k,
                       act};
-      // x was encoded by the small-batch router when only routed experts run here
-      return moe::launch_ffn_quant(&set, 1, d, x, T, lay, small && &W == &X, s);
+      // x was encoded by the router when only routed experts run here
+      return moe::launch_ffn_quant(&set, 1, d, x, T, lay, enc && &W == &X, s);
     };
     e = run(X, E, R, f.row_token, f.offsets, f.rows);
     if (e == hipSuccess && has_sh) e = run(S, 1, T, nullptr, nullptr, f.sh_rows);

@@ -137,15 +137,17 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
                          const uint8_t* mask, int T,
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s);
-// Up to kSmallT tokens: logits, then one launch for selection and the x
-// encoding (xq/xs, see the FFN workspace); no permutation (the FFN groups the
-// pairs itself, FfnSet::pairs_idx).
+// Logits, then one launch for the selection and the x encoding (xq/xs, see
+// the FFN workspace), which replaces the FFN's own encoding when every expert
+// set of the layer reads the same digits.  No permutation: up to kSmallT
+// tokens the FFN groups the pairs itself (FfnSet::pairs_idx), beyond that
+// launch_permute follows.
 constexpr int kSmallT = 16;
-hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
-                               const uint8_t* mask,
-                               int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, bool perm,
-                               int* split_cnt, hipStream_t s);
+hipError_t launch_router_encode(int router, const float* x, const float* wr, const float* bias,
+                                const uint8_t* mask,
+                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
+                                float* partial, int8_t* xq, float* xs, bool perm,
+                                int* split_cnt, hipStream_t s);
 // counts[e] += number of topk_idx entries equal to e (entries outside [0, E) skipped)
 hipError_t launch_expert_counts(const int32_t* idx, long long n, int E, unsigned long long* counts,
                                 hipStream_t s);

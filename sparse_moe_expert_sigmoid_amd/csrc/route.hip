@@ -481,17 +481,23 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
   return launch_select<4>(partial, nchunk, bias, mask, T, E, k, router, scale, idx, w, s);
 }
 
-hipError_t launch_router_small(int router, const float* x, const float* wr, const float* bias,
-                               const uint8_t* mask,
-                               int T, int d, int E, int k, float scale, int32_t* idx, float* w,
-                               float* partial, int8_t* xq, float* xs, bool perm,
-                               int* split_cnt, hipStream_t s) {
+hipError_t launch_router_encode(int router, const float* x, const float* wr, const float* bias,
+                                const uint8_t* mask,
+                                int T, int d, int E, int k, float scale, int32_t* idx, float* w,
+                                float* partial, int8_t* xq, float* xs, bool perm,
+                                int* split_cnt, hipStream_t s) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
   {
     TimedLaunch tl(K_ROUTER_LOGITS, s);
-    dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
-    hipLaunchKernelGGL(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
-                       partial);
+    if (T <= 32) {
+      dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
+      hipLaunchKernelGGL(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+                         partial);
+    } else {
+      dim3 grid((E + 63) / 64, (T + 63) / 64, nchunk);
+      hipLaunchKernelGGL(router_logits_tile_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+                         partial);
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
