@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const float* _
 // experts 32 (w & 1) .. + 31 and tokens 32 (w >> 1) .. + 31 (2 x 2 blocks, 4
 // chains each).  The slice moves through LDS 16 steps (64 inputs) at a time
 // as planes [q][row][step]: one 16-byte read gives a lane 4 consecutive steps.
-// The next 64 inputs are loaded into registers while the current ones are
-// multiplied.
+// Two groups of 64 inputs are in flight in registers while the current one is
+// multiplied (one group ahead left the loads about one MFMA phase to land).
 constexpr int kLtSteps = 16;           // steps staged at a time
 constexpr int kLtLd = kLtSteps + 4;    // row stride in floats (16-byte aligned, conflict-free)
 
@@ -131,11 +131,18 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const float* __
     wsrc[u] = wr + (size_t)min(e0 + row, E - 1) * d + kbeg + 4 * st;
     xsrc[u] = x + (size_t)min(t0 + row, T - 1) * d + kbeg + 4 * st;
   }
-  float4 wv[4], xv[4];
+  // two groups of 64 inputs in flight in registers (wv[g], xv[g] hold group
+  // sub with sub % 2 == g); a slice has at most 4 groups, so the loop unrolls
+  float4 wv[2][4], xv[2][4];
+  constexpr int kGrp = 4 * kLtSteps;  // inputs per group
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    wv[u] = *reinterpret_cast<const float4*>(wsrc[u]);
-    xv[u] = *reinterpret_cast<const float4*>(xsrc[u]);
+  for (int g = 0; g < 2; ++g) {
+    const int nx = (g < nsub ? g : nsub - 1) * kGrp;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wv[g][u] = *reinterpret_cast<const float4*>(wsrc[u] + nx);
+      xv[g][u] = *reinterpret_cast<const float4*>(xsrc[u] + nx);
+    }
   }
   v4f acc[2][2][4];
 #pragma unroll
@@ -145,42 +152,46 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const float* __
 #pragma unroll
       for (int h = 0; h < 4; ++h) acc[a][b][h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int sub = 0; sub < nsub; ++sub) {
-    if (sub > 0) __syncthreads();  // every read of the previous 16 steps is done
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int f = threadIdx.x + 256 * u, row = f >> 4, st = f & 15;
-      wl[0][row][st] = wv[u].x;
-      wl[1][row][st] = wv[u].y;
-      wl[2][row][st] = wv[u].z;
-      wl[3][row][st] = wv[u].w;
-      xl[0][row][st] = xv[u].x;
-      xl[1][row][st] = xv[u].y;
-      xl[2][row][st] = xv[u].z;
-      xl[3][row][st] = xv[u].w;
-    }
-    __syncthreads();
-    {  // the next 64 inputs (the last group re-reads its own: in bounds, unused)
-      const int nx = (sub + 1 < nsub ? sub + 1 : sub) * 4 * kLtSteps;
+  for (int sub = 0; sub < kRouterChunk / kGrp; ++sub) {
+    if (sub < nsub) {
+      const int g = sub & 1;
+      if (sub > 0) __syncthreads();  // every read of the previous 16 steps is done
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        wv[u] = *reinterpret_cast<const float4*>(wsrc[u] + nx);
-        xv[u] = *reinterpret_cast<const float4*>(xsrc[u] + nx);
+        const int f = threadIdx.x + 256 * u, row = f >> 4, st = f & 15;
+        wl[0][row][st] = wv[g][u].x;
+        wl[1][row][st] = wv[g][u].y;
+        wl[2][row][st] = wv[g][u].z;
+        wl[3][row][st] = wv[g][u].w;
+        xl[0][row][st] = xv[g][u].x;
+        xl[1][row][st] = xv[g][u].y;
+        xl[2][row][st] = xv[g][u].z;
+        xl[3][row][st] = xv[g][u].w;
       }
-    }
+      __syncthreads();
+      {  // the group after next (past the end: the last group again, unused)
+        const int nx = (sub + 2 < nsub ? sub + 2 : nsub - 1) * kGrp;
 #pragma unroll
-    for (int s4 = 0; s4 < kLtSteps / 4; ++s4) {
-      float4 av[2], bv[2];
+        for (int u = 0; u < 4; ++u) {
+          wv[g][u] = *reinterpret_cast<const float4*>(wsrc[u] + nx);
+          xv[g][u] = *reinterpret_cast<const float4*>(xsrc[u] + nx);
+        }
+      }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        av[a] = *reinterpret_cast<const float4*>(&wl[q][er + 16 * a + i][4 * s4]);
+      for (int s4 = 0; s4 < kLtSteps / 4; ++s4) {
+        float4 av[2], bv[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bv[b] = *reinterpret_cast<const float4*>(&xl[q][tr + 16 * b + i][4 * s4]);
+        for (int a = 0; a < 2; ++a)
+          av[a] = *reinterpret_cast<const float4*>(&wl[q][er + 16 * a + i][4 * s4]);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b)
+          bv[b] = *reinterpret_cast<const float4*>(&xl[q][tr + 16 * b + i][4 * s4]);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) logit_steps4(av[a], bv[b], acc[a][b]);
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) logit_steps4(av[a], bv[b], acc[a][b]);
+      }
     }
   }
 #pragma unroll
