@@ -331,20 +331,45 @@ __device__ inline void select_token(const float* __restrict__ partial, int nchun
                (0xffffffffu - (unsigned)e);
     }
   }
+  // Top k in two rounds of rank counting (keys are distinct: the expert id
+  // sits in the low word).  Only a key among the top k of its wavefront's
+  // 64 EPT keys can be among the token's top k, and every key above a token
+  // top-k key is such a candidate too, so ranking the 4 k candidates among
+  // themselves gives the same ranks as ranking against all E keys, with
+  // 64 EPT + 4 k comparisons per key instead of E.  Slots of wavefronts with
+  // fewer than k keys stay 0, below every key.
+  __shared__ unsigned long long cand[4 * kMaxK];
+  __shared__ float cand_s[4 * kMaxK];
 #pragma unroll
   for (int m = 0; m < EPT; ++m) keys[gtid + 256 * m] = gtid + 256 * m < E ? key[m] : 0ull;
+  if (gtid < 4 * k) cand[gtid] = 0ull;
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < EPT; ++m) {
     const int e = gtid + 256 * m;
     if (!active || e >= E) continue;
     int rank = 0;
+#pragma unroll
+    for (int mm = 0; mm < EPT; ++mm) {
+      const unsigned long long* kw = keys + 256 * mm + kWave * wave;
 #pragma unroll 16
-    for (int q = 0; q < E; ++q) rank += keys[q] > key[m] ? 1 : 0;
+      for (int q = 0; q < kWave; ++q) rank += kw[q] > key[m] ? 1 : 0;
+    }
     if (rank < k) {
+      cand[wave * k + rank] = key[m];
+      cand_s[wave * k + rank] = sc[m];
+    }
+  }
+  __syncthreads();
+  if (active && gtid < 4 * k) {
+    const unsigned long long c = cand[gtid];
+    int rank = 0;
+    for (int q = 0; q < 4 * k; ++q) rank += cand[q] > c ? 1 : 0;
+    if (rank < k) {  // (an empty slot ranks below the k real candidates)
+      const int e = (int)(0xffffffffu - (unsigned)(c & 0xffffffffull));
       idx[(size_t)t * k + rank] = e;
       if (idx_lds) idx_lds[t * k + rank] = e;
-      sel_s[rank] = sc[m];
+      sel_s[rank] = cand_s[gtid];
     }
   }
   __syncthreads();
