@@ -1635,9 +1635,18 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
                        const float* xs, const FfnWs& ws, hipStream_t s) {
   const int tiles = a.tiles + b.tiles;
   const int imax = a.inter > b.inter ? a.inter : b.inter;
-  // split K across more wavefronts when the tiles alone cannot fill the chip
+  // split K across more wavefronts when the tiles alone cannot fill the chip:
+  // 4 ways (1024-thread workgroups, one per CU) while the units fit one per
+  // CU for int4, whose waves stream half the bytes per K-step (measured:
+  // Qwen-shaped T = 2 gate/up 20.6 -> 17.4 us; past one round it lost);
+  // int8 takes 4 ways only below half the CUs (4 ways at 288 units lost)
   const long long blocks = (long long)tiles * (imax / 64);
-  const int ks = blocks >= 2LL * g_cu_count ? 1 : (blocks >= g_cu_count / 2 ? 2 : 4);
+  const auto kway = [](long long units) {
+    if (units >= 2LL * g_cu_count) return 1;
+    const long long four_below = FMT == 1 ? g_cu_count / 2 : (long long)g_cu_count + 1;
+    return units < four_below ? 4 : 2;
+  };
+  const int ks = kway(blocks);
   // and across workgroups when the units do not spread evenly over the CUs
   const int ksteps = FMT == 1 ? d / kKStep : d / 128;  // K-steps (int4: spans) per unit
   // (only the small-batch launches split: they are the ones that leave CUs idle)
@@ -1668,7 +1677,7 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long long dblocks = (long long)tiles * (d / 64);
-  const int dks = dblocks >= 2LL * g_cu_count ? 1 : (dblocks >= g_cu_count / 2 ? 2 : 4);
+  const int dks = kway(dblocks);
   const int dsteps = FMT == 1 ? imax / kKStep : imax / 128;
   const bool ng2 = FMT == 1 && dks == 1 && d % 128 == 0;
   SplitK dsk{1, 1, ws.cnt, ws.part};
