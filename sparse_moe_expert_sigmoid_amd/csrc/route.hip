@@ -10,7 +10,7 @@
 // second adds the slices in order, so a token's logits never depend on T or on
 // the launch shape.
 // The second kernel runs one workgroup per token and ranks the selection keys
-// by counting (no sequential arg-max rounds).
+// by counting in two rounds (no sequential arg-max rounds).
 #include "internal.h"
 
 namespace moe {
@@ -409,10 +409,11 @@ hipError_t launch_select(const float* partial, int nchunk, const float* bias,
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ small T: fused tail
+// ------------------------------------------------------------------ selection + encoding
 // After the logits kernel, one workgroup per token selects that token's
 // experts (select_token) and encodes its row of x as two-digit int8 for the
-// FFN kernels, which then group the (token, slot) pairs themselves.
+// FFN kernels (which, for small batches, then group the (token, slot) pairs
+// themselves; larger batches are permuted first).
 template <int EPT>
 __global__ __launch_bounds__(256) void router_tail_kernel(
     const float* __restrict__ partial, int nchunk, const float* __restrict__ x, int d,

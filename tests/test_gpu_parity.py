@@ -99,8 +99,9 @@ def test_route_batch_invariance(ctx):
 @pytest.mark.parametrize("d", [64, 320])
 def test_route_short_last_slice(ctx, d):
     # d not a multiple of the 256-wide logit slice: the last slice is short.
-    # Small T (16x16 tiles, one 256 step) and T > 32 (64x64 tiles, 64 steps)
-    # must both match the oracle and each other bit for bit.
+    # Small T (the per-chain logits kernel) and T > 32 (the 64x64 tile
+    # kernel, 64 inputs staged at a time) must both match the oracle and each
+    # other bit for bit.
     got = {}
     for T in (1, 8, 40):
         inp = inputs("tiny", d=d, T=T, E=24, k=4, xseed=0x4D6F45A0)
