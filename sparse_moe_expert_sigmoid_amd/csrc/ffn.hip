@@ -746,6 +746,14 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[q][c] = 0.0f;
 
+  // int8: the output-row scales, loaded before the loop (its waits cover
+  // them; after it they cost a round trip at the end of every workgroup)
+  float sdn[NG][4];
+#pragma unroll
+  for (int q = 0; q < NG; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      sdn[q][c] = FMT == 1 ? G.sdn[(size_t)job.e * d + c0 + 16 * q + 4 * g + c] : 1.0f;
   if (FMT == 1) {
     const int nsteps = I / kKStep;
     const int s_beg = ksl * nsteps / nsl, s_end = (ksl + 1) * nsteps / nsl;
@@ -865,10 +873,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   for (int q = 0; q < NG; ++q) {
     float res[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int n = c0 + 16 * q + 4 * g + c;
-      res[c] = FMT == 1 ? G.sdn[(size_t)job.e * d + n] * acc[q][c] : acc[q][c];
-    }
+    for (int c = 0; c < 4; ++c) res[c] = FMT == 1 ? sdn[q][c] * acc[q][c] : acc[q][c];
     *reinterpret_cast<float4*>(G.out + (size_t)r * d + c0 + 16 * q + 4 * g) =
         make_float4(res[0], res[1], res[2], res[3]);
   }
