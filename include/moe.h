@@ -24,8 +24,10 @@
  *    and return without synchronising the host; data-dependent sizes (how
  *    many rows each expert received) stay on the device.
  *  - Errors are return codes; nothing aborts or throws across the ABI.  All
- *    argument checks are host code and run before anything is enqueued; on
- *    failure nothing is launched and moe_last_error() names the argument.
+ *    argument checks are host code and run before anything is enqueued
+ *    (including moe_forward's check that its small-batch launch plan fits the
+ *    workspace's split-K join area); on failure nothing is launched and
+ *    moe_last_error() names the argument.
  *  - T == 0 is a valid no-op.  A moe_ctx must not be used by two host
  *    threads at once.  Work enqueued on one stream runs in order; calls that
  *    share a workspace must not overlap on different streams.
@@ -194,7 +196,7 @@ moe_status moe_workspace_size(const moe_ctx* ctx, int T, int k, int E, int d, in
  *   w_router  [E][d] fp32
  *   bias      [E] fp32 selection bias (sigmoid router; NULL = zero); must be NULL
  *             for the softmax router
- *   k         1 <= k <= min(E, 16); E <= 1024; d a multiple of 64
+ *   k         1 <= k <= min(E, 16); E <= 1024; d a multiple of 64, at most 16384
  *   scale     multiplies the renormalised weights (2.446 for the Kimi-style
  *             sigmoid router, 1 for softmax); finite
  *   topk_idx  [T][k] int32 out: expert ids by descending selection key, ties to

@@ -45,11 +45,12 @@
 /* elementwise functions                                               */
 /* ------------------------------------------------------------------ */
 
-/* logistic function 1 / (1 + e^-z)  ([K] "sigmoid scores") */
+/* logistic function 1 / (1 + e^-z): the router's scores in [K] are sigmoids */
 double oracle_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
-/* SiLU(z) = z * sigmoid(z)  ([K] "the 256 routed experts ... with SiLU";
- * [Q] "Accuracy": activation='silu', the source's hidden_act) */
+/* SiLU(z) = z * sigmoid(z): the routed experts' activation in [K] ("Conversion
+ * notes", mixture-of-experts bullet) and in [Q] ("Accuracy" names silu as the
+ * hidden activation) */
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* GELU in its tanh form, z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))): the
@@ -89,7 +90,8 @@ static void select_topk(const float* key, int n, int k, int32_t* out, unsigned c
  *           correction bias, weights renormalised and scaled by 2.446; [C]: the bias is a
  *           selection bias)
  *  softmax: p = softmax(l); top k by p; w_j = scale * p_{e_j} / sum_j' p_{e_j'}
- *           ([Q] "the router, its softmax, the top 8 and their renormalization")
+ *           ([Q] "Conversion Notes": softmax, top-8 selection and renormalisation
+ *           run as ordinary ops beside the moe op)
  *  gap = key_(k) - key_(k+1) of the sorted fp32 keys (+inf when k == E).
  */
 static void route_token(int router, const float* x, const float* wr, const float* bias,

@@ -2,9 +2,10 @@
 
     python -m sparse_moe_expert_sigmoid_amd.build
 
-Compiles every csrc/*.hip into libmoe_mi355x.so beside this file with hipcc
-(cross-compiles without a GPU).  Packed fp32 VALU ops are disabled for the
-device code.  Always recompiles.
+Compiles every csrc/*.hip (device code, hipcc; cross-compiles without a GPU)
+and csrc/*.cc (host-only argument checks, the host compiler through hipcc)
+into libmoe_mi355x.so beside this file.  Packed fp32 VALU ops are disabled
+for the device code.  Always recompiles.
 """
 from __future__ import annotations
 
@@ -21,8 +22,14 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
 def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cc"):
+        cmd = [HIPCC, *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,7 +42,8 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) +
+                  glob.glob(os.path.join(HERE, "csrc", "*.cc")))
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []

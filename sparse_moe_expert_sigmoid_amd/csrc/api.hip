@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/moe.h"
+#include "checks.h"
 #include "internal.h"
 
 namespace moe {
@@ -64,7 +65,7 @@ struct moe_ctx {
   int cu_count;
   int max_lds;
   char arch[64];
-  char err[512];
+  char err[moe::kErrBytes];
   bool timing;
   moe::KernelTimer timer;
 };
@@ -81,8 +82,6 @@ moe_status fail(moe_ctx* ctx, moe_status st, const char* fmt, ...) {
   va_end(ap);
   return st;
 }
-
-bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
 // Run f with ctx->device current, restoring the caller's device afterwards.
 struct DeviceGuard {
@@ -116,67 +115,6 @@ void release_timer(moe::KernelTimer& t) {
   t.marks.clear();
   t.next = 0;
   t.dropped = 0;
-}
-
-// moe_forward workspace: router partials | idx | w | offsets | row_token |
-// token_row | rows [R][d] | shared rows [T][d] | FFN workspace.
-struct FwdWs {
-  float* partial;
-  int32_t* idx;
-  float* w;
-  int32_t* offsets;
-  int32_t* row_token;
-  int32_t* token_row;
-  float* rows;
-  float* sh_rows;
-  void* ffn;
-  size_t ffn_bytes;
-  size_t bytes;
-};
-
-size_t ffn_need(int T, int R, int d, int inter, int fmt);
-
-FwdWs fwd_layout(void* base, const moe_layer* L, int T) {
-  FwdWs f{};
-  const int E = L->experts.n_experts, d = L->experts.d, k = L->k;
-  const int R = T * k;
-  const bool has_sh = L->shared.n_experts > 0;
-  size_t off = 0;
-  char* b = static_cast<char*>(base);
-  auto take = [&](size_t n) {
-    char* p = b ? b + off : nullptr;
-    off = moe::align_up(off + n, 256);
-    return p;
-  };
-  f.partial = reinterpret_cast<float*>(take(moe::route_ws_bytes(T, d, E)));
-  f.idx = reinterpret_cast<int32_t*>(take((size_t)R * 4));
-  f.w = reinterpret_cast<float*>(take((size_t)R * 4));
-  f.offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  f.row_token = reinterpret_cast<int32_t*>(take((size_t)R * 4));
-  f.token_row = reinterpret_cast<int32_t*>(take((size_t)R * 4));
-  f.rows = reinterpret_cast<float*>(take((size_t)R * d * 4));
-  f.sh_rows = has_sh ? reinterpret_cast<float*>(take((size_t)T * d * 4)) : nullptr;
-  const bool fused = has_sh && L->shared.fmt == L->experts.fmt &&
-                     L->shared.layout == L->experts.layout && L->experts.fmt != MOE_W_FP32;
-  size_t ffn;
-  if (fused) {
-    int Rs[2] = {R, T}, Is[2] = {L->experts.inter, L->shared.inter};
-    ffn = moe::ffn_ws_layout(nullptr, T, d, 2, Rs, Is, true).bytes;
-  } else {
-    ffn = ffn_need(T, R, d, L->experts.inter, L->experts.fmt);
-    if (has_sh) {
-      size_t s2 = ffn_need(T, T, d, L->shared.inter, L->shared.fmt);
-      ffn = ffn > s2 ? ffn : s2;
-    }
-  }
-  f.ffn_bytes = ffn;
-  f.ffn = take(ffn);
-  f.bytes = off;
-  return f;
-}
-
-size_t ffn_need(int T, int R, int d, int inter, int fmt) {
-  return moe::ffn_ws_layout(nullptr, T, d, 1, &R, &inter, fmt != MOE_W_FP32).bytes;
 }
 
 }  // namespace
@@ -299,17 +237,10 @@ moe_status moe_workspace_size(const moe_ctx* cctx, int T, int k, int E, int d, i
                               size_t* bytes) {
   moe_ctx* ctx = const_cast<moe_ctx*>(cctx);
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (!bytes) return fail(ctx, MOE_E_INVALID, "moe_workspace_size: bytes is NULL");
-  if (T < 0 || k < 1 || E < 1 || d < 1 || inter < 1)
-    return fail(ctx, MOE_E_INVALID,
-                "moe_workspace_size: need T >= 0, k >= 1, E >= 1, d >= 1, inter >= 1 "
-                "(got T=%d k=%d E=%d d=%d inter=%d)", T, k, E, d, inter);
-  if (fmt < MOE_W_FP32 || fmt > MOE_W_INT4_B128)
-    return fail(ctx, MOE_E_INVALID, "moe_workspace_size: unknown weight format %d", fmt);
-  const long long R = (long long)T * k;
-  if (R > 0x7fffffffLL) return fail(ctx, MOE_E_INVALID, "moe_workspace_size: T*k overflows");
+  moe_status st = moe::check_workspace_size(ctx->err, T, k, E, d, inter, fmt, bytes);
+  if (st != MOE_OK) return st;
   size_t a = moe::route_ws_bytes(T, d, E);
-  size_t b = ffn_need(T, (int)R, d, inter, fmt);
+  size_t b = moe::ffn_need(T, T * k, d, inter, fmt);
   *bytes = a > b ? a : b;
   return MOE_OK;
 }
@@ -327,32 +258,9 @@ moe_status moe_route_masked(moe_ctx* ctx, int router, const float* x, const floa
                             int k, float scale, int32_t* topk_idx, float* topk_w, void* ws,
                             size_t ws_bytes, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (router != MOE_ROUTER_SIGMOID_BIAS && router != MOE_ROUTER_SOFTMAX)
-    return fail(ctx, MOE_E_INVALID, "moe_route: unknown router %d", router);
-  if (T < 0) return fail(ctx, MOE_E_INVALID, "moe_route: T=%d is negative", T);
-  if (E < 1 || E > moe::kMaxE)
-    return fail(ctx, MOE_E_INVALID, "moe_route: E=%d outside [1, %d]", E, moe::kMaxE);
-  if (k < 1 || k > E || k > moe::kMaxK)
-    return fail(ctx, MOE_E_INVALID, "moe_route: k=%d outside [1, min(E=%d, %d)]", k, E,
-                moe::kMaxK);
-  if (d < 1) return fail(ctx, MOE_E_INVALID, "moe_route: d=%d", d);
-  if (d % 64 != 0)
-    return fail(ctx, MOE_E_UNSUPPORTED, "moe_route: d=%d is not a multiple of 64", d);
-  if (!std::isfinite(scale)) return fail(ctx, MOE_E_INVALID, "moe_route: scale is not finite");
-  if (router == MOE_ROUTER_SOFTMAX && bias)
-    return fail(ctx, MOE_E_INVALID, "moe_route: the softmax router takes no bias");
-  if (T == 0) return MOE_OK;
-  if (!x || !w_router || !topk_idx || !topk_w)
-    return fail(ctx, MOE_E_INVALID, "moe_route: %s is NULL",
-                !x ? "x" : !w_router ? "w_router" : !topk_idx ? "topk_idx" : "topk_w");
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(bias) || !aligned16(topk_idx) ||
-      !aligned16(topk_w))
-    return fail(ctx, MOE_E_INVALID, "moe_route: a pointer is not 16-byte aligned");
-  const size_t need = moe::route_ws_bytes(T, d, E);
-  if (!ws || ws_bytes < need || !aligned16(ws))
-    return fail(ctx, MOE_E_WORKSPACE, "moe_route: workspace %s (need %zu bytes, got %zu)",
-                !ws ? "is NULL" : !aligned16(ws) ? "is not 16-byte aligned" : "too small",
-                need, ws_bytes);
+  moe_status st = moe::check_route(ctx->err, router, x, w_router, bias, T, d, E, k, scale,
+                                   topk_idx, topk_w, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_route: hipSetDevice(%d) failed", ctx->device);
   hipError_t e = moe::launch_router(router, x, w_router, bias, mask, T, d, E, k, scale,
@@ -364,16 +272,8 @@ moe_status moe_route_masked(moe_ctx* ctx, int router, const float* x, const floa
 moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
                              unsigned long long* counts, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (T < 0 || k < 1 || (long long)T * k > 0x7fffffffLL)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: T=%d k=%d", T, k);
-  if (E < 1 || E > moe::kMaxE)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: E=%d outside [1, %d]", E, moe::kMaxE);
-  if (T == 0) return MOE_OK;
-  if (!topk_idx || !counts)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: %s is NULL",
-                !topk_idx ? "topk_idx" : "counts");
-  if (!aligned16(topk_idx) || (reinterpret_cast<uintptr_t>(counts) & 7) != 0)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_counts: a pointer is misaligned");
+  moe_status st = moe::check_expert_counts(ctx->err, topk_idx, T, k, E, counts);
+  if (st != MOE_OK || T == 0) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok)
     return fail(ctx, MOE_E_DEVICE, "moe_expert_counts: hipSetDevice(%d) failed", ctx->device);
@@ -385,23 +285,8 @@ moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k
 moe_status moe_quantize(moe_ctx* ctx, int fmt, int in_type, const void* w, long long rows,
                         int K, void* codes, float* scales, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (fmt != MOE_W_INT8_ROW && fmt != MOE_W_INT4_B32 && fmt != MOE_W_INT4_B128)
-    return fail(ctx, MOE_E_UNSUPPORTED, "moe_quantize: format %d has no quantizer", fmt);
-  if (in_type != MOE_IN_F32 && in_type != MOE_IN_BF16)
-    return fail(ctx, MOE_E_INVALID, "moe_quantize: unknown input type %d", in_type);
-  if (rows < 0) return fail(ctx, MOE_E_INVALID, "moe_quantize: rows=%lld is negative", rows);
-  const int kmul = fmt == MOE_W_INT8_ROW ? 8 : (fmt == MOE_W_INT4_B32 ? 32 : 128);
-  if (K < kmul || K % kmul != 0 || K > (1 << 24))
-    return fail(ctx, MOE_E_UNSUPPORTED,
-                "moe_quantize: K=%d must be a positive multiple of %d, at most 2^24", K, kmul);
-  if (rows > (1LL << 32) || rows > (1LL << 40) / K)
-    return fail(ctx, MOE_E_UNSUPPORTED, "moe_quantize: rows above 2^32 or rows*K above 2^40");
-  if (rows == 0) return MOE_OK;
-  if (!w || !codes || !scales)
-    return fail(ctx, MOE_E_INVALID, "moe_quantize: %s is NULL",
-                !w ? "w" : !codes ? "codes" : "scales");
-  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales))
-    return fail(ctx, MOE_E_INVALID, "moe_quantize: a pointer is not 16-byte aligned");
+  moe_status st = moe::check_quantize(ctx->err, fmt, in_type, w, rows, K, codes, scales);
+  if (st != MOE_OK || rows == 0) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_quantize: hipSetDevice(%d) failed", ctx->device);
   hipError_t e = moe::launch_quantize(fmt, in_type, w, rows, K, codes, scales,
@@ -412,20 +297,8 @@ moe_status moe_quantize(moe_ctx* ctx, int fmt, int in_type, const void* w, long 
 moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
                        int32_t* offsets, int32_t* row_token, int32_t* token_row, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (T < 0) return fail(ctx, MOE_E_INVALID, "moe_permute: T=%d is negative", T);
-  if (E < 1 || E > moe::kMaxE)
-    return fail(ctx, MOE_E_INVALID, "moe_permute: E=%d outside [1, %d]", E, moe::kMaxE);
-  if (k < 1 || k > moe::kMaxK)
-    return fail(ctx, MOE_E_INVALID, "moe_permute: k=%d outside [1, %d]", k, moe::kMaxK);
-  if ((long long)T * k > 0x7fffffffLL)
-    return fail(ctx, MOE_E_INVALID, "moe_permute: T*k overflows");
-  if (!offsets) return fail(ctx, MOE_E_INVALID, "moe_permute: offsets is NULL");
-  if (T > 0 && (!topk_idx || !row_token || !token_row))
-    return fail(ctx, MOE_E_INVALID, "moe_permute: %s is NULL",
-                !topk_idx ? "topk_idx" : !row_token ? "row_token" : "token_row");
-  if (!aligned16(topk_idx) || !aligned16(offsets) || !aligned16(row_token) ||
-      !aligned16(token_row))
-    return fail(ctx, MOE_E_INVALID, "moe_permute: a pointer is not 16-byte aligned");
+  moe_status st = moe::check_permute(ctx->err, topk_idx, T, k, E, offsets, row_token, token_row);
+  if (st != MOE_OK) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_permute: hipSetDevice(%d) failed", ctx->device);
   if (T == 0) {  // every expert is empty: offsets = 0 (a fill kernel, not a memset node)
@@ -437,66 +310,13 @@ moe_status moe_permute(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int 
   return device_result(ctx, e, "moe_permute");
 }
 
-namespace {
-moe_status check_weights(moe_ctx* ctx, const char* fn, const char* which, const moe_weights* w) {
-  if (w->fmt < MOE_W_FP32 || w->fmt > MOE_W_INT4_B128)
-    return fail(ctx, MOE_E_INVALID, "%s: %s: unknown weight format %d", fn, which, w->fmt);
-  if (w->n_experts < 1 || w->d < 1 || w->inter < 1)
-    return fail(ctx, MOE_E_INVALID, "%s: %s: n_experts=%d d=%d inter=%d", fn, which,
-                w->n_experts, w->d, w->inter);
-  if (w->d > moe::kMaxWidth || w->inter > moe::kMaxWidth)
-    return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: d=%d and inter=%d must be at most %d", fn,
-                which, w->d, w->inter, moe::kMaxWidth);
-  const int mult = w->fmt == MOE_W_INT4_B32 || w->fmt == MOE_W_INT4_B128 ? 128 : 64;
-  if (w->d % mult != 0 || w->inter % mult != 0)
-    return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: d=%d and inter=%d must be multiples of %d", fn,
-                which, w->d, w->inter, mult);
-  if (w->layout != MOE_LAYOUT_ROWS && w->layout != MOE_LAYOUT_TILED)
-    return fail(ctx, MOE_E_INVALID, "%s: %s: unknown layout %d", fn, which, w->layout);
-  if (w->layout == MOE_LAYOUT_TILED && w->fmt == MOE_W_FP32)
-    return fail(ctx, MOE_E_UNSUPPORTED, "%s: %s: fp32 weights have no tiled layout", fn, which);
-  if (!w->w_gate_up || !w->w_down)
-    return fail(ctx, MOE_E_INVALID, "%s: %s: weights are NULL", fn, which);
-  if (w->fmt != MOE_W_FP32 && (!w->s_gate_up || !w->s_down))
-    return fail(ctx, MOE_E_INVALID, "%s: %s: scales are NULL for a quantised format", fn, which);
-  if (!aligned16(w->w_gate_up) || !aligned16(w->w_down) || !aligned16(w->s_gate_up) ||
-      !aligned16(w->s_down))
-    return fail(ctx, MOE_E_INVALID, "%s: %s: a pointer is not 16-byte aligned", fn, which);
-  return MOE_OK;
-}
-
-}  // namespace
-
 moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const float* x, int T,
                           const int32_t* row_token, const int32_t* offsets, int R_max,
                           float* rows_out, void* ws, size_t ws_bytes, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (!w) return fail(ctx, MOE_E_INVALID, "moe_expert_ffn: weights is NULL");
-  if (act != MOE_ACT_SILU && act != MOE_ACT_GELU_TANH)
-    return fail(ctx, MOE_E_UNSUPPORTED,
-                "moe_expert_ffn: unsupported activation=%d (MOE_ACT_SILU=0 or "
-                "MOE_ACT_GELU_TANH=1)", act);
-  {
-    moe_status st = check_weights(ctx, "moe_expert_ffn", "weights", w);
-    if (st != MOE_OK) return st;
-  }
-  if (T < 0 || R_max < 0)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_ffn: T=%d R_max=%d", T, R_max);
-  if (!offsets && w->n_experts != 1)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_ffn: offsets may be NULL only for one expert");
-  if (!offsets && !row_token && R_max > T)
-    return fail(ctx, MOE_E_INVALID,
-                "moe_expert_ffn: with identity rows R_max=%d may not exceed T=%d", R_max, T);
-  if (T == 0 || R_max == 0) return MOE_OK;
-  if (!x || !rows_out)
-    return fail(ctx, MOE_E_INVALID, "moe_expert_ffn: %s is NULL", !x ? "x" : "rows_out");
-  if (!aligned16(x) || !aligned16(row_token) || !aligned16(offsets) || !aligned16(rows_out))
-    return fail(ctx, MOE_E_INVALID, "moe_expert_ffn: a pointer is not 16-byte aligned");
-  const size_t need = ffn_need(T, R_max, w->d, w->inter, w->fmt);
-  if (!ws || ws_bytes < need || !aligned16(ws))
-    return fail(ctx, MOE_E_WORKSPACE, "moe_expert_ffn: workspace %s (need %zu bytes, got %zu)",
-                !ws ? "is NULL" : !aligned16(ws) ? "is not 16-byte aligned" : "too small", need,
-                ws_bytes);
+  moe_status st = moe::check_expert_ffn(ctx->err, w, act, x, T, row_token, offsets, R_max,
+                                        rows_out, ws, ws_bytes);
+  if (st != MOE_OK || T == 0 || R_max == 0) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok)
     return fail(ctx, MOE_E_DEVICE, "moe_expert_ffn: hipSetDevice(%d) failed", ctx->device);
@@ -518,48 +338,13 @@ moe_status moe_expert_ffn(moe_ctx* ctx, const moe_weights* w, int act, const flo
   return device_result(ctx, e, "moe_expert_ffn");
 }
 
-namespace {
-moe_status check_layer(moe_ctx* ctx, const char* fn, const moe_layer* L) {
-  if (!L) return fail(ctx, MOE_E_INVALID, "%s: layer is NULL", fn);
-  moe_status st = check_weights(ctx, fn, "experts", &L->experts);
-  if (st != MOE_OK) return st;
-  const int E = L->experts.n_experts, d = L->experts.d;
-  if (L->router != MOE_ROUTER_SIGMOID_BIAS && L->router != MOE_ROUTER_SOFTMAX)
-    return fail(ctx, MOE_E_INVALID, "%s: unknown router %d", fn, L->router);
-  if (E > moe::kMaxE)
-    return fail(ctx, MOE_E_INVALID, "%s: E=%d above %d", fn, E, moe::kMaxE);
-  if (L->k < 1 || L->k > E || L->k > moe::kMaxK)
-    return fail(ctx, MOE_E_INVALID, "%s: k=%d outside [1, min(E=%d, %d)]", fn, L->k, E,
-                moe::kMaxK);
-  if (!std::isfinite(L->scale)) return fail(ctx, MOE_E_INVALID, "%s: scale is not finite", fn);
-  if (L->router == MOE_ROUTER_SOFTMAX && L->bias)
-    return fail(ctx, MOE_E_INVALID, "%s: the softmax router takes no bias", fn);
-  if (!L->w_router) return fail(ctx, MOE_E_INVALID, "%s: w_router is NULL", fn);
-  if (!aligned16(L->w_router) || !aligned16(L->bias))
-    return fail(ctx, MOE_E_INVALID, "%s: a pointer is not 16-byte aligned", fn);
-  if (L->shared.n_experts != 0) {
-    if (L->shared.n_experts != 1)
-      return fail(ctx, MOE_E_INVALID, "%s: shared.n_experts=%d (0 or 1)", fn,
-                  L->shared.n_experts);
-    st = check_weights(ctx, fn, "shared", &L->shared);
-    if (st != MOE_OK) return st;
-    if (L->shared.d != d)
-      return fail(ctx, MOE_E_INVALID, "%s: shared.d=%d differs from d=%d", fn, L->shared.d, d);
-  }
-  return MOE_OK;
-}
-}  // namespace
-
 moe_status moe_layer_workspace_size(const moe_ctx* cctx, const moe_layer* L, int T,
                                     size_t* bytes) {
   moe_ctx* ctx = const_cast<moe_ctx*>(cctx);
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (!bytes) return fail(ctx, MOE_E_INVALID, "moe_layer_workspace_size: bytes is NULL");
-  moe_status st = check_layer(ctx, "moe_layer_workspace_size", L);
+  moe_status st = moe::check_layer_workspace_size(ctx->err, L, T, bytes);
   if (st != MOE_OK) return st;
-  if (T < 0 || (long long)T * L->k > 0x7fffffffLL)
-    return fail(ctx, MOE_E_INVALID, "moe_layer_workspace_size: T=%d", T);
-  *bytes = fwd_layout(nullptr, L, T).bytes;
+  *bytes = moe::fwd_layout(nullptr, L, T).bytes;
   return MOE_OK;
 }
 
@@ -567,40 +352,25 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
                        const float* residual, float* y, int32_t* topk_idx, float* topk_w,
                        void* ws, size_t ws_bytes, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  moe_status st = check_layer(ctx, "moe_forward", L);
-  if (st != MOE_OK) return st;
-  if (act != MOE_ACT_SILU && act != MOE_ACT_GELU_TANH)
-    return fail(ctx, MOE_E_UNSUPPORTED,
-                "moe_forward: unsupported activation=%d (MOE_ACT_SILU=0 or MOE_ACT_GELU_TANH=1)",
-                act);
-  if (T < 0 || (long long)T * L->k > 0x7fffffffLL)
-    return fail(ctx, MOE_E_INVALID, "moe_forward: T=%d", T);
-  if (T == 0) return MOE_OK;
-  if (!x || !y) return fail(ctx, MOE_E_INVALID, "moe_forward: %s is NULL", !x ? "x" : "y");
-  if (!aligned16(x) || !aligned16(y) || !aligned16(residual) || !aligned16(topk_idx) ||
-      !aligned16(topk_w))
-    return fail(ctx, MOE_E_INVALID, "moe_forward: a pointer is not 16-byte aligned");
-  FwdWs f = fwd_layout(ws, L, T);
-  if (!ws || ws_bytes < f.bytes || !aligned16(ws))
-    return fail(ctx, MOE_E_WORKSPACE, "moe_forward: workspace %s (need %zu bytes, got %zu)",
-                !ws ? "is NULL" : !aligned16(ws) ? "is not 16-byte aligned" : "too small",
-                f.bytes, ws_bytes);
+  moe_status st = moe::check_forward(ctx->err, L, act, x, T, residual, y, topk_idx, topk_w, ws,
+                                     ws_bytes, moe::device_cu_count());
+  if (st != MOE_OK || T == 0) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_forward: hipSetDevice(%d) failed", ctx->device);
+  const moe::FwdWs f = moe::fwd_layout(ws, L, T);
   hipStream_t s = (hipStream_t)stream;
   const int E = L->experts.n_experts, d = L->experts.d, k = L->k, R = T * k;
   int32_t* idx = topk_idx ? topk_idx : f.idx;
   float* w = topk_w ? topk_w : f.w;
   const bool has_sh = L->shared.n_experts > 0;
-  const bool fused = has_sh && L->shared.fmt == L->experts.fmt &&
-                     L->shared.layout == L->experts.layout && L->experts.fmt != MOE_W_FP32;
+  const bool fused = moe::layer_fused(L);
   const moe_weights& X = L->experts;
   const moe_weights& S = L->shared;
   // When every expert set reads x as digits, the selection kernel encodes x
   // too (its row loads overlap the selection); small batches also skip the
   // permutation (the FFN groups the pairs itself).
   const bool enc = X.fmt != MOE_W_FP32 && (fused || !has_sh);
-  const bool small = enc && T <= moe::kSmallT;
+  const bool small = moe::forward_small(L, T);
   hipError_t e;
   if (enc) {
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
@@ -658,30 +428,12 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
 moe_status moe_tile_weights(moe_ctx* ctx, const moe_weights* src, void* dst_gate_up,
                             void* dst_down, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (!src) return fail(ctx, MOE_E_INVALID, "moe_tile_weights: src is NULL");
-  moe_status st = check_weights(ctx, "moe_tile_weights", "src", src);
+  moe_status st = moe::check_tile_weights(ctx->err, src, dst_gate_up, dst_down);
   if (st != MOE_OK) return st;
-  if (src->fmt == MOE_W_FP32)
-    return fail(ctx, MOE_E_UNSUPPORTED, "moe_tile_weights: fp32 weights have no tiled layout");
-  if (src->layout != MOE_LAYOUT_ROWS)
-    return fail(ctx, MOE_E_INVALID, "moe_tile_weights: src layout must be MOE_LAYOUT_ROWS");
-  if (!dst_gate_up || !dst_down || !aligned16(dst_gate_up) || !aligned16(dst_down))
-    return fail(ctx, MOE_E_INVALID, "moe_tile_weights: a destination is NULL or misaligned");
-  const long long E = src->n_experts, d = src->d, I = src->inter;
-  const long long half = src->fmt == MOE_W_INT8_ROW ? 1 : 2;
-  const long long gu_bytes = E * 2 * I * d / half, dn_bytes = E * d * I / half;
-  auto overlap = [](const void* a, long long na, const void* b, long long nb) {
-    const char* pa = static_cast<const char*>(a);
-    const char* pb = static_cast<const char*>(b);
-    return pa < pb + nb && pb < pa + na;
-  };
-  if (overlap(dst_gate_up, gu_bytes, src->w_gate_up, gu_bytes) ||
-      overlap(dst_down, dn_bytes, src->w_down, dn_bytes) ||
-      overlap(dst_gate_up, gu_bytes, dst_down, dn_bytes))
-    return fail(ctx, MOE_E_INVALID, "moe_tile_weights: buffers overlap");
   DeviceGuard g(ctx->device);
   if (!g.ok)
     return fail(ctx, MOE_E_DEVICE, "moe_tile_weights: hipSetDevice(%d) failed", ctx->device);
+  const long long E = src->n_experts, d = src->d, I = src->inter;
   hipError_t e = moe::launch_tile_weights(src->fmt, src->w_gate_up, dst_gate_up, E * 2 * I,
                                           (int)d, (hipStream_t)stream);
   if (e == hipSuccess)
@@ -694,17 +446,9 @@ moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row
                        const float* topk_w, const float* shared, const float* residual, int T,
                        int k, int d, float* y, void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  if (T < 0 || k < 1 || k > moe::kMaxK || d < 1)
-    return fail(ctx, MOE_E_INVALID, "moe_combine: T=%d k=%d d=%d", T, k, d);
-  if (d % 4 != 0)
-    return fail(ctx, MOE_E_UNSUPPORTED, "moe_combine: d=%d is not a multiple of 4", d);
-  if (T == 0) return MOE_OK;
-  if (!rows || !topk_w || !y)
-    return fail(ctx, MOE_E_INVALID, "moe_combine: %s is NULL",
-                !rows ? "rows" : !topk_w ? "topk_w" : "y");
-  if (!aligned16(rows) || !aligned16(token_row) || !aligned16(topk_w) || !aligned16(shared) ||
-      !aligned16(residual) || !aligned16(y))
-    return fail(ctx, MOE_E_INVALID, "moe_combine: a pointer is not 16-byte aligned");
+  moe_status st = moe::check_combine(ctx->err, rows, token_row, topk_w, shared, residual, T, k, d,
+                                     y);
+  if (st != MOE_OK || T == 0) return st;
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_combine: hipSetDevice(%d) failed", ctx->device);
   hipError_t e = moe::launch_combine(rows, token_row, topk_w, shared, residual, T, k, d, y,

@@ -140,7 +140,8 @@ template <typename V, int N>
 __device__ inline bool split_join(const SplitK& sk, int unit, int slot0, int kw, int n, int grp,
                                   bool holder, V* v, int* flag_sm) {
   // slot layout [grp][c][lane]: each store and load of a value is 256
-  // contiguous bytes over the wavefront
+  // contiguous bytes over the wavefront; grp < 4 (the column groups)
+  static_assert(4 * N * kWave * sizeof(V) <= kSplitSlotBytes, "a slot holds 4 groups");
   V* base = reinterpret_cast<V*>(sk.part);
   constexpr size_t kPer = kSplitSlotBytes / sizeof(V);
   const int lane = threadIdx.x & (kWave - 1);
@@ -1591,73 +1592,19 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(const float* __restrict__ 
 
 int g_cu_count = 256;
 
-// Workgroups per work unit (K split) for a launch of `units` units on the
-// chip: the time of a launch follows its busiest CU, ceil(units n / CUs)
-// workgroups of 1/n unit each plus a fixed cost per workgroup (tile lookup,
-// the first loads' latency, the join through device-coherent memory; about
-// half a unit's streaming at decode sizes, measured), so n = 1 unless CUs
-// would sit idle.  Each wavefront keeps at least min_steps K-steps.
-inline int split_ways(long long units, int ksteps_per_wave_at_1, int min_steps) {
-  const long long cus = g_cu_count;
-  int best = 1;
-  double best_cost = 1e30;
-  for (int n = 1; n <= 8; ++n) {
-    if (n > 1 && (units * n > kSplitSlots || ksteps_per_wave_at_1 / n < min_steps)) break;
-    const double waves = (double)((units * n + cus - 1) / cus);
-    const double cost = waves * (1.0 / n + 0.5);
-    if (cost < best_cost * 0.97) {
-      best_cost = cost;
-      best = n;
-    }
-  }
-  return best;
-}
-
-// Split plan for a launch of t0 + t1 tiles (groups 0 and 1) x gx column
-// units: every unit alike (n0 = n1 from split_ways) when CUs would otherwise
-// sit idle; else, when group 0's units fit the chip and group 1's spill over
-// it (e.g. 256 routed units and the shared expert's 32 at one token), group 1
-// alone splits into enough small workgroups that each CU takes one beside its
-// group-0 unit.  kpw: K-steps per wavefront unsplit.  Returns false when the
-// join area cannot hold the plan's slots and counts.
-inline bool plan_split(long long t0, long long t1, int gx, int kpw, int min_steps, int& n0,
-                       int& n1) {
-  const long long u0 = t0 * gx, u1 = t1 * gx, cus = g_cu_count;
-  n0 = n1 = split_ways(u0 + u1, kpw, min_steps);
-  if (n0 == 1 && u1 > 0 && u0 <= cus && u0 + u1 > cus) {
-    int n = (int)((cus + u1 - 1) / u1);
-    n = n < 8 ? n : 8;
-    while (n > 1 && (kpw / n < min_steps || u1 * n > kSplitSlots)) --n;
-    n1 = n;
-  }
-  if (n0 == 1 && n1 == 1) return true;
-  const long long slots = (n0 > 1 ? u0 * n0 : 0) + (n1 > 1 ? u1 * n1 : 0);
-  return slots <= kSplitSlots && u0 + u1 <= kSplitSlots;
-}
-
 template <int FMT, int LAY, bool PAIRS>
 hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8_t* xq,
                        const float* xs, const FfnWs& ws, hipStream_t s) {
   const int tiles = a.tiles + b.tiles;
   const int imax = a.inter > b.inter ? a.inter : b.inter;
-  // split K across more wavefronts when the tiles alone cannot fill the chip:
-  // 4 ways (1024-thread workgroups, one per CU) while the units fit one per
-  // CU for int4, whose waves stream half the bytes per K-step (measured:
-  // Qwen-shaped T = 2 gate/up 20.6 -> 17.4 us; past one round it lost);
-  // int8 takes 4 ways only below half the CUs (4 ways at 288 units lost)
-  const long long blocks = (long long)tiles * (imax / 64);
-  const auto kway = [](long long units) {
-    if (units >= 2LL * g_cu_count) return 1;
-    const long long four_below = FMT == 1 ? g_cu_count / 2 : (long long)g_cu_count + 1;
-    return units < four_below ? 4 : 2;
-  };
-  const int ks = kway(blocks);
-  // and across workgroups when the units do not spread evenly over the CUs
-  const int ksteps = FMT == 1 ? d / kKStep : d / 128;  // K-steps (int4: spans) per unit
-  // (only the small-batch launches split: they are the ones that leave CUs idle)
-  SplitK sk{1, 1, ws.cnt, ws.part};
-  if (PAIRS && !plan_split(a.tiles, b.tiles, imax / 64, ksteps / ks, 2, sk.n0, sk.n1))
-    return hipErrorInvalidValue;  // beyond the join area (the plan keeps within it)
+  // K split inside and across workgroups (plan.h); the C ABI ran the same plan
+  // before anything was enqueued and refused one beyond the join area, so this
+  // check cannot fail on a call that passed it
+  FfnPlan plan{};
+  plan_launches(FMT == 1 ? 1 : 2, a.tiles, b.tiles, imax, d, g_cu_count, PAIRS, plan);
+  if (!plan.ok) return hipErrorInvalidValue;
+  const int ks = plan.gu.ks;
+  SplitK sk{plan.gu.n0, plan.gu.n1, ws.cnt, ws.part};
   const bool gsplit = sk.n0 > 1 || sk.n1 > 1;
   const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
   // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
@@ -1681,13 +1628,9 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
 #undef MOE_GU
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long dblocks = (long long)tiles * (d / 64);
-  const int dks = kway(dblocks);
-  const int dsteps = FMT == 1 ? imax / kKStep : imax / 128;
-  const bool ng2 = FMT == 1 && dks == 1 && d % 128 == 0;
-  SplitK dsk{1, 1, ws.cnt, ws.part};
-  if (PAIRS && !ng2 && !plan_split(a.tiles, b.tiles, d / 64, dsteps / dks, 2, dsk.n0, dsk.n1))
-    return hipErrorInvalidValue;
+  const int dks = plan.dn.ks;
+  const bool ng2 = plan.dn.ng2;
+  SplitK dsk{plan.dn.n0, plan.dn.n1, ws.cnt, ws.part};
   const bool dsplit = dsk.n0 > 1 || dsk.n1 > 1;
   const int dgy = dsplit ? a.tiles * dsk.n0 + b.tiles * dsk.n1 : tiles;
   const size_t lds_dn =
@@ -1713,6 +1656,7 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
 }  // namespace
 
 void set_device_info(int cu_count) { g_cu_count = cu_count > 0 ? cu_count : 256; }
+int device_cu_count() { return g_cu_count; }
 
 hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* sig, bool perm,
                               int* split_cnt, hipStream_t s) {
@@ -1813,21 +1757,10 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     return sets[0].layout == 1 ? launch_gemm_pair<kTiled>(grp[0], grp[1], d, ws.xq, ws.xs, s)
                                : launch_gemm_pair<kRows>(grp[0], grp[1], d, ws.xq, ws.xs, s);
   }
-  // rows per tile: at most 16 (the MFMA N side); small batches use fewer; wide
-  // rows use fewer so that a tile's staged rows (x digits for gate/up, h
-  // digits and block scales for down) fit the LDS beside the kernels' largest
-  // static arrays (the K-slice partials, under 50 KB)
-  int mt = T < kTileRows ? (T > 0 ? T : 1) : kTileRows;
-  {
-    size_t per_row = (size_t)2 * d + 16;
-    for (int q = 0; q < nsets; ++q) {
-      const size_t dn = (size_t)2 * sets[q].inter + 16 + (size_t)(sets[q].inter / 64) * 4;
-      if (dn > per_row) per_row = dn;
-    }
-    const size_t cap = (kLdsBytes - 50 * 1024) / per_row;
-    if (cap < 1) return hipErrorInvalidValue;
-    if ((size_t)mt > cap) mt = (int)cap;
-  }
+  // rows per tile (plan.h): at most 16, fewer for small batches and wide rows
+  int inters[2] = {sets[0].inter, nsets > 1 ? sets[1].inter : 0};
+  const int mt = ffn_tile_rows(T, d, nsets, inters);
+  if (mt < 1) return hipErrorInvalidValue;
   Group grp[2] = {};
   for (int q = 0; q < nsets; ++q) {
     const FfnSet& f = sets[q];

@@ -6,76 +6,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "layout.h"
+
 namespace moe {
 
-// ---------------------------------------------------------------- sizes
+// sizes, limits and the workspace layouts: layout.h (plain host C++)
 constexpr int kWave = 64;              // CDNA wavefront width
-constexpr int kRouterChunk = 256;      // router logits are summed in fixed 256-input chunks
-constexpr int kMaxK = 16;              // top-k limit
-constexpr int kMaxE = 1024;            // experts per layer limit
-constexpr int kMaxWidth = 16384;       // d and inter limit
-constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup (gfx950)
-constexpr int kKStep = 64;             // K of one int8 MFMA (16x16x64)
-constexpr int kTileRows = 16;          // routed rows per FFN tile (MFMA N)
-
-inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
-// ---------------------------------------------------------------- workspace layout
-// Router: fp32 partial logits [ceil(d/256)][T][E].
-inline size_t route_ws_bytes(int T, int d, int E) {
-  size_t chunks = (size_t)((d + kRouterChunk - 1) / kRouterChunk);
-  return align_up(chunks * (size_t)T * (size_t)E * sizeof(float), 256);
-}
-
-// Expert FFN, quantised formats (per expert set q = 0, 1):
-//   xq    [T][2][d] int8     activations as two int8 digits (see ffn.hip)
-//   xs    [T] fp32           per-row power-of-two scale of xq
-//   hq[q] [R_q][2][I_q] int8 h = silu(gate) * up as two digits
-//   hs[q] [R_q][I_q/64] fp32 scale per row and 64-column block
-// fp32 format: h [R][I] fp32 only.
-struct FfnWs {
-  int8_t* xq;
-  float* xs;
-  int8_t* hq[2];
-  float* hs[2];
-  float* h;
-  int* cnt;     // split-K arrival counters (kSplitSlots), zero between launches
-  float* part;  // split-K partial sums (kSplitSlots slots of kSplitSlotBytes)
-  size_t bytes;
-};
-
-// Decode launches with fewer work units than the chip has CUs (or a few more)
-// split K across workgroups: unit u's n workgroups write partial sums into
-// slots u*n .. u*n+n-1 and the last to arrive adds them in slot order.
-constexpr int kSplitSlots = 1024;
-constexpr size_t kSplitSlotBytes = 16384;
-
-// rows/inter of up to two expert sets sharing one x
-inline FfnWs ffn_ws_layout(void* base, int T, int d, int nsets, const int* R, const int* inter,
-                           bool quantised) {
-  FfnWs w{};
-  size_t off = 0;
-  char* b = static_cast<char*>(base);
-  auto take = [&](size_t n) {
-    char* p = b ? b + off : nullptr;
-    off = align_up(off + n, 256);
-    return p;
-  };
-  if (quantised) {
-    w.xq = reinterpret_cast<int8_t*>(take((size_t)T * 2 * d));
-    w.xs = reinterpret_cast<float*>(take((size_t)T * sizeof(float)));
-    for (int q = 0; q < nsets; ++q) {
-      w.hq[q] = reinterpret_cast<int8_t*>(take((size_t)R[q] * 2 * inter[q]));
-      w.hs[q] = reinterpret_cast<float*>(take((size_t)R[q] * (inter[q] / 64) * sizeof(float)));
-    }
-    w.cnt = reinterpret_cast<int*>(take((size_t)kSplitSlots * sizeof(int)));
-    w.part = reinterpret_cast<float*>(take((size_t)kSplitSlots * kSplitSlotBytes));
-  } else {
-    w.h = reinterpret_cast<float*>(take((size_t)R[0] * inter[0] * sizeof(float)));
-  }
-  w.bytes = off;
-  return w;
-}
+constexpr size_t kLdsBytes = kPlanLdsBytes;  // LDS per workgroup (gfx950)
+constexpr int kKStep = kPlanKStep;     // K of one int8 MFMA (16x16x64)
+constexpr int kTileRows = kPlanTileRows;  // routed rows per FFN tile (MFMA N)
 
 // One expert set for the quantised FFN launchers.
 struct FfnSet {
@@ -95,14 +34,6 @@ struct FfnSet {
   int k;
   int act;                   // gate activation: 0 silu, 1 gelu_tanh
 };
-
-// Upper bound on the number of FFN tiles (kTileRows rows of one expert each)
-// for R rows spread over E experts: sum_e ceil(c_e/MT) <= n + (R - n)/MT with
-// n = min(E, R) non-empty experts at most.
-inline int max_tiles(int R, int E, int mt) {
-  int n = R < E ? R : E;
-  return n + (R - n + mt - 1) / mt;
-}
 
 // ---------------------------------------------------------------- kernel timer
 // Measurement aid (off unless a context turns it on): each launch is
@@ -142,7 +73,6 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
 // set of the layer reads the same digits.  No permutation: up to kSmallT
 // tokens the FFN groups the pairs itself (FfnSet::pairs_idx), beyond that
 // launch_permute follows.
-constexpr int kSmallT = 16;
 hipError_t launch_router_encode(int router, const float* x, const float* wr, const float* bias,
                                 const uint8_t* mask,
                                 int T, int d, int E, int k, float scale, int32_t* idx, float* w,
@@ -163,6 +93,7 @@ hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* si
 hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
                             const FfnWs& ws, bool x_encoded, hipStream_t s);
 void set_device_info(int cu_count);
+int device_cu_count();
 // Row-major codes [nrows][K] (int4: K/2 bytes per row) -> tiled layout.
 hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nrows, int K,
                                hipStream_t s);

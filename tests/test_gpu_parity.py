@@ -594,3 +594,39 @@ def test_layer_gemm_path_wide_inter(ctx):
     kw = dict(T=128, d=256, E=4, k=2, inter=4224, shared="int8_row", shared_inter=4224,
               xseed=0x4D6F4594)
     _forward_vs_oracle(ctx, "tiny", **kw)
+
+
+# ------------------------------------------------------------------ T = 1024 as 4 x 256 chunks
+
+def test_forward_kimi_prefill_4x256_chunks(ctx):
+    # The Kimi-shaped prefill (d = 2304, E = 256, I = 2048, int8 shared
+    # expert) run as four chunks of 256 tokens, the way the chunked prefill is
+    # timed.  At T = 256 the rows per expert (2048 over 256 experts) stay below
+    # the grouped GEMM's threshold, so this takes the 16-row tile kernels with
+    # the shared expert in the same launches, at the layer's real width.  Both
+    # the one-call layer and the five separate calls are compared with the
+    # oracle on sampled tokens of every chunk (tokens are independent, so the
+    # oracle of token 256 c + t is the chunk's token t).
+    import torch
+    inp = inputs("kimi_prefill")
+    s = inp.spec
+    L = device_layer(ctx, "kimi_prefill")
+    local = np.array([0, 1, 37, 100, 128, 199, 254, 255])
+    for c in range(4):
+        xc = to_dev(inp.x[256 * c: 256 * (c + 1)])
+        tokens = 256 * c + local
+        oy, oidx, ow, ogap = oracle.layer_of(inp, tokens=tokens)
+        _, _, _, logits = oracle.route(s.router, inp.x[tokens], inp.wr, inp.bias, s.k, s.scale,
+                                       want_logits=True)
+        keys = oracle_keys(s.router, logits, inp.bias)
+        for path in ("forward", "staged"):
+            print(f"[chunk] kimi_prefill chunk {c} path {path}", flush=True)
+            y = L.forward_fused(xc) if path == "forward" else L(xc)
+            torch.cuda.synchronize()
+            gy = y.cpu().numpy()[local]
+            exc = compare_route(L.idx.cpu().numpy()[local], L.w.cpu().numpy()[local], oidx, ow,
+                                ogap, keys, s.scale)
+            keep = np.setdiff1d(np.arange(len(local)), exc)
+            ratio = compare_outputs(gy, oy, keep)
+            _log(test="forward_4x256", config="kimi_prefill", chunk=c, path=path, T=256,
+                 checked_tokens=len(local), excused=len(exc), err_over_max=ratio)
