@@ -314,6 +314,25 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* layer, int act, const floa
                        const float* residual, float* y, int32_t* topk_idx, float* topk_w,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It runs exactly moe_forward's kernels, with the
+ * library's own scratch array (a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process ends)
+ * as the workspace; it allocates nothing.  Every call on a GPU shares that
+ * GPU's array and leaves its contents behind, so calls that overlap on one GPU
+ * (on two streams, or from two threads) race: serialise them.  A layer whose
+ * moe_layer_workspace_size at T exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_E_UNSUPPORTED before anything is enqueued (40 MiB covers a Kimi-shaped
+ * layer, d = 2304, E = 256, I = 2048 with its int8 shared expert, up to
+ * T = 186, and a Qwen-shaped int4 layer, d = 2048, E = 128, I = 768, up to
+ * T = 290).  Arguments, checks, results and other errors as for
+ * moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (40u * 1024u * 1024u)
+moe_status moe_forward_noalloc(moe_ctx* ctx, const moe_layer* layer, int act, const float* x,
+                               int T, const float* residual, float* y, int32_t* topk_idx,
+                               float* topk_w, void* stream);
+
 /* Kernel timing, a measurement aid for benchmarks; off by default.
  * moe_timing(ctx, capacity > 0) creates 2*capacity HIP events (host-side
  * allocation, outside any call path) and from then on brackets every kernel

@@ -33,7 +33,9 @@ FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B3
 EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
-           "moe_tile_weights", "moe_route_masked", "moe_expert_counts", "moe_quantize")
+           "moe_tile_weights", "moe_route_masked", "moe_expert_counts", "moe_quantize",
+           "moe_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 40 * 1024 * 1024
 
 
 class MoeError(RuntimeError):
@@ -97,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                              ctypes.POINTER(sz)]
     lib.moe_forward.argtypes = [vp, ctypes.POINTER(moe_layer), ci, vp, ci, vp, vp, vp, vp, vp, sz,
                                 vp]
+    lib.moe_forward_noalloc.argtypes = [vp, ctypes.POINTER(moe_layer), ci, vp, ci, vp, vp, vp, vp,
+                                        vp]
     lib.moe_tile_weights.argtypes = [vp, ctypes.POINTER(moe_weights), vp, vp, vp]
     lib.moe_timing.argtypes = [vp, ci]
     lib.moe_timing_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), ci,
@@ -104,7 +108,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
               "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
               "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts",
-              "moe_quantize"):
+              "moe_quantize", "moe_forward_noalloc"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -213,6 +217,12 @@ class Context:
             self.handle, ctypes.byref(layer), act, _p(x), T, _p(residual), _p(y), _p(topk_idx),
             _p(topk_w), _p(ws), ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
             _stream(stream)))
+
+    def moe_forward_noalloc(self, layer: "moe_layer", act, x, T, residual, y, topk_idx, topk_w,
+                            stream=None):
+        self._check(self.lib.moe_forward_noalloc(
+            self.handle, ctypes.byref(layer), act, _p(x), T, _p(residual), _p(y), _p(topk_idx),
+            _p(topk_w), _stream(stream)))
 
     def moe_tile_weights(self, src: "DeviceExperts", dst_gate_up, dst_down, stream=None):
         w = src.struct()

@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <cmath>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -68,9 +68,39 @@ struct moe_ctx {
   char err[moe::kErrBytes];
   bool timing;
   moe::KernelTimer timer;
+  void* scratch;  // this device's copy of `scratch` (below), for moe_forward_noalloc
 };
 
+// The workspace of moe_forward_noalloc: one copy per GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never device memory: every host use goes through the address
+// hipGetSymbolAddress returns for the current device (scratch_address).
+static constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on `device`, taken once per device with
+// that device current.  NULL (and the HIP error in *err) on failure.
+void* scratch_address(int device, hipError_t* err) {
+  *err = hipSuccess;
+  if (device < 0 || device >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[device]) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_dev[device] = ptr;
+  }
+  return g_scratch_dev[device];
+}
 
 thread_local char g_create_err[512] = "";
 
@@ -159,6 +189,16 @@ moe_status moe_create(int device, moe_ctx** out) {
   snprintf(ctx->arch, sizeof(ctx->arch), "%s", prop.gcnArchName);
   ctx->err[0] = '\0';
   ctx->timing = false;
+  {
+    DeviceGuard g(device);
+    hipError_t se = g.ok ? hipSuccess : hipErrorInvalidDevice;
+    ctx->scratch = g.ok ? scratch_address(device, &se) : nullptr;
+    if (!ctx->scratch) {
+      delete ctx;
+      return fail(nullptr, MOE_E_DEVICE, "moe_create: address of the scratch array on device %d: "
+                  "%s", device, hipGetErrorString(se));
+    }
+  }
 
   moe::set_device_info(ctx->cu_count);
   *out = ctx;
@@ -348,15 +388,16 @@ moe_status moe_layer_workspace_size(const moe_ctx* cctx, const moe_layer* L, int
   return MOE_OK;
 }
 
-moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x, int T,
-                       const float* residual, float* y, int32_t* topk_idx, float* topk_w,
-                       void* ws, size_t ws_bytes, void* stream) {
-  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
-  moe_status st = moe::check_forward(ctx->err, L, act, x, T, residual, y, topk_idx, topk_w, ws,
-                                     ws_bytes, moe::device_cu_count());
-  if (st != MOE_OK || T == 0) return st;
+}  // extern "C"
+
+namespace {
+// The layer after its checks passed, with ws (at least fwd_layout's bytes)
+// as the workspace: every launch of moe_forward and moe_forward_noalloc.
+moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float* x, int T,
+                          const float* residual, float* y, int32_t* topk_idx, float* topk_w,
+                          void* ws, void* stream, const char* fn) {
   DeviceGuard g(ctx->device);
-  if (!g.ok) return fail(ctx, MOE_E_DEVICE, "moe_forward: hipSetDevice(%d) failed", ctx->device);
+  if (!g.ok) return fail(ctx, MOE_E_DEVICE, "%s: hipSetDevice(%d) failed", fn, ctx->device);
   const moe::FwdWs f = moe::fwd_layout(ws, L, T);
   hipStream_t s = (hipStream_t)stream;
   const int E = L->experts.n_experts, d = L->experts.d, k = L->k, R = T * k;
@@ -422,7 +463,38 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
   if (e == hipSuccess)  // small batches leave the rows in (token, slot) order
     e = moe::launch_combine(f.rows, small ? nullptr : f.token_row, w,
                             has_sh ? f.sh_rows : nullptr, residual, T, k, d, y, s);
-  return device_result(ctx, e, "moe_forward");
+  return device_result(ctx, e, fn);
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x, int T,
+                       const float* residual, float* y, int32_t* topk_idx, float* topk_w,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  moe_status st = moe::check_forward(ctx->err, "moe_forward", L, act, x, T, residual, y,
+                                     topk_idx, topk_w, ws, ws_bytes, moe::device_cu_count());
+  if (st != MOE_OK || T == 0) return st;
+  return forward_launch(ctx, L, act, x, T, residual, y, topk_idx, topk_w, ws, stream,
+                        "moe_forward");
+}
+
+moe_status moe_forward_noalloc(moe_ctx* ctx, const moe_layer* L, int act, const float* x, int T,
+                               const float* residual, float* y, int32_t* topk_idx,
+                               float* topk_w, void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  moe_status st = moe::check_forward(ctx->err, "moe_forward_noalloc", L, act, x, T, residual, y,
+                                     topk_idx, topk_w, ctx->scratch, kScratchBytes,
+                                     moe::device_cu_count());
+  if (st == MOE_E_WORKSPACE)  // the layer at T needs more than the library's scratch
+    return fail(ctx, MOE_E_UNSUPPORTED,
+                "moe_forward_noalloc: T=%d needs %zu bytes of workspace, above the %zu-byte "
+                "scratch array; call moe_forward with a workspace", T,
+                moe::fwd_layout(nullptr, L, T).bytes, kScratchBytes);
+  if (st != MOE_OK || T == 0) return st;
+  return forward_launch(ctx, L, act, x, T, residual, y, topk_idx, topk_w, ctx->scratch, stream,
+                        "moe_forward_noalloc");
 }
 
 moe_status moe_tile_weights(moe_ctx* ctx, const moe_weights* src, void* dst_gate_up,

@@ -237,26 +237,26 @@ moe_status check_layer_workspace_size(char* err, const moe_layer* L, int T, cons
   return MOE_OK;
 }
 
-moe_status check_forward(char* err, const moe_layer* L, int act, const float* x, int T,
-                         const float* residual, const float* y, const int32_t* topk_idx,
+moe_status check_forward(char* err, const char* fn, const moe_layer* L, int act, const float* x,
+                         int T, const float* residual, const float* y, const int32_t* topk_idx,
                          const float* topk_w, const void* ws, size_t ws_bytes, int cu_count) {
-  moe_status st = check_layer(err, "moe_forward", L);
+  moe_status st = check_layer(err, fn, L);
   if (st != MOE_OK) return st;
   if (act != MOE_ACT_SILU && act != MOE_ACT_GELU_TANH)
     return errorf(err, MOE_E_UNSUPPORTED,
-                  "moe_forward: unsupported activation=%d (MOE_ACT_SILU=0 or MOE_ACT_GELU_TANH=1)",
-                  act);
+                  "%s: unsupported activation=%d (MOE_ACT_SILU=0 or MOE_ACT_GELU_TANH=1)",
+                  fn, act);
   if (T < 0 || (long long)T * L->k > 0x7fffffffLL)
-    return errorf(err, MOE_E_INVALID, "moe_forward: T=%d", T);
+    return errorf(err, MOE_E_INVALID, "%s: T=%d", fn, T);
   if (T == 0) return MOE_OK;
-  if (!x || !y) return errorf(err, MOE_E_INVALID, "moe_forward: %s is NULL", !x ? "x" : "y");
+  if (!x || !y) return errorf(err, MOE_E_INVALID, "%s: %s is NULL", fn, !x ? "x" : "y");
   if (!aligned16(x) || !aligned16(y) || !aligned16(residual) || !aligned16(topk_idx) ||
       !aligned16(topk_w))
-    return errorf(err, MOE_E_INVALID, "moe_forward: a pointer is not 16-byte aligned");
+    return errorf(err, MOE_E_INVALID, "%s: a pointer is not 16-byte aligned", fn);
   const FwdWs f = fwd_layout(nullptr, L, T);
   if (const char* why = ws_problem(ws, ws_bytes, f.bytes))
-    return errorf(err, MOE_E_WORKSPACE, "moe_forward: workspace %s (need %zu bytes, got %zu)",
-                  why, f.bytes, ws_bytes);
+    return errorf(err, MOE_E_WORKSPACE, "%s: workspace %s (need %zu bytes, got %zu)", fn, why,
+                  f.bytes, ws_bytes);
   if (forward_small(L, T)) {
     // small batches may split K across workgroups, which meet in the
     // workspace's join area: the launch plan (plan.h, the one the launcher
@@ -266,8 +266,8 @@ moe_status check_forward(char* err, const moe_layer* L, int act, const float* x,
                                layer_fused(L) ? L->shared.inter : 0, cu_count, true);
     if (!p.ok)
       return errorf(err, MOE_E_UNSUPPORTED,
-                    "moe_forward: the small-batch launch plan for T=%d, E=%d, d=%d, inter=%d "
-                    "exceeds the split-K join area (%d slots)", T, X.n_experts, X.d, X.inter,
+                    "%s: the small-batch launch plan for T=%d, E=%d, d=%d, inter=%d "
+                    "exceeds the split-K join area (%d slots)", fn, T, X.n_experts, X.d, X.inter,
                     kSplitSlots);
   }
   return MOE_OK;

@@ -39,8 +39,9 @@ moe_status check_expert_ffn(char* err, const moe_weights* w, int act, const floa
 moe_status check_layer(char* err, const char* fn, const moe_layer* L);
 moe_status check_layer_workspace_size(char* err, const moe_layer* L, int T, const size_t* bytes);
 // cu_count: the device's compute units (the small-batch launch plan depends on it)
-moe_status check_forward(char* err, const moe_layer* L, int act, const float* x, int T,
-                         const float* residual, const float* y, const int32_t* topk_idx,
+// fn: the entry point's name for the messages (moe_forward, moe_forward_noalloc)
+moe_status check_forward(char* err, const char* fn, const moe_layer* L, int act, const float* x,
+                         int T, const float* residual, const float* y, const int32_t* topk_idx,
                          const float* topk_w, const void* ws, size_t ws_bytes, int cu_count);
 moe_status check_tile_weights(char* err, const moe_weights* src, const void* dst_gate_up,
                               const void* dst_down);

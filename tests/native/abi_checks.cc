@@ -207,48 +207,48 @@ static void forward_cases() {
   float* y = dev<float>(41);
   void* ws = dev<void>(42);
   const size_t need = fwd_layout(nullptr, &L, 8).bytes;
-  EXPECT(check_forward(g_err, &L, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256), MOE_OK,
+  EXPECT(check_forward(g_err, "moe_forward", &L, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256), MOE_OK,
          nullptr);
-  EXPECT(check_forward(g_err, &L, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need - 1, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &L, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need - 1, 256),
          MOE_E_WORKSPACE, "too small");
-  EXPECT(check_forward(g_err, &L, 3, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &L, 3, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_UNSUPPORTED, "activation");
-  EXPECT(check_forward(g_err, &L, 0, x, -1, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &L, 0, x, -1, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "T=-1");
-  EXPECT(check_forward(g_err, &L, 0, x, 8, misaligned<float>(43), y, nullptr, nullptr, ws, need,
+  EXPECT(check_forward(g_err, "moe_forward", &L, 0, x, 8, misaligned<float>(43), y, nullptr, nullptr, ws, need,
                        256),
          MOE_E_INVALID, "aligned");
-  EXPECT(check_forward(g_err, &L, 0, nullptr, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &L, 0, nullptr, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "x is NULL");
-  EXPECT(check_forward(g_err, nullptr, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", nullptr, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "layer is NULL");
   moe_layer b = L;
   b.k = 17;
-  EXPECT(check_forward(g_err, &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "k=17");
   b = L;
   b.router = MOE_ROUTER_SOFTMAX;
-  EXPECT(check_forward(g_err, &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "bias");
   b = L;
   b.shared.n_experts = 2;
-  EXPECT(check_forward(g_err, &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "shared.n_experts");
   b = L;
   b.shared.d = 1024;
-  EXPECT(check_forward(g_err, &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "shared.d");
   b = L;
   b.w_router = nullptr;
-  EXPECT(check_forward(g_err, &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
+  EXPECT(check_forward(g_err, "moe_forward", &b, 0, x, 8, nullptr, y, nullptr, nullptr, ws, need, 256),
          MOE_E_INVALID, "w_router");
   // every small-batch shape with k <= 16 fits the join area on 256 CUs
   for (int T = 1; T <= 16; ++T) {
     const size_t nT = fwd_layout(nullptr, &L, T).bytes;
-    EXPECT(check_forward(g_err, &L, 0, x, T, nullptr, y, nullptr, nullptr, ws, nT, 256), MOE_OK,
+    EXPECT(check_forward(g_err, "moe_forward", &L, 0, x, T, nullptr, y, nullptr, nullptr, ws, nT, 256), MOE_OK,
            nullptr);
   }
-  EXPECT(check_forward(g_err, &L, 0, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+  EXPECT(check_forward(g_err, "moe_forward", &L, 0, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                        256),
          MOE_OK, nullptr);
   size_t bytes = 0;
