@@ -89,6 +89,13 @@ def _load():
     return lib
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel loops from now on (for timing it
+    on one thread); the OpenMP runtime is the one the oracle library loaded."""
+    _load()
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
 def _p(a: Optional[np.ndarray]):
     if a is None:
         return None
