@@ -72,6 +72,13 @@ WORKLOADS = {
                     "Qwen3-shaped MoE layer decode: T=1, d=2048, E=128, top-8 softmax, "
                     "I=768 SwiGLU, int4 block-32 experts, no shared expert"),
     "qwen_prefill": ("qwen_prefill", 1, "Qwen3-shaped MoE layer, T=128"),
+    "qwen_prefill_1024": ("qwen_prefill", 1,
+                          "Qwen3-shaped MoE layer prefill, T=1024 (the pages' prefill length): "
+                          "d=2048, E=128, top-8 softmax, I=768 SwiGLU, int4 block-32 experts, "
+                          "no shared expert", {"T": 1024}),
+    "qwen_prefill_1024_b128": ("qwen_prefill", 1,
+                               "Qwen3-shaped MoE layer prefill, T=1024, int4 block-128 experts",
+                               {"T": 1024, "fmt": "int4_b128"}),
     "qwen_decode_b128": ("qwen_decode", 1,
                          "Qwen3-shaped MoE layer decode as qwen_decode, int4 experts with one "
                          "scale per block of 128 inputs", {"fmt": "int4_b128"}),

@@ -20,7 +20,7 @@ const char* const kKernelNames[K_COUNT] = {
     "encode_rows",   "ffn_i8_gate_up",  "ffn_i8_down",     "ffn_i4_gate_up",
     "ffn_i4_down",   "ffn_f32_gate_up", "ffn_f32_down",    "combine",
     "router_tail",   "ffn_i8_gate_up_gemm", "ffn_i8_down_gemm", "quant_i8_rows",
-    "quant_i4_blocks"};
+    "quant_i4_blocks", "ffn_i4_gate_up_gemm", "ffn_i4_down_gemm"};
 
 // Event pairs recorded around launches while a context has timing on.
 struct KernelTimer {

@@ -1653,6 +1653,333 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------------ int4 grouped GEMM
+// Prefill for int4 experts (blocks of 32 or 128 along the input), gate/up
+// (DOWN = false) and down (DOWN = true) in one kernel shape: tiles of 64 rows
+// of one expert x 512 weight rows (gate/up: 256 h columns as their gate and up
+// rows; down: 512 output columns), 8 wavefronts of 64 rows x 64 weight rows
+// (4 fragments of 16).  Per 128-input span a double-buffered LDS ring slot
+// takes, straight from global memory (global_load_lds): the 32 weight blocks
+// of the tiled layout (1 KB: 16 rows x 128 inputs), the tile's activation
+// digits (x for gate/up, h for down; 2 KB per 16 rows and digit, in the int4
+// digit order, laid out [half][lane][16 B] so that each lane reads its own
+// 32 bytes without bank conflicts) and the weight rows' block scales.  The
+// digits are the MFMA A operand (a lane's accumulators are 4 tile rows of one
+// weight row, so it needs one weight scale per block); each block of 32
+// inputs takes one 16x16x32 MFMA per digit on codes unpacked as 16 * code;
+// the two int32 digit sums join as 256 p0 + p1 (exact) and fold into fp32
+// with the block's scale raised to 2^-14 (block 128: the span's four blocks
+// accumulate in int32 and fold once).  down also applies the h scale of the
+// row and span (one per 128 h columns, written by the gate/up epilogue).
+constexpr int k4Rows = 64;                        // tile rows
+constexpr int k4Frags = 4;                        // weight fragments per wavefront
+constexpr int k4NA = kPWaves * k4Frags;           // weight blocks per span (32)
+constexpr int k4Cols = 16 * k4NA;                 // weight rows per workgroup (512)
+constexpr int k4Dig = (k4Rows / 16) * 2 * 2048;   // digit bytes per span (16 KB)
+constexpr int k4MaxSpans = 64;                    // h scales staged per row (I <= 8192)
+
+template <int FMT>
+struct G4Shape {
+  static constexpr int SCB = FMT == 2 ? 16 : 4;   // scale bytes per weight row and span
+  static constexpr int SC_OFF = k4NA * kPBlk + k4Dig;
+  static constexpr int SLOT = SC_OFF + k4Cols * SCB;  // 56 KB (block 32), 50 KB (block 128)
+};
+
+// Direct global-to-LDS load of 4 bytes per lane: lane l's word lands at dst + 4 l.
+__device__ inline void lds_load4(const void* src, int8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+template <int FMT, bool DOWN>
+__global__ __launch_bounds__(512) void gemm4_kernel(Group g0, Group g1, int d,
+                                                    const int8_t* __restrict__ xq,
+                                                    const float* __restrict__ xs) {
+  using S = G4Shape<FMT>;
+  __shared__ __attribute__((aligned(16))) int8_t ring0[S::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t ring1[S::SLOT];
+  __shared__ float red_max[kPWaves][k4Rows];
+  __shared__ float hsc_sm[DOWN ? k4Rows : 1][DOWN ? k4MaxSpans : 1];
+  __shared__ int tok_sm[k4Rows];
+  Job job;
+  if (!find_job(g0, g1, k4Rows, blockIdx.y, job)) return;
+  // (the tile is uniform over the workgroup: scalar registers, scalar branches)
+  job.g = __builtin_amdgcn_readfirstlane(job.g);
+  job.e = __builtin_amdgcn_readfirstlane(job.e);
+  job.r0 = __builtin_amdgcn_readfirstlane(job.r0);
+  job.nr = __builtin_amdgcn_readfirstlane(job.nr);
+  const Group G = job.g == 0 ? g0 : g1;
+  const int I = G.inter;
+  const int K = DOWN ? I : d;                      // inputs of the product
+  const int N = DOWN ? d : I;                      // output columns (gate/up: h columns)
+  const int cb = blockIdx.x * (DOWN ? k4Cols : k4Cols / 2);
+  if (cb >= N) return;
+  // (wave-uniform values go to scalar registers: the load addresses below
+  // are a scalar base plus the lane's offset)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, g = lane >> 4;
+  const int r0 = job.r0, nr = job.nr;
+  const int ntg = min(4, (nr + 15) / 16);           // row groups holding tile rows
+  const int nsp = K / 128;                          // spans
+  const int nb = FMT == 2 ? K / 32 : K / 128;       // scale blocks per weight row
+  for (int j = threadIdx.x; j < k4Rows; j += blockDim.x)
+    tok_sm[j] = j < nr ? (DOWN ? r0 + j : (G.row_token ? G.row_token[r0 + j] : r0 + j)) : -1;
+  if (DOWN) {  // h scale of each tile row and span, with the 1/256 of the digit join
+    for (int q = threadIdx.x; q < k4Rows * nsp; q += blockDim.x) {
+      const int j = q / nsp, m = q % nsp;
+      hsc_sm[j][m] = j < nr ? G.hs[(size_t)(r0 + j) * nsp + m] * (1.0f / 256.0f) : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // weight row of local column jc (gate/up: jc < 256 gate rows cb + jc, then the
+  // up rows I + cb + jc - 256; down: output rows cb + jc), clamped into the matrix
+  auto wrow = [=](int jc) {
+    if (DOWN) return min(cb + jc, N - 1);
+    const int h = min(cb + (jc & 255), N - 1);
+    return jc < 256 ? h : I + h;
+  };
+  const uint8_t* W = static_cast<const uint8_t*>(DOWN ? G.wdn : G.wgu);
+  const float* SC = DOWN ? G.sdn : G.sgu;
+  const size_t wrows = DOWN ? (size_t)d : (size_t)2 * I;   // weight rows per expert
+  // this wavefront's loads per span: weight blocks 4w..4w+3, digit chunks 2w, 2w+1
+  // (chunk c: row group c/4, digit (c/2)%2, half c%2), scale chunk w (64 rows)
+  const uint8_t* asrc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int blk = 4 * wave + u;  // 16 weight rows from local column 16 blk
+    // (N and I are multiples of 128: a clamped block start stays 16-row aligned)
+    asrc[u] = W + ((size_t)job.e * wrows + (wrow(16 * blk) & ~15)) * (K / 2) + 16 * lane;
+  }
+  const int8_t* bsrc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = 2 * wave + u;
+    const int j = 16 * (c >> 2) + i;
+    const int row = tok_sm[j] >= 0 ? tok_sm[j] : tok_sm[0];
+    const int8_t* base = DOWN ? G.hq + (size_t)row * 2 * I : xq + (size_t)row * 2 * d;
+    bsrc[u] = base + ((c >> 1) & 1) * K + 32 * g + 16 * (c & 1);
+  }
+  const float* ssrc = SC + ((size_t)job.e * wrows + wrow(64 * wave + lane)) * nb;
+  // part 0, 1: two weight blocks each; 2: the digit chunks; 3: the scales.  The
+  // parts of the next span are issued between the current span's fragments:
+  // a wavefront that issues all seven loads at once stalls until the CU's
+  // memory pipeline takes them, and the span's arithmetic waits with it
+  auto issue = [&](int8_t* slot, int m, int part) {
+    const int ms = min(m, nsp - 1);
+    if (part < 2) {
+#pragma unroll
+      for (int u = 2 * part; u < 2 * part + 2; ++u)
+        lds_load16(asrc[u] + (size_t)ms * 1024, slot + (4 * wave + u) * kPBlk);
+    } else if (part == 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        lds_load16(bsrc[u] + 128 * ms, slot + k4NA * kPBlk + (2 * wave + u) * kPBlk);
+    } else {
+      if constexpr (FMT == 2) lds_load16(ssrc + 4 * ms, slot + S::SC_OFF + wave * 1024);
+      else lds_load4(ssrc + ms, slot + S::SC_OFF + wave * 256);
+    }
+  };
+
+  // this wavefront's fragments: gate/up: gate blocks 2w, 2w+1 and the up blocks
+  // 16 + 2w, 17 + 2w (the same h columns); down: blocks 4w..4w+3
+  int fblk[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) fblk[f] = DOWN ? 4 * wave + f : (f < 2 ? 2 * wave + f : 14 + 2 * wave + f);
+  const int c0 = DOWN ? cb + 64 * wave : cb + 32 * wave;  // first output column of the wavefront
+  const bool active = c0 < N;
+  float acc[4][4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[f][t][c] = 0.0f;
+  const v4i zero = {0, 0, 0, 0};
+
+  // the span loop unrolled by two, so that each slot is a known LDS array
+#define G4_SPAN(CUR, NXT, M) \
+  { \
+    MOE_WAIT_VM(0); /* this span's loads, issued during the last span */ \
+    ring_barrier(); \
+    { \
+  /* the span's digits of every row group in registers (rows past the tile */ \
+  /* are real rows again; their results are never stored), then one weight */ \
+  /* fragment at a time: unpack, then its MFMAs and folds for each row group */ \
+  /* (block 32: every (fragment, row group) reads its digits from LDS again, */ \
+  /* which keeps its registers below the 256 of two wavefronts per SIMD) */ \
+      constexpr int XT = FMT == 2 ? 1 : 4;  /* row groups whose digits stay in registers */ \
+      long x0[XT][4], x1[XT][4];  /* [row group][block], digit 0 and 1 */ \
+      float hs4[4][4];  /* down: h scale (with 1/256) of tile row 16 t + 4 g + c */ \
+      auto load_digits = [&](int t, long* d0, long* d1) { \
+        const int8_t* db = (CUR) + k4NA * kPBlk + 4 * t * kPBlk;  /* chunks (t, digit, half) */ \
+        const v2l a0 = *reinterpret_cast<const v2l*>(db + 16 * lane); \
+        const v2l a1 = *reinterpret_cast<const v2l*>(db + kPBlk + 16 * lane); \
+        const v2l b0 = *reinterpret_cast<const v2l*>(db + 2 * kPBlk + 16 * lane); \
+        const v2l b1 = *reinterpret_cast<const v2l*>(db + 3 * kPBlk + 16 * lane); \
+        d0[0] = a0.x; d0[1] = a0.y; d0[2] = a1.x; d0[3] = a1.y; \
+        d1[0] = b0.x; d1[1] = b0.y; d1[2] = b1.x; d1[3] = b1.y; \
+      }; \
+_Pragma("unroll") \
+      for (int t = 0; t < 4; ++t) { \
+        if (XT == 4) load_digits(t, x0[t % XT], x1[t % XT]); \
+_Pragma("unroll") \
+        for (int c = 0; c < 4; ++c) hs4[t][c] = DOWN ? hsc_sm[16 * t + 4 * g + c][(M)] : 1.0f; \
+      } \
+_Pragma("unroll") \
+      for (int f = 0; f < 4; ++f) { \
+       if (active) { \
+        long wq[4];  /* unpacked weight codes of the fragment's 4 blocks */ \
+        float sc[4];  /* their scales, raised to 2^-14, with the 1/16 of the unpacking */ \
+        { \
+          const v4i w = lds_frag((CUR) + fblk[f] * kPBlk, lane); \
+_Pragma("unroll") \
+          for (int q = 0; q < 4; ++q) wq[q] = unpack8_int4_x16((unsigned)w[q]); \
+          if constexpr (FMT == 2) { \
+            const v4f sv = *reinterpret_cast<const v4f*>((CUR) + S::SC_OFF + (16 * fblk[f] + i) * 16); \
+_Pragma("unroll") \
+            for (int q = 0; q < 4; ++q) sc[q] = fmaxf(sv[q], kScaleFloor) * kInv16; \
+          } else { \
+            sc[0] = fmaxf(*reinterpret_cast<const float*>((CUR) + S::SC_OFF + (16 * fblk[f] + i) * 4), \
+                          kScaleFloor) * kInv16; \
+          } \
+        } \
+_Pragma("unroll") \
+        for (int t = 0; t < 4; ++t) { \
+          if (t >= ntg) break; \
+          if constexpr (FMT == 2) { \
+            load_digits(t, x0[0], x1[0]); \
+  /* the span's four blocks summed with their scales, then (down) times */ \
+  /* the rows' h scales: sum_m hs[row][m] sum_q s[col][q] p_q */ \
+            float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f}; \
+_Pragma("unroll") \
+            for (int q = 0; q < 4; ++q) { \
+              const v4i p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[0][q], wq[q], zero, 0, 0, 0); \
+              const v4i p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[0][q], wq[q], zero, 0, 0, 0); \
+_Pragma("unroll") \
+              for (int c = 0; c < 4; ++c) sp[c] = fmaf(sc[q], (float)(p0[c] * 256 + p1[c]), sp[c]); \
+            } \
+_Pragma("unroll") \
+            for (int c = 0; c < 4; ++c) \
+              acc[f][t][c] = DOWN ? fmaf(hs4[t][c], sp[c], acc[f][t][c]) : acc[f][t][c] + sp[c]; \
+ \
+          } else { \
+            v4i p0 = zero, p1 = zero; \
+_Pragma("unroll") \
+            for (int q = 0; q < 4; ++q) { \
+              p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[t % XT][q], wq[q], p0, 0, 0, 0); \
+              p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[t % XT][q], wq[q], p1, 0, 0, 0); \
+            } \
+_Pragma("unroll") \
+            for (int c = 0; c < 4; ++c) {  /* |p0| < 2^22: each digit sum exact in fp32 */ \
+              const float v = fmaf((float)p0[c], 256.0f, (float)p1[c]); \
+              acc[f][t][c] = fmaf(DOWN ? sc[0] * hs4[t][c] : sc[0], v, acc[f][t][c]); \
+            } \
+          } \
+        } \
+       } /* active */ \
+        issue(NXT, (M) + 1, f); /* (the last span re-reads a span) */ \
+      } \
+    } \
+    ring_barrier();  /* every wavefront is done with CUR before it is refilled */ \
+ \
+  }
+#pragma unroll
+  for (int part = 0; part < 4; ++part) issue(ring0, 0, part);
+  int m = 0;
+  for (; m + 2 <= nsp; m += 2) {
+    G4_SPAN(ring0, ring1, m)
+    G4_SPAN(ring1, ring0, m + 1)
+  }
+  if (m < nsp) G4_SPAN(ring0, ring1, m)
+#undef G4_SPAN
+  MOE_WAIT_VM(0);
+
+  if constexpr (DOWN) {
+    if (!active) return;
+    // lane (i, g) holds tile rows 16 t + 4 g + c of output column c0 + 16 f + i
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int col = c0 + 16 * f + i;
+      if (col >= N) continue;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 16 * t + 4 * g + c;
+          if (j < nr) G.out[(size_t)(r0 + j) * d + col] = acc[f][t][c];
+        }
+    }
+  } else {
+    // h = act(gate) * up for tile rows 16 t + 4 g + c, h column c0 + 16 fq + i
+    // (fq = 0, 1; gate in fragments 0, 1, up in 2, 3), encoded as two digits per
+    // row and 128-column span (the span's four wavefronts meet in red_max); the
+    // digits go through LDS (the ring, free now) so that rows are stored in
+    // 16-byte pieces, in the int4 digit order the down kernel reads
+    float h[2][4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float sig[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int tj = tok_sm[16 * t + 4 * g + c];
+        sig[c] = xs[tj >= 0 ? tj : tok_sm[0]] * (1.0f / 256.0f);
+      }
+      float mx[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        mx[c] = 0.0f;
+#pragma unroll
+        for (int fq = 0; fq < 2; ++fq) {
+          const bool ok = active && c0 + 16 * fq + i < N;
+          const float gt = acc[fq][t][c] * sig[c], up = acc[2 + fq][t][c] * sig[c];
+          h[fq][t][c] = ok ? act_f(G.act, gt) * up : 0.0f;
+          mx[c] = fmaxf(mx[c], fabsf(h[fq][t][c]));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], o, kWave));
+      }
+      if (i == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red_max[wave][16 * t + 4 * g + c] = mx[c];
+      }
+    }
+    __syncthreads();
+    // staging [row][digit][256 bytes] in ring0 (32 KB of its 56 / 50 KB)
+    int8_t* stg = ring0;
+    const int sp = wave >> 2;  // this wavefront's 128-column span within the 256
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 16 * t + 4 * g + c;
+        const float m = fmaxf(fmaxf(red_max[4 * sp][j], red_max[4 * sp + 1][j]),
+                              fmaxf(red_max[4 * sp + 2][j], red_max[4 * sp + 3][j]));
+        const int p = digit_exponent(m);
+#pragma unroll
+        for (int fq = 0; fq < 2; ++fq) {
+          int d0, d1;
+          two_digits(h[fq][t][c], p, d0, d1);
+          const int lc = 32 * wave + 16 * fq + i;  // column within the 256
+          const int pos = 128 * (lc >> 7) + int4_digit_pos(lc & 127);
+          stg[j * 512 + pos] = (int8_t)d0;
+          stg[j * 512 + 256 + pos] = (int8_t)d1;
+        }
+        if ((wave & 3) == 0 && i == 0 && j < nr && cb + 128 * sp < N)
+          G.hs[(size_t)(r0 + j) * (I / 128) + (cb >> 7) + sp] = m > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+      }
+    __syncthreads();
+    const int valid = min(256, N - cb);  // bytes per digit row inside the matrix
+    for (int q = threadIdx.x; q < k4Rows * 2 * 16; q += blockDim.x) {
+      const int j = q >> 5, dg = (q >> 4) & 1, ch = q & 15;
+      if (j >= nr || 16 * ch >= valid) continue;
+      *reinterpret_cast<v4i*>(G.hq + (size_t)(r0 + j) * 2 * I + dg * I + cb + 16 * ch) =
+          *reinterpret_cast<const v4i*>(stg + j * 512 + dg * 256 + 16 * ch);
+    }
+  }
+}
+
 }  // namespace
 
 void set_device_info(int cu_count) { g_cu_count = cu_count > 0 ? cu_count : 256; }
@@ -1734,6 +2061,31 @@ hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const flo
   return hipGetLastError();
 }
 
+// int4 grouped GEMM pair (gemm4_kernel): gate/up, then down.
+template <int FMT>
+hipError_t launch_gemm4_pair(Group a, Group b, int d, const int8_t* xq, const float* xs,
+                             hipStream_t s) {
+  auto tiles_of = [](const Group& G) {
+    if (G.R <= 0) return 0;
+    return G.offsets ? max_tiles(G.R, G.E, k4Rows) : (G.R + k4Rows - 1) / k4Rows;
+  };
+  a.tiles = tiles_of(a);
+  b.tiles = tiles_of(b);
+  const int imax = a.inter > b.inter ? a.inter : b.inter;
+  const int tiles = a.tiles + b.tiles;
+  {
+    TimedLaunch tl(K_FFN_I4_GATE_UP_GEMM, s);
+    hipLaunchKernelGGL((gemm4_kernel<FMT, false>), dim3((imax + k4Cols / 2 - 1) / (k4Cols / 2),
+                       tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  TimedLaunch tl(K_FFN_I4_DOWN_GEMM, s);
+  hipLaunchKernelGGL((gemm4_kernel<FMT, true>), dim3((d + k4Cols - 1) / k4Cols, tiles),
+                     dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
                             const FfnWs& ws, bool x_encoded, hipStream_t s) {
   hipError_t err = hipSuccess;
@@ -1741,6 +2093,23 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
     // int4 kernels read the digits in their permuted order (encode8)
     err = launch_encode_rows(x, T, d, ws.xq, ws.xs, sets[0].fmt != 1, ws.cnt, s);
     if (err != hipSuccess) return err;
+  }
+  // int4 (tiled codes) with many rows per expert: the int4 grouped GEMM
+  const int imax4 = nsets > 1 && sets[1].inter > sets[0].inter ? sets[1].inter : sets[0].inter;
+  if (sets[0].fmt != 1 && sets[0].layout == 1 && sets[0].pairs_idx == nullptr &&
+      sets[0].R >= 16LL * sets[0].E && imax4 <= 128 * k4MaxSpans) {
+    Group grp[2] = {};
+    for (int q = 0; q < nsets; ++q) {
+      const FfnSet& f = sets[q];
+      Group& G = grp[q];
+      G.E = f.E; G.inter = f.inter; G.R = f.R;
+      G.wgu = f.wgu; G.sgu = f.sgu; G.wdn = f.wdn; G.sdn = f.sdn;
+      G.row_token = f.row_token; G.offsets = f.offsets;
+      G.hq = f.hq; G.hs = f.hs; G.out = f.out; G.act = f.act;
+    }
+    if (nsets < 2) grp[1].inter = grp[0].inter;
+    return sets[0].fmt == 2 ? launch_gemm4_pair<2>(grp[0], grp[1], d, ws.xq, ws.xs, s)
+                            : launch_gemm4_pair<3>(grp[0], grp[1], d, ws.xq, ws.xs, s);
   }
   // int8 with many rows per expert: grouped GEMM
   if (sets[0].fmt == 1 && sets[0].pairs_idx == nullptr && sets[0].R >= 16LL * sets[0].E) {

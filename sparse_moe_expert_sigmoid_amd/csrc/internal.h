@@ -42,7 +42,8 @@ enum KernelId {
   K_ROUTER_LOGITS, K_ROUTER_TOPK, K_PERMUTE, K_FILL, K_ENCODE_ROWS,
   K_FFN_I8_GATE_UP, K_FFN_I8_DOWN, K_FFN_I4_GATE_UP, K_FFN_I4_DOWN,
   K_FFN_F32_GATE_UP, K_FFN_F32_DOWN, K_COMBINE, K_ROUTER_TAIL, K_FFN_I8_GATE_UP_GEMM,
-  K_FFN_I8_DOWN_GEMM, K_QUANT_I8, K_QUANT_I4, K_COUNT
+  K_FFN_I8_DOWN_GEMM, K_QUANT_I8, K_QUANT_I4, K_FFN_I4_GATE_UP_GEMM, K_FFN_I4_DOWN_GEMM,
+  K_COUNT
 };
 extern const char* const kKernelNames[K_COUNT];
 
