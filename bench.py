@@ -20,8 +20,11 @@ several processes, the median): every workload runs in --procs separate
 processes (default 3); in each, W warm-up steps, then exactly K steps, each
 bracketed by HIP events on the launch stream between two synchronisations;
 a process reports the median step, the line reports the median of the
-process medians and p10/p90 over all timed steps.  Decode steps (T <= 16)
-are replayed from HIP graphs, one per weight copy.
+process medians and p10/p90 over all timed steps.  Single layers launch
+eagerly (the launches run ahead of the GPU); their decode steps are also
+replayed from HIP graphs, one per weight copy, and reported beside
+(hip_graph_ms_per_step; slower for one layer).  The stack's decode step is
+replayed as one HIP graph of all its layers.
 
 Weight copies: a single-layer step alternates between identical copies of
 the expert weights in separate HBM allocations, as many as make the bytes a
@@ -275,16 +278,18 @@ def measure_layer(name: str, args) -> dict:
             else:
                 L.forward(xs[c], stream=stream)
 
+    # the timed steps launch eagerly: for a single layer the launches run ahead of
+    # the GPU, and replaying HIP graphs measured slower; decode steps are also
+    # timed as graph replays, reported beside
+    per, total = timed_steps(run_eager, steps, warmup, stream)
+    graph_ms = None
     use_graph = decode and chunks == 1 and not args.no_graph
     if use_graph:
         graphs = [capture(lambda L=L: L.forward_fused(xs[0]) if args.path == "fused"
                           else L.forward(xs[0]), stream) for L in layers]
-
-        def step(i):
-            graphs[i % copies].replay()
-    else:
-        step = run_eager
-    per, total = timed_steps(step, steps, warmup, stream)
+        gper, _ = timed_steps(lambda i: graphs[i % copies].replay(), steps, warmup, stream)
+        graph_ms = float(np.median(gper))
+        del graphs
 
     act_bytes = spec.T * d * 4 * 2                      # x read once, y written once
     router_bytes = (E * d + (E if inputs.bias is not None else 0)) * 4 * chunks
@@ -317,17 +322,15 @@ def measure_layer(name: str, args) -> dict:
               "inter": I, "router": spec.router, "expert_format": spec.fmt,
               "shared_expert": spec.shared, "weight_copies": copies,
               "touched_bytes_per_step": int(touched_bytes), "activation": args.act,
-              "hip_graph": use_graph,
+              "timed_as": "eager launches (one moe_forward call per step)",
               "entry_point": "moe_forward" if args.path == "fused" else
               "moe_route+moe_permute+moe_expert_ffn x2+moe_combine",
               "parallelism": "single GPU"}
     out = {"workload": name, "T": spec.T, "steps": steps, "warmup": warmup, "step_ms": per,
            "total_ms": total, "step_bytes": int(step_bytes), "step_flops": step_flops,
            "roofline": roofline, "kernels": kernels, "config": config,
-           "dtype": dtype_of(spec.fmt),
+           "dtype": dtype_of(spec.fmt), "graph_ms": graph_ms,
            "data": "synthetic (seeded generator; random weights of the stated shapes)"}
-    if use_graph:
-        del graphs
     return out
 
 
@@ -507,6 +510,8 @@ def summarize(runs: list) -> dict:
            "mean_ms_per_step": round(float(np.median([r["total_ms"] / r["steps"]
                                                       for r in runs])), 5),
            "steps": r0["steps"], "warmup": r0["warmup"], "processes": len(runs)}
+    if r0.get("graph_ms"):
+        out["hip_graph_ms_per_step"] = round(float(np.median([r["graph_ms"] for r in runs])), 5)
     if r0["T"]:
         out["tokens_per_s"] = round(r0["T"] / s, 1)
     else:
@@ -759,6 +764,7 @@ def main():
         "timing": {"processes": p["processes"], "ms_per_process": p["ms_per_process"],
                    "ms_p10": p["ms_p10"], "ms_p90": p["ms_p90"],
                    "mean_ms_per_step": p["mean_ms_per_step"],
+                   "hip_graph_ms_per_step": p.get("hip_graph_ms_per_step"),
                    "protocol": "median over processes of each process's median step; "
                                "p10/p90 over every timed step; per-step HIP events on the "
                                "launch stream"},
