@@ -582,15 +582,23 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
               }
             }
           } else {
+            // one scale for the span: blocks in pairs through the 16x16x64 MFMA
+            // (the 16x16x32 form takes as long on this chip for half the work)
             v4i pa0 = zero, pa1 = zero, pb0 = zero, pb1 = zero;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const long qa = unpack8_int4_x16((unsigned)wa4[u][q]);
-              const long qb = unpack8_int4_x16((unsigned)wb4[u][q]);
-              pa0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[q], qa, pa0, 0, 0, 0);
-              pa1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[q], qa, pa1, 0, 0, 0);
-              pb0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[q], qb, pb0, 0, 0, 0);
-              pb1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[q], qb, pb1, 0, 0, 0);
+            for (int q = 0; q < 4; q += 2) {
+              const long qa0 = unpack8_int4_x16((unsigned)wa4[u][q]);
+              const long qa1 = unpack8_int4_x16((unsigned)wa4[u][q + 1]);
+              const long qb0 = unpack8_int4_x16((unsigned)wb4[u][q]);
+              const long qb1 = unpack8_int4_x16((unsigned)wb4[u][q + 1]);
+              const v4i qa = {(int)qa0, (int)(qa0 >> 32), (int)qa1, (int)(qa1 >> 32)};
+              const v4i qb = {(int)qb0, (int)(qb0 >> 32), (int)qb1, (int)(qb1 >> 32)};
+              const v4i xa = {(int)x0[q], (int)(x0[q] >> 32), (int)x0[q + 1], (int)(x0[q + 1] >> 32)};
+              const v4i xc = {(int)x1[q], (int)(x1[q] >> 32), (int)x1[q + 1], (int)(x1[q + 1] >> 32)};
+              pa0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, qa, pa0, 0, 0, 0);
+              pa1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xc, qa, pa1, 0, 0, 0);
+              pb0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, qb, pb0, 0, 0, 0);
+              pb1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xc, qb, pb1, 0, 0, 0);
             }
             const float t1 = fmaxf(s1[u].x, kScaleFloor) * kInv16;
             const float t2 = fmaxf(s2[u].x, kScaleFloor) * kInv16;
@@ -831,12 +839,19 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
           }
         }
       } else {
-        v4i p0[2] = {zero, zero}, p1[2] = {zero, zero};
+        // blocks 2h, 2h+1 (one h scale per 64) through one 16x16x64 MFMA per digit
+        v4i p0[2], p1[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const long wq = unpack8_int4_x16((unsigned)w4[q]);
-          p0[q >> 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x0[q], p0[q >> 1], 0, 0, 0);
-          p1[q >> 1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(wq, x1[q], p1[q >> 1], 0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          const long w0 = unpack8_int4_x16((unsigned)w4[2 * hh]);
+          const long w1 = unpack8_int4_x16((unsigned)w4[2 * hh + 1]);
+          const v4i wv = {(int)w0, (int)(w0 >> 32), (int)w1, (int)(w1 >> 32)};
+          const v4i xa = {(int)x0[2 * hh], (int)(x0[2 * hh] >> 32), (int)x0[2 * hh + 1],
+                          (int)(x0[2 * hh + 1] >> 32)};
+          const v4i xc = {(int)x1[2 * hh], (int)(x1[2 * hh] >> 32), (int)x1[2 * hh + 1],
+                          (int)(x1[2 * hh + 1] >> 32)};
+          p0[hh] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, xa, zero, 0, 0, 0);
+          p1[hh] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, xc, zero, 0, 0, 0);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1865,11 +1880,19 @@ _Pragma("unroll") \
               acc[f][t][c] = DOWN ? fmaf(hs4[t][c], sp[c], acc[f][t][c]) : acc[f][t][c] + sp[c]; \
  \
           } else { \
+            /* one scale for the span: blocks 0, 1 and 2, 3 go through the 16x16x64 */ \
+            /* MFMA in pairs (a lane's K values of two blocks side by side in A and */ \
+            /* B; the 16x16x32 form takes as long on this chip for half the work) */ \
             v4i p0 = zero, p1 = zero; \
 _Pragma("unroll") \
-            for (int q = 0; q < 4; ++q) { \
-              p0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x0[t % XT][q], wq[q], p0, 0, 0, 0); \
-              p1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(x1[t % XT][q], wq[q], p1, 0, 0, 0); \
+            for (int q = 0; q < 4; q += 2) { \
+              const v4i wv = {(int)wq[q], (int)(wq[q] >> 32), (int)wq[q + 1], (int)(wq[q + 1] >> 32)}; \
+              const long* xa = x0[t % XT]; \
+              const long* xb = x1[t % XT]; \
+              const v4i av = {(int)xa[q], (int)(xa[q] >> 32), (int)xa[q + 1], (int)(xa[q + 1] >> 32)}; \
+              const v4i bv = {(int)xb[q], (int)(xb[q] >> 32), (int)xb[q + 1], (int)(xb[q + 1] >> 32)}; \
+              p0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, wv, p0, 0, 0, 0); \
+              p1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bv, wv, p1, 0, 0, 0); \
             } \
 _Pragma("unroll") \
             for (int c = 0; c < 4; ++c) {  /* |p0| < 2^22: each digit sum exact in fp32 */ \
