@@ -20,11 +20,12 @@ several processes, the median): every workload runs in --procs separate
 processes (default 3); in each, W warm-up steps, then exactly K steps, each
 bracketed by HIP events on the launch stream between two synchronisations;
 a process reports the median step, the line reports the median of the
-process medians and p10/p90 over all timed steps.  Single layers launch
-eagerly (the launches run ahead of the GPU); their decode steps are also
-replayed from HIP graphs, one per weight copy, and reported beside
-(hip_graph_ms_per_step; slower for one layer).  The stack's decode step is
-replayed as one HIP graph of all its layers.
+process medians and p10/p90 over all timed steps.  Single layers are timed
+with eager launches and, at decode sizes, also as HIP-graph replays (one
+graph per weight copy); the line takes the faster and names it (timed_as):
+one-token steps are bound by the host's launch rate when launched eagerly,
+longer ones run ahead of the GPU.  The stack's decode step is replayed as
+one HIP graph of all its layers.
 
 Weight copies: a single-layer step alternates between identical copies of
 the expert weights in separate HBM allocations, as many as make the bytes a
@@ -33,7 +34,16 @@ experts in the 256 MB last-level cache from the steps before.  The stack is
 cold by size.
 
 Per-kernel durations for the rooflines come from a separate pass with HIP
-events around every launch (moe_timing), after the timed region.
+events around every launch (moe_timing), after the timed region; the event
+records inflate them a little (kernels_note gives their sum per step beside
+the timed step).
+
+Attainable peaks: after the workloads, a fresh process runs the library's
+probes (moe_probe_read, moe_probe_mfma): a non-temporal streaming read of
+each HBM-bound roofline's bytes per launch, from regions the previous
+launches did not touch, and int8 MFMA loops of both shapes.  Each roofline
+then carries `attainable` (the probe's figure and achieved / attainable)
+beside the published peak it is priced against.
 cpu_baseline: the CPU oracle, as it stands, on a bounded sample of the
 primary workload, all host threads and one thread.
 """
@@ -278,18 +288,22 @@ def measure_layer(name: str, args) -> dict:
             else:
                 L.forward(xs[c], stream=stream)
 
-    # the timed steps launch eagerly: for a single layer the launches run ahead of
-    # the GPU, and replaying HIP graphs measured slower; decode steps are also
-    # timed as graph replays, reported beside
+    # Steps are timed with eager launches and, for decode (T <= 16), also as
+    # HIP-graph replays (one graph per weight copy).  The line reports the faster
+    # of the two and names it: a short step (one token) is bound by the host's
+    # launch rate when launched eagerly, while for longer steps the eager
+    # launches run ahead of the GPU and the graph's inter-node gaps cost more.
     per, total = timed_steps(run_eager, steps, warmup, stream)
-    graph_ms = None
+    eager_ms, graph_ms, timed_as = float(np.median(per)), None, "eager launches"
     use_graph = decode and chunks == 1 and not args.no_graph
     if use_graph:
         graphs = [capture(lambda L=L: L.forward_fused(xs[0]) if args.path == "fused"
                           else L.forward(xs[0]), stream) for L in layers]
-        gper, _ = timed_steps(lambda i: graphs[i % copies].replay(), steps, warmup, stream)
+        gper, gtotal = timed_steps(lambda i: graphs[i % copies].replay(), steps, warmup, stream)
         graph_ms = float(np.median(gper))
         del graphs
+        if graph_ms < eager_ms:
+            per, total, timed_as = gper, gtotal, "HIP-graph replays"
 
     act_bytes = spec.T * d * 4 * 2                      # x read once, y written once
     router_bytes = (E * d + (E if inputs.bias is not None else 0)) * 4 * chunks
@@ -322,14 +336,14 @@ def measure_layer(name: str, args) -> dict:
               "inter": I, "router": spec.router, "expert_format": spec.fmt,
               "shared_expert": spec.shared, "weight_copies": copies,
               "touched_bytes_per_step": int(touched_bytes), "activation": args.act,
-              "timed_as": "eager launches (one moe_forward call per step)",
+              "timed_as": timed_as,
               "entry_point": "moe_forward" if args.path == "fused" else
               "moe_route+moe_permute+moe_expert_ffn x2+moe_combine",
               "parallelism": "single GPU"}
     out = {"workload": name, "T": spec.T, "steps": steps, "warmup": warmup, "step_ms": per,
            "total_ms": total, "step_bytes": int(step_bytes), "step_flops": step_flops,
            "roofline": roofline, "kernels": kernels, "config": config,
-           "dtype": dtype_of(spec.fmt), "graph_ms": graph_ms,
+           "dtype": dtype_of(spec.fmt), "graph_ms": graph_ms, "eager_ms": eager_ms,
            "data": "synthetic (seeded generator; random weights of the stated shapes)"}
     return out
 
@@ -476,8 +490,80 @@ def measure_quant(name: str, args) -> dict:
             "data": "synthetic (seeded N(0, 0.02^2) weights rounded to bf16)"}
 
 
+PROBE_BUFFER_BYTES = 4 << 30       # the read probe's source, far above the 256 MB MALL
+PROBE_BLOCKS_PER_CU = (4, 8, 16)   # read-probe grids tried; the fastest counts
+PROBE_REPS = 20
+
+
+def measure_peaks(sizes) -> dict:
+    """Attainable ceilings on this GPU: a plain streaming read of each size in
+    `sizes` (bytes; each launch reads a region the previous launches did not
+    touch, so no launch finds its bytes in the MALL), and int8 MFMA loops of
+    both shapes.  Each figure is the median of PROBE_REPS event-timed launches;
+    the read takes the fastest of a few grid sizes."""
+    import torch
+    from sparse_moe_expert_sigmoid_amd import Context
+    from sparse_moe_expert_sigmoid_amd.binding import (MOE_PROBE_MFMA_16X16X64,
+                                                       MOE_PROBE_MFMA_32X32X32)
+    ctx = Context(0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    buf = torch.empty(PROBE_BUFFER_BYTES, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+
+    def timed(launch, reps=PROBE_REPS):
+        for i in range(3):
+            launch(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record(stream)
+            launch(3 + i)
+            ev[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)]))
+
+    reads = []
+    for size in sorted(set(int(x) for x in sizes)):
+        nbytes = max(16, min(size, PROBE_BUFFER_BYTES) // 16 * 16)
+        slots = max(1, PROBE_BUFFER_BYTES // nbytes)
+        best = None
+        for bpc in PROBE_BLOCKS_PER_CU:
+            def launch(i, bpc=bpc):
+                off = (i % slots) * nbytes
+                ctx.moe_probe_read(buf[off:off + nbytes], nbytes, sink, blocks=bpc * cus,
+                                   stream=stream)
+            ms = timed(launch)
+            if best is None or ms < best[0]:
+                best = (ms, bpc)
+        reads.append({"bytes": nbytes, "us": round(best[0] * 1e3, 2),
+                      "gbps": round(nbytes / (best[0] / 1e3) / 1e9, 1),
+                      "blocks_per_cu": best[1]})
+    del buf
+    mfma = {}
+    for shape, label, ops in ((MOE_PROBE_MFMA_16X16X64, "i8_16x16x64", 16 * 16 * 64 * 2),
+                              (MOE_PROBE_MFMA_32X32X32, "i8_32x32x32", 32 * 32 * 32 * 2)):
+        iters, blocks = 512, 8 * cus
+        ms = timed(lambda i: ctx.moe_probe_mfma(shape, iters, sink, blocks=blocks,
+                                                stream=stream))
+        total = blocks * 4 * iters * 32 * ops
+        mfma[label] = {"tops": round(total / (ms / 1e3) / 1e12, 1), "us": round(ms * 1e3, 1),
+                       "ops_per_launch": total}
+    return {"workload": "peaks", "read": reads, "mfma": mfma,
+            "probe": "moe_probe_read / moe_probe_mfma (streaming read, each wavefront "
+                     "8 KB contiguous per step with 8 loads of 16 B in flight per lane; "
+                     "MFMA loop of 4 independent accumulator chains per wavefront, "
+                     "8 workgroups of 256 threads per CU); median of %d event-timed "
+                     "launches" % PROBE_REPS}
+
+
 def child(args):
     import torch
+    if args.child == "peaks":
+        sizes = [int(x) for x in (args.probe_sizes or "").split(",") if x]
+        print("@@RESULT " + json.dumps(measure_peaks(sizes + [2 << 30])), flush=True)
+        return
     for name in args.child.split(","):
         if name in STACK_WORKLOADS:
             r = measure_stack(name, args)
@@ -512,6 +598,7 @@ def summarize(runs: list) -> dict:
            "steps": r0["steps"], "warmup": r0["warmup"], "processes": len(runs)}
     if r0.get("graph_ms"):
         out["hip_graph_ms_per_step"] = round(float(np.median([r["graph_ms"] for r in runs])), 5)
+        out["eager_ms_per_step"] = round(float(np.median([r["eager_ms"] for r in runs])), 5)
     if r0["T"]:
         out["tokens_per_s"] = round(r0["T"] / s, 1)
     else:
@@ -529,6 +616,13 @@ def summarize(runs: list) -> dict:
         kernels[kname] = {"launches": r0["kernels"][kname]["launches"],
                           "avg_us": round(float(np.median(avg)), 2)}
     out["kernels"] = kernels
+    if kernels:
+        ksum = sum(v["launches"] * v["avg_us"] for v in kernels.values()) / r0["steps"] / 1e3
+        out["kernels_note"] = (
+            "avg_us per kernel from HIP events around every launch, in a pass of its own: "
+            "each pair of event records adds GPU time between launches, so these sum to "
+            f"{ksum:.4f} ms per step against the {ms:.4f} ms timed step (event-inflated; "
+            "the rocprofv3 kernel-trace figures under profiles/ carry no event overhead)")
     rl = r0["roofline"]
     if rl and rl["kernel"] in kernels:
         avg_s = kernels[rl["kernel"]]["avg_us"] / 1e6
@@ -659,6 +753,46 @@ def cpu_baseline_stack(name: str, budget_s: float) -> dict:
                       f"to {st.layers} layers", **info}
 
 
+def attach_peaks(summaries: dict) -> None:
+    """Runs the peak probes in a fresh process and adds to each roofline the
+    attainable ceiling beside the published one: for an HBM-bound kernel the
+    probe's streaming read of that kernel's algorithmic bytes per launch, for a
+    matrix-core-bound one the 16x16x64 int8 MFMA loop."""
+    sizes = sorted({int(sm["roofline"]["bytes_per_launch"]) for sm in summaries.values()
+                    if sm.get("roofline") and sm["roofline"].get("bytes_per_launch")})
+    log("[bench] attainable-peak probes")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--child", "peaks",
+                        "--probe-sizes", ",".join(str(x) for x in sizes)],
+                       stdout=subprocess.PIPE, text=True)
+    peaks = None
+    for line in r.stdout.splitlines():
+        if line.startswith("@@RESULT "):
+            peaks = json.loads(line[len("@@RESULT "):])
+        elif line.strip():
+            log(line)
+    if r.returncode != 0 or peaks is None:
+        log(f"[bench] peak probes failed with status {r.returncode}; stopping")
+        sys.exit(r.returncode if r.returncode > 0 else 1)
+    by_size = {x["bytes"]: x for x in peaks["read"]}
+    for sm in summaries.values():
+        roof = sm.get("roofline")
+        if not roof:
+            continue
+        if roof["bound"] == "hbm":
+            rd = by_size.get(int(roof["bytes_per_launch"]) // 16 * 16)
+            if rd:
+                roof["attainable"] = {"value": rd["gbps"], "unit": "GB/s",
+                                      "frac": round(roof["achieved"] / rd["gbps"], 4),
+                                      "probe": f"streaming read of {rd['bytes']} B, "
+                                               f"{rd['us']} us"}
+        else:
+            m = peaks["mfma"]["i8_16x16x64"]
+            roof["attainable"] = {"value": m["tops"], "unit": "TFLOP/s",
+                                  "frac": round(roof["achieved"] / m["tops"], 4),
+                                  "probe": "int8 16x16x64 MFMA loop"}
+    summaries["_peaks"] = peaks
+
+
 def run_children(names, args) -> dict:
     """Runs the workloads in args.procs fresh processes, one after the other;
     returns {name: [result per process]}.  Stops at the first failure."""
@@ -715,7 +849,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the attainable-peak probes (streaming read, MFMA loop)")
     ap.add_argument("--child", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--probe-sizes", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -736,6 +873,8 @@ def main():
     results = run_children(names, args)
     summaries = {n: summarize(results[n]) for n in names}
     p = summaries[primary]
+    if not args.no_peaks:
+        attach_peaks(summaries)
 
     cpu = None
     if not args.no_cpu:
@@ -765,6 +904,7 @@ def main():
                    "ms_p10": p["ms_p10"], "ms_p90": p["ms_p90"],
                    "mean_ms_per_step": p["mean_ms_per_step"],
                    "hip_graph_ms_per_step": p.get("hip_graph_ms_per_step"),
+                   "eager_ms_per_step": p.get("eager_ms_per_step"),
                    "protocol": "median over processes of each process's median step; "
                                "p10/p90 over every timed step; per-step HIP events on the "
                                "launch stream"},
@@ -776,6 +916,8 @@ def main():
         "roofline": p["roofline"],
         "cpu_baseline": cpu,
         "kernels": p["kernels"],
+        "kernels_note": p.get("kernels_note"),
+        "attainable_peaks": summaries.get("_peaks"),
         "workloads": {n: summaries[n] for n in names[1:]},
     }
     print(json.dumps(out), flush=True)

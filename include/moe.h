@@ -333,6 +333,30 @@ moe_status moe_forward_noalloc(moe_ctx* ctx, const moe_layer* layer, int act, co
                                int T, const float* residual, float* y, int32_t* topk_idx,
                                float* topk_w, void* stream);
 
+/* Attainable-peak probes, a measurement aid for benchmarks: they compute
+ * nothing of the layer.  A caller times them (events on `stream`) to state
+ * the ceilings the chip reaches in practice beside its published peaks.
+ * moe_probe_read: one launch of `blocks` workgroups of 256 threads (0: 8 per
+ * compute unit) that reads `bytes` bytes of device memory from buf (16-byte
+ * aligned; bytes a multiple of 16, at least 16) in 16-byte loads, 8 in flight
+ * per lane, and discards them.
+ * moe_probe_mfma: one launch of `blocks` workgroups of 256 threads (0: 8 per
+ * compute unit) in which every wavefront runs `iters` rounds of 32 int8
+ * MFMAs (four independent accumulator chains), shape MOE_PROBE_MFMA_16X16X64
+ * (32768 operations each) or MOE_PROBE_MFMA_32X32X32 (65536); a launch
+ * performs blocks * 4 * iters * 32 * (operations per MFMA) int8 operations.
+ * Both may write up to 16 bytes of sink (device memory, 16-byte aligned).
+ * Errors: MOE_E_INVALID for NULL or misaligned pointers, sizes out of range
+ * (bytes < 16 or not a multiple of 16, iters < 1, blocks < 0 or > 2^20, an
+ * unknown shape), MOE_E_DEVICE if the launch fails; nothing is launched on
+ * an error. */
+#define MOE_PROBE_MFMA_16X16X64 0
+#define MOE_PROBE_MFMA_32X32X32 1
+moe_status moe_probe_read(moe_ctx* ctx, const void* buf, size_t bytes, int blocks, void* sink,
+                          void* stream);
+moe_status moe_probe_mfma(moe_ctx* ctx, int shape, int iters, int blocks, void* sink,
+                          void* stream);
+
 /* Kernel timing, a measurement aid for benchmarks; off by default.
  * moe_timing(ctx, capacity > 0) creates 2*capacity HIP events (host-side
  * allocation, outside any call path) and from then on brackets every kernel

@@ -25,6 +25,7 @@ MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 ACT = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = 0, 1
 MOE_IN_F32, MOE_IN_BF16 = 0, 1
+MOE_PROBE_MFMA_16X16X64, MOE_PROBE_MFMA_32X32X32 = 0, 1
 
 ROUTER = {"sigmoid_bias": MOE_ROUTER_SIGMOID_BIAS, "softmax": MOE_ROUTER_SOFTMAX}
 FMT = {"fp32": MOE_W_FP32, "int8_row": MOE_W_INT8_ROW, "int4_b32": MOE_W_INT4_B32,
@@ -34,7 +35,7 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
            "moe_tile_weights", "moe_route_masked", "moe_expert_counts", "moe_quantize",
-           "moe_forward_noalloc")
+           "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma")
 MOE_NOALLOC_SCRATCH_BYTES = 40 * 1024 * 1024
 
 
@@ -102,13 +103,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_noalloc.argtypes = [vp, ctypes.POINTER(moe_layer), ci, vp, ci, vp, vp, vp, vp,
                                         vp]
     lib.moe_tile_weights.argtypes = [vp, ctypes.POINTER(moe_weights), vp, vp, vp]
+    lib.moe_probe_read.argtypes = [vp, vp, sz, ci, vp, vp]
+    lib.moe_probe_mfma.argtypes = [vp, ci, ci, ci, vp, vp]
     lib.moe_timing.argtypes = [vp, ci]
     lib.moe_timing_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), ci,
                                     ctypes.POINTER(ci)]
     for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
               "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
               "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts",
-              "moe_quantize", "moe_forward_noalloc"):
+              "moe_quantize", "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -228,6 +231,14 @@ class Context:
         w = src.struct()
         self._check(self.lib.moe_tile_weights(self.handle, ctypes.byref(w), _p(dst_gate_up),
                                               _p(dst_down), _stream(stream)))
+
+    def moe_probe_read(self, buf, nbytes: int, sink, blocks: int = 0, stream=None):
+        self._check(self.lib.moe_probe_read(self.handle, _p(buf), nbytes, blocks, _p(sink),
+                                            _stream(stream)))
+
+    def moe_probe_mfma(self, shape: int, iters: int, sink, blocks: int = 0, stream=None):
+        self._check(self.lib.moe_probe_mfma(self.handle, shape, iters, blocks, _p(sink),
+                                            _stream(stream)))
 
     def moe_timing(self, capacity: int):
         self._check(self.lib.moe_timing(self.handle, capacity))

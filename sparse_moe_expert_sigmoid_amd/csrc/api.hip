@@ -528,4 +528,30 @@ moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row
   return device_result(ctx, e, "moe_combine");
 }
 
+moe_status moe_probe_read(moe_ctx* ctx, const void* buf, size_t bytes, int blocks, void* sink,
+                          void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  moe_status st = moe::check_probe_read(ctx->err, buf, bytes, blocks, sink);
+  if (st != MOE_OK) return st;
+  DeviceGuard g(ctx->device);
+  if (!g.ok)
+    return fail(ctx, MOE_E_DEVICE, "moe_probe_read: hipSetDevice(%d) failed", ctx->device);
+  const int nb = blocks > 0 ? blocks : 8 * ctx->cu_count;
+  return device_result(ctx, moe::launch_probe_read(buf, bytes, nb, sink, (hipStream_t)stream),
+                       "moe_probe_read");
+}
+
+moe_status moe_probe_mfma(moe_ctx* ctx, int shape, int iters, int blocks, void* sink,
+                          void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  moe_status st = moe::check_probe_mfma(ctx->err, shape, iters, blocks, sink);
+  if (st != MOE_OK) return st;
+  DeviceGuard g(ctx->device);
+  if (!g.ok)
+    return fail(ctx, MOE_E_DEVICE, "moe_probe_mfma: hipSetDevice(%d) failed", ctx->device);
+  const int nb = blocks > 0 ? blocks : 8 * ctx->cu_count;
+  return device_result(ctx, moe::launch_probe_mfma(shape, iters, nb, sink, (hipStream_t)stream),
+                       "moe_probe_mfma");
+}
+
 }  // extern "C"

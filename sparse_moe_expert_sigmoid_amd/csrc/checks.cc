@@ -317,4 +317,32 @@ moe_status check_combine(char* err, const float* rows, const int32_t* token_row,
   return MOE_OK;
 }
 
+moe_status check_probe_read(char* err, const void* buf, size_t bytes, int blocks,
+                            const void* sink) {
+  if (bytes < 16 || bytes % 16 != 0)
+    return errorf(err, MOE_E_INVALID, "moe_probe_read: bytes=%zu is not a positive multiple "
+                  "of 16", bytes);
+  if (blocks < 0 || blocks > kProbeMaxBlocks)
+    return errorf(err, MOE_E_INVALID, "moe_probe_read: blocks=%d outside [0, %d]", blocks,
+                  kProbeMaxBlocks);
+  if (!buf || !sink)
+    return errorf(err, MOE_E_INVALID, "moe_probe_read: %s is NULL", !buf ? "buf" : "sink");
+  if (!aligned16(buf) || !aligned16(sink))
+    return errorf(err, MOE_E_INVALID, "moe_probe_read: a pointer is not 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status check_probe_mfma(char* err, int shape, int iters, int blocks, const void* sink) {
+  if (shape != MOE_PROBE_MFMA_16X16X64 && shape != MOE_PROBE_MFMA_32X32X32)
+    return errorf(err, MOE_E_INVALID, "moe_probe_mfma: unknown shape %d", shape);
+  if (iters < 1) return errorf(err, MOE_E_INVALID, "moe_probe_mfma: iters=%d", iters);
+  if (blocks < 0 || blocks > kProbeMaxBlocks)
+    return errorf(err, MOE_E_INVALID, "moe_probe_mfma: blocks=%d outside [0, %d]", blocks,
+                  kProbeMaxBlocks);
+  if (!sink) return errorf(err, MOE_E_INVALID, "moe_probe_mfma: sink is NULL");
+  if (!aligned16(sink))
+    return errorf(err, MOE_E_INVALID, "moe_probe_mfma: sink is not 16-byte aligned");
+  return MOE_OK;
+}
+
 }  // namespace moe

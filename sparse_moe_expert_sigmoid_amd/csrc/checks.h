@@ -48,6 +48,10 @@ moe_status check_tile_weights(char* err, const moe_weights* src, const void* dst
 moe_status check_combine(char* err, const float* rows, const int32_t* token_row,
                          const float* topk_w, const float* shared, const float* residual, int T,
                          int k, int d, const float* y);
+moe_status check_probe_read(char* err, const void* buf, size_t bytes, int blocks,
+                            const void* sink);
+moe_status check_probe_mfma(char* err, int shape, int iters, int blocks, const void* sink);
+constexpr int kProbeMaxBlocks = 1 << 20;
 
 // Whether moe_forward at T tokens runs the small-batch path (the router
 // encodes x and the FFN kernels group the pairs themselves).

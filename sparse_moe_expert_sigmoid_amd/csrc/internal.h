@@ -95,6 +95,13 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
                             const FfnWs& ws, bool x_encoded, hipStream_t s);
 void set_device_info(int cu_count);
 int device_cu_count();
+
+// Attainable-peak probes (probe.hip): a streaming read of `bytes` (a multiple
+// of 16) and `iters` rounds of 32 int8 MFMAs per wavefront (shape 0: 16x16x64,
+// 1: 32x32x32), each over `blocks` workgroups of 256 threads; sink >= 16 bytes.
+hipError_t launch_probe_read(const void* buf, size_t bytes, int blocks, void* sink,
+                             hipStream_t s);
+hipError_t launch_probe_mfma(int shape, int iters, int blocks, void* sink, hipStream_t s);
 // Row-major codes [nrows][K] (int4: K/2 bytes per row) -> tiled layout.
 hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nrows, int K,
                                hipStream_t s);

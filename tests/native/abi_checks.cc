@@ -317,8 +317,31 @@ static void combine_tile_quant_cases() {
          MOE_E_UNSUPPORTED, "2^32");
 }
 
+static void probe_cases() {
+  const void* buf = dev<void>(81);
+  void* sink = dev<void>(82);
+  EXPECT(check_probe_read(g_err, buf, 1 << 20, 0, sink), MOE_OK, nullptr);
+  EXPECT(check_probe_read(g_err, buf, 1000, 0, sink), MOE_E_INVALID, "multiple of 16");
+  EXPECT(check_probe_read(g_err, buf, 0, 0, sink), MOE_E_INVALID, "bytes=0");
+  EXPECT(check_probe_read(g_err, buf, 1 << 20, -1, sink), MOE_E_INVALID, "blocks=-1");
+  EXPECT(check_probe_read(g_err, buf, 1 << 20, kProbeMaxBlocks + 1, sink), MOE_E_INVALID,
+         "blocks=");
+  EXPECT(check_probe_read(g_err, nullptr, 1 << 20, 0, sink), MOE_E_INVALID, "buf is NULL");
+  EXPECT(check_probe_read(g_err, misaligned<void>(83), 1 << 20, 0, sink), MOE_E_INVALID,
+         "aligned");
+  EXPECT(check_probe_mfma(g_err, MOE_PROBE_MFMA_16X16X64, 16, 0, sink), MOE_OK, nullptr);
+  EXPECT(check_probe_mfma(g_err, MOE_PROBE_MFMA_32X32X32, 16, 2048, sink), MOE_OK, nullptr);
+  EXPECT(check_probe_mfma(g_err, 2, 16, 0, sink), MOE_E_INVALID, "shape");
+  EXPECT(check_probe_mfma(g_err, MOE_PROBE_MFMA_16X16X64, 0, 0, sink), MOE_E_INVALID, "iters");
+  EXPECT(check_probe_mfma(g_err, MOE_PROBE_MFMA_16X16X64, 16, 0, nullptr), MOE_E_INVALID,
+         "sink is NULL");
+  EXPECT(check_probe_mfma(g_err, MOE_PROBE_MFMA_16X16X64, 16, 0, misaligned<void>(84)),
+         MOE_E_INVALID, "aligned");
+}
+
 int main() {
   route_cases();
+  probe_cases();
   permute_counts_cases();
   ffn_cases();
   forward_cases();
