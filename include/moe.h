@@ -235,6 +235,23 @@ moe_status moe_route_masked(moe_ctx* ctx, int router, const float* x, const floa
 moe_status moe_expert_counts(moe_ctx* ctx, const int32_t* topk_idx, int T, int k, int E,
                              unsigned long long* counts, void* stream);
 
+/* Expert restriction (Kimi-Linear-48B-A3B-Code-CMF listing, "How it was made",
+ * step 3): from the selection counts a calibration run recorded (moe_expert_counts),
+ * the smallest set of experts that carries the share `cover` of all selections.
+ * Experts are taken by descending count, equal counts by ascending id, until
+ * the running sum reaches cover * total (the comparison in double precision:
+ * (double) running >= cover * (double) total; none is needed when that product
+ * is 0); the set is then padded in the same order to min(k, E) experts so that
+ * a token can still select k.
+ *   counts  [E] uint64 device (E in [1, 1024]); cover in [0, 1]; k >= 1
+ *   keep    [E] int32 device out: the kept ids ascending in keep[0..n-1], -1 after
+ *   n_keep  [1] int32 device out: n
+ * One workgroup, asynchronous on `stream`.  Errors: MOE_E_INVALID for E, k
+ * or cover out of range and NULL or misaligned pointers (16-byte alignment);
+ * nothing is launched on an error. */
+moe_status moe_coverage_set(moe_ctx* ctx, const unsigned long long* counts, int E, double cover,
+                            int k, int32_t* keep, int32_t* n_keep, void* stream);
+
 /* Group the T*k (token, slot) pairs by expert (Qwen3 card, Conversion Notes:
  * only the routed experts are computed for each token).  Stable: within an
  * expert, rows follow (t, j) order.

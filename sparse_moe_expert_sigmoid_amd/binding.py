@@ -35,7 +35,7 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
            "moe_tile_weights", "moe_route_masked", "moe_expert_counts", "moe_quantize",
-           "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma")
+           "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma", "moe_coverage_set")
 MOE_NOALLOC_SCRATCH_BYTES = 40 * 1024 * 1024
 
 
@@ -104,6 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         vp]
     lib.moe_tile_weights.argtypes = [vp, ctypes.POINTER(moe_weights), vp, vp, vp]
     lib.moe_probe_read.argtypes = [vp, vp, sz, ci, vp, vp]
+    lib.moe_coverage_set.argtypes = [vp, vp, ci, ctypes.c_double, ci, vp, vp, vp]
     lib.moe_probe_mfma.argtypes = [vp, ci, ci, ci, vp, vp]
     lib.moe_timing.argtypes = [vp, ci]
     lib.moe_timing_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), ci,
@@ -111,7 +112,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in ("moe_create", "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn",
               "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
               "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts",
-              "moe_quantize", "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma"):
+              "moe_quantize", "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma",
+              "moe_coverage_set"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -182,6 +184,10 @@ class Context:
     def moe_expert_counts(self, topk_idx, T, k, E, counts, stream=None):
         self._check(self.lib.moe_expert_counts(self.handle, _p(topk_idx), T, k, E, _p(counts),
                                                _stream(stream)))
+
+    def moe_coverage_set(self, counts, E, cover, k, keep, n_keep, stream=None):
+        self._check(self.lib.moe_coverage_set(self.handle, _p(counts), E, float(cover), k,
+                                              _p(keep), _p(n_keep), _stream(stream)))
 
     def moe_quantize(self, fmt, w, codes, scales, stream=None):
         """w: [rows, K] fp32 or bf16 device tensor; fmt MOE_W_INT8_ROW or

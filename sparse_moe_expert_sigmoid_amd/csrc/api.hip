@@ -528,6 +528,19 @@ moe_status moe_combine(moe_ctx* ctx, const float* rows, const int32_t* token_row
   return device_result(ctx, e, "moe_combine");
 }
 
+moe_status moe_coverage_set(moe_ctx* ctx, const unsigned long long* counts, int E, double cover,
+                            int k, int32_t* keep, int32_t* n_keep, void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  moe_status st = moe::check_coverage_set(ctx->err, counts, E, cover, k, keep, n_keep);
+  if (st != MOE_OK) return st;
+  DeviceGuard g(ctx->device);
+  if (!g.ok)
+    return fail(ctx, MOE_E_DEVICE, "moe_coverage_set: hipSetDevice(%d) failed", ctx->device);
+  return device_result(ctx, moe::launch_coverage_set(counts, E, cover, k, keep, n_keep,
+                                                     (hipStream_t)stream),
+                       "moe_coverage_set");
+}
+
 moe_status moe_probe_read(moe_ctx* ctx, const void* buf, size_t bytes, int blocks, void* sink,
                           void* stream) {
   if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;

@@ -317,6 +317,21 @@ moe_status check_combine(char* err, const float* rows, const int32_t* token_row,
   return MOE_OK;
 }
 
+moe_status check_coverage_set(char* err, const unsigned long long* counts, int E, double cover,
+                              int k, const int32_t* keep, const int32_t* n_keep) {
+  if (E < 1 || E > kMaxE)
+    return errorf(err, MOE_E_INVALID, "moe_coverage_set: E=%d outside [1, %d]", E, kMaxE);
+  if (k < 1) return errorf(err, MOE_E_INVALID, "moe_coverage_set: k=%d must be positive", k);
+  if (!(cover >= 0.0 && cover <= 1.0))
+    return errorf(err, MOE_E_INVALID, "moe_coverage_set: cover=%g outside [0, 1]", cover);
+  if (!counts || !keep || !n_keep)
+    return errorf(err, MOE_E_INVALID, "moe_coverage_set: %s is NULL",
+                  !counts ? "counts" : !keep ? "keep" : "n_keep");
+  if (!aligned16(counts) || !aligned16(keep) || !aligned16(n_keep))
+    return errorf(err, MOE_E_INVALID, "moe_coverage_set: a pointer is not 16-byte aligned");
+  return MOE_OK;
+}
+
 moe_status check_probe_read(char* err, const void* buf, size_t bytes, int blocks,
                             const void* sink) {
   if (bytes < 16 || bytes % 16 != 0)

@@ -48,6 +48,8 @@ moe_status check_tile_weights(char* err, const moe_weights* src, const void* dst
 moe_status check_combine(char* err, const float* rows, const int32_t* token_row,
                          const float* topk_w, const float* shared, const float* residual, int T,
                          int k, int d, const float* y);
+moe_status check_coverage_set(char* err, const unsigned long long* counts, int E, double cover,
+                              int k, const int32_t* keep, const int32_t* n_keep);
 moe_status check_probe_read(char* err, const void* buf, size_t bytes, int blocks,
                             const void* sink);
 moe_status check_probe_mfma(char* err, int shape, int iters, int blocks, const void* sink);

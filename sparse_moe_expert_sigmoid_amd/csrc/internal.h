@@ -101,6 +101,10 @@ int device_cu_count();
 // 1: 32x32x32), each over `blocks` workgroups of 256 threads; sink >= 16 bytes.
 hipError_t launch_probe_read(const void* buf, size_t bytes, int blocks, void* sink,
                              hipStream_t s);
+// Expert restriction (restrict.hip): kept ids ascending in keep[0..n-1], -1
+// after, n in *n_keep; E <= kMaxE.
+hipError_t launch_coverage_set(const unsigned long long* counts, int E, double cover, int k,
+                               int32_t* keep, int32_t* n_keep, hipStream_t s);
 hipError_t launch_probe_mfma(int shape, int iters, int blocks, void* sink, hipStream_t s);
 // Row-major codes [nrows][K] (int4: K/2 bytes per row) -> tiled layout.
 hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nrows, int K,

@@ -85,12 +85,11 @@ class MoEStack:
         sliced layers, or of masked full layers with masked=True.  Returns
         (stack, [kept ids per layer])."""
         from .restrict import coverage_set, expert_mask
-        c = counts.cpu().numpy() if isinstance(counts, torch.Tensor) else counts
-        if len(c) != len(self.layers):
+        if len(counts) != len(self.layers):
             raise ValueError("counts needs one row per layer")
         keeps, layers = [], []
         for l, L in enumerate(self.layers):
-            keep = coverage_set(c[l][:L.E], cover, L.k)
+            keep = coverage_set(self.ctx, counts[l][:L.E], cover, L.k)
             keeps.append(keep)
             layers.append(L.with_mask(expert_mask(keep, L.E, L.device)) if masked
                           else L.restricted(keep))

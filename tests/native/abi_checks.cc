@@ -317,6 +317,27 @@ static void combine_tile_quant_cases() {
          MOE_E_UNSUPPORTED, "2^32");
 }
 
+static void coverage_cases() {
+  const unsigned long long* c = dev<unsigned long long>(91);
+  int32_t* keep = dev<int32_t>(92);
+  int32_t* n = dev<int32_t>(93);
+  EXPECT(check_coverage_set(g_err, c, 256, 0.95, 8, keep, n), MOE_OK, nullptr);
+  EXPECT(check_coverage_set(g_err, c, 1024, 0.0, 1, keep, n), MOE_OK, nullptr);
+  EXPECT(check_coverage_set(g_err, c, 1, 1.0, 16, keep, n), MOE_OK, nullptr);
+  EXPECT(check_coverage_set(g_err, c, 0, 0.95, 8, keep, n), MOE_E_INVALID, "E=0");
+  EXPECT(check_coverage_set(g_err, c, 1025, 0.95, 8, keep, n), MOE_E_INVALID, "E=1025");
+  EXPECT(check_coverage_set(g_err, c, 256, 1.2, 8, keep, n), MOE_E_INVALID, "cover");
+  EXPECT(check_coverage_set(g_err, c, 256, -0.1, 8, keep, n), MOE_E_INVALID, "cover");
+  EXPECT(check_coverage_set(g_err, c, 256, 0.0 / 0.0, 8, keep, n), MOE_E_INVALID, "cover");
+  EXPECT(check_coverage_set(g_err, c, 256, 0.95, 0, keep, n), MOE_E_INVALID, "k=0");
+  EXPECT(check_coverage_set(g_err, nullptr, 256, 0.95, 8, keep, n), MOE_E_INVALID,
+         "counts is NULL");
+  EXPECT(check_coverage_set(g_err, c, 256, 0.95, 8, keep, nullptr), MOE_E_INVALID,
+         "n_keep is NULL");
+  EXPECT(check_coverage_set(g_err, c, 256, 0.95, 8, misaligned<int32_t>(94), n), MOE_E_INVALID,
+         "aligned");
+}
+
 static void probe_cases() {
   const void* buf = dev<void>(81);
   void* sink = dev<void>(82);
@@ -342,6 +363,7 @@ static void probe_cases() {
 int main() {
   route_cases();
   probe_cases();
+  coverage_cases();
   permute_counts_cases();
   ffn_cases();
   forward_cases();

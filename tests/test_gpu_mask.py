@@ -8,7 +8,8 @@ layer: router rows, bias and expert weights of the allowed experts only,
 renumbered 0..n-1, with the oracle's ids mapped back to the full numbering.
 The oracle's own mask-equals-slice pin is a CPU test.  The per-expert routing
 frequencies (step 2 of the same listing) are checked against a bincount of the
-selected ids, accumulated over two calls.
+selected ids, accumulated over two calls, and the kept set chosen from them
+(moe_coverage_set, step 3) against the oracle's greedy choice.
 """
 import numpy as np
 import pytest
@@ -228,6 +229,42 @@ def _tiny_stack(ctx, layers=3, T=256, d=256, E=64, k=6, inter=128):
         inps.append(inp)
         out.append(MoELayer.from_inputs(ctx, inp))
     return MoEStack(ctx, out), inps
+
+
+def test_coverage_set_matches_oracle(ctx):
+    # moe_coverage_set against the oracle's greedy choice on random and
+    # adversarial counts: ties (few distinct values), zeros, counts above 2^40,
+    # covers 0 and 1, k above and below the set size, E up to the 1024 maximum
+    from sparse_moe_expert_sigmoid_amd.restrict import coverage_set
+    n = 0
+    for trial in range(160):
+        E = [1, 2, 7, 32, 128, 256, 300, 1000, 1024][trial % 9]
+        hi = [0, 1, 3, 100, 127][trial % 5]
+        c = S.randint8(0xC0FF, trial, (E,), 0, hi).astype(np.uint64)
+        if trial % 11 == 0:
+            c = c * np.uint64(1 << 40)                   # large counts
+        cd = _dev(c.view(np.int64))
+        for cover in (0.0, 0.3, 0.73, 0.95, 1.0):
+            for k in (1, 8, 16):
+                got = coverage_set(ctx, cd, cover, k)
+                want = oracle.coverage_set(c, cover, k)
+                assert np.array_equal(got, want), (trial, E, cover, k)
+                n += 1
+    log_result(test="coverage_set", cases=n)
+
+
+def test_coverage_set_rejects_bad_arguments(ctx):
+    import torch
+    from sparse_moe_expert_sigmoid_amd import MoeError
+    from sparse_moe_expert_sigmoid_amd.restrict import coverage_set
+    c = torch.ones(4, dtype=torch.int64, device="cuda:0")
+    for cover, k in ((1.2, 1), (-0.1, 1), (0.5, 0)):
+        with pytest.raises(MoeError):
+            coverage_set(ctx, c, cover, k)
+    with pytest.raises(MoeError):
+        coverage_set(ctx, torch.ones(1025, dtype=torch.int64, device="cuda:0"), 0.5, 1)
+    with pytest.raises(ValueError):
+        coverage_set(ctx, torch.ones(0, dtype=torch.int64, device="cuda:0"), 0.5, 1)
 
 
 def test_restriction_from_recorded_counts(ctx):
