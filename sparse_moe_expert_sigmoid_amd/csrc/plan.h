@@ -80,18 +80,20 @@ inline bool split_fits(long long u0, int n0, long long u1, int n1) {
 // units: every unit alike (n0 = n1 from split_ways) when CUs would otherwise
 // sit idle; else, when group 0's units fit the chip and group 1's spill over
 // it (e.g. 256 routed units and the shared expert's 32 at one token), group 1
-// alone splits into enough small workgroups that each CU takes one beside its
-// group-0 unit.  kpw: K-steps per wavefront unsplit.  Returns false when the
-// join area cannot hold the plan's slots and counts.
+// alone splits into small workgroups, enough for every other CU to take one
+// beside its group-0 unit (Kimi-shaped gate/up at one token, 32 shared units:
+// 4 ways 21.7 us, 8 ways 23.4 us, 2 ways 23.9 us, event-timed).  kpw: K-steps
+// per wavefront unsplit.  Returns false when the join area cannot hold the
+// plan's slots and counts.
 inline bool plan_split(long long t0, long long t1, int gx, int kpw, int min_steps, long long cus,
                        int& n0, int& n1) {
   const long long u0 = t0 * gx, u1 = t1 * gx;
   n0 = n1 = split_ways(u0 + u1, kpw, min_steps, cus);
   if (n0 == 1 && u1 > 0 && u0 <= cus && u0 + u1 > cus) {
-    int n = (int)((cus + u1 - 1) / u1);
+    int n = (int)((cus + 2 * u1 - 1) / (2 * u1));
     n = n < 8 ? n : 8;
     while (n > 1 && (kpw / n < min_steps || u1 * n > kSplitSlots)) --n;
-    n1 = n;
+    n1 = n < 1 ? 1 : n;
   }
   return split_fits(u0, n0, u1, n1);
 }
@@ -137,10 +139,15 @@ inline void plan_launches(int fmt, long long tiles0, long long tiles1, int imax,
   const int ksteps = fmt == 1 ? d / kPlanKStep : d / 128;  // K-steps (int4: spans) per unit
   if (pairs && !plan_split(tiles0, tiles1, imax / 64, ksteps / p.gu.ks, 2, cus, p.gu.n0, p.gu.n1))
     p.ok = false;
+  // int8 down takes two 64-column blocks per 256-thread workgroup unless the
+  // units are too few even for that (4-way K slices): at one Kimi-shaped
+  // token (324 units) 162 such workgroups beat 324 of 512 threads with 2 K
+  // slices (14.7 against 15.3 us, event-timed)
   p.dn.ks = kway(tiles * (d / 64));
   p.dn.n0 = p.dn.n1 = 1;
   const int dsteps = fmt == 1 ? imax / kPlanKStep : imax / 128;
-  p.dn.ng2 = fmt == 1 && p.dn.ks == 1 && d % 128 == 0;
+  p.dn.ng2 = fmt == 1 && p.dn.ks <= 2 && d % 128 == 0;
+  if (p.dn.ng2) p.dn.ks = 1;
   if (pairs && !p.dn.ng2 &&
       !plan_split(tiles0, tiles1, d / 64, dsteps / p.dn.ks, 2, cus, p.dn.n0, p.dn.n1))
     p.ok = false;
