@@ -376,10 +376,12 @@ moe_status moe_probe_mfma(moe_ctx* ctx, int shape, int iters, int blocks, void* 
 
 /* Kernel timing, a measurement aid for benchmarks; off by default.
  * moe_timing(ctx, capacity > 0) creates 2*capacity HIP events (host-side
- * allocation, outside any call path) and from then on brackets every kernel
- * launch of the calls above with a pair of events recorded on that launch's
- * stream; capacity = 0 switches it off and frees the events.  Event records
- * add a little GPU time between kernels, so time plain runs separately.
+ * allocation, outside any call path) and from then on has every kernel
+ * launch of the calls above record its kernel's start and stop on a pair of
+ * them (hipExtLaunchKernel: the dispatch's own timestamps, so the time
+ * excludes the dispatch and no event packet sits between kernels); capacity
+ * = 0 switches it off and frees the events.  Not for stream capture: time
+ * plain runs separately.
  * moe_timing_read synchronises on the recorded events and returns, per
  * kernel that ran, the number of launches and their summed duration, then
  * forgets them; out[] receives at most max_out entries and *n_out the number

@@ -22,7 +22,8 @@ const char* const kKernelNames[K_COUNT] = {
     "router_tail",   "ffn_i8_gate_up_gemm", "ffn_i8_down_gemm", "quant_i8_rows",
     "quant_i4_blocks", "ffn_i4_gate_up_gemm", "ffn_i4_down_gemm"};
 
-// Event pairs recorded around launches while a context has timing on.
+// Event pairs that launches record their kernels' start and stop on while a
+// context has timing on.
 struct KernelTimer {
   struct Mark {
     int id;
@@ -33,30 +34,27 @@ struct KernelTimer {
   size_t next = 0;
   long long dropped = 0;
   int open_id = -1;
-  hipEvent_t open_a = nullptr;
 };
 
 thread_local KernelTimer* g_timer = nullptr;
 
-void timer_begin(int id, hipStream_t s) {
-  KernelTimer* t = g_timer;
-  if (t->next + 2 > t->pool.size()) {
-    t->open_id = -1;
-    ++t->dropped;
-    return;
-  }
-  t->open_a = t->pool[t->next++];
-  t->open_id = id;
-  (void)hipEventRecord(t->open_a, s);
-}
+void timer_open(int id) { g_timer->open_id = id; }
 
-void timer_end(hipStream_t s) {
+void timer_close() { g_timer->open_id = -1; }
+
+bool timer_take(hipEvent_t* start, hipEvent_t* stop) {
   KernelTimer* t = g_timer;
-  if (t->open_id < 0) return;
-  hipEvent_t b = t->pool[t->next++];
-  (void)hipEventRecord(b, s);
-  t->marks.push_back({t->open_id, t->open_a, b});
+  if (t->open_id < 0) return false;
+  const int id = t->open_id;
   t->open_id = -1;
+  if (t->next + 2 > t->pool.size()) {
+    ++t->dropped;
+    return false;
+  }
+  *start = t->pool[t->next++];
+  *stop = t->pool[t->next++];
+  t->marks.push_back({id, *start, *stop});
+  return true;
 }
 }  // namespace moe
 

@@ -76,7 +76,7 @@ hipError_t launch_combine(const float* rows, const int32_t* token_row, const flo
   const int blocks = (int)((n + 255) / 256);
   TimedLaunch tl(K_COMBINE, s);
 #define MOE_COMBINE(KM, TRV)                                                                   \
-  hipLaunchKernelGGL((combine_kernel<KM, TRV>), dim3(blocks), dim3(256), 0, s, rows, token_row, w, \
+  moe_launch((combine_kernel<KM, TRV>), dim3(blocks), dim3(256), 0, s, rows, token_row, w, \
                      shared, residual, T, k, d, y)
   if (k <= 8) {
     if (token_row) MOE_COMBINE(8, true);

@@ -1625,7 +1625,7 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
   const size_t lds_gu = PAIRS ? emax : (size_t)mt * (2 * d + 16);
 #define MOE_GU(KSV, SPL)                                                                 \
-  hipLaunchKernelGGL((gate_up_kernel<FMT, LAY, KSV, PAIRS, 1, SPL>), grid, dim3(256 * KSV), \
+  moe_launch((gate_up_kernel<FMT, LAY, KSV, PAIRS, 1, SPL>), grid, dim3(256 * KSV), \
                      lds_gu, s, a, b, d, mt, xq, xs, sk)
   {
     TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
@@ -1651,7 +1651,7 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   const size_t lds_dn =
       PAIRS ? emax : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
 #define MOE_DN(KSV, NGV, SPL)                                                               \
-  hipLaunchKernelGGL((down_kernel<FMT, LAY, KSV, PAIRS, NGV, SPL>),                         \
+  moe_launch((down_kernel<FMT, LAY, KSV, PAIRS, NGV, SPL>),                         \
                      dim3(d / (64 * NGV), dgy), dim3(256 * KSV), lds_dn, s, a, b, d, mt, dsk)
   TimedLaunch tl(FMT == 1 ? K_FFN_I8_DOWN : K_FFN_I4_DOWN, s);
   if (ng2) MOE_DN(1, 2, false);
@@ -2012,7 +2012,7 @@ hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* si
                               int* split_cnt, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   TimedLaunch tl(K_ENCODE_ROWS, s);
-  hipLaunchKernelGGL(encode_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, v, n, K, q, sig,
+  moe_launch(encode_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, s, v, n, K, q, sig,
                      perm, split_cnt);
   return hipGetLastError();
 }
@@ -2023,10 +2023,10 @@ hipError_t launch_tile_weights(int fmt, const void* src, void* dst, long long nr
   if (chunks <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((chunks + 255) / 256);
   if (fmt == 1)
-    hipLaunchKernelGGL(tile_weights_kernel<1>, dim3(blocks), dim3(256), 0, s,
+    moe_launch(tile_weights_kernel<1>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), nrows, K);
   else
-    hipLaunchKernelGGL(tile_weights_kernel<2>, dim3(blocks), dim3(256), 0, s,
+    moe_launch(tile_weights_kernel<2>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), nrows, K);
   return hipGetLastError();
 }
@@ -2048,13 +2048,13 @@ hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const flo
       using S = GuShape<2>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      hipLaunchKernelGGL((gate_up_gemm_kernel<LAY, 2>), dim3((imax + S::COLS - 1) / S::COLS,
+      moe_launch((gate_up_gemm_kernel<LAY, 2>), dim3((imax + S::COLS - 1) / S::COLS,
                          a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
     } else {
       using S = GuShape<1>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      hipLaunchKernelGGL((gate_up_gemm_kernel<LAY, 1>), dim3((imax + S::COLS - 1) / S::COLS,
+      moe_launch((gate_up_gemm_kernel<LAY, 1>), dim3((imax + S::COLS - 1) / S::COLS,
                          a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
     }
   }
@@ -2066,20 +2066,20 @@ hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const flo
       using S = DnShape<2, kDnFrags>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      hipLaunchKernelGGL((down_gemm_kernel<LAY, 2, kDnFrags>), dim3((d + S::COLS - 1) / S::COLS,
+      moe_launch((down_gemm_kernel<LAY, 2, kDnFrags>), dim3((d + S::COLS - 1) / S::COLS,
                          a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d);
     } else {
       using S = DnShape<1, kDnFrags>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      hipLaunchKernelGGL((down_gemm_kernel<LAY, 1, kDnFrags>), dim3((d + S::COLS - 1) / S::COLS,
+      moe_launch((down_gemm_kernel<LAY, 1, kDnFrags>), dim3((d + S::COLS - 1) / S::COLS,
                          a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d);
     }
     return hipGetLastError();
   }
   a.tiles = tiles_of(a, kDRows);
   b.tiles = tiles_of(b, kDRows);
-  hipLaunchKernelGGL(down_gemm64_kernel<LAY>, dim3((d + 127) / 128, a.tiles + b.tiles),
+  moe_launch(down_gemm64_kernel<LAY>, dim3((d + 127) / 128, a.tiles + b.tiles),
                      dim3(kPWaves * kWave), 0, s, a, b, d);
   return hipGetLastError();
 }
@@ -2098,13 +2098,13 @@ hipError_t launch_gemm4_pair(Group a, Group b, int d, const int8_t* xq, const fl
   const int tiles = a.tiles + b.tiles;
   {
     TimedLaunch tl(K_FFN_I4_GATE_UP_GEMM, s);
-    hipLaunchKernelGGL((gemm4_kernel<FMT, false>), dim3((imax + k4Cols / 2 - 1) / (k4Cols / 2),
+    moe_launch((gemm4_kernel<FMT, false>), dim3((imax + k4Cols / 2 - 1) / (k4Cols / 2),
                        tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   TimedLaunch tl(K_FFN_I4_DOWN_GEMM, s);
-  hipLaunchKernelGGL((gemm4_kernel<FMT, true>), dim3((d + k4Cols - 1) / k4Cols, tiles),
+  moe_launch((gemm4_kernel<FMT, true>), dim3((d + k4Cols - 1) / k4Cols, tiles),
                      dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
   return hipGetLastError();
 }
@@ -2194,13 +2194,13 @@ hipError_t launch_ffn_f32(const float* wgu, const float* wdn, int E, int d, int 
   const int tiles = offsets ? max_tiles(R, E, kTileRows) : (R + kTileRows - 1) / kTileRows;
   {
     TimedLaunch tl(K_FFN_F32_GATE_UP, s);
-    hipLaunchKernelGGL(ffn_f32_kernel<0>, dim3((inter + 3) / 4, tiles), dim3(256), 0, s, wgu,
+    moe_launch(ffn_f32_kernel<0>, dim3((inter + 3) / 4, tiles), dim3(256), 0, s, wgu,
                        x, row_token, offsets, E, d, inter, R, act, h);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   TimedLaunch tl(K_FFN_F32_DOWN, s);
-  hipLaunchKernelGGL(ffn_f32_kernel<1>, dim3((d + 3) / 4, tiles), dim3(256), 0, s, wdn, h,
+  moe_launch(ffn_f32_kernel<1>, dim3((d + 3) / 4, tiles), dim3(256), 0, s, wdn, h,
                      row_token, offsets, E, inter, d, R, 0, rows_out);
   return hipGetLastError();
 }

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -49,18 +50,35 @@ extern const char* const kKernelNames[K_COUNT];
 
 struct KernelTimer;
 extern thread_local KernelTimer* g_timer;  // set by the API for the duration of a call
-void timer_begin(int id, hipStream_t s);
-void timer_end(hipStream_t s);
+// A TimedLaunch scope names the kernel of the one launch inside it.  With a
+// timer on, that launch (moe_launch) has the runtime record the kernel's own
+// start and stop on a pair of the timer's events (hipExtLaunchKernel: the
+// dispatch's timestamps, no event packets queued between kernels), so a
+// kernel's time excludes its dispatch and the kernels around it overlap as
+// they do untimed.
+void timer_open(int id);
+void timer_close();
+bool timer_take(hipEvent_t* start, hipEvent_t* stop);  // the open scope's pair, once
 
 struct TimedLaunch {
-  hipStream_t s;
-  TimedLaunch(int id, hipStream_t st) : s(st) {
-    if (g_timer) timer_begin(id, s);
+  TimedLaunch(int id, hipStream_t) {
+    if (g_timer) timer_open(id);
   }
   ~TimedLaunch() {
-    if (g_timer) timer_end(s);
+    if (g_timer) timer_close();
   }
 };
+
+// Every kernel launch of the library.
+template <typename... Args, typename F = void (*)(Args...)>
+inline void moe_launch(F kernel, const dim3& grid, const dim3& block, uint32_t shmem,
+                       hipStream_t s, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_timer && timer_take(&a, &b))
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, a, b, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.

@@ -145,7 +145,7 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   TimedLaunch tl(K_FILL, s);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  moe_launch(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 
@@ -172,7 +172,7 @@ hipError_t launch_expert_counts(const int32_t* idx, long long n, int E,
   long long blocks = (n + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(expert_counts_kernel, dim3((unsigned)blocks), dim3(256),
+  moe_launch(expert_counts_kernel, dim3((unsigned)blocks), dim3(256),
                      (size_t)E * sizeof(unsigned int), s, idx, n, E, counts);
   return hipGetLastError();
 }
@@ -197,7 +197,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
   const long long chunks = (n + (long long)W * seg - 1) / ((long long)W * seg);
   const size_t lds = (size_t)W * E * 12 + (size_t)E * 8;
   TimedLaunch tl(K_PERMUTE, s);
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)chunks), dim3(W * kWave), lds, s, idx,
+  moe_launch(permute_kernel, dim3((unsigned)chunks), dim3(W * kWave), lds, s, idx,
                      (int)n, k, E, seg, offsets, row_token, token_row);
   return hipGetLastError();
 }

@@ -91,17 +91,17 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int iters, in
 
 hipError_t launch_probe_read(const void* buf, size_t bytes, int blocks, void* sink,
                              hipStream_t s) {
-  hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(kProbeThreads), 0, s,
+  moe_launch(probe_read_kernel, dim3(blocks), dim3(kProbeThreads), 0, s,
                      static_cast<const v4i*>(buf), bytes / 16, static_cast<int*>(sink));
   return hipGetLastError();
 }
 
 hipError_t launch_probe_mfma(int shape, int iters, int blocks, void* sink, hipStream_t s) {
   if (shape == 0)
-    hipLaunchKernelGGL(probe_mfma_kernel<0>, dim3(blocks), dim3(kProbeThreads), 0, s, iters,
+    moe_launch(probe_mfma_kernel<0>, dim3(blocks), dim3(kProbeThreads), 0, s, iters,
                        static_cast<int*>(sink));
   else
-    hipLaunchKernelGGL(probe_mfma_kernel<1>, dim3(blocks), dim3(kProbeThreads), 0, s, iters,
+    moe_launch(probe_mfma_kernel<1>, dim3(blocks), dim3(kProbeThreads), 0, s, iters,
                        static_cast<int*>(sink));
   return hipGetLastError();
 }

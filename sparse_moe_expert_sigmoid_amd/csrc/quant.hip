@@ -315,7 +315,8 @@ template <int IN, int J>
 hipError_t launch_i8_j(const void* w, long long rows, int K, int8_t* q, float* s,
                        hipStream_t st) {
   const long long blocks = (rows + 3) / 4;  // rows <= 2^32: at most 2^30 workgroups
-  quant_i8_rows_kernel<IN, J><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, rows, K, q, s);
+  moe_launch(quant_i8_rows_kernel<IN, J>, dim3((unsigned)blocks), dim3(256), 0, st, w, rows, K, q,
+             s);
   return hipGetLastError();
 }
 
@@ -335,8 +336,8 @@ hipError_t launch_i8(const void* w, long long rows, int K, int8_t* q, float* s,
       const long long cap = resident_blocks(quant_i8_long_rows_kernel<IN>);
       long long blocks = (rows + 3) / 4;
       blocks = blocks < cap ? blocks : cap;
-      quant_i8_long_rows_kernel<IN><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, rows, K,
-                                                                                  q, s);
+      moe_launch(quant_i8_long_rows_kernel<IN>, dim3((unsigned)blocks), dim3(256), 0, st, w,
+                 rows, K, q, s);
       return hipGetLastError();
     }
   }
@@ -347,8 +348,8 @@ hipError_t launch_i4(const void* w, long long rows, int K, uint8_t* q, float* s,
                      hipStream_t st) {
   const long long pairs = rows * (long long)(K / 16);  // a multiple of LPB: K % (16 LPB) == 0
   const long long blocks = (pairs + 256 * kI4Pairs - 1) / (256 * kI4Pairs);
-  quant_i4_blocks_kernel<IN, LPB><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(w, pairs, q,
-                                                                               s);
+  moe_launch(quant_i4_blocks_kernel<IN, LPB>, dim3((unsigned)blocks), dim3(256), 0, st, w, pairs,
+             q, s);
   return hipGetLastError();
 }
 

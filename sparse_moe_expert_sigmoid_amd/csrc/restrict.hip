@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kMaxE) void coverage_set_kernel(
 hipError_t launch_coverage_set(const unsigned long long* counts, int E, double cover, int k,
                                int32_t* keep, int32_t* n_keep, hipStream_t s) {
   const int threads = (E + 63) / 64 * 64;
-  hipLaunchKernelGGL(coverage_set_kernel, dim3(1), dim3(threads), 0, s, counts, E, cover, k,
+  moe_launch(coverage_set_kernel, dim3(1), dim3(threads), 0, s, counts, E, cover, k,
                      keep, n_keep);
   return hipGetLastError();
 }

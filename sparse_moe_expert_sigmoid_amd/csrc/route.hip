@@ -403,7 +403,7 @@ hipError_t launch_select(const float* partial, int nchunk, const float* bias,
                          const uint8_t* mask, int T, int E, int k,
                          int router, float scale, int32_t* idx, float* w, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TOPK, s);
-  hipLaunchKernelGGL(router_select_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, bias,
+  moe_launch(router_select_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, bias,
                      mask,
                      T, E, k, router, scale, idx, w);
   return hipGetLastError();
@@ -485,7 +485,7 @@ hipError_t launch_tail(const float* partial, int nchunk, const float* x, int d, 
                        int T, int E, int k, int router, float scale, int32_t* idx, float* w,
                        int8_t* xq, float* xs, bool perm, int* split_cnt, hipStream_t s) {
   TimedLaunch tl(K_ROUTER_TAIL, s);
-  hipLaunchKernelGGL(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
+  moe_launch(router_tail_kernel<EPT>, dim3(T), dim3(256), 0, s, partial, nchunk, x, d,
                      bias, mask, T, E, k, router, scale, idx, w, xq, xs, perm, split_cnt);
   return hipGetLastError();
 }
@@ -501,11 +501,11 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
   TimedLaunch tl(K_ROUTER_LOGITS, s);
   if (T <= 32) {
     dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
-    hipLaunchKernelGGL(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+    moe_launch(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
                        partial);
   } else {
     dim3 grid((E + 63) / 64, (T + 63) / 64, nchunk);
-    hipLaunchKernelGGL(router_logits_tile_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+    moe_launch(router_logits_tile_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
                        partial);
   }
   }
@@ -528,11 +528,11 @@ hipError_t launch_router_encode(int router, const float* x, const float* wr, con
     TimedLaunch tl(K_ROUTER_LOGITS, s);
     if (T <= 32) {
       dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
-      hipLaunchKernelGGL(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+      moe_launch(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
                          partial);
     } else {
       dim3 grid((E + 63) / 64, (T + 63) / 64, nchunk);
-      hipLaunchKernelGGL(router_logits_tile_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
+      moe_launch(router_logits_tile_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
                          partial);
     }
   }
