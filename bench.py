@@ -33,10 +33,10 @@ step touches, times (copies - 1), exceed 600 MB, so that no step finds its
 experts in the 256 MB last-level cache from the steps before.  The stack is
 cold by size.
 
-Per-kernel durations for the rooflines come from a separate pass with HIP
-events around every launch (moe_timing), after the timed region; the event
-records inflate them a little (kernels_note gives their sum per step beside
-the timed step).
+Per-kernel durations for the rooflines come from a pass of their own after
+the timed region, in which every launch records its kernel's start and stop
+timestamps on a pair of HIP events (moe_timing, through hipExtLaunchKernel);
+kernels_note gives their sum per step beside the timed step.
 
 Attainable peaks: after the workloads, a fresh process runs the library's
 probes (moe_probe_read, moe_probe_mfma): a non-temporal streaming read of
@@ -219,8 +219,8 @@ def capture(fn, stream):
 
 
 def kernel_pass(ctx, run, n: int) -> dict:
-    """Per-kernel launch counts and durations over n eager runs, from HIP events
-    recorded around every launch on its stream."""
+    """Per-kernel launch counts and durations over n eager runs, from the start
+    and stop timestamps each launch records on a pair of HIP events."""
     import torch
     ctx.moe_timing(64 * n * 64)
     for i in range(n):
@@ -619,10 +619,10 @@ def summarize(runs: list) -> dict:
     if kernels:
         ksum = sum(v["launches"] * v["avg_us"] for v in kernels.values()) / r0["steps"] / 1e3
         out["kernels_note"] = (
-            "avg_us per kernel from HIP events around every launch, in a pass of its own: "
-            "each pair of event records adds GPU time between launches, so these sum to "
-            f"{ksum:.4f} ms per step against the {ms:.4f} ms timed step (event-inflated; "
-            "the rocprofv3 kernel-trace figures under profiles/ carry no event overhead)")
+            "avg_us per kernel from the start and stop timestamps of each dispatch "
+            "(hipExtLaunchKernel with an event pair, moe_timing), in a pass of its own after "
+            f"the timed steps: they sum to {ksum:.4f} ms per step against the {ms:.4f} ms "
+            "timed step; the gaps between kernels make up the rest")
     rl = r0["roofline"]
     if rl and rl["kernel"] in kernels:
         avg_s = kernels[rl["kernel"]]["avg_us"] / 1e6
@@ -645,8 +645,9 @@ def summarize(runs: list) -> dict:
         roof["traffic"] = rl["traffic"]
         roof["avg_launch_us"] = round(avg_s * 1e6, 2)
         roof["launches_per_step"] = rl["launches_per_step"]
-        roof["duration_source"] = ("HIP events around each launch on its stream, separate "
-                                   "pass; median over processes of the mean launch")
+        roof["duration_source"] = ("each dispatch's start and stop timestamps (hipExtLaunchKernel "
+                                   "with HIP events, moe_timing), a pass of its own after the "
+                                   "timed steps; median over processes of the mean launch")
         out["roofline"] = roof
     else:
         out["roofline"] = None
