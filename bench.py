@@ -328,8 +328,9 @@ def measure_layer(name: str, args) -> dict:
                     + (R * I + spec.T * Is) * 2 + (R * I + spec.T * Is) // 64 * 4)
         roofline = {"bound": "hbm", "kernel": dom, "bytes_per_launch": int(per_step / launches),
                     "launches_per_step": launches,
-                    "traffic": counter_traffic(name, "gate_up_gemm_kernel" if gemm
-                                               else "gate_up_kernel<")}
+                    "traffic": counter_traffic(name, "gate_up_kernel<" if not gemm else
+                                               "gemm4_kernel" if "i4" in gemm
+                                               else "gate_up_gemm_kernel")}
         if gemm:
             roofline["flops_per_launch"] = 2.0 * (R * 2 * I * d + spec.T * 2 * Is * d) / launches
     config = {"workload": desc, "T": spec.T, "chunks": chunks, "d": d, "E": E, "k": k,
@@ -410,7 +411,8 @@ def measure_stack(name: str, args) -> dict:
         roofline = {"bound": "mfma", "kernel": gemm,
                     "flops_per_launch": st.layers * 2.0 * (R * 2 * I * d + T * 2 * Is * d)
                     / launches, "launches_per_step": launches,
-                    "traffic": counter_traffic(name, "gate_up_gemm_kernel")}
+                    "traffic": counter_traffic(name, "gemm4_kernel" if "i4" in gemm
+                                               else "gate_up_gemm_kernel")}
     else:
         kname = "ffn_i4_gate_up" if int4 else "ffn_i8_gate_up"
         if kname in kernels:
@@ -775,12 +777,13 @@ def attach_peaks(summaries: dict) -> None:
         log(f"[bench] peak probes failed with status {r.returncode}; stopping")
         sys.exit(r.returncode if r.returncode > 0 else 1)
     by_size = {x["bytes"]: x for x in peaks["read"]}
+    probe_bytes = lambda n: max(16, min(int(n), PROBE_BUFFER_BYTES) // 16 * 16)
     for sm in summaries.values():
         roof = sm.get("roofline")
         if not roof:
             continue
         if roof["bound"] == "hbm":
-            rd = by_size.get(int(roof["bytes_per_launch"]) // 16 * 16)
+            rd = by_size.get(probe_bytes(roof["bytes_per_launch"]))
             if rd:
                 roof["attainable"] = {"value": rd["gbps"], "unit": "GB/s",
                                       "frac": round(roof["achieved"] / rd["gbps"], 4),
