@@ -8,6 +8,8 @@ that meet in the scratch array's join area), then the Qwen-shaped int4 layer
 at T = 3 on the same array.  Every call must give moe_forward's routing and
 output bit for bit, and match the oracle (expert sets exact, outputs within
 2e-3 of max|y|).  A layer too large for the array is refused before any launch.
+The T = 8 call is also captured in a HIP graph and replayed, with other
+calls on the same array between the replays.
 """
 import numpy as np
 import pytest
@@ -63,3 +65,49 @@ def test_forward_noalloc_matches_forward(gpu):
     qwen = S.make_layer(S.spec("qwen_decode", T=3))
     Q = MoELayer.from_inputs(ctx, qwen)
     _check(ctx, Q, qwen, 3)
+
+
+def test_forward_noalloc_in_a_hip_graph(gpu):
+    # The callers this entry point is for include code under HIP graph
+    # capture: the Kimi-shaped T = 8 call captured once, replayed four times
+    # with eager work between the replays (a T = 1 call that leaves other
+    # contents in the shared scratch array, and y and the routing outputs
+    # overwritten), each replay equal to the eager call bit for bit.
+    import torch
+    from sparse_moe_expert_sigmoid_amd import Context, MoELayer
+    ctx = Context(0)
+    kimi = S.make_layer(S.spec("kimi_decode"))
+    L = MoELayer.from_inputs(ctx, kimi)
+    d, k = kimi.spec.d, kimi.spec.k
+    x = torch.from_numpy(np.ascontiguousarray(kimi.x[:8])).to("cuda:0")
+    x1 = x[:1].contiguous()
+    y = torch.empty((8, d), dtype=torch.float32, device="cuda:0")
+    idx = torch.empty((8, k), dtype=torch.int32, device="cuda:0")
+    w = torch.empty((8, k), dtype=torch.float32, device="cuda:0")
+    y1 = torch.empty((1, d), dtype=torch.float32, device="cuda:0")
+    print("[noalloc] graph capture, Kimi-shaped T=8", flush=True)
+    ctx.moe_forward_noalloc(L.desc, L.act, x, 8, x, y, idx, w)
+    torch.cuda.synchronize()
+    y_ref, idx_ref, w_ref = y.clone(), idx.clone(), w.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on the capture stream
+        ctx.moe_forward_noalloc(L.desc, L.act, x, 8, x, y, idx, w, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.moe_forward_noalloc(L.desc, L.act, x, 8, x, y, idx, w,
+                                stream=torch.cuda.current_stream())
+    for rep in range(4):
+        ctx.moe_forward_noalloc(L.desc, L.act, x1, 1, None, y1, None, None)
+        y.fill_(float("nan"))
+        idx.fill_(-1)
+        w.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_ref) and torch.equal(w, w_ref), f"replay {rep}"
+        assert torch.equal(y, y_ref), f"replay {rep}"
+    del g
+    log_result(test="forward_noalloc_graph", replays=4)
