@@ -688,12 +688,13 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
 // (mt x I/64 floats), then the K-slice partials.
 // NG: 16-row weight groups per wavefront (2 for int8 without K split, so each
 // workgroup streams 128 output rows and its prologue is amortised over more
-// bytes).
-template <int FMT, int LAY, int KS, bool PAIRS, int NG, bool SPLIT>
-__global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int d, int mt,
-                                                        SplitK sk) {
+// bytes).  CG: 16-row column groups per workgroup (4; 2 gives a finer grid
+// when the units are few).
+template <int FMT, int LAY, int KS, bool PAIRS, int NG, bool SPLIT, int CG = 4>
+__global__ __launch_bounds__(kWave * CG * KS) void down_kernel(Group g0, Group g1, int d, int mt,
+                                                               SplitK sk) {
   extern __shared__ int8_t lds[];
-  __shared__ float red_acc[KS > 1 ? (KS - 1) * 4 * 64 * 4 : 1];
+  __shared__ float red_acc[KS > 1 ? (KS - 1) * CG * 64 * 4 : 1];
   __shared__ int rows_sm[kTileRows], sh_sm[3], last_sm;
   int vtile = blockIdx.y, kw = 0, nsplit = 1, slot0 = 0;  // (see SplitK)
   if constexpr (SPLIT) {
@@ -730,10 +731,10 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   }
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int cg = wave & 3, kp = wave >> 2;
+  const int cg = wave % CG, kp = wave / CG;
   // K slice of this wavefront: slice kw * KS + kp of nsplit * KS
   const int ksl = kw * KS + kp, nsl = nsplit * KS;
-  const int c0 = blockIdx.x * 64 * NG + cg * 16 * NG;  // output rows of this wavefront
+  const int c0 = (blockIdx.x * CG + cg) * 16 * NG;  // output rows of this wavefront
   const int i = lane & 15, g = lane >> 4;
   const bool jv = i < job.nr;
   // Small batches (PAIRS, h rows from L2): lanes of rows past the tile read
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
   }
   if (KS > 1) {  // (NG == 1 whenever KS > 1)
     if (kp > 0) {
-      float* dst = red_acc + (((kp - 1) * 4 + cg) * 64 + lane) * 4;
+      float* dst = red_acc + (((kp - 1) * CG + cg) * 64 + lane) * 4;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dst[c] = acc[0][c];
     }
@@ -873,7 +874,7 @@ __global__ __launch_bounds__(256 * KS) void down_kernel(Group g0, Group g1, int 
     if (!SPLIT && kp != 0) return;
     if (kp == 0) {
       for (int q = 1; q < KS; ++q) {
-        const float* src = red_acc + (((q - 1) * 4 + cg) * 64 + lane) * 4;
+        const float* src = red_acc + (((q - 1) * CG + cg) * 64 + lane) * 4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[0][c] += src[c];
       }
@@ -1654,7 +1655,10 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   moe_launch((down_kernel<FMT, LAY, KSV, PAIRS, NGV, SPL>),                         \
                      dim3(d / (64 * NGV), dgy), dim3(256 * KSV), lds_dn, s, a, b, d, mt, dsk)
   TimedLaunch tl(FMT == 1 ? K_FFN_I8_DOWN : K_FFN_I4_DOWN, s);
-  if (ng2) MOE_DN(1, 2, false);
+  if (plan.dn.cg == 2)  // 32-column workgroups, 2 K slices, no split (plan.h)
+    moe_launch((down_kernel<FMT, LAY, 2, PAIRS, 1, false, 2>), dim3(d / 32, tiles), dim3(256),
+               lds_dn, s, a, b, d, mt, dsk);
+  else if (ng2) MOE_DN(1, 2, false);
   else if (dsplit) {
     if (dks == 1) MOE_DN(1, 1, PAIRS);
     else if (dks == 2) MOE_DN(2, 1, PAIRS);

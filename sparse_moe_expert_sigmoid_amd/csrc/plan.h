@@ -104,9 +104,11 @@ inline bool plan_split(long long t0, long long t1, int gx, int kpw, int min_step
 //           workgroups; only small batches, whose pairs the kernels group
 //           themselves, split)
 //   ng2 (down only): two 64-column blocks per workgroup
+//   cg (down only): 16-column groups per workgroup (4, or 2 for a finer grid)
 struct LaunchSplit {
   int ks, n0, n1;
   bool ng2;
+  int cg;
 };
 struct FfnPlan {
   int mt;  // rows per tile
@@ -136,19 +138,23 @@ inline void plan_launches(int fmt, long long tiles0, long long tiles1, int imax,
   p.gu.ks = kway(tiles * (imax / 64));
   p.gu.n0 = p.gu.n1 = 1;
   p.gu.ng2 = false;
+  p.gu.cg = 4;
   const int ksteps = fmt == 1 ? d / kPlanKStep : d / 128;  // K-steps (int4: spans) per unit
   if (pairs && !plan_split(tiles0, tiles1, imax / 64, ksteps / p.gu.ks, 2, cus, p.gu.n0, p.gu.n1))
     p.ok = false;
-  // int8 down takes two 64-column blocks per 256-thread workgroup unless the
-  // units are too few even for that (4-way K slices): at one Kimi-shaped
-  // token (324 units) 162 such workgroups beat 324 of 512 threads with 2 K
-  // slices (14.7 against 15.3 us, event-timed)
+  // int8 down: with enough units for one K slice per workgroup, two 64-column
+  // blocks per 256-thread workgroup (fewer, longer streams); with fewer (2-way
+  // K slices), 32-column workgroups of 2 x 2 wavefronts instead, so that the
+  // busiest CU streams fewer bytes: at one Kimi-shaped token (324 units of
+  // 64 columns) 648 of them take 11.1 us, against 12.7 us for 162 two-block
+  // workgroups and 15.3 us for 324 of 512 threads (2 K slices, 4 groups)
   p.dn.ks = kway(tiles * (d / 64));
   p.dn.n0 = p.dn.n1 = 1;
+  p.dn.cg = 4;
   const int dsteps = fmt == 1 ? imax / kPlanKStep : imax / 128;
-  p.dn.ng2 = fmt == 1 && p.dn.ks <= 2 && d % 128 == 0;
-  if (p.dn.ng2) p.dn.ks = 1;
-  if (pairs && !p.dn.ng2 &&
+  p.dn.ng2 = fmt == 1 && p.dn.ks == 1 && d % 128 == 0;
+  if (fmt == 1 && p.dn.ks == 2 && d % 32 == 0) p.dn.cg = 2;
+  if (pairs && !p.dn.ng2 && p.dn.cg == 4 &&
       !plan_split(tiles0, tiles1, d / 64, dsteps / p.dn.ks, 2, cus, p.dn.n0, p.dn.n1))
     p.ok = false;
 }

@@ -69,10 +69,13 @@ int main() {
     FfnPlan p = plan_ffn(1, 8, 64, 256, true, 2304, 2048, 2048, 256, true);
     if (!p.ok || p.gu.n0 != 1 || p.gu.n1 != 1) ++bad_known;
     // Kimi-shaped T = 1: 256 routed units beside the shared expert's 32, split 4
-    // ways; down: two column blocks per workgroup, no K split
+    // ways; down: 32-column workgroups with 2 K slices, no split across workgroups
     p = plan_ffn(1, 1, 8, 256, true, 2304, 2048, 2048, 256, true);
     if (!p.ok || p.gu.n0 != 1 || p.gu.n1 != 4 || p.tiles0 != 8 || p.tiles1 != 1) ++bad_known;
-    if (!p.dn.ng2 || p.dn.ks != 1 || p.dn.n0 != 1 || p.dn.n1 != 1) ++bad_known;
+    if (p.dn.ng2 || p.dn.cg != 2 || p.dn.ks != 2 || p.dn.n0 != 1 || p.dn.n1 != 1) ++bad_known;
+    // Kimi-shaped T = 8: down two column blocks per workgroup
+    p = plan_ffn(1, 8, 64, 256, true, 2304, 2048, 2048, 256, true);
+    if (!p.dn.ng2 || p.dn.cg != 4 || p.dn.ks != 1) ++bad_known;
     // Qwen-shaped T = 1 (int4 b32, E = 128, d = 2048, I = 768, no shared): gate/up 2 ways
     p = plan_ffn(2, 1, 8, 128, true, 2048, 768, 0, 256, true);
     if (!p.ok || p.gu.n0 != 2 || p.gu.n1 != 2) ++bad_known;
