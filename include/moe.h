@@ -350,6 +350,42 @@ moe_status moe_forward_noalloc(moe_ctx* ctx, const moe_layer* layer, int act, co
                                int T, const float* residual, float* y, int32_t* topk_idx,
                                float* topk_w, void* stream);
 
+/* Layers chained without a combine launch between them (decode-size stacks,
+ * x_{l+1} = x_l + MoE_l(x_l); Qwen3-30B-A3B model card, "Conversion Notes":
+ * the residual add follows the moe op).  A layer's output, y = sum over slots
+ * j of w[t][j] * rows[t*k + j] (slot order) + shared[t] + residual[t], is the
+ * combine of moe_combine; it can be left pending and formed by the next
+ * layer's router launch, which reads x anyway: one launch fewer per layer.
+ * moe_forward_chained runs the layer as moe_forward does, except that
+ *   - its input is x (in == NULL), or the pending output `in` of the previous
+ *     chained call (x == NULL), which the router launch sums exactly as
+ *     moe_combine would and stores into x_out [T][d] (device, 16-byte
+ *     aligned, overlapping none of in's arrays): x_out is the layer's input
+ *     from then on, bit for bit the y an unchained layer would have written;
+ *   - it does not combine: it fills *out (host struct) with its own pending
+ *     output: rows and shared rows in ws, the weights in topk_w (or ws), and
+ *     the residual = the layer's input (x, or x_out).  They stay valid until
+ *     ws, topk_w or that input is written again; complete them with
+ *     moe_combine(out->rows, NULL, out->w, out->shared, out->residual, T,
+ *     out->k, out->d, y) or pass them to the next chained call, which must
+ *     use another workspace.
+ * Only the small-batch path chains: T <= 16, quantised routed experts and,
+ * if there is a shared expert, one in the routed experts' format and layout
+ * (one pair of FFN launches); in (if given) must have in->T == T and
+ * in->d == the layer's d.  Anything else returns MOE_E_UNSUPPORTED or
+ * MOE_E_INVALID before any launch; the other checks are moe_forward's. */
+typedef struct {
+    const float* rows;      /* [T*k][d] routed expert rows, (token, slot) order */
+    const float* shared;    /* [T][d] shared expert rows, or NULL */
+    const float* w;         /* [T][k] router weights */
+    const float* residual;  /* [T][d], or NULL */
+    int T, k, d;
+} moe_pending;
+moe_status moe_forward_chained(moe_ctx* ctx, const moe_layer* layer, int act, const float* x,
+                               const moe_pending* in, float* x_out, int T, moe_pending* out,
+                               int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Attainable-peak probes, a measurement aid for benchmarks: they compute
  * nothing of the layer.  A caller times them (events on `stream`) to state
  * the ceilings the chip reaches in practice beside its published peaks.

@@ -35,7 +35,8 @@ EXPORTS = ("moe_create", "moe_destroy", "moe_last_error", "moe_status_string",
            "moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_timing", "moe_timing_read", "moe_layer_workspace_size", "moe_forward",
            "moe_tile_weights", "moe_route_masked", "moe_expert_counts", "moe_quantize",
-           "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma", "moe_coverage_set")
+           "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma", "moe_coverage_set",
+           "moe_forward_chained")
 MOE_NOALLOC_SCRATCH_BYTES = 40 * 1024 * 1024
 
 
@@ -58,6 +59,13 @@ class moe_layer(ctypes.Structure):
                 ("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("experts", moe_weights), ("shared", moe_weights),
                 ("expert_mask", ctypes.c_void_p)]
+
+
+class moe_pending(ctypes.Structure):
+    """A layer's output left pending by moe_forward_chained (device pointers)."""
+    _fields_ = [("rows", ctypes.c_void_p), ("shared", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("residual", ctypes.c_void_p), ("T", ctypes.c_int), ("k", ctypes.c_int),
+                ("d", ctypes.c_int)]
 
 
 class moe_kernel_time(ctypes.Structure):
@@ -105,6 +113,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_tile_weights.argtypes = [vp, ctypes.POINTER(moe_weights), vp, vp, vp]
     lib.moe_probe_read.argtypes = [vp, vp, sz, ci, vp, vp]
     lib.moe_coverage_set.argtypes = [vp, vp, ci, ctypes.c_double, ci, vp, vp, vp]
+    lib.moe_forward_chained.argtypes = [vp, ctypes.POINTER(moe_layer), ci, vp,
+                                        ctypes.POINTER(moe_pending), vp, ci,
+                                        ctypes.POINTER(moe_pending), vp, vp, vp, sz, vp]
     lib.moe_probe_mfma.argtypes = [vp, ci, ci, ci, vp, vp]
     lib.moe_timing.argtypes = [vp, ci]
     lib.moe_timing_read.argtypes = [vp, ctypes.POINTER(moe_kernel_time), ci,
@@ -113,7 +124,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
               "moe_combine", "moe_timing", "moe_timing_read", "moe_layer_workspace_size",
               "moe_forward", "moe_tile_weights", "moe_route_masked", "moe_expert_counts",
               "moe_quantize", "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma",
-              "moe_coverage_set"):
+              "moe_coverage_set", "moe_forward_chained"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -232,6 +243,24 @@ class Context:
         self._check(self.lib.moe_forward_noalloc(
             self.handle, ctypes.byref(layer), act, _p(x), T, _p(residual), _p(y), _p(topk_idx),
             _p(topk_w), _stream(stream)))
+
+    def moe_forward_chained(self, layer: "moe_layer", act, x, pending_in, x_out, T, topk_idx,
+                            topk_w, ws, stream=None, ws_bytes=None) -> "moe_pending":
+        """One chained layer: input x (a tensor) or pending_in (the moe_pending of
+        the previous call, whose sum goes to x_out); returns this layer's
+        moe_pending."""
+        out = moe_pending()
+        self._check(self.lib.moe_forward_chained(
+            self.handle, ctypes.byref(layer), act, _p(x),
+            ctypes.byref(pending_in) if pending_in is not None else None, _p(x_out), T,
+            ctypes.byref(out), _p(topk_idx), _p(topk_w), _p(ws),
+            ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes, _stream(stream)))
+        return out
+
+    def moe_combine_pending(self, p: "moe_pending", y, stream=None):
+        """Completes a pending output into y with moe_combine."""
+        self._check(self.lib.moe_combine(self.handle, p.rows, None, p.w, p.shared, p.residual,
+                                         p.T, p.k, p.d, _p(y), _stream(stream)))
 
     def moe_tile_weights(self, src: "DeviceExperts", dst_gate_up, dst_down, stream=None):
         w = src.struct()

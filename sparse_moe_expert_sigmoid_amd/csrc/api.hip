@@ -391,9 +391,13 @@ moe_status moe_layer_workspace_size(const moe_ctx* cctx, const moe_layer* L, int
 namespace {
 // The layer after its checks passed, with ws (at least fwd_layout's bytes)
 // as the workspace: every launch of moe_forward and moe_forward_noalloc.
+// chain (moe_forward_chained): the router launch forms x from the previous
+// layer's pending output; pend: leave this layer's output pending there
+// instead of combining (both only on the small-batch path, checked before).
 moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float* x, int T,
                           const float* residual, float* y, int32_t* topk_idx, float* topk_w,
-                          void* ws, void* stream, const char* fn) {
+                          void* ws, void* stream, const char* fn,
+                          const moe::ChainIn* chain = nullptr, moe_pending* pend = nullptr) {
   DeviceGuard g(ctx->device);
   if (!g.ok) return fail(ctx, MOE_E_DEVICE, "%s: hipSetDevice(%d) failed", fn, ctx->device);
   const moe::FwdWs f = moe::fwd_layout(ws, L, T);
@@ -418,7 +422,7 @@ moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float
     const bool perm = X.fmt == MOE_W_INT4_B32 || X.fmt == MOE_W_INT4_B128;
     e = moe::launch_router_encode(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
                                   k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, lay.cnt,
-                                  s);
+                                  s, chain);
     if (e == hipSuccess && !small)
       e = moe::launch_permute(idx, T, k, E, f.offsets, f.row_token, f.token_row, s);
   } else {
@@ -458,6 +462,11 @@ moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float
     e = run(X, E, R, f.row_token, f.offsets, f.rows);
     if (e == hipSuccess && has_sh) e = run(S, 1, T, nullptr, nullptr, f.sh_rows);
   }
+  if (e == hipSuccess && pend) {  // the next chained layer (or a moe_combine) sums them
+    *pend = moe_pending{f.rows, has_sh ? f.sh_rows : nullptr, w, chain ? chain->x_out : x, T, k,
+                        d};
+    return MOE_OK;
+  }
   if (e == hipSuccess)  // small batches leave the rows in (token, slot) order
     e = moe::launch_combine(f.rows, small ? nullptr : f.token_row, w,
                             has_sh ? f.sh_rows : nullptr, residual, T, k, d, y, s);
@@ -476,6 +485,24 @@ moe_status moe_forward(moe_ctx* ctx, const moe_layer* L, int act, const float* x
   if (st != MOE_OK || T == 0) return st;
   return forward_launch(ctx, L, act, x, T, residual, y, topk_idx, topk_w, ws, stream,
                         "moe_forward");
+}
+
+moe_status moe_forward_chained(moe_ctx* ctx, const moe_layer* L, int act, const float* x,
+                               const moe_pending* in, float* x_out, int T, moe_pending* out,
+                               int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (check_ctx(ctx) != MOE_OK) return MOE_E_INVALID;
+  moe_status st = moe::check_forward_chained(ctx->err, L, act, x, in, x_out, T, out, topk_idx,
+                                             topk_w, ws, ws_bytes, moe::device_cu_count());
+  if (st != MOE_OK) return st;
+  if (T == 0) {
+    *out = moe_pending{nullptr, nullptr, nullptr, nullptr, 0, L->k, L->experts.d};
+    return MOE_OK;
+  }
+  moe::ChainIn chain{};
+  if (in) chain = moe::ChainIn{in->rows, in->shared, in->w, in->residual, in->k, x_out};
+  return forward_launch(ctx, L, act, in ? x_out : x, T, nullptr, nullptr, topk_idx, topk_w, ws,
+                        stream, "moe_forward_chained", in ? &chain : nullptr, out);
 }
 
 moe_status moe_forward_noalloc(moe_ctx* ctx, const moe_layer* L, int act, const float* x, int T,

@@ -273,6 +273,53 @@ moe_status check_forward(char* err, const char* fn, const moe_layer* L, int act,
   return MOE_OK;
 }
 
+moe_status check_forward_chained(char* err, const moe_layer* L, int act, const float* x,
+                                 const moe_pending* in, const float* x_out, int T,
+                                 const moe_pending* out, const int32_t* topk_idx,
+                                 const float* topk_w, const void* ws, size_t ws_bytes,
+                                 int cu_count) {
+  const char* fn = "moe_forward_chained";
+  if (!out) return errorf(err, MOE_E_INVALID, "%s: out is NULL", fn);
+  if ((x == nullptr) == (in == nullptr))
+    return errorf(err, MOE_E_INVALID, "%s: give exactly one of x and in", fn);
+  moe_status st = check_layer(err, fn, L);
+  if (st != MOE_OK) return st;
+  if (T < 0) return errorf(err, MOE_E_INVALID, "%s: T=%d", fn, T);
+  if (T > kSmallT || (T > 0 && !forward_small(L, T)))
+    return errorf(err, MOE_E_UNSUPPORTED,
+                  "%s: only layers on the small-batch path chain (T <= %d, quantised experts, "
+                  "a shared expert in the routed experts' format and layout)", fn, kSmallT);
+  if (in) {
+    const int d = L->experts.d;
+    if (in->T != T || in->d != d || in->k < 1 || in->k > kMaxK)
+      return errorf(err, MOE_E_INVALID, "%s: in has T=%d d=%d k=%d (layer: T=%d d=%d)", fn,
+                    in->T, in->d, in->k, T, d);
+    if (T > 0) {
+      if (!in->rows || !in->w || !x_out)
+        return errorf(err, MOE_E_INVALID, "%s: %s is NULL", fn,
+                      !in->rows ? "in->rows" : !in->w ? "in->w" : "x_out");
+      if (!aligned16(in->rows) || !aligned16(in->w) || !aligned16(in->shared) ||
+          !aligned16(in->residual) || !aligned16(x_out))
+        return errorf(err, MOE_E_INVALID, "%s: a pointer is not 16-byte aligned", fn);
+      auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+        if (!a || !b) return false;
+        const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+        return pa < pb + nb && pb < pa + na;
+      };
+      const size_t row = (size_t)d * sizeof(float), nx = (size_t)T * row;
+      if (overlap(x_out, nx, in->rows, (size_t)T * in->k * row) ||
+          overlap(x_out, nx, in->shared, nx) || overlap(x_out, nx, in->residual, nx) ||
+          overlap(x_out, nx, in->w, (size_t)T * in->k * sizeof(float)))
+        return errorf(err, MOE_E_INVALID, "%s: x_out overlaps the pending input", fn);
+    }
+  }
+  // the rest as moe_forward's (the layer's input is x_out when chained; the
+  // output rows stay in ws, so x stands in for y)
+  const float* xin = in ? x_out : x;
+  return check_forward(err, fn, L, act, xin, T, nullptr, xin, topk_idx, topk_w, ws, ws_bytes,
+                       cu_count);
+}
+
 moe_status check_tile_weights(char* err, const moe_weights* src, const void* dst_gate_up,
                               const void* dst_down) {
   if (!src) return errorf(err, MOE_E_INVALID, "moe_tile_weights: src is NULL");

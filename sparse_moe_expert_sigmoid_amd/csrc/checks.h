@@ -43,6 +43,11 @@ moe_status check_layer_workspace_size(char* err, const moe_layer* L, int T, cons
 moe_status check_forward(char* err, const char* fn, const moe_layer* L, int act, const float* x,
                          int T, const float* residual, const float* y, const int32_t* topk_idx,
                          const float* topk_w, const void* ws, size_t ws_bytes, int cu_count);
+moe_status check_forward_chained(char* err, const moe_layer* L, int act, const float* x,
+                                 const moe_pending* in, const float* x_out, int T,
+                                 const moe_pending* out, const int32_t* topk_idx,
+                                 const float* topk_w, const void* ws, size_t ws_bytes,
+                                 int cu_count);
 moe_status check_tile_weights(char* err, const moe_weights* src, const void* dst_gate_up,
                               const void* dst_down);
 moe_status check_combine(char* err, const float* rows, const int32_t* token_row,

@@ -87,16 +87,28 @@ hipError_t launch_router(int router, const float* x, const float* wr, const floa
                          const uint8_t* mask, int T,
                          int d, int E, int k, float scale, int32_t* idx, float* w,
                          float* partial, hipStream_t s);
+// The previous layer's pending output (moe_forward_chained) that the logits
+// launch sums into this layer's input x_out before multiplying it.
+struct ChainIn {
+  const float* rows;      // [T*k][d], (token, slot) order
+  const float* shared;    // [T][d] or NULL
+  const float* w;         // [T][k]
+  const float* residual;  // [T][d] or NULL
+  int k;
+  float* x_out;           // [T][d]
+};
 // Logits, then one launch for the selection and the x encoding (xq/xs, see
 // the FFN workspace), which replaces the FFN's own encoding when every expert
 // set of the layer reads the same digits.  No permutation: up to kSmallT
 // tokens the FFN groups the pairs itself (FfnSet::pairs_idx), beyond that
-// launch_permute follows.
+// launch_permute follows.  chain non-NULL (T <= 16): the logits launch first
+// forms x, the previous layer's pending output, into chain->x_out, and x is
+// ignored (hipErrorInvalidValue for T > 16 or chain->k outside [1, 16]).
 hipError_t launch_router_encode(int router, const float* x, const float* wr, const float* bias,
                                 const uint8_t* mask,
                                 int T, int d, int E, int k, float scale, int32_t* idx, float* w,
                                 float* partial, int8_t* xq, float* xs, bool perm,
-                                int* split_cnt, hipStream_t s);
+                                int* split_cnt, hipStream_t s, const ChainIn* chain = nullptr);
 // counts[e] += number of topk_idx entries equal to e (entries outside [0, E) skipped)
 hipError_t launch_expert_counts(const int32_t* idx, long long n, int E, unsigned long long* counts,
                                 hipStream_t s);

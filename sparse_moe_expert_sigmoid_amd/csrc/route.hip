@@ -101,6 +101,74 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const float* _
   logit_store(v, e0, t0, lane, c, T, E, partial);
 }
 
+// Chained layers (T <= 16, moe_forward_chained): the previous layer's output
+// is still pending as its rows, and this launch forms the x slice it needs as
+// the combine would (the k weighted rows in slot order by fused
+// multiply-adds, then the shared row, then the residual), one element per
+// thread with all of its loads in flight, into LDS; the workgroups of expert
+// block 0 also store the slice as the layer's input.  The logits then follow
+// the small kernel's chains exactly, with the x operand read from LDS, so
+// they equal an unchained call's bit for bit.
+template <int KMAX>
+__global__ __launch_bounds__(256) void router_logits_chain_kernel(ChainIn ch,
+                                                                  const float* __restrict__ wr,
+                                                                  int T, int d, int E,
+                                                                  float* __restrict__ partial) {
+  constexpr int kChainSteps = kRouterChunk / 16;
+  __shared__ float x_sm[16][kRouterChunk];
+  __shared__ v4f chain_sm[4][kWave];
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16, c = blockIdx.z;
+  const int kbeg = c * kRouterChunk;
+  const int width = min(kRouterChunk, d - kbeg);
+  const int nt = min(16, T - t0);
+  for (int q = threadIdx.x; q < nt * width; q += blockDim.x) {
+    const int tl = q / width, col = kbeg + q % width, t = t0 + tl;
+    const size_t o = (size_t)t * d + col;
+    float v[KMAX], wj[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int jj = j < ch.k ? j : 0;
+      v[j] = ch.rows[(size_t)(t * ch.k + jj) * d + col];
+      wj[j] = ch.w[(size_t)t * ch.k + jj];
+    }
+    const float shv = ch.shared ? ch.shared[o] : 0.0f;
+    const float rsv = ch.residual ? ch.residual[o] : 0.0f;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) acc = fmaf(j < ch.k ? wj[j] : 0.0f, v[j], acc);
+    if (ch.shared) acc += shv;
+    if (ch.residual) acc += rsv;
+    x_sm[tl][q % width] = acc;
+    if (blockIdx.x == 0) ch.x_out[o] = acc;
+  }
+  __syncthreads();
+  const int nm = width / 16;  // steps per chain in this slice
+  const int h = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, q = lane >> 4;
+  const float* wa = wr + (size_t)min(e0 + i, E - 1) * d + kbeg + 4 * h + q;
+  const float* xb = &x_sm[min(i, nt - 1)][4 * h + q];
+  float a[kChainSteps], b[kChainSteps];
+#pragma unroll
+  for (int m = 0; m < kChainSteps; ++m) {
+    const int mc = min(m, nm - 1);
+    a[m] = wa[16 * mc];
+    b[m] = xb[16 * mc];
+  }
+  const v4f acc = nm == 16  ? logit_chain<16>(a, b)
+                  : nm == 12 ? logit_chain<12>(a, b)
+                  : nm == 8  ? logit_chain<8>(a, b)
+                             : logit_chain<4>(a, b);
+  chain_sm[h][lane] = acc;
+  __syncthreads();
+  if (h != 0) return;
+  const v4f c0 = chain_sm[0][lane], c1 = chain_sm[1][lane];
+  const v4f c2 = chain_sm[2][lane], c3 = chain_sm[3][lane];
+  v4f v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = (c0[r] + c1[r]) + (c2[r] + c3[r]);
+  logit_store(v, e0, t0, lane, c, T, E, partial);
+}
+
 // Larger batches: 64 experts x 64 tokens per workgroup, wavefront w owning
 // experts 32 (w & 1) .. + 31 and tokens 32 (w >> 1) .. + 31 (2 x 2 blocks, 4
 // chains each).  The slice moves through LDS 16 steps (64 inputs) at a time
@@ -522,11 +590,23 @@ hipError_t launch_router_encode(int router, const float* x, const float* wr, con
                                 const uint8_t* mask,
                                 int T, int d, int E, int k, float scale, int32_t* idx, float* w,
                                 float* partial, int8_t* xq, float* xs, bool perm,
-                                int* split_cnt, hipStream_t s) {
+                                int* split_cnt, hipStream_t s, const ChainIn* chain) {
   const int nchunk = (d + kRouterChunk - 1) / kRouterChunk;
+  if (chain) {
+    if (T > 16 || chain->k < 1 || chain->k > kMaxK) return hipErrorInvalidValue;
+    x = chain->x_out;  // the selection encodes the formed input
+  }
   {
     TimedLaunch tl(K_ROUTER_LOGITS, s);
-    if (T <= 32) {
+    if (chain) {
+      dim3 grid((E + 15) / 16, 1, nchunk);
+      if (chain->k <= 8)
+        moe_launch(router_logits_chain_kernel<8>, grid, dim3(256), 0, s, *chain, wr, T, d, E,
+                   partial);
+      else
+        moe_launch(router_logits_chain_kernel<kMaxK>, grid, dim3(256), 0, s, *chain, wr, T, d,
+                   E, partial);
+    } else if (T <= 32) {
       dim3 grid((E + 15) / 16, (T + 15) / 16, nchunk);
       moe_launch(router_logits_small_kernel, grid, dim3(256), 0, s, x, wr, T, d, E,
                          partial);

@@ -6,8 +6,15 @@ The residual add sits after the moe op (Qwen3-30B-A3B model card,
 "Conversion Notes"), so each layer passes its input as moe_forward's
 residual.  Activations ping-pong between two [T, d] buffers; the input x_0 is
 never written, so a captured HIP graph of the whole stack can be replayed on
-the same input.  All buffers, including one workspace shared by every layer,
-are allocated by alloc(T), never inside forward().
+the same input.  All buffers, including the workspaces, are allocated by
+alloc(T), never inside forward().
+
+At decode sizes (T <= 16, every layer on the small-batch path) the layers
+chain (moe_forward_chained): each layer leaves its output pending and the
+next layer's router launch forms it, so a layer takes one launch fewer; the
+last layer's output is completed by moe_combine.  The results are bit for
+bit those of one moe_forward per layer.  Two workspaces alternate (a layer
+reads the previous one's rows from its workspace).
 """
 from __future__ import annotations
 
@@ -15,7 +22,7 @@ from typing import Callable, List, Optional
 
 import torch
 
-from .binding import Context, DeviceExperts, MOE_W_INT8_ROW
+from .binding import Context, DeviceExperts, MOE_W_FP32, MOE_W_INT8_ROW
 from .layer import MoELayer
 
 
@@ -45,6 +52,9 @@ class MoEStack:
         self.w = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in self.layers]
         need = max(self.ctx.moe_layer_workspace_size(L.desc, T) for L in self.layers)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.chain = 0 < T <= 16 and all(_chains(L) for L in self.layers)
+        self.ws2 = (torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if self.chain
+                    else None)
         self._T = T
 
     def forward(self, x0: torch.Tensor, stream=None,
@@ -63,6 +73,8 @@ class MoEStack:
         T, d = x0.shape
         assert d == self.d and x0.dtype == torch.float32 and x0.is_contiguous()
         self.alloc(T)
+        if self.chain and before_layer is None and after_layer is None:
+            return self._forward_chained(x0, stream, counts)
         cur = x0
         for l, L in enumerate(self.layers):
             if before_layer is not None:
@@ -77,7 +89,28 @@ class MoEStack:
             cur = out
         return cur
 
+    def _forward_chained(self, x0, stream, counts):
+        T = x0.shape[0]
+        ws = (self.ws, self.ws2)
+        pend = None
+        for l, L in enumerate(self.layers):
+            if pend is None:
+                pend = self.ctx.moe_forward_chained(L.desc, L.act, x0, None, None, T, self.idx[l],
+                                                    self.w[l], ws[l % 2], stream)
+            else:
+                # the input x_l is formed into buf[(l - 1) % 2], the buffer the
+                # unchained run writes layer l - 1's output to
+                pend = self.ctx.moe_forward_chained(L.desc, L.act, None, pend,
+                                                    self.buf[(l - 1) % 2], T, self.idx[l],
+                                                    self.w[l], ws[l % 2], stream)
+            if counts is not None:
+                self.ctx.moe_expert_counts(self.idx[l], T, L.k, L.E, counts[l], stream)
+        out = self.buf[(len(self.layers) - 1) % 2]
+        self.ctx.moe_combine_pending(pend, out, stream)
+        return out
+
     __call__ = forward
+
 
     def restricted(self, counts, cover: float = 0.95, masked: bool = False):
         """Per layer, the smallest expert set carrying `cover` of the recorded
@@ -133,3 +166,12 @@ class MoEStack:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         return MoEStack(ctx, out)
+
+
+def _chains(L) -> bool:
+    """Whether the layer runs on the chained (small-batch) path: quantised
+    routed experts and no shared expert, or one in their format and layout."""
+    if L.experts.fmt == MOE_W_FP32:
+        return False
+    sh = L.shared
+    return sh is None or (sh.fmt == L.experts.fmt and sh.layout == L.experts.layout)

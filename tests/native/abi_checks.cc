@@ -338,6 +338,59 @@ static void coverage_cases() {
          "aligned");
 }
 
+static void chained_cases() {
+  moe_layer L = kimi_layer();
+  const float* x = dev<float>(100);
+  float* x_out = dev<float>(101);
+  void* ws = dev<void>(102);
+  const size_t need = fwd_layout(nullptr, &L, 1).bytes;
+  moe_pending in{dev<float>(103), dev<float>(104), dev<float>(105), dev<float>(106), 1, 8, 2304};
+  moe_pending out{};
+  EXPECT(check_forward_chained(g_err, &L, 0, x, nullptr, nullptr, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_OK, nullptr);
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &in, x_out, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_OK, nullptr);
+  EXPECT(check_forward_chained(g_err, &L, 0, x, &in, x_out, 1, &out, nullptr, nullptr, ws, need,
+                               256), MOE_E_INVALID, "exactly one");
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, nullptr, x_out, 1, &out, nullptr, nullptr,
+                               ws, need, 256), MOE_E_INVALID, "exactly one");
+  EXPECT(check_forward_chained(g_err, &L, 0, x, nullptr, nullptr, 1, nullptr, nullptr, nullptr, ws,
+                               need, 256), MOE_E_INVALID, "out is NULL");
+  EXPECT(check_forward_chained(g_err, &L, 0, x, nullptr, nullptr, 17, &out, nullptr, nullptr, ws,
+                               fwd_layout(nullptr, &L, 17).bytes, 256),
+         MOE_E_UNSUPPORTED, "small-batch");
+  moe_layer f = L;  // an fp32 shared expert runs apart: no chaining
+  f.shared.fmt = MOE_W_FP32;
+  f.shared.layout = MOE_LAYOUT_ROWS;
+  f.shared.s_gate_up = nullptr;
+  f.shared.s_down = nullptr;
+  EXPECT(check_forward_chained(g_err, &f, 0, x, nullptr, nullptr, 1, &out, nullptr, nullptr, ws,
+                               fwd_layout(nullptr, &f, 1).bytes, 256),
+         MOE_E_UNSUPPORTED, "small-batch");
+  moe_pending bad = in;
+  bad.T = 2;
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &bad, x_out, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_E_INVALID, "in has T=2");
+  bad = in;
+  bad.k = 17;
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &bad, x_out, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_E_INVALID, "k=17");
+  bad = in;
+  bad.rows = nullptr;
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &bad, x_out, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_E_INVALID, "in->rows is NULL");
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &in, nullptr, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_E_INVALID, "x_out is NULL");
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &in, misaligned<float>(107), 1, &out,
+                               nullptr, nullptr, ws, need, 256), MOE_E_INVALID, "aligned");
+  bad = in;
+  bad.residual = x_out;  // the sum would overwrite values it still reads
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &bad, x_out, 1, &out, nullptr, nullptr, ws,
+                               need, 256), MOE_E_INVALID, "overlaps");
+  EXPECT(check_forward_chained(g_err, &L, 0, nullptr, &in, x_out, 1, &out, nullptr, nullptr, ws,
+                               need - 1, 256), MOE_E_WORKSPACE, "too small");
+}
+
 static void probe_cases() {
   const void* buf = dev<void>(81);
   void* sink = dev<void>(82);
@@ -364,6 +417,7 @@ int main() {
   route_cases();
   probe_cases();
   coverage_cases();
+  chained_cases();
   permute_counts_cases();
   ffn_cases();
   forward_cases();

@@ -19,6 +19,11 @@ The Qwen3-shaped stack (48 distinct layers, d=2048, E=128, softmax top 8,
 I=768, int4 block-32 experts, no shared expert; about 18 GB drawn on the GPU)
 is checked the same way at decode (T=1 and a few tokens) and through a HIP
 graph of all 48 layers.
+
+At decode sizes the stacks chain their layers (moe_forward_chained, the
+combine formed by the next layer's router launch); the teacher-forced runs
+use per-layer hooks and so one moe_forward per layer, and the chained run
+must equal that run bit for bit (routing and output), at T = 1, 4 and 16.
 """
 import numpy as np
 import pytest
@@ -301,3 +306,34 @@ def test_qwen_stack_decode_T4_teacher_forced(qwen_stack):
 
 def test_qwen_stack_decode_graph_replays_match_eager(qwen_stack):
     _graph_replays_match_eager(qwen_stack[1], _qwen_x(1))
+
+
+# ------------------------------------------------------------ chained layers
+
+def _chained_equals_unchained(stk, x0_host, T):
+    # the stack's decode path chains the layers (moe_forward_chained: each
+    # layer's combine formed by the next layer's router launch); a no-op
+    # hook makes the same stack run one moe_forward per layer instead
+    import torch
+    x0 = torch.from_numpy(np.ascontiguousarray(x0_host[:T])).to("cuda:0")
+    print(f"[chained] T={T}", flush=True)
+    chained = stk.forward(x0).clone()
+    idx_c = [i.clone() for i in stk.idx]
+    w_c = [w.clone() for w in stk.w]
+    assert stk.chain
+    plain = stk.forward(x0, after_layer=lambda l, a, b: None).clone()
+    torch.cuda.synchronize()
+    for l in range(len(stk.layers)):
+        assert torch.equal(idx_c[l], stk.idx[l]) and torch.equal(w_c[l], stk.w[l]), l
+    assert torch.equal(chained, plain)
+    _log(test="stack_chained", T=T, layers=len(stk.layers), bit_identical=True)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_stack_chained_equals_unchained(stack, T):
+    _chained_equals_unchained(stack[1], S.stack_x(S.stack_spec(4096)), T)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_qwen_stack_chained_equals_unchained(qwen_stack, T):
+    _chained_equals_unchained(qwen_stack[1], _qwen_x(16), T)
