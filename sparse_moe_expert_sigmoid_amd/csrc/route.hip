@@ -121,6 +121,15 @@ __global__ __launch_bounds__(256) void router_logits_chain_kernel(ChainIn ch,
   const int kbeg = c * kRouterChunk;
   const int width = min(kRouterChunk, d - kbeg);
   const int nt = min(16, T - t0);
+  const int nm = width / 16;  // steps per chain in this slice
+  const int h = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int i = lane & 15, q4 = lane >> 4;
+  // the router rows do not depend on x: their loads go out first, and their
+  // latency overlaps the sum below
+  const float* wa = wr + (size_t)min(e0 + i, E - 1) * d + kbeg + 4 * h + q4;
+  float a[kChainSteps], b[kChainSteps];
+#pragma unroll
+  for (int m = 0; m < kChainSteps; ++m) a[m] = wa[16 * min(m, nm - 1)];
   for (int q = threadIdx.x; q < nt * width; q += blockDim.x) {
     const int tl = q / width, col = kbeg + q % width, t = t0 + tl;
     const size_t o = (size_t)t * d + col;
@@ -142,18 +151,9 @@ __global__ __launch_bounds__(256) void router_logits_chain_kernel(ChainIn ch,
     if (blockIdx.x == 0) ch.x_out[o] = acc;
   }
   __syncthreads();
-  const int nm = width / 16;  // steps per chain in this slice
-  const int h = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int i = lane & 15, q = lane >> 4;
-  const float* wa = wr + (size_t)min(e0 + i, E - 1) * d + kbeg + 4 * h + q;
-  const float* xb = &x_sm[min(i, nt - 1)][4 * h + q];
-  float a[kChainSteps], b[kChainSteps];
+  const float* xb = &x_sm[min(i, nt - 1)][4 * h + q4];
 #pragma unroll
-  for (int m = 0; m < kChainSteps; ++m) {
-    const int mc = min(m, nm - 1);
-    a[m] = wa[16 * mc];
-    b[m] = xb[16 * mc];
-  }
+  for (int m = 0; m < kChainSteps; ++m) b[m] = xb[16 * min(m, nm - 1)];
   const v4f acc = nm == 16  ? logit_chain<16>(a, b)
                   : nm == 12 ? logit_chain<12>(a, b)
                   : nm == 8  ? logit_chain<8>(a, b)
