@@ -971,7 +971,15 @@ struct GuShape {
 
 #define RING_SLOT(q) ((q) == 0 ? ring0 : (q) == 1 ? ring1 : (q) == 2 ? ring2 : ring3)
 
-template <int LAY, int WT>
+// Gate activation fixed at compile time (ACT = 0 silu, 1 gelu_tanh), or chosen
+// per expert set at run time (ACT = -1): with it fixed, the epilogue's values
+// need no branch each.
+template <int ACT>
+__device__ inline float act_t(int act, float z) {
+  return ACT == 0 ? silu_f(z) : ACT == 1 ? gelu_tanh_f(z) : act_f(act, z);
+}
+
+template <int LAY, int WT, int ACT>
 __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, int d,
                                                            const int8_t* __restrict__ xq,
                                                            const float* __restrict__ xs) {
@@ -1065,7 +1073,34 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
 #pragma unroll
   for (int q = 0; q < S::NS - 1; ++q) issue(RING_SLOT(q), q);
 
-#define GU_STEP(STEP, Q)                                                                      \
+// A wavefront with all four row groups valid (ntg == 4) reads all twelve
+// fragments of the K-step at once and then runs its 32 MFMAs: with the row
+// groups behind run-time conditions each group's reads wait until the
+// previous group's MFMAs are issued, four LDS round trips per K-step.
+#define GU_STEP(STEP, Q) { if (ntg == 4) GU_FULL(STEP, Q) else GU_PART(STEP, Q) }
+#define GU_FULL(STEP, Q)                                                                      \
+  {                                                                                           \
+    MOE_WAIT_VM(S::WAIT);                                                                     \
+    ring_barrier();                                                                           \
+    if (active) {                                                                             \
+      const int8_t* slot = RING_SLOT(Q);                                                      \
+      v4i a[4], b[4][2];                                                                      \
+      _Pragma("unroll") for (int f = 0; f < 4; ++f) a[f] = lds_frag(slot + ablk[f] * kPBlk, lane); \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        const int8_t* bb = slot + (S::NA + 2 * (4 * wt + t)) * kPBlk;                         \
+        b[t][0] = lds_frag(bb, lane);                                                         \
+        b[t][1] = lds_frag(bb + kPBlk, lane);                                                 \
+      }                                                                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                      \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t)                                           \
+        _Pragma("unroll") for (int f = 0; f < 4; ++f) {                                       \
+          acc[f][t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b[t][0], acc[f][t][0], 0, 0, 0); \
+          acc[f][t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f], b[t][1], acc[f][t][1], 0, 0, 0); \
+        }                                                                                     \
+    }                                                                                         \
+    issue(RING_SLOT(((Q) + S::NS - 1) % S::NS), (STEP) + S::NS - 1);                          \
+  }
+#define GU_PART(STEP, Q)                                                                  \
   {                                                                                           \
     MOE_WAIT_VM(S::WAIT);                                                                     \
     ring_barrier();                                                                           \
@@ -1108,6 +1143,8 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
     if (s0 + 1 < nsteps) GU_STEP(s0 + 1, 1)
   }
 #undef GU_STEP
+#undef GU_FULL
+#undef GU_PART
   MOE_WAIT_VM(0);
 
   // epilogue: h per row, one scale per row and 128-column block (4 wavefronts)
@@ -1121,14 +1158,12 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
     for (int q = 0; q < 2; ++q) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float gt = rv ? sgate[q][c] * sig[t] *
-                                  ((float)acc[q][t][0][c] + (float)acc[q][t][1][c] * (1.0f / 256.0f))
-                            : 0.0f;
-        const float upv = rv ? sup[q][c] * sig[t] *
-                                   ((float)acc[2 + q][t][0][c] +
-                                    (float)acc[2 + q][t][1][c] * (1.0f / 256.0f))
-                             : 0.0f;
-        h[q][t][c] = act_f(G.act, gt) * upv;
+        const float gt = sgate[q][c] * sig[t] *
+                         ((float)acc[q][t][0][c] + (float)acc[q][t][1][c] * (1.0f / 256.0f));
+        const float upv = sup[q][c] * sig[t] *
+                          ((float)acc[2 + q][t][0][c] + (float)acc[2 + q][t][1][c] * (1.0f / 256.0f));
+        const float hv = act_t<ACT>(G.act, gt) * upv;
+        h[q][t][c] = rv ? hv : 0.0f;
         mx = fmaxf(mx, fabsf(h[q][t][c]));
       }
     }
@@ -2046,20 +2081,36 @@ hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const flo
   // gate/up: 64-row tiles x 256 columns below 96 rows per expert on average,
   // else 128-row tiles x 128 columns
   const bool tall = a.R >= 96LL * a.E;
+  // one activation for both sets (templated epilogue), else chosen per set at run time
+  const int act = (b.R <= 0 || a.act == b.act) ? a.act : -1;
   {
     TimedLaunch tl(K_FFN_I8_GATE_UP_GEMM, s);
     if (tall) {
       using S = GuShape<2>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      moe_launch((gate_up_gemm_kernel<LAY, 2>), dim3((imax + S::COLS - 1) / S::COLS,
-                         a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+      if (act == 0)
+        moe_launch((gate_up_gemm_kernel<LAY, 2, 0>), dim3((imax + S::COLS - 1) / S::COLS,
+                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+      else if (act == 1)
+        moe_launch((gate_up_gemm_kernel<LAY, 2, 1>), dim3((imax + S::COLS - 1) / S::COLS,
+                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+      else
+        moe_launch((gate_up_gemm_kernel<LAY, 2, -1>), dim3((imax + S::COLS - 1) / S::COLS,
+                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
     } else {
       using S = GuShape<1>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      moe_launch((gate_up_gemm_kernel<LAY, 1>), dim3((imax + S::COLS - 1) / S::COLS,
-                         a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+      if (act == 0)
+        moe_launch((gate_up_gemm_kernel<LAY, 1, 0>), dim3((imax + S::COLS - 1) / S::COLS,
+                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+      else if (act == 1)
+        moe_launch((gate_up_gemm_kernel<LAY, 1, 1>), dim3((imax + S::COLS - 1) / S::COLS,
+                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
+      else
+        moe_launch((gate_up_gemm_kernel<LAY, 1, -1>), dim3((imax + S::COLS - 1) / S::COLS,
+                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
     }
   }
   hipError_t err = hipGetLastError();
