@@ -971,12 +971,12 @@ struct GuShape {
 
 #define RING_SLOT(q) ((q) == 0 ? ring0 : (q) == 1 ? ring1 : (q) == 2 ? ring2 : ring3)
 
-// Gate activation fixed at compile time (ACT = 0 silu, 1 gelu_tanh), or chosen
-// per expert set at run time (ACT = -1): with it fixed, the epilogue's values
-// need no branch each.
+// Gate activation fixed at compile time (ACT = 0 silu, 1 gelu_tanh), so that
+// the epilogue's values need no branch each.  Both expert sets of a launch
+// take the layer's activation.
 template <int ACT>
-__device__ inline float act_t(int act, float z) {
-  return ACT == 0 ? silu_f(z) : ACT == 1 ? gelu_tanh_f(z) : act_f(act, z);
+__device__ inline float act_t(float z) {
+  return ACT == 1 ? gelu_tanh_f(z) : silu_f(z);
 }
 
 template <int LAY, int WT, int ACT>
@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(512) void gate_up_gemm_kernel(Group g0, Group g1, i
                          ((float)acc[q][t][0][c] + (float)acc[q][t][1][c] * (1.0f / 256.0f));
         const float upv = sup[q][c] * sig[t] *
                           ((float)acc[2 + q][t][0][c] + (float)acc[2 + q][t][1][c] * (1.0f / 256.0f));
-        const float hv = act_t<ACT>(G.act, gt) * upv;
+        const float hv = act_t<ACT>(gt) * upv;
         h[q][t][c] = rv ? hv : 0.0f;
         mx = fmaxf(mx, fabsf(h[q][t][c]));
       }
@@ -2081,35 +2081,28 @@ hipError_t launch_gemm_pair(Group a, Group b, int d, const int8_t* xq, const flo
   // gate/up: 64-row tiles x 256 columns below 96 rows per expert on average,
   // else 128-row tiles x 128 columns
   const bool tall = a.R >= 96LL * a.E;
-  // one activation for both sets (templated epilogue), else chosen per set at run time
-  const int act = (b.R <= 0 || a.act == b.act) ? a.act : -1;
+  const int act = a.act;  // the layer's activation, the same for both sets
   {
     TimedLaunch tl(K_FFN_I8_GATE_UP_GEMM, s);
     if (tall) {
       using S = GuShape<2>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      if (act == 0)
-        moe_launch((gate_up_gemm_kernel<LAY, 2, 0>), dim3((imax + S::COLS - 1) / S::COLS,
-                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
-      else if (act == 1)
+      if (act == 1)
         moe_launch((gate_up_gemm_kernel<LAY, 2, 1>), dim3((imax + S::COLS - 1) / S::COLS,
                            a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
       else
-        moe_launch((gate_up_gemm_kernel<LAY, 2, -1>), dim3((imax + S::COLS - 1) / S::COLS,
+        moe_launch((gate_up_gemm_kernel<LAY, 2, 0>), dim3((imax + S::COLS - 1) / S::COLS,
                            a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
     } else {
       using S = GuShape<1>;
       a.tiles = tiles_of(a, S::ROWS);
       b.tiles = tiles_of(b, S::ROWS);
-      if (act == 0)
-        moe_launch((gate_up_gemm_kernel<LAY, 1, 0>), dim3((imax + S::COLS - 1) / S::COLS,
-                           a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
-      else if (act == 1)
+      if (act == 1)
         moe_launch((gate_up_gemm_kernel<LAY, 1, 1>), dim3((imax + S::COLS - 1) / S::COLS,
                            a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
       else
-        moe_launch((gate_up_gemm_kernel<LAY, 1, -1>), dim3((imax + S::COLS - 1) / S::COLS,
+        moe_launch((gate_up_gemm_kernel<LAY, 1, 0>), dim3((imax + S::COLS - 1) / S::COLS,
                            a.tiles + b.tiles), dim3(kPWaves * kWave), 0, s, a, b, d, xq, xs);
     }
   }
