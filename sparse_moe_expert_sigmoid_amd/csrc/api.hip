@@ -414,15 +414,22 @@ moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float
   // permutation (the FFN groups the pairs itself).
   const bool enc = X.fmt != MOE_W_FP32 && (fused || !has_sh);
   const bool small = moe::forward_small(L, T);
+  // x digits in the order the routed experts' kernels read (int4: permuted)
+  const bool perm = X.fmt == MOE_W_INT4_B32 || X.fmt == MOE_W_INT4_B128;
+  // one token: the gate/up launch selects and encodes for itself (SelIn)
+  const bool selfsel = enc && small && T == 1 && E <= 256 && moe::sel_fits(d);
+  moe::SelIn si{};
+  if (selfsel)
+    si = moe::SelIn{f.partial, (d + moe::kRouterChunk - 1) / moe::kRouterChunk, L->bias,
+                    L->expert_mask, E, k, L->router, L->scale, chain ? chain->x_out : x,
+                    idx, w, perm};
   hipError_t e;
   if (enc) {
     int Rs[2] = {R, T}, Is[2] = {X.inter, S.inter};
     moe::FfnWs lay = moe::ffn_ws_layout(f.ffn, T, d, fused ? 2 : 1, Rs, Is, true);
-    // x digits in the order the routed experts' kernels read (int4: permuted)
-    const bool perm = X.fmt == MOE_W_INT4_B32 || X.fmt == MOE_W_INT4_B128;
     e = moe::launch_router_encode(L->router, x, L->w_router, L->bias, L->expert_mask, T, d, E,
                                   k, L->scale, idx, w, f.partial, lay.xq, lay.xs, perm, lay.cnt,
-                                  s, chain);
+                                  s, chain, selfsel);
     if (e == hipSuccess && !small)
       e = moe::launch_permute(idx, T, k, E, f.offsets, f.row_token, f.token_row, s);
   } else {
@@ -440,7 +447,7 @@ moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float
          f.offsets, lay.hq[0], lay.hs[0], f.rows, small ? idx : nullptr, k, act},
         {S.fmt, S.layout, 1, S.inter, T, S.w_gate_up, S.s_gate_up, S.w_down, S.s_down, nullptr,
          nullptr, lay.hq[1], lay.hs[1], f.sh_rows, nullptr, 1, act}};
-    e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, enc, s);
+    e = moe::launch_ffn_quant(sets, 2, d, x, T, lay, enc, s, selfsel ? &si : nullptr);
   } else {
     auto run = [&](const moe_weights& W, int Ew, int Rw, const int32_t* rt, const int32_t* of,
                    float* out) -> hipError_t {
@@ -457,7 +464,8 @@ moe_status forward_launch(moe_ctx* ctx, const moe_layer* L, int act, const float
                       W.s_down, rt, of, lay.hq[0], lay.hs[0], out, pairs ? idx : nullptr, k,
                       act};
       // x was encoded by the router when only routed experts run here
-      return moe::launch_ffn_quant(&set, 1, d, x, T, lay, enc && &W == &X, s);
+      return moe::launch_ffn_quant(&set, 1, d, x, T, lay, enc && &W == &X, s,
+                                   selfsel && &W == &X ? &si : nullptr);
     };
     e = run(X, E, R, f.row_token, f.offsets, f.rows);
     if (e == hipSuccess && has_sh) e = run(S, 1, T, nullptr, nullptr, f.sh_rows);

@@ -34,6 +34,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -352,11 +353,20 @@ constexpr float kInv16 = 1.0f / 16.0f;          // the unpacked codes carry a fa
 // PAIRS (small batches): rows are the (token, slot) pairs grouped in-kernel.
 // The tile's activation digit rows are staged in LDS (mt rows of 2d bytes); a
 // workgroup covers NCB column blocks of 64 in turn.
-template <int FMT, int LAY, int KS, bool PAIRS, int NCB, bool SPLIT>
+// SEL (one token, SelIn): the launch selects the token's experts and encodes
+// its row of x itself, in front of the weight loads, instead of a selection
+// launch before it.  The x row's loads go out first, so that they overlap
+// the selection; every routed workgroup ranks the experts from the logit
+// slices with the router's own select_token (the same keys, order and
+// weights), keeps the indices in LDS and takes tile t's expert from slot t;
+// the launch's first workgroup also stores the indices and weights.  Every
+// workgroup encodes the row into LDS as two-digit int8 with one scale, as the
+// router's selection launch does, and the K loop reads the digits from there.
+template <int FMT, int LAY, int KS, bool PAIRS, int NCB, bool SPLIT, bool SEL = false>
 __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, int d, int mt,
                                                            const int8_t* __restrict__ xq,
                                                            const float* __restrict__ xs,
-                                                           SplitK sk) {
+                                                           SplitK sk, SelIn sel) {
   extern __shared__ int8_t lds[];
   __shared__ float red_max[4][16];
   // K-slice partials: int8 path 16 ints per lane, int4 path 8 floats per lane
@@ -374,8 +384,70 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
     const bool first = vtile < g0.tiles;
     if ((int)blockIdx.x * 64 * NCB >= (first ? g0.inter : g1.inter)) return;
   }
+  float sel_xs = 0.0f;  // SEL: the x row's scale
+  __shared__ int sel_idx[SEL ? kMaxK : 1];
+  if constexpr (SEL) {
+    __shared__ unsigned long long sel_keys[KS][256];
+    __shared__ float sel_red[KS][4], sel_s[KS][kMaxK], sel_w[kMaxK], sel_xred[4 * KS];
+    const int tid = threadIdx.x, n8 = d / 8;
+    float4 xv[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int c = tid + 256 * KS * m;
+      const bool ok = c < n8;
+      const float* src = sel.x + 8 * (ok ? c : 0);
+      xv[m][0] = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[m][1] = ok ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (vtile < g0.tiles) {  // routed workgroups (the whole workgroup takes part)
+      const int grp = tid >> 8;
+      const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
+      select_token<1>(sel.partial, sel.nchunk, sel.bias, sel.mask, 1, sel.E, sel.k, sel.router,
+                      sel.scale, 0, grp == 0, tid & 255, sel_keys[grp], sel_red[grp],
+                      sel_s[grp], lead ? sel.idx : sel_idx, lead ? sel.w : sel_w, sel_idx);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][h].x), fabsf(xv[m][h].y)),
+                             fmaxf(fabsf(xv[m][h].z), fabsf(xv[m][h].w))));
+    mx = wave_max_f(mx);
+    if ((tid & (kWave - 1)) == 0) sel_xred[tid / kWave] = mx;
+    __syncthreads();
+    mx = 0.0f;
+    for (int q = 0; q < 4 * KS; ++q) mx = fmaxf(mx, sel_xred[q]);
+    const int p = digit_exponent(mx);
+    uint2* q0 = reinterpret_cast<uint2*>(lds);
+    uint2* q1 = reinterpret_cast<uint2*>(lds + d);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int c = tid + 256 * KS * m;
+      if (c >= n8) continue;
+      uint2 w0, w1;
+      encode8(xv[m][0], xv[m][1], p, sel.perm, w0, w1);
+      const int dst = sel.perm ? int4_digit_chunk(c) : c;
+      q0[dst] = w0;
+      q1[dst] = w1;
+    }
+    sel_xs = mx > 0.0f ? ldexpf(1.0f, -p) : 0.0f;
+    __syncthreads();
+  }
   Job job;
-  if (PAIRS) {  // the expert histogram uses the dynamic LDS area
+  if (SEL && vtile < g0.tiles) {  // slot vtile of the token (as find_rows at one token)
+    const int e = sel_idx[vtile];
+    if (e < 0 || e >= g0.E) return;
+    job.g = 0;
+    job.e = e;
+    job.r0 = 0;
+    job.nr = 1;
+    if (threadIdx.x == 0) {
+      rows_sm[0] = vtile;
+      toks_sm[0] = 0;
+    }
+    __syncthreads();
+  } else if (PAIRS) {  // the expert histogram uses the dynamic LDS area
     if (!find_rows(g0, g1, mt, vtile, job, rows_sm, toks_sm, reinterpret_cast<int*>(lds),
                    sh_sm, true))
       return;
@@ -405,7 +477,9 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
     return PAIRS ? toks_sm[j] : row_token ? gload<int>(row_token + r0 + j) : r0 + j;
   };
   const int8_t* xb0;
-  if (PAIRS) {
+  if (SEL) {
+    xb0 = lds;
+  } else if (PAIRS) {
     xb0 = xq + (size_t)tile_tok(min(i, job.nr - 1)) * 2 * d;
   } else {
     const int ldr = 2 * d + 16;
@@ -422,7 +496,7 @@ __global__ __launch_bounds__(256 * KS) void gate_up_kernel(Group g0, Group g1, i
   // x scale of tile rows 4g+c: loaded only after the main loop, unconditionally
   // from clamped rows, so no load in front of the loop is conditional
   auto x_scale = [=](int c) {
-    const float v = gload<float>(xs + tile_tok(min(4 * g + c, nr - 1)));
+    const float v = SEL ? sel_xs : gload<float>(xs + tile_tok(min(4 * g + c, nr - 1)));
     return 4 * g + c < nr ? v : 0.0f;
   };
 
@@ -1645,7 +1719,7 @@ int g_cu_count = 256;
 
 template <int FMT, int LAY, bool PAIRS>
 hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8_t* xq,
-                       const float* xs, const FfnWs& ws, hipStream_t s) {
+                       const float* xs, const FfnWs& ws, hipStream_t s, const SelIn* sel) {
   const int tiles = a.tiles + b.tiles;
   const int imax = a.inter > b.inter ? a.inter : b.inter;
   // K split inside and across workgroups (plan.h); the C ABI ran the same plan
@@ -1660,9 +1734,17 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   const size_t emax = (size_t)(a.E > b.E ? a.E : b.E) * sizeof(int);  // histogram
   // PAIRS: the expert histogram only (x digits come from L2); tiles: x rows
   const size_t lds_gu = PAIRS ? emax : (size_t)mt * (2 * d + 16);
-#define MOE_GU(KSV, SPL)                                                                 \
-  moe_launch((gate_up_kernel<FMT, LAY, KSV, PAIRS, 1, SPL>), grid, dim3(256 * KSV), \
-                     lds_gu, s, a, b, d, mt, xq, xs, sk)
+  // SEL: the token's x digits (2d bytes) in the dynamic area
+  const size_t lds_sel = lds_gu > (size_t)(2 * d) ? lds_gu : (size_t)(2 * d);
+#define MOE_GU(KSV, SPL)                                                                   \
+  do {                                                                                     \
+    if (PAIRS && sel)                                                                      \
+      moe_launch((gate_up_kernel<FMT, LAY, KSV, PAIRS, 1, SPL, PAIRS>), grid,              \
+                 dim3(256 * KSV), lds_sel, s, a, b, d, mt, xq, xs, sk, *sel);              \
+    else                                                                                   \
+      moe_launch((gate_up_kernel<FMT, LAY, KSV, PAIRS, 1, SPL>), grid, dim3(256 * KSV),    \
+                 lds_gu, s, a, b, d, mt, xq, xs, sk, SelIn{});                             \
+  } while (0)
   {
     TimedLaunch tl(FMT == 1 ? K_FFN_I8_GATE_UP : K_FFN_I4_GATE_UP, s);
     dim3 grid(imax / 64, gsplit ? a.tiles * sk.n0 + b.tiles * sk.n1 : tiles);
@@ -2158,7 +2240,7 @@ hipError_t launch_gemm4_pair(Group a, Group b, int d, const int8_t* xq, const fl
 }
 
 hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
-                            const FfnWs& ws, bool x_encoded, hipStream_t s) {
+                            const FfnWs& ws, bool x_encoded, hipStream_t s, const SelIn* sel) {
   hipError_t err = hipSuccess;
   if (!x_encoded) {
     // int4 kernels read the digits in their permuted order (encode8)
@@ -2226,8 +2308,8 @@ hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x
   const bool tiled = sets[0].layout == 1;
   const bool pairs = sets[0].pairs_idx != nullptr || (nsets > 1 && sets[1].pairs_idx != nullptr);
 #define MOE_PAIR(F, L)                                                               \
-  (pairs ? launch_pair<F, L, true>(grp[0], grp[1], d, mt, ws.xq, ws.xs, ws, s)       \
-         : launch_pair<F, L, false>(grp[0], grp[1], d, mt, ws.xq, ws.xs, ws, s))
+  (pairs ? launch_pair<F, L, true>(grp[0], grp[1], d, mt, ws.xq, ws.xs, ws, s, sel)  \
+         : launch_pair<F, L, false>(grp[0], grp[1], d, mt, ws.xq, ws.xs, ws, s, nullptr))
   if (sets[0].fmt == 1) return tiled ? MOE_PAIR(1, kTiled) : MOE_PAIR(1, kRows);
   if (sets[0].fmt == 3) return tiled ? MOE_PAIR(3, kTiled) : MOE_PAIR(3, kRows);
   return tiled ? MOE_PAIR(2, kTiled) : MOE_PAIR(2, kRows);

@@ -104,11 +104,31 @@ struct ChainIn {
 // launch_permute follows.  chain non-NULL (T <= 16): the logits launch first
 // forms x, the previous layer's pending output, into chain->x_out, and x is
 // ignored (hipErrorInvalidValue for T > 16 or chain->k outside [1, 16]).
+// logits_only: the logits launch alone, which then clears split_cnt; the
+// one-token FFN launch selects and encodes for itself (SelIn).
 hipError_t launch_router_encode(int router, const float* x, const float* wr, const float* bias,
                                 const uint8_t* mask,
                                 int T, int d, int E, int k, float scale, int32_t* idx, float* w,
                                 float* partial, int8_t* xq, float* xs, bool perm,
-                                int* split_cnt, hipStream_t s, const ChainIn* chain = nullptr);
+                                int* split_cnt, hipStream_t s, const ChainIn* chain = nullptr,
+                                bool logits_only = false);
+// One token whose selection and x digits the gate/up launch makes itself
+// (launch_ffn_quant, sel non-NULL): every workgroup of the routed set ranks
+// the experts from the logit slices as the router's selection kernel does,
+// the launch's first workgroup stores topk_idx and topk_w for the down launch
+// and the combine, and every workgroup encodes the token's row of x into LDS.
+struct SelIn {
+  const float* partial;  // logit slices [nchunk][1][E]
+  int nchunk;
+  const float* bias;     // selection bias [E] or NULL
+  const uint8_t* mask;   // allowed experts [E] or NULL
+  int E, k, router;
+  float scale;
+  const float* x;        // the token's row [d]
+  int32_t* idx;          // [k] out
+  float* w;              // [k] out
+  bool perm;             // int4 digit order
+};
 // counts[e] += number of topk_idx entries equal to e (entries outside [0, E) skipped)
 hipError_t launch_expert_counts(const int32_t* idx, long long n, int E, unsigned long long* counts,
                                 hipStream_t s);
@@ -122,7 +142,8 @@ hipError_t launch_encode_rows(const float* v, int n, int K, int8_t* q, float* si
 // Encodes x (unless x_encoded) and runs gate/up then down for 1 or 2 expert
 // sets (same format) in one pair of launches.
 hipError_t launch_ffn_quant(const FfnSet* sets, int nsets, int d, const float* x, int T,
-                            const FfnWs& ws, bool x_encoded, hipStream_t s);
+                            const FfnWs& ws, bool x_encoded, hipStream_t s,
+                            const SelIn* sel = nullptr);
 void set_device_info(int cu_count);
 int device_cu_count();
 

@@ -18,6 +18,10 @@ constexpr size_t kPlanLdsBytes = 160 * 1024;
 constexpr int kSplitSlots = 1024;
 constexpr size_t kSplitSlotBytes = 16384;
 
+// One token whose gate/up launch selects and encodes for itself: each of at
+// least 256 threads holds at most two groups of 8 inputs of the x row.
+inline bool sel_fits(int d) { return d % 8 == 0 && d <= 2 * 256 * 8; }
+
 // Upper bound on the number of FFN tiles (mt rows of one expert each) for R
 // rows spread over E experts: sum_e ceil(c_e/mt) <= n + (R - n)/mt with
 // n = min(E, R) non-empty experts at most.

@@ -96,5 +96,13 @@ int main() {
   if (split_fits(10, 0, 0, 1)) ++bad_refuse;                           // malformed
   printf("refusals: %lld mismatches\n", bad_refuse);
   g_fail += bad_refuse;
+
+  // one-token self-selection: the x row in at most two groups of 8 per thread
+  // of a 256-thread workgroup
+  long long bad_sel = 0;
+  if (!sel_fits(2304) || !sel_fits(2048) || !sel_fits(4096) || !sel_fits(64)) ++bad_sel;
+  if (sel_fits(4104) || sel_fits(4160) || sel_fits(2308)) ++bad_sel;
+  printf("self-selection sizes: %lld mismatches\n", bad_sel);
+  g_fail += bad_sel;
   return g_fail == 0 ? 0 : 1;
 }
