@@ -63,19 +63,25 @@ CASES = [
     ("sigmoid_bias", 300, 8, 8, 9, 256, "int4_b32"),        # E > 256, exactly k allowed
     ("softmax", 128, 8, 33, 24, 256, "int4_b32"),
     ("softmax", 40, 4, 9, 3, 64, "int8_row"),
+    # one token, every expert set reading digits: the gate/up launch selects itself
+    ("softmax", 128, 8, 33, 1, 256, "int4_b32"),
+    ("softmax", 40, 4, 9, 1, 64, "int8_row"),
+    ("sigmoid_bias", 64, 8, 20, 1, 128, "int8_row", "int8_row"),
 ]
 
 
-@pytest.mark.parametrize("router,E,k,kept,T,d,fmt", CASES)
-def test_masked_layer_equals_oracle_on_slice(ctx, router, E, k, kept, T, d, fmt):
+@pytest.mark.parametrize("case", CASES)
+def test_masked_layer_equals_oracle_on_slice(ctx, case):
     import torch
     from sparse_moe_expert_sigmoid_amd import MoELayer
+    router, E, k, kept, T, d, fmt = case[:7]
+    # shared expert: fp32 beside the sigmoid router unless the case names one
+    shared = case[7] if len(case) > 7 else ("fp32" if router == "sigmoid_bias" else None)
     scale = 2.446 if router == "sigmoid_bias" else 1.0
     step = 128 if fmt == "int4_b32" else 64
     spec = S.spec("tiny", T=T, d=d, E=E, k=k, inter=step, router=router,
-                  scale=float(np.float32(scale)), fmt=fmt,
-                  shared="fp32" if router == "sigmoid_bias" else None,
-                  shared_inter=step if router == "sigmoid_bias" else 0,
+                  scale=float(np.float32(scale)), fmt=fmt, shared=shared,
+                  shared_inter=step if shared else 0,
                   xseed=0x4D61534B + T, wseed=0x4D61534C + E)
     inp = S.make_layer(spec)
     keep, m = _keep_mask(E, kept, 0x4D61 + E)

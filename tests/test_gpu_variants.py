@@ -68,6 +68,9 @@ def _layer_case(ctx, name, act="silu", tokens=None, tiled=True, fused_too=True, 
     dict(T=300, E=16, k=4, shared="int8_row", shared_inter=256),   # grouped GEMM (75 rows/expert)
     dict(T=24, fmt="int4_b32", d=256, inter=128, shared=None, shared_inter=0),
     dict(T=3, fmt="int4_b128", d=256, inter=256, shared=None, shared_inter=0),
+    # one token: the gate/up launch selects and encodes for itself
+    dict(T=1, E=16, k=4, shared="int8_row", shared_inter=128),
+    dict(T=1, fmt="int4_b32", d=256, inter=128, shared=None, shared_inter=0),
 ])
 def test_gelu_tanh_layer_matches_oracle(ctx, kw):
     _layer_case(ctx, "tiny", act="gelu_tanh", xseed=0x6E4C0000 + kw["T"], **kw)
