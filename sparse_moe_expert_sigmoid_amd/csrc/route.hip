@@ -10,7 +10,9 @@
 // second adds the slices in order, so a token's logits never depend on T or on
 // the launch shape.
 // The second kernel runs one workgroup per token and ranks the selection keys
-// by counting in two rounds (no sequential arg-max rounds).
+// by counting in two rounds (no sequential arg-max rounds; select.h).  For one
+// token whose expert sets all read digits, the gate/up launch runs that
+// selection itself and only the first kernel runs here (logits_only).
 #include "internal.h"
 #include "select.h"
 
