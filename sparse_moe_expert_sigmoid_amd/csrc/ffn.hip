@@ -1380,7 +1380,11 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
   // int32 sums need no clearing, and an odd step (1) closes it and folds it
   // into fp32.  PAR = 2: parity known at run time only (3 slots; unrolling
   // those by 6 spills), the sums cleared after each fold.
-#define DN_STEP(STEP, Q, PAR)                                                                 \
+// As in the gate/up GEMM, a wavefront with all four row groups valid runs a
+// copy of the step without the per-row-group conditions (DN_FULL), so that
+// its fragment reads need not wait for the previous group's MFMAs.
+#define DN_STEP(STEP, Q, PAR) { if (ntg == 4) DN_STEP1(STEP, Q, PAR, true) else DN_STEP1(STEP, Q, PAR, false) }
+#define DN_STEP1(STEP, Q, PAR, full)                                                          \
   {                                                                                           \
     MOE_WAIT_VM(S::WAIT);                                                                     \
     ring_barrier();                                                                           \
@@ -1390,7 +1394,7 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
       _Pragma("unroll") for (int f = 0; f < NF; ++f)                                          \
         a[f] = lds_frag(slot + (NF * wc + f) * kPBlk, lane);                                  \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
-        if (t < ntg) {                                                                        \
+        if (full || t < ntg) {                                                                \
           const int8_t* bb = slot + (S::NA + 2 * (4 * wt + t)) * kPBlk;                       \
           const v4i b0 = lds_frag(bb, lane);                                                  \
           const v4i b1 = lds_frag(bb + kPBlk, lane);                                          \
@@ -1405,7 +1409,7 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
       if ((PAR == 1) || (PAR == 2 && ((STEP) & 1)) || (STEP) == last) { /* block end */       \
         const int blk = (STEP) >> 1;                                                          \
         _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                       \
-          if (t < ntg) {                                                                      \
+          if (full || t < ntg) {                                                              \
             const float sg = sc_sm[64 * wt + 16 * t + i][blk];                                \
             _Pragma("unroll") for (int f = 0; f < NF; ++f) {                                  \
               _Pragma("unroll") for (int c = 0; c < 4; ++c)                                   \
@@ -1440,6 +1444,7 @@ __global__ __launch_bounds__(512) void down_gemm_kernel(Group g0, Group g1, int 
     if (s0 + 1 < nsteps) DN_STEP(s0 + 1, 1, 2)
   }
 #undef DN_STEP
+#undef DN_STEP1
   MOE_WAIT_VM(0);
   if (!active) return;
   // lane (i, g) holds output columns c0 + 16 f + 4 g + c of tile row 64 wt + 16 t + i;
