@@ -821,7 +821,22 @@ __global__ __launch_bounds__(kWave * CG * KS) void down_kernel(Group g0, Group g
   const int r = PAIRS ? rows_sm[ii] : job.r0 + ii;
   const int8_t* hb0 = PAIRS ? G.hq + (size_t)r * 2 * I : lds + ii * ldr;
   const int8_t* hb1 = hb0 + I;
-  const float* hsr = PAIRS ? G.hs + (size_t)r * nhb : lds_s + ii * nhb;
+  // small int8 batches with two row groups per wavefront: the tile's h block
+  // scales, staged in LDS (the expert histogram's area, free once the rows
+  // are found), so that the K loop reads each step's scale from LDS and issues
+  // only weight and digit loads (Kimi-shaped T = 8 down 52.2 -> 50.9 us; the
+  // int4 down at one token and T = 2 were slower with it, so they keep
+  // reading the scales from L2)
+  constexpr bool kStageHs = PAIRS && FMT == 1 && NG == 2;
+  if (kStageHs) {
+    float* sc = reinterpret_cast<float*>(lds);
+    for (int q = threadIdx.x; q < job.nr * nhb; q += blockDim.x)
+      sc[q] = G.hs[(size_t)rows_sm[q / nhb] * nhb + q % nhb];
+    __syncthreads();
+  }
+  const float* hsr = kStageHs ? reinterpret_cast<const float*>(lds) + ii * nhb
+                     : PAIRS  ? G.hs + (size_t)r * nhb
+                              : lds_s + ii * nhb;
   const size_t row0 = (size_t)job.e * d + c0;
   const v4i zero = {0, 0, 0, 0};
   float acc[NG][4];
@@ -1771,8 +1786,11 @@ hipError_t launch_pair(const Group& a, const Group& b, int d, int mt, const int8
   SplitK dsk{plan.dn.n0, plan.dn.n1, ws.cnt, ws.part};
   const bool dsplit = dsk.n0 > 1 || dsk.n1 > 1;
   const int dgy = dsplit ? a.tiles * dsk.n0 + b.tiles * dsk.n1 : tiles;
-  const size_t lds_dn =
-      PAIRS ? emax : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
+  // PAIRS: the expert histogram, then (int8, two row groups per wavefront)
+  // the tile's h block scales
+  const size_t lds_hs = (size_t)mt * (imax / 64) * sizeof(float);
+  const size_t lds_dn = PAIRS ? (emax > lds_hs ? emax : lds_hs)
+                              : (size_t)mt * (2 * imax + 16) + (size_t)mt * (imax / 64) * 4;
 #define MOE_DN(KSV, NGV, SPL)                                                               \
   moe_launch((down_kernel<FMT, LAY, KSV, PAIRS, NGV, SPL>),                         \
                      dim3(d / (64 * NGV), dgy), dim3(256 * KSV), lds_dn, s, a, b, d, mt, dsk)
