@@ -630,3 +630,43 @@ def test_forward_kimi_prefill_4x256_chunks(ctx):
             ratio = compare_outputs(gy, oy, keep)
             _log(test="forward_4x256", config="kimi_prefill", chunk=c, path=path, T=256,
                  checked_tokens=len(local), excused=len(exc), err_over_max=ratio)
+
+
+# ------------------------------------------------------------------ a large batch
+
+def test_forward_kimi_prefill_T65536_sampled(ctx):
+    # The Kimi-shaped layer at T = 65536 through moe_forward: 524288 routed
+    # rows, so the expert rows (4.8 GB of fp32) and the h digits (2.1 GB)
+    # span more than 2^31 bytes and every row offset into them needs 64-bit
+    # arithmetic.  Sampled tokens: both ends, the middle, and tokens whose
+    # experts (as the GPU routed them) sit at the top of the permuted rows,
+    # checked against the oracle token by token (tokens are independent).
+    import torch
+    T = 65536
+    try:
+        inp = inputs("kimi_prefill", T=T)
+        s = inp.spec
+        L = device_layer(ctx, "kimi_prefill", T=T)
+        print(f"[large] kimi_prefill T={T} forward", flush=True)
+        y = L.forward_fused(to_dev(inp.x))
+        torch.cuda.synchronize()
+        gidx = L.idx.cpu().numpy()
+        top = np.flatnonzero((gidx >= s.E - 3).any(axis=1))
+        tokens = np.unique(np.concatenate([[0, 1, T // 2 - 1, T // 2, T - 2, T - 1],
+                                           top[:4], top[-4:]]))
+        gy = y.cpu().numpy()[tokens]
+        gw = L.w.cpu().numpy()[tokens]
+        del y
+        oy, oidx, ow, ogap = oracle.layer_of(inp, tokens=tokens)
+        _, _, _, logits = oracle.route(s.router, inp.x[tokens], inp.wr, inp.bias, s.k, s.scale,
+                                       want_logits=True)
+        keys = oracle_keys(s.router, logits, inp.bias)
+        exc = compare_route(gidx[tokens], gw, oidx, ow, ogap, keys, s.scale)
+        keep = np.setdiff1d(np.arange(len(tokens)), exc)
+        ratio = compare_outputs(gy, oy, keep)
+        _log(test="forward_large", config="kimi_prefill", T=T, checked_tokens=len(tokens),
+             excused=len(exc), err_over_max=ratio)
+    finally:
+        _LAYERS.clear()
+        _CACHE.pop(("kimi_prefill", (("T", T),)), None)
+        torch.cuda.empty_cache()
