@@ -634,20 +634,22 @@ def test_forward_kimi_prefill_4x256_chunks(ctx):
 
 # ------------------------------------------------------------------ a large batch
 
-def test_forward_kimi_prefill_T65536_sampled(ctx):
-    # The Kimi-shaped layer at T = 65536 through moe_forward: 524288 routed
-    # rows, so the expert rows (4.8 GB of fp32) and the h digits (2.1 GB)
-    # span more than 2^31 bytes and every row offset into them needs 64-bit
-    # arithmetic.  Sampled tokens: both ends, the middle, and tokens whose
-    # experts (as the GPU routed them) sit at the top of the permuted rows,
-    # checked against the oracle token by token (tokens are independent).
+@pytest.mark.parametrize("name", ["kimi_prefill", "qwen_prefill"])
+def test_forward_T65536_sampled(ctx, name):
+    # A layer at T = 65536 through moe_forward: 524288 routed rows, so the
+    # expert rows (4.8 GB of fp32 for the Kimi-shaped layer, 4.3 GB for the
+    # Qwen-shaped one) span more than 2^31 bytes and every row offset into
+    # them needs 64-bit arithmetic (int8 grouped GEMM and int4 grouped GEMM).
+    # Sampled tokens: both ends, the middle, and tokens whose experts (as the
+    # GPU routed them) sit at the top of the permuted rows, checked against
+    # the oracle token by token (tokens are independent).
     import torch
     T = 65536
     try:
-        inp = inputs("kimi_prefill", T=T)
+        inp = inputs(name, T=T)
         s = inp.spec
-        L = device_layer(ctx, "kimi_prefill", T=T)
-        print(f"[large] kimi_prefill T={T} forward", flush=True)
+        L = device_layer(ctx, name, T=T)
+        print(f"[large] {name} T={T} forward", flush=True)
         y = L.forward_fused(to_dev(inp.x))
         torch.cuda.synchronize()
         gidx = L.idx.cpu().numpy()
@@ -664,9 +666,9 @@ def test_forward_kimi_prefill_T65536_sampled(ctx):
         exc = compare_route(gidx[tokens], gw, oidx, ow, ogap, keys, s.scale)
         keep = np.setdiff1d(np.arange(len(tokens)), exc)
         ratio = compare_outputs(gy, oy, keep)
-        _log(test="forward_large", config="kimi_prefill", T=T, checked_tokens=len(tokens),
+        _log(test="forward_large", config=name, T=T, checked_tokens=len(tokens),
              excused=len(exc), err_over_max=ratio)
     finally:
         _LAYERS.clear()
-        _CACHE.pop(("kimi_prefill", (("T", T),)), None)
+        _CACHE.pop((name, (("T", T),)), None)
         torch.cuda.empty_cache()
