@@ -672,3 +672,49 @@ def test_forward_T65536_sampled(ctx, name):
         _LAYERS.clear()
         _CACHE.pop((name, (("T", T),)), None)
         torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ path boundaries
+
+@pytest.mark.parametrize("name,T,kernel,permute", [
+    ("kimi_prefill", 16, "ffn_i8_gate_up", False),       # small batch: pairs grouped in-kernel
+    ("kimi_prefill", 17, "ffn_i8_gate_up", True),        # 16-row tiles over the permutation
+    ("kimi_prefill", 511, "ffn_i8_gate_up", True),       # R = 4088 < 16 E: still the tiles
+    ("kimi_prefill", 512, "ffn_i8_gate_up_gemm", True),  # R = 4096 = 16 E: the grouped GEMM
+    ("qwen_prefill", 255, "ffn_i4_gate_up", True),       # R = 2040 < 16 E
+    ("qwen_prefill", 256, "ffn_i4_gate_up_gemm", True),  # R = 2048: the int4 grouped GEMM
+])
+def test_forward_path_boundaries(ctx, name, T, kernel, permute):
+    # moe_forward on either side of each switch between kernel families (by
+    # batch size, and by rows per expert R / E against 16), checked against the
+    # oracle on sampled tokens; the kernel timer shows which family ran.
+    # Tokens are independent, so the first T tokens of a longer seeded batch
+    # serve as the batch.
+    import torch
+    kw = {} if name == "kimi_prefill" else {"T": 1024}  # (kimi_prefill is T = 1024)
+    inp = inputs(name, **kw)
+    s = inp.spec
+    L = device_layer(ctx, name, **kw)
+    x = np.ascontiguousarray(inp.x[:T])
+    print(f"[boundary] {name} T={T}", flush=True)
+    ctx.moe_timing(256)
+    try:
+        y = L.forward_fused(to_dev(x))
+        torch.cuda.synchronize()
+        names = set(ctx.moe_timing_read())
+    finally:
+        ctx.moe_timing(0)
+    assert kernel in names, sorted(names)
+    assert ("permute" in names) == permute, sorted(names)
+    tokens = np.unique(np.concatenate([np.arange(0, T, max(1, T // 12)), [T - 1]]))
+    gy = y.cpu().numpy()[tokens]
+    oy, oidx, ow, ogap = oracle.layer_of(inp, tokens=tokens)
+    _, _, _, logits = oracle.route(s.router, inp.x[tokens], inp.wr, inp.bias, s.k, s.scale,
+                                   want_logits=True)
+    keys = oracle_keys(s.router, logits, inp.bias)
+    exc = compare_route(L.idx.cpu().numpy()[tokens], L.w.cpu().numpy()[tokens], oidx, ow, ogap,
+                        keys, s.scale)
+    keep = np.setdiff1d(np.arange(len(tokens)), exc)
+    ratio = compare_outputs(gy, oy, keep)
+    _log(test="forward_boundary", config=name, T=T, kernel=kernel, checked_tokens=len(tokens),
+         excused=len(exc), err_over_max=ratio)
