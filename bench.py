@@ -45,7 +45,8 @@ launches did not touch, and int8 MFMA loops of both shapes.  Each roofline
 then carries `attainable` (the probe's figure and achieved / attainable)
 beside the published peak it is priced against.
 cpu_baseline: the CPU oracle, as it stands, on a bounded sample of the
-primary workload, all host threads and one thread.
+primary workload, all host threads and one thread; other_configs holds the
+same for the other single-layer configurations on shorter samples.
 """
 from __future__ import annotations
 
@@ -887,6 +888,14 @@ def main():
             cpu = cpu_baseline_stack(primary, args.cpu_budget)
         elif primary in WORKLOADS:
             cpu = cpu_baseline(primary, args.cpu_budget, args.act)
+            # the other single-layer configurations (tiny; the Kimi-shaped
+            # layer at prefill size; the Qwen-shaped layer at T = 1 and 128),
+            # each on a shorter sample, all host threads and one thread
+            info_keys = set(host_info())
+            cpu["other_configs"] = {
+                n: {k: v for k, v in cpu_baseline(n, args.cpu_budget / 6, args.act).items()
+                    if k not in info_keys}
+                for n in ("tiny", "kimi_prefill", "qwen_decode", "qwen_prefill") if n != primary}
 
     quant = primary in QUANT_WORKLOADS
     out = {
